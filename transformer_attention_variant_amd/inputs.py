@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the Multi-Token Attention forward.
+
+This module only draws random numbers and lays out buffers; it holds none of
+the method's arithmetic.  It is the one piece shared by the GPU path's tests
+and benchmark and by the CPU oracle's tests.
+
+The workloads stand in for the ones on the page "Multi-Token Attention —
+Paper Graph": the toy block-location task (section 4.1 / Table 1: c_q = L = 2
+query letters, c_k = 2N-1 = 9 for N = 5), the 880M-parameter model's attention
+layer ("Training configuration": 16 heads, context 2048), its 4K-context
+finetune with multi-needle retrieval (Figure 3), and a sweep over the kernel
+sizes of the Table 5 ablations.  No dataset or trained weight is used: every
+tensor is drawn from a seeded ``torch.Generator``.
+
+Kernels are "identity plus noise": the key-query kernel is a delta at
+(i'=0, j'=0), stored at column floor(c_k/2), and each head-mixing block is the
+identity ("Practical Design Choices": identity initialisation), with Gaussian
+noise added to every entry.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+from typing import Dict, List
+
+import torch
+
+PRE = 0
+POST = 1
+F32 = 0
+BF16 = 1
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class MTAConfig:
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    c_q: int
+    c_k: int
+    c_h: int
+    kq_place: int = PRE
+    head_place: int = POST
+    dtype: str = "bf16"
+    qkv_std: float = 1.0
+    theta_std: float = 0.05
+    head_std: float = 0.05
+    layer: int = 1
+    needles: int = 0
+    needle_queries: int = 32
+    seed: int = 0
+    gn_eps: float = 1e-5
+    gn_random: bool = False
+
+    @property
+    def depth_scale(self) -> float:
+        # the layer-dependent depth scale: 1 / sqrt(layer)
+        return 1.0 / math.sqrt(self.layer)
+
+    @property
+    def groups(self) -> int:
+        return self.H // self.c_h
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def causal_logits(self) -> int:
+        """Causal (query, key) pairs over all heads: B*H*T(T+1)/2."""
+        return self.B * self.H * self.T * (self.T + 1) // 2
+
+    def alg_flops(self) -> Dict[str, float]:
+        """Algorithmic FLOP, each causal logit counted once: QK^T and PV on the
+        matrix cores (4d), the key-query stencil (2 c_q c_k) and the head mix
+        (2 c_h) on the vector ALUs."""
+        n = float(self.causal_logits())
+        return {
+            "contraction": n * 4 * self.d,
+            "stencil": n * 2 * self.c_q * self.c_k,
+            "mix": n * 2 * self.c_h,
+        }
+
+    def io_bytes(self) -> int:
+        """Compulsory HBM bytes of one call: read q, k, v, write out."""
+        el = 4 if self.dtype == "f32" else 2
+        return 4 * self.B * self.H * self.T * self.d * el
+
+    def short(self) -> str:
+        kq = "pre" if self.kq_place == PRE else "post"
+        hd = "pre" if self.head_place == PRE else "post"
+        return (f"{self.name}:B{self.B}H{self.H}T{self.T}d{self.d}"
+                f"_cq{self.c_q}ck{self.c_k}ch{self.c_h}_kq{kq}_head{hd}_{self.dtype}")
+
+
+def _configs() -> Dict[str, MTAConfig]:
+    c = {}
+    c["tiny"] = MTAConfig("tiny", B=1, H=4, T=128, d=32, c_q=3, c_k=5, c_h=2,
+                          dtype="f32", qkv_std=1.0, theta_std=0.05, head_std=0.05,
+                          layer=1, seed=1000)
+    c["toy"] = MTAConfig("toy", B=64, H=4, T=256, d=64, c_q=2, c_k=9, c_h=2,
+                         dtype="f32", qkv_std=1.0, theta_std=0.1, head_std=0.1,
+                         layer=1, seed=1001)
+    s = 1.0 / math.sqrt(2.0)
+    c["layer2k"] = MTAConfig("layer2k", B=4, H=16, T=2048, d=128, c_q=6, c_k=11, c_h=2,
+                             dtype="bf16", qkv_std=s, theta_std=0.02, head_std=0.02,
+                             layer=4, seed=1002)
+    c["needle4k"] = MTAConfig("needle4k", B=2, H=16, T=4096, d=128, c_q=6, c_k=11, c_h=2,
+                              dtype="bf16", qkv_std=s, theta_std=0.02, head_std=0.02,
+                              layer=4, needles=6, seed=1003)
+    for (cq, ck) in ((4, 9), (6, 11), (8, 15)):
+        for ch in (2, 4):
+            for kq in (PRE, POST):
+                nm = f"sweep8k_{cq}x{ck}_ch{ch}_{'pre' if kq == PRE else 'post'}"
+                c[nm] = MTAConfig(nm, B=1, H=32, T=8192, d=128, c_q=cq, c_k=ck, c_h=ch,
+                                  kq_place=kq, head_place=POST, dtype="bf16",
+                                  qkv_std=1.0, theta_std=0.05, head_std=0.05,
+                                  layer=24, seed=1004)
+    return c
+
+
+CONFIGS: Dict[str, MTAConfig] = _configs()
+SWEEP: List[str] = [k for k in CONFIGS if k.startswith("sweep8k_")]
+HEADLINE = "needle4k"
+
+
+def small(name: str = "small", **kw) -> MTAConfig:
+    """A small ad-hoc configuration for tests (defaults: fp32, identity+noise)."""
+    base = dict(B=1, H=2, T=64, d=32, c_q=3, c_k=5, c_h=2, dtype="f32",
+                qkv_std=1.0, theta_std=0.1, head_std=0.1, layer=1, seed=7)
+    base.update(kw)
+    return MTAConfig(name, **base)
+
+
+def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
+    """Draw the inputs of one configuration.
+
+    Order of draws from ``torch.Generator().manual_seed(cfg.seed)``: Q, K, V,
+    key-query kernel noise, head kernel noise, GroupNorm affine (only if
+    ``gn_random``), then the needle positions and directions.  Q, K, V are drawn
+    in fp32 and rounded to the run dtype (round to nearest even); kernels and
+    GroupNorm parameters stay fp32.
+    """
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    q = torch.randn(shp, generator=g) * cfg.qkv_std
+    k = torch.randn(shp, generator=g) * cfg.qkv_std
+    v = torch.randn(shp, generator=g) * cfg.qkv_std
+
+    theta = torch.randn((cfg.H, cfg.c_q, cfg.c_k), generator=g) * cfg.theta_std
+    theta[:, 0, cfg.c_k // 2] += 1.0           # delta at (i'=0, j'=0)
+    w = torch.randn((cfg.groups, cfg.c_h, cfg.c_h), generator=g) * cfg.head_std
+    w += torch.eye(cfg.c_h).expand(cfg.groups, cfg.c_h, cfg.c_h)
+
+    if cfg.gn_random:
+        gn_w = 1.0 + 0.5 * torch.randn((cfg.H, cfg.d), generator=g)
+        gn_b = 0.5 * torch.randn((cfg.H, cfg.d), generator=g)
+    else:
+        gn_w = torch.ones((cfg.H, cfg.d))
+        gn_b = torch.zeros((cfg.H, cfg.d))
+
+    if cfg.needles:
+        # Multi-needle retrieval stand-in: per batch row, `needles` key
+        # positions (uniform without replacement, in random order) carry 3x a
+        # per-head direction u, and the last `needle_queries` queries carry u.
+        nq = min(cfg.needle_queries, cfg.T)
+        span = max(cfg.T - nq, cfg.needles)
+        for b in range(cfg.B):
+            pos = torch.randperm(span, generator=g)[: cfg.needles]
+            for h in range(cfg.H):
+                u = torch.randn((cfg.d,), generator=g) * cfg.qkv_std
+                k[b, h, pos] = 3.0 * u
+                q[b, h, cfg.T - nq:] += u
+
+    dt = DTYPES[cfg.dtype]
+    out = {
+        "q": q.to(dt).contiguous(),
+        "k": k.to(dt).contiguous(),
+        "v": v.to(dt).contiguous(),
+        "theta_kq": theta.float().contiguous(),
+        "theta_head": w.float().contiguous(),
+        "gn_w": gn_w.float().contiguous(),
+        "gn_b": gn_b.float().contiguous(),
+    }
+    if device != "cpu":
+        out = {kk: t.to(device) for kk, t in out.items()}
+    return out
+
+
+def with_(cfg: MTAConfig, **kw) -> MTAConfig:
+    return replace(cfg, **kw)

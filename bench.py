@@ -1,0 +1,182 @@
+"""Benchmark of the MTA forward on one MI355X.
+
+One step = one ``mta_forward`` call over one batch of the workload (the whole
+hot path: logits, key-query convolution, softmax, head mix, P V, GroupNorm),
+inputs resident in HBM.  Default workload: the 4K-context layer with planted
+needles (B=2, H=16, T=4096, d=128, c_q=6, c_k=11, c_h=2, bf16).
+
+Prints one JSON line with tokens/s, effective TFLOP/s, the roofline of the
+kernel (per-launch duration from HIP events recorded on the launch stream
+around every launch of the timed region) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MTA fwd tokens/s & eff. TFLOP/s at T=4096, fraction of MFMA/VALU peak"
+PEAK_VALU_TFLOPS = 157.3   # fp32 vector, 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+PEAK_MFMA_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="needle4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows per (batch, head group) unit in the oracle sample (from the end)")
+    ap.add_argument("--cpu-units", type=int, default=0, help="units in the oracle sample (0 = all)")
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the MTA "
+              "forward here is a single-GPU kernel; multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from transformer_attention_variant_amd import binding
+    from transformer_attention_variant_amd import inputs as I
+
+    cfg = I.CONFIGS[args.config]
+    inp = I.generate(cfg)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    out = torch.empty_like(dev["q"])
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        binding.forward_cfg(cfg, dev, out=out, stream=stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        binding.forward_cfg(cfg, dev, out=out, stream=stream)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = ms_total / K
+    ms_launch = float(np.mean(launch_ms))
+    tokens = cfg.B * cfg.T
+    value = tokens / (ms_step / 1e3)
+
+    fl = cfg.alg_flops()
+    alu_flops = fl["stencil"] + fl["mix"]
+    all_flops = fl["contraction"] + fl["stencil"] + fl["mix"]
+    t = ms_launch / 1e3
+    mfma_peak = PEAK_MFMA_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_MFMA_F32_TFLOPS
+    traffic = None
+    if os.path.exists(args.traffic_file):
+        try:
+            tr = json.load(open(args.traffic_file))
+            traffic = tr.get(cfg.name, {}).get("bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+    roof = {
+        "bound": "alu",
+        "achieved": round(alu_flops / t / 1e12, 3),
+        "peak": PEAK_VALU_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(alu_flops / t / 1e12 / PEAK_VALU_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "mta_fwd_kernel",
+        "work": "key-query stencil 2*c_q*c_k + head mix 2*c_h FLOP per causal logit",
+    }
+    mfma = {
+        "achieved": round(fl["contraction"] / t / 1e12, 2),
+        "peak": mfma_peak,
+        "unit": "TFLOP/s",
+        "frac": round(fl["contraction"] / t / 1e12 / mfma_peak, 4),
+        "work": "QK^T + PV, 4*d FLOP per causal logit",
+    }
+    hbm = {"achieved_GBs": round(cfg.io_bytes() / t / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
+           "bytes": cfg.io_bytes(), "work": "read q,k,v + write out"}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; stand-in shapes for the pages' workloads)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.T,
+                   "head_dim": cfg.d, "c_q": cfg.c_q, "c_k": cfg.c_k, "c_h": cfg.c_h,
+                   "kq_place": "pre" if cfg.kq_place == I.PRE else "post",
+                   "head_place": "pre" if cfg.head_place == I.PRE else "post",
+                   "needles": cfg.needles, "depth_scale": cfg.depth_scale, "global_batch": cfg.B,
+                   "parallelism": "single GPU"},
+        "eff_tflops": round(all_flops / t / 1e12, 2),
+        "ms_per_launch": round(ms_launch, 4),
+        "roofline": roof,
+        "mfma": mfma,
+        "hbm": hbm,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, inp, args):
+    """The CPU oracle (float64, literal; untuned) on a bounded sample: the last
+    ``cpu_rows`` rows of ``cpu_units`` (batch, head group) units.  Each output
+    row costs the same in the oracle (it forms every row over all T keys), so
+    the full-workload time is the sample time scaled by rows."""
+    import oracle
+    U = cfg.B * cfg.groups
+    nu = U if args.cpu_units <= 0 else min(U, args.cpu_units)
+    rows = min(cfg.T, args.cpu_rows)
+    units = list(range(nu))
+    threads = oracle.default_threads()
+    q, k, v = (oracle._f64(inp[n]) for n in ("q", "k", "v"))
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q,
+                   c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
+                   eps=cfg.gn_eps, depth_scale=cfg.depth_scale, rows=(cfg.T - rows, cfg.T), units=units,
+                   chunk=32, threads=threads, lib=lib)
+    dt = time.perf_counter() - t0
+    full = dt * (U * cfg.T) / (nu * rows)
+    return {"value": round(cfg.B * cfg.T / full, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nu} of {U} (batch, head group) units x last {rows} of {cfg.T} rows "
+                      f"({nu * rows * cfg.c_h} row-heads) in {dt:.2f} s; scaled by rows to the full "
+                      f"workload ({full:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

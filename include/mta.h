@@ -1,0 +1,126 @@
+/*
+ * mta.h — C ABI of the MI355X (gfx950) Multi-Token Attention forward.
+ *
+ * The operation is the MTA attention forward of the page "Multi-Token
+ * Attention — Paper Graph" (summary of arXiv 2504.00927), section 3.4:
+ *   1. logits  Ahat = Q K^T / sqrt(d)               ("Standard Multi-Head
+ *      Attention");
+ *   2. key-query convolution Conv2d_theta over the (query, key) plane of each
+ *      head, kernel c_q x c_k, either before the softmax with two-pass masking
+ *      Softmax(Mask_-inf(Conv2d(Mask_0(Ahat)))), or after it,
+ *      Mask_0(Conv2d(Softmax(Mask_-inf(Ahat))))     ("Key-Query Convolution",
+ *      Eq. 4 and the two-pass / post-softmax forms);
+ *   3. head mixing within non-overlapping groups of c_h heads,
+ *      A^a_new = sum_b w_ab A^b, after the softmax (Eq. 7) or on the logits
+ *      before it                                    ("Head Mixing Convolution");
+ *   4. O^h = A^h V^h per head;
+ *   5. GroupNorm over each head's d channels with a per-channel affine, times
+ *      a scalar depth scale                         ("Group Normalization with
+ *      Sigmoid Gating" / the overview page's "Group Normalization with Depth
+ *      Scaling").
+ * When both convolutions sit on the same side of the softmax the key-query
+ * convolution runs first.  Positions outside [0, T) are zero padding for the
+ * key-query convolution.  The scale is fixed at 1/sqrt(d).
+ *
+ * Conventions
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
+ *    16-byte aligned.  The library allocates no memory and keeps no state
+ *    between calls; calls are thread-safe.
+ *  - The call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  The caller keeps every buffer alive until the stream work is
+ *    done.  `cfg` is read before the call returns.
+ *  - Errors: validation runs on the host before any device work.  On a
+ *    negative return nothing was launched and `out` is untouched.  A device
+ *    fault surfaces at the caller's next synchronisation.  No exception
+ *    crosses the ABI and the library prints nothing.
+ */
+#ifndef MTA_H_
+#define MTA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Placement of a convolution relative to the softmax. */
+#define MTA_PRE_SOFTMAX 0
+#define MTA_POST_SOFTMAX 1
+
+/* Element type of q, k, v and out.  Kernels and GroupNorm parameters are
+ * always float32; all intermediate arithmetic is float32 (contractions
+ * accumulate in float32 on the matrix cores; with MTA_BF16 the probabilities
+ * enter the A·V product as bf16). */
+#define MTA_F32 0
+#define MTA_BF16 1
+
+/* Status codes. */
+#define MTA_OK 0
+#define MTA_ERR_NULL_ARG -1      /* a required pointer is NULL                 */
+#define MTA_ERR_BAD_SHAPE -2     /* B,H,T < 0, H % c_h != 0, kernel size < 1   */
+#define MTA_ERR_BAD_PLACEMENT -3 /* kq_place / head_place not 0 or 1           */
+#define MTA_ERR_BAD_DTYPE -4     /* dtype not MTA_F32 / MTA_BF16               */
+#define MTA_ERR_MISALIGNED -5    /* a tensor pointer is not 16-byte aligned    */
+#define MTA_ERR_UNSUPPORTED -6   /* valid but outside this build's limits:
+                                    head_dim not in {32,64,128}, c_h not in
+                                    {1,2,4}, c_q > 16, c_k > 31, T > 2^24      */
+#define MTA_ERR_LAUNCH -7        /* the kernel launch reported an error        */
+#define MTA_ERR_BAD_VALUE -8     /* gn_eps <= 0 or not finite, depth_scale not
+                                    finite                                      */
+
+/* Problem description (all fields read synchronously). */
+typedef struct mta_config {
+    int32_t batch;      /* B >= 0                                              */
+    int32_t heads;      /* H >= 1, a multiple of c_h                           */
+    int32_t seq_len;    /* T >= 0                                              */
+    int32_t head_dim;   /* d in {32, 64, 128}                                  */
+    int32_t c_q;        /* key-query kernel size along queries, 1..16         */
+    int32_t c_k;        /* key-query kernel size along keys, 1..31            */
+    int32_t c_h;        /* heads per mixing group, 1, 2 or 4                   */
+    int32_t kq_place;   /* MTA_PRE_SOFTMAX (two-pass masking) | MTA_POST_SOFTMAX */
+    int32_t head_place; /* MTA_PRE_SOFTMAX | MTA_POST_SOFTMAX                  */
+    int32_t dtype;      /* MTA_F32 | MTA_BF16                                  */
+    float gn_eps;       /* GroupNorm epsilon (> 0), e.g. 1e-5                  */
+    float depth_scale;  /* scalar applied after the affine, e.g. 1/sqrt(layer) */
+} mta_config;
+
+/*
+ * mta_forward — the whole MTA attention forward (steps 1-5 above).
+ *
+ *  q, k, v     [B][H][T][d] of cfg->dtype, row-major.
+ *  theta_kq    float32 [H][c_q][c_k]; element [h][i'][jj] weighs query offset
+ *              i' (0 = the current query, i' > 0 = earlier queries) and key
+ *              offset j' = jj - floor(c_k/2), which reads key j - j'
+ *              (j' runs over [-floor(c_k/2), ceil(c_k/2)-1]).  The identity
+ *              kernel is 1 at [h][0][floor(c_k/2)].
+ *  theta_head  float32 [H/c_h][c_h][c_h]; element [g][a][b] is the weight of
+ *              source head g*c_h+b in output head g*c_h+a (heads are grouped
+ *              contiguously).
+ *  gn_w, gn_b  float32 [H][d]: GroupNorm affine per head and channel.
+ *  cfg         problem description.
+ *  out         [B][H][T][d] of cfg->dtype; every element is written.
+ *  stream      hipStream_t to launch on (NULL: default stream).
+ * Returns MTA_OK or a negative MTA_ERR_* code (see above).  B == 0 or T == 0
+ * returns MTA_OK without launching.
+ */
+int mta_forward(const void *q, const void *k, const void *v,
+                const float *theta_kq, const float *theta_head,
+                const float *gn_w, const float *gn_b,
+                const mta_config *cfg, void *out, void *stream);
+
+/* Host-only check of a configuration against the limits of this build; the
+ * same validation mta_forward runs (pointer checks excepted).  Returns MTA_OK
+ * or the MTA_ERR_* code mta_forward would return. */
+int mta_check_config(const mta_config *cfg);
+
+/* Static description of a status code (never NULL). */
+const char *mta_status_string(int status);
+
+/* ABI version: 100 * major + minor. */
+int mta_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTA_H_ */

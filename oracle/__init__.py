@@ -81,6 +81,14 @@ def max_threads() -> int:
     return int(load().mta_oracle_max_threads())
 
 
+def default_threads() -> int:
+    """Threads for the oracle: OMP_NUM_THREADS if set, else the CPU count,
+    capped at 16 (the CPU share of one GPU on the test machines)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = int(env) if env and env.isdigit() else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
 def forward(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
             kq_place=0, head_place=1, eps=1e-5, depth_scale=1.0,
             rows: Optional[Sequence[int]] = None, units: Optional[Sequence[int]] = None,
@@ -102,7 +110,7 @@ def forward(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
     else:
         ua = (ctypes.c_int * len(units))(*[int(u) for u in units])
         up, nu = ua, len(units)
-    nt = threads if threads is not None else (os.cpu_count() or 1)
+    nt = threads if threads is not None else default_threads()
     rc = lib.mta_oracle_forward(_p(q), _p(k), _p(v), _p(th), _p(w), _p(gw), _p(gb),
                                 B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                                 float(eps), float(depth_scale), r0, r1, up, nu,

@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every symbol include/mta.h declares,
+and its host-side validation returns the documented codes before any device
+work (these tests make no GPU call and run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_attention_variant_amd import binding
+from transformer_attention_variant_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from transformer_attention_variant_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mta.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mta_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mta_abi_version() == 100
+    for code in list(binding.STATUS) + [-99]:
+        s = lib.mta_status_string(code)
+        assert s and len(s.decode()) > 0
+
+
+def cfg(**kw):
+    base = dict(B=2, H=4, T=100, d=128, c_q=6, c_k=11, c_h=2, kq_place=0, head_place=1, dtype=1,
+                gn_eps=1e-5, depth_scale=0.5)
+    base.update(kw)
+    return binding.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(B=0), 0), (dict(T=0), 0),
+    (dict(B=-1), -2), (dict(T=-5), -2), (dict(H=0), -2), (dict(d=0), -2),
+    (dict(c_q=0), -2), (dict(c_k=0), -2), (dict(c_h=0), -2), (dict(H=6, c_h=4), -2),
+    (dict(kq_place=2), -3), (dict(head_place=-1), -3),
+    (dict(dtype=7), -4),
+    (dict(gn_eps=0.0), -8), (dict(gn_eps=float("nan")), -8), (dict(depth_scale=float("inf")), -8),
+    (dict(d=96), -6), (dict(d=256), -6), (dict(H=8, c_h=8), -6), (dict(H=3, c_h=3), -6),
+    (dict(c_q=17), -6), (dict(c_k=32), -6), (dict(T=(1 << 24) + 1), -6),
+    (dict(c_q=16, c_k=31), 0), (dict(c_k=4), 0), (dict(d=32, dtype=0), 0),
+])
+def test_check_config(lib, kw, code):
+    c = cfg(**kw)
+    assert lib.mta_check_config(ctypes.byref(c)) == code
+
+
+def test_forward_rejects_before_any_device_work(lib):
+    c = cfg()
+    good = 0x10000  # never dereferenced: every call below returns during validation
+    args = [good] * 7
+    assert lib.mta_forward(*args, None, good, None) == -1                 # NULL cfg
+    bad = cfg(c_h=3)
+    assert lib.mta_forward(*args, ctypes.byref(bad), good, None) == -2
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert lib.mta_forward(*a, ctypes.byref(c), good, None) == -1
+    assert lib.mta_forward(*args, ctypes.byref(c), None, None) == -1      # NULL out
+    for i in range(3):
+        a = list(args)
+        a[i] = good + 8                                                   # q/k/v not 16-byte aligned
+        assert lib.mta_forward(*a, ctypes.byref(c), good, None) == -5
+    assert lib.mta_forward(*args, ctypes.byref(c), good + 4, None) == -5  # out misaligned
+    a = list(args)
+    a[3] = good + 2                                                       # theta not 4-byte aligned
+    assert lib.mta_forward(*a, ctypes.byref(c), good, None) == -5
+
+
+def test_empty_problem_launches_nothing(lib):
+    # B == 0 or T == 0 succeeds without touching pointers (NULL is fine)
+    for kw in (dict(B=0), dict(T=0)):
+        c = cfg(**kw)
+        assert lib.mta_forward(None, None, None, None, None, None, None, ctypes.byref(c), None, None) == 0
+
+
+def test_config_layout_matches_header():
+    # 10 int32 + 2 float32, no padding
+    assert ctypes.sizeof(binding.MtaConfig) == 48
+    names = [f[0] for f in binding.MtaConfig._fields_]
+    src = open(os.path.join(ROOT, "include", "mta.h")).read()
+    body = src[src.index("typedef struct mta_config"):src.index("} mta_config;")]
+    hdr = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
+    assert hdr == names
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    c = I.small(T=8)
+    inp = I.generate(c)
+    with pytest.raises(ValueError):
+        binding.forward_cfg(c, inp)

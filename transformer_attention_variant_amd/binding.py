@@ -1,0 +1,128 @@
+"""Thin ctypes binding of the C ABI in include/mta.h.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+of ``libmta.so``.  PyTorch supplies device memory and the stream.  There is no
+fallback: without the built library, or without a GPU, ``forward`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+from . import inputs as I
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmta.so")
+
+MTA_OK = 0
+STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA_ERR_BAD_PLACEMENT",
+          -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
+          -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
+# names declared in include/mta.h
+EXPORTS = ("mta_forward", "mta_check_config", "mta_status_string", "mta_abi_version")
+
+
+class MtaConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("c_q", ctypes.c_int32), ("c_k", ctypes.c_int32),
+                ("c_h", ctypes.c_int32), ("kq_place", ctypes.c_int32), ("head_place", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("gn_eps", ctypes.c_float), ("depth_scale", ctypes.c_float)]
+
+
+class MTAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libmta.so (raises if it has not been built)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run transformer_attention_variant_amd/build.py "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    vp = ctypes.c_void_p
+    lib.mta_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MtaConfig), vp, vp]
+    lib.mta_forward.restype = ctypes.c_int
+    lib.mta_check_config.argtypes = [ctypes.POINTER(MtaConfig)]
+    lib.mta_check_config.restype = ctypes.c_int
+    lib.mta_status_string.argtypes = [ctypes.c_int]
+    lib.mta_status_string.restype = ctypes.c_char_p
+    lib.mta_abi_version.argtypes = []
+    lib.mta_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_config(B, H, T, d, c_q, c_k, c_h, kq_place=I.PRE, head_place=I.POST, dtype=I.BF16,
+                gn_eps=1e-5, depth_scale=1.0) -> MtaConfig:
+    return MtaConfig(B, H, T, d, c_q, c_k, c_h, kq_place, head_place, dtype, gn_eps, depth_scale)
+
+
+def status_string(code: int) -> str:
+    return load().mta_status_string(int(code)).decode()
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.Tensor,
+            theta_head: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor, *, c_q: int, c_k: int,
+            c_h: int, kq_place: int = I.PRE, head_place: int = I.POST, gn_eps: float = 1e-5,
+            depth_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """MTA forward on the GPU through ``mta_forward``.  q, k, v: [B,H,T,d]
+    float32 or bfloat16 CUDA tensors; theta_kq [H,c_q,c_k], theta_head
+    [H/c_h,c_h,c_h], gn_w/gn_b [H,d] float32.  Asynchronous on ``stream``
+    (default: torch's current stream)."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("theta_kq", theta_kq), ("theta_head", theta_head), ("gn_w", gn_w), ("gn_b", gn_b)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("theta_kq", theta_kq), ("theta_head", theta_head),
+                    ("gn_w", gn_w), ("gn_b", gn_b)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tuple(theta_kq.shape) != (H, c_q, c_k) or tuple(theta_head.shape) != (H // max(c_h, 1), c_h, c_h) \
+            or tuple(gn_w.shape) != (H, d) or tuple(gn_b.shape) != (H, d):
+        raise ValueError("parameter shapes do not match (theta_kq [H,c_q,c_k], theta_head [H/c_h,c_h,c_h], "
+                         "gn_w/gn_b [H,d])")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous CUDA tensor like q")
+    cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
+                      I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.mta_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(),
+                         theta_head.data_ptr(), gn_w.data_ptr(), gn_b.data_ptr(), ctypes.byref(cfg),
+                         out.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != MTA_OK:
+        raise MTAError(rc, status_string(rc))
+    return out
+
+
+def forward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    return forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"],
+                   inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place,
+                   head_place=cfg.head_place, gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
+                   out=out, stream=stream)

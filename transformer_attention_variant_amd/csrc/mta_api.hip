@@ -1,0 +1,117 @@
+// mta_api.hip — the C ABI declared in include/mta.h: host-side validation,
+// kernel selection and the asynchronous launch on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "mta.h"
+#include "mta_launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int validate(const mta_config *c)
+{
+    if (!c) return MTA_ERR_NULL_ARG;
+    if (c->batch < 0 || c->heads < 1 || c->seq_len < 0 || c->head_dim < 1) return MTA_ERR_BAD_SHAPE;
+    if (c->c_q < 1 || c->c_k < 1 || c->c_h < 1 || c->heads % c->c_h != 0) return MTA_ERR_BAD_SHAPE;
+    if ((c->kq_place != MTA_PRE_SOFTMAX && c->kq_place != MTA_POST_SOFTMAX) ||
+        (c->head_place != MTA_PRE_SOFTMAX && c->head_place != MTA_POST_SOFTMAX))
+        return MTA_ERR_BAD_PLACEMENT;
+    if (c->dtype != MTA_F32 && c->dtype != MTA_BF16) return MTA_ERR_BAD_DTYPE;
+    if (!(c->gn_eps > 0.0f) || !isfinite(c->gn_eps) || !isfinite(c->depth_scale)) return MTA_ERR_BAD_VALUE;
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return MTA_ERR_UNSUPPORTED;
+    if (c->c_h != 1 && c->c_h != 2 && c->c_h != 4) return MTA_ERR_UNSUPPORTED;
+    if (c->c_q > mta::MAX_CQ || c->c_k > mta::MAX_CK) return MTA_ERR_UNSUPPORTED;
+    if (c->seq_len > (1 << 24)) return MTA_ERR_UNSUPPORTED;
+    // the grid is one workgroup per (batch, head group, 64-row query tile)
+    const int64_t n_qt = (c->seq_len + mta::BM - 1) / mta::BM;
+    const int64_t grid = n_qt * (int64_t)c->batch * (c->heads / c->c_h);
+    if (grid > INT32_MAX) return MTA_ERR_UNSUPPORTED;
+    return MTA_OK;
+}
+
+size_t lds_bytes(const mta::Params &p, int dtype, int d, int ch)
+{
+    const int ckp = (p.c_k + 3) & ~3;
+    size_t b = (size_t)p.nbuf * mta::EXT_R * p.pitch * 4 + (size_t)2 * ch * mta::EXT_R * 4;
+    b += (size_t)((ch * p.c_q * ckp + 3) & ~3) * 4 + (size_t)((ch * ch + 3) & ~3) * 4;
+    if (dtype == MTA_BF16) {
+        b += d == 32 ? mta::vbuf_bytes<mta::bf16_t, 32>()
+                     : d == 64 ? mta::vbuf_bytes<mta::bf16_t, 64>() : mta::vbuf_bytes<mta::bf16_t, 128>();
+    } else {
+        b += d == 32 ? mta::vbuf_bytes<float, 32>()
+                     : d == 64 ? mta::vbuf_bytes<float, 64>() : mta::vbuf_bytes<float, 128>();
+    }
+    return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mta_abi_version(void) { return 100; }
+
+int mta_check_config(const mta_config *cfg) { return validate(cfg); }
+
+const char *mta_status_string(int s)
+{
+    switch (s) {
+    case MTA_OK: return "ok";
+    case MTA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MTA_ERR_BAD_SHAPE: return "invalid shape (B,H,T,d, kernel sizes, or H not a multiple of c_h)";
+    case MTA_ERR_BAD_PLACEMENT: return "convolution placement must be pre- (0) or post-softmax (1)";
+    case MTA_ERR_BAD_DTYPE: return "dtype must be MTA_F32 or MTA_BF16";
+    case MTA_ERR_MISALIGNED: return "tensor pointer not aligned (16 bytes for q,k,v,out; 4 for float params)";
+    case MTA_ERR_UNSUPPORTED: return "configuration outside this build's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
+    case MTA_ERR_LAUNCH: return "kernel launch failed";
+    case MTA_ERR_BAD_VALUE: return "gn_eps must be finite and > 0, depth_scale finite";
+    default: return "unknown status";
+    }
+}
+
+int mta_forward(const void *q, const void *k, const void *v, const float *theta_kq,
+                const float *theta_head, const float *gn_w, const float *gn_b,
+                const mta_config *cfg, void *out, void *stream)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;  // empty: nothing to do
+    if (!q || !k || !v || !theta_kq || !theta_head || !gn_w || !gn_b || !out) return MTA_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(theta_kq) ||
+        !aligned4(theta_head) || !aligned4(gn_w) || !aligned4(gn_b))
+        return MTA_ERR_MISALIGNED;
+
+    const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
+    const int post = cfg->kq_place == MTA_POST_SOFTMAX;
+    const int hpre = cfg->head_place == MTA_PRE_SOFTMAX;
+    mta::LaunchFn fn = cfg->dtype == MTA_BF16 ? mta::find_launch_bf16(d, ch, cq, ck, post, hpre)
+                                              : mta::find_launch_f32(d, ch, cq, ck, post, hpre);
+    if (!fn) return MTA_ERR_UNSUPPORTED;
+
+    mta::Params p;
+    p.q = q; p.k = k; p.v = v;
+    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b;
+    p.out = out;
+    p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
+    p.G = cfg->heads / ch;
+    p.units = cfg->batch * p.G;
+    p.n_qt = (cfg->seq_len + mta::BM - 1) / mta::BM;
+    p.head_pre = cfg->head_place == MTA_PRE_SOFTMAX;
+    p.hl = (ck + 1) / 2 - 1;
+    p.ncb = (mta::BN + ck - 1 + 15) / 16;
+    p.pitch = p.ncb * 16 + 4;
+    p.nbuf = (post && p.head_pre) ? ch : 1;
+    p.sc = 1.4426950408889634f / sqrtf((float)d);
+    p.eps = cfg->gn_eps;
+    p.depth_scale = cfg->depth_scale;
+
+    const int grid = p.n_qt * p.units;
+    const size_t lds = lds_bytes(p, cfg->dtype, d, ch);
+    if (lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
+    const hipError_t e = fn(p, grid, lds, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+}
+
+}  // extern "C"

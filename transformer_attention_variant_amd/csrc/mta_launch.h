@@ -1,0 +1,30 @@
+// mta_launch.h — launch helpers shared by the instantiation units and the ABI.
+#pragma once
+
+#include "mta_fwd_kernel.h"
+
+namespace mta {
+
+typedef hipError_t (*LaunchFn)(const Params &p, int grid, size_t lds, hipStream_t s);
+
+template <typename DT, int D, int CH, int CQ, int CK, bool POST, bool HPRE>
+hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
+{
+    auto fn = mta_fwd_kernel<DT, D, CH, CQ, CK, POST, HPRE>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, s, p);
+    return hipGetLastError();
+}
+
+// Kernel lookup per element type; null when (d, c_h) is not instantiated.
+// Kernel sizes (c_q, c_k) with a compile-time stencil get it when the head mix
+// follows the softmax; every other case runs the runtime-sized stencil of the
+// same kernel template.
+LaunchFn find_launch_f32(int d, int ch, int cq, int ck, int post, int hpre);
+LaunchFn find_launch_bf16(int d, int ch, int cq, int ck, int post, int hpre);
+
+}  // namespace mta

@@ -37,9 +37,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="needle4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
-                    help="rows per (batch, head group) unit in the oracle sample (from the end)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows per (batch, head group) unit in the oracle sample, from the end (0 = all)")
     ap.add_argument("--cpu-units", type=int, default=0, help="units in the oracle sample (0 = all)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB `steps` times "
+                         "(calibrates the HBM byte counters) and exit")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -58,6 +61,16 @@ def main():
     import torch
     from transformer_attention_variant_amd import binding
     from transformer_attention_variant_amd import inputs as I
+
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "calls": args.steps}))
+        return
 
     cfg = I.CONFIGS[args.config]
     inp = I.generate(cfg)
@@ -159,7 +172,7 @@ def cpu_baseline(cfg, inp, args):
     import oracle
     U = cfg.B * cfg.groups
     nu = U if args.cpu_units <= 0 else min(U, args.cpu_units)
-    rows = min(cfg.T, args.cpu_rows)
+    rows = cfg.T if args.cpu_rows <= 0 else min(cfg.T, args.cpu_rows)
     units = list(range(nu))
     threads = oracle.default_threads()
     q, k, v = (oracle._f64(inp[n]) for n in ("q", "k", "v"))

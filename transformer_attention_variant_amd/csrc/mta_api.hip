@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "mta.h"
+#include "mta_fwd_v2.h"
 #include "mta_launch.h"
 
 namespace {
@@ -86,9 +87,6 @@ int mta_forward(const void *q, const void *k, const void *v, const float *theta_
     const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
     const int post = cfg->kq_place == MTA_POST_SOFTMAX;
     const int hpre = cfg->head_place == MTA_PRE_SOFTMAX;
-    mta::LaunchFn fn = cfg->dtype == MTA_BF16 ? mta::find_launch_bf16(d, ch, cq, ck, post, hpre)
-                                              : mta::find_launch_f32(d, ch, cq, ck, post, hpre);
-    if (!fn) return MTA_ERR_UNSUPPORTED;
 
     mta::Params p;
     p.q = q; p.k = k; p.v = v;
@@ -108,8 +106,35 @@ int mta_forward(const void *q, const void *k, const void *v, const float *theta_
     p.depth_scale = cfg->depth_scale;
 
     const int grid = p.n_qt * p.units;
-    const size_t lds = lds_bytes(p, cfg->dtype, d, ch);
-    if (lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
+    // the pipelined 8-wave kernel where it is instantiated and fits in LDS,
+    // else the general 4-wave kernel
+    mta::LaunchFn fn = nullptr;
+    size_t lds = 0;
+    if (cfg->dtype == MTA_BF16) {
+        // stencil on the matrix cores first, then the fp32 VALU stencil
+        const int ncb0 = p.ncb, pitch0 = p.pitch;
+        for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {
+            // the matrix-core stencil reads a 32-column window past each
+            // 16-key output block: the tile must span at least 80 columns
+            p.ncb = (ms && ncb0 < 5) ? 5 : ncb0;
+            p.pitch = p.ncb * 16 + 4;
+            fn = mta::find_launch_v2(d, ch, cq, ck, post, hpre, ms);
+            if (fn) {
+                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0).total;
+                if (lds > 160 * 1024) fn = nullptr;
+            }
+        }
+        if (!fn) {
+            p.ncb = ncb0;
+            p.pitch = pitch0;
+        }
+    }
+    if (!fn) {
+        fn = cfg->dtype == MTA_BF16 ? mta::find_launch_bf16(d, ch, cq, ck, post, hpre)
+                                    : mta::find_launch_f32(d, ch, cq, ck, post, hpre);
+        lds = lds_bytes(p, cfg->dtype, d, ch);
+    }
+    if (!fn || lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
     const hipError_t e = fn(p, grid, lds, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
 }

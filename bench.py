@@ -43,13 +43,58 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB `steps` times "
                          "(calibrates the HBM byte counters) and exit")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPYF_DIR", "COPYW_DIR"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark and of "
+                         "--copy-mb into HBM bytes per launch, update --traffic-file, and exit")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
 
 
+def _pmc_avg(d, counter, match):
+    """Mean of `counter` (KiB per dispatch) over dispatches whose kernel name
+    contains `match`, from a rocprofv3 --pmc csv run directory."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for '{match}' under {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(args):
+    """HBM traffic per launch of the MTA kernel.  FETCH_SIZE and WRITE_SIZE are
+    read per dispatch; each is scaled by the ratio of the known byte count of a
+    plain device copy (--copy-mb) to what the same counter reports for it."""
+    fdir, wdir, cfdir, cwdir = args.summarize_pmc
+    kf, nk = _pmc_avg(fdir, "FETCH_SIZE", "mta_fwd")
+    kw, _ = _pmc_avg(wdir, "WRITE_SIZE", "mta_fwd")
+    cf, _ = _pmc_avg(cfdir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _pmc_avg(cwdir, "WRITE_SIZE", "copyBuffer")
+    copy_kib = args.copy_mb * 1024 if args.copy_mb else 512 * 1024
+    sf, sw = copy_kib / cf, copy_kib / cw
+    rd, wr = kf * sf * 1024, kw * sw * 1024
+    entry = {"bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
+             "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": sf, "write_scale": sw,
+             "dispatches": nk, "copy_mib": copy_kib // 1024}
+    db = {}
+    if os.path.exists(args.traffic_file):
+        db = json.load(open(args.traffic_file))
+    db[args.config] = entry
+    with open(args.traffic_file, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+    print(json.dumps({args.config: entry}))
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the MTA "

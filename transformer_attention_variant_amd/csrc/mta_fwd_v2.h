@@ -28,7 +28,8 @@ namespace v2 {
 
 constexpr int NW = 8;
 constexpr int NT = 64 * NW;
-constexpr int VP = BN + 8;  // bf16 pitch of the transposed V tile
+template <int D>
+__host__ __device__ constexpr int vpitch() { return D + 8; }  // bf16 pitch of the row-major V tile
 
 struct Layout {
     int s_off, k_off, q_off, v_off, p_off, st_off, xs_off, th_off, w_off, gn_off, tf_off, total;
@@ -46,7 +47,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb,
     L.s_off = o;  o += sb32 > sbhl ? sb32 : sbhl;           // logit / probability tile (fp32, or bf16 hi+lo)
     L.k_off = o;  o += ncb * 16 * KP * 2;                   // K tile with key halo (bf16)
     L.q_off = o;  o += EXT_R * KP * 2;                      // Q tile with the 16 rows above (bf16)
-    L.v_off = o;  o += D * VP * 2;                          // V tile, transposed (bf16)
+    L.v_off = o;  o += BN * KP * 2;                         // V tile, row-major (bf16)
     L.p_off = o;  o += CH * 4 * 2 * 64 * 16;                // mixed probabilities [a][rw][chunk][lane] x 8 bf16
     L.st_off = o; o += 2 * CH * EXT_R * 4;                  // final row statistics m, 1/l per tile row
     L.xs_off = o; o += 2 * CH * EXT_R * 2 * 4;              // per-half partial statistics
@@ -129,18 +130,18 @@ __device__ inline void store_q(const Pref<D> &r, bf16_t *qbuf, int tid)
     }
 }
 
-// V rows [j0, j0 + BN) of one head; stored transposed, vbuf[d][key].
-// Consecutive threads take consecutive keys of one 8-channel group.
+// V rows [j0, j0 + BN) of one head, stored row-major; the P.V product reads
+// it with the transposing LDS load.
 template <int D>
 __device__ inline void load_v(Pref<D> &r, const bf16_t *vh, int j0, int T, int tid)
 {
 #pragma unroll
     for (int it = 0; it < Pref<D>::VL; ++it) {
         const int idx = tid + it * NT;
-        const int key = idx % BN, c8 = idx / BN;
+        const int key = idx / Pref<D>::C8, c8 = idx % Pref<D>::C8;
         const int kj = j0 + key;
-        r.v[it] = (c8 < Pref<D>::C8 && kj < T) ? *reinterpret_cast<const bf16x8 *>(vh + (size_t)kj * D + 8 * c8)
-                                               : zero8();
+        r.v[it] = (key < BN && kj < T) ? *reinterpret_cast<const bf16x8 *>(vh + (size_t)kj * D + 8 * c8)
+                                        : zero8();
     }
 }
 
@@ -150,12 +151,22 @@ __device__ inline void store_v(const Pref<D> &r, bf16_t *vbuf, int tid)
 #pragma unroll
     for (int it = 0; it < Pref<D>::VL; ++it) {
         const int idx = tid + it * NT;
-        const int key = idx % BN, c8 = idx / BN;
-        if (c8 < Pref<D>::C8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vbuf[(8 * c8 + e) * VP + key] = r.v[it][e];
-        }
+        const int key = idx / Pref<D>::C8, c8 = idx % Pref<D>::C8;
+        if (key < BN) *reinterpret_cast<bf16x8 *>(vbuf + key * vpitch<D>() + 8 * c8) = r.v[it];
     }
+}
+
+// Transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group, element
+// e = 0..3 of lane i is the (i mod 4)-th element of the 4-element row addressed
+// by lane 4e + i/4.  With lane j addressing V[kb + j/4][d0 + 4(j%4)],
+// lane i receives V[kb + e][d0 + i], e = 0..3: four consecutive keys of its
+// own d column.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline s16x4 lds_read_tr4(const bf16_t *vbuf, int pitch, int kb, int d0, int j)
+{
+    const bf16_t *a = vbuf + (kb + (j >> 2)) * pitch + d0 + 4 * (j & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(a));
 }
 
 // ---------------------------------------------------------------------------
@@ -184,6 +195,9 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
     const int qi = i0 - HALO + rho;
+    // block-uniform classification: every entry causal and inside [0, T), or not
+    const int q_lo = i0 - HALO + rb * 16, k_lo = j0 - hl + cb * 16;
+    const bool all_ok = (k_lo >= 0) && (k_lo + 15 <= q_lo) && (q_lo + 15 < T);
     float m = 0.f, il = 0.f;
     if (MODE == PROB) {
         m = st_m[rho];
@@ -193,11 +207,13 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
     bf16x4 h4, l4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int kj = j0 - hl + e0 + r;
-        const bool ok = (kj >= 0) && (kj <= qi) && (qi < T);
         float x = acc[r] * sc;
         if (MODE == PROB) x = __builtin_amdgcn_exp2f(x - m) * il;
-        x = ok ? x : 0.f;
+        if (!all_ok) {
+            const int kj = j0 - hl + e0 + r;
+            const bool ok = (kj >= 0) && (kj <= qi) && (qi < T);
+            x = ok ? x : 0.f;
+        }
         bf16_t hh, ll;
         split_hl(x, hh, ll);
         h4[r] = hh;
@@ -232,6 +248,50 @@ __device__ inline void build_theta_frags(bf16x8 *tf, const float *th_s, int CH, 
     }
 }
 
+// Kernel fragments of one head, resident in registers: th[i'][plane].
+template <int CQ>
+struct ThetaFrags {
+    bf16x8 f[CQ][2];
+};
+
+template <int CQ>
+__device__ inline void load_theta_frags(ThetaFrags<CQ> &t, const bf16x8 *tf, int lane)
+{
+#pragma unroll
+    for (int ip = 0; ip < CQ; ++ip) {
+        t.f[ip][0] = tf[(ip * 2 + 0) * 64 + lane];
+        t.f[ip][1] = tf[(ip * 2 + 1) * 64 + lane];
+    }
+}
+
+template <int CQ>
+__device__ inline void stencil_mfma_reg(const bf16_t *xh, const bf16_t *xl, int ph, int rho, int kh,
+                                        const ThetaFrags<CQ> &tfr, int lane, float out[8])
+{
+    const int g4 = lane >> 4;
+    // six independent accumulation chains (2 blocks x 3 products), summed at the end
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0, c0 = a0, c1 = a0;
+#pragma unroll
+    for (int ip = 0; ip < CQ; ++ip) {
+        const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
+        const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
+        const bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
+        const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
+        const bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h0, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h1, a1, 0, 0, 0);
+        b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], l0, b0, 0, 0, 0);
+        b1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], l1, b1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][1], h0, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][1], h1, c1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        out[r] = (a0[r] + b0[r]) + c0[r];
+        out[4 + r] = (a1[r] + b1[r]) + c1[r];
+    }
+}
+
 // Two 16-key output blocks (keys 32kh + 16t + 4*(lane/16) + r, t = 0,1) of row
 // 16rw + lane%16.  out[4t + r].
 template <int CQ>
@@ -239,7 +299,8 @@ __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, 
                                     const bf16x8 *tf, int lane, float out[8])
 {
     const int g4 = lane >> 4;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // six independent accumulation chains (2 blocks x 3 products), summed at the end
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0, c0 = a0, c1 = a0;
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip) {
         const bf16x8 th = tf[(ip * 2 + 0) * 64 + lane];
@@ -249,17 +310,17 @@ __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, 
         const bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
         const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
         const bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h1, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l1, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h1, acc1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h0, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h1, a1, 0, 0, 0);
+        b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l0, b0, 0, 0, 0);
+        b1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l1, b1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h0, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h1, c1, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        out[r] = acc0[r];
-        out[4 + r] = acc1[r];
+        out[r] = (a0[r] + b0[r]) + c0[r];
+        out[4 + r] = (a1[r] + b1[r]) + c1[r];
     }
 }
 
@@ -267,7 +328,7 @@ __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, 
 // Logit tile of one head from the Q and K tiles in LDS.  Wave (rw, kh):
 // own-row block 1+rw for column blocks kh, kh+2, ...; the waves with kh == 1
 // also take the HALO block's column blocks rw, rw+4, ... (only if c_q > 1).
-template <int D, int MODE, bool HL>
+template <int D, int MODE, bool HL, int NCB>
 __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, const bf16_t *kbuf,
                                       const Params &p, int i0, int j0, const float *st_m, const float *st_il,
                                       int rw, int kh, int lane)
@@ -281,7 +342,8 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 8 * t);
     }
-    for (int cb = kh; cb < p.ncb; cb += 2) {
+#pragma unroll
+    for (int cb = kh; cb < NCB; cb += 2) {
         const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
@@ -295,7 +357,8 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
         const bf16_t *qr = qbuf + l16 * (D + 8) + dq;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 8 * t);
-        for (int cb = rw; cb < p.ncb; cb += 4) {
+#pragma unroll
+        for (int cb = rw; cb < NCB; cb += 4) {
             const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
 #pragma unroll
             for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
@@ -305,6 +368,56 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
             else
                 store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
         }
+    }
+}
+
+// Same tile with the wave's Q fragments already in registers (own-row block
+// and, for the waves that take it, the halo block).
+template <int D, int MODE, bool HL, int NCB>
+__device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown, const QFrag<D> &qhalo,
+                                       const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh,
+                                       int lane)
+{
+    const int l16 = lane & 15, dq = (lane >> 4) * (D / 4);
+    bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
+    bf16_t *xl = xh + EXT_R * ph;
+    QFrag<D> kf;
+#pragma unroll
+    for (int cb = kh; cb < NCB; cb += 2) {
+        const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+        const f32x4 acc = qk_mfma<D>(kf, qown);
+        if (HL)
+            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+        else
+            store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+    }
+    if (kh == 1 && p.c_q > 1) {
+#pragma unroll
+        for (int cb = rw; cb < NCB; cb += 4) {
+            const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+            const f32x4 acc = qk_mfma<D>(kf, qhalo);
+            if (HL)
+                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+            else
+                store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+        }
+    }
+}
+
+template <int D>
+__device__ inline void load_qfrags(QFrag<D> &qown, QFrag<D> &qhalo, const bf16_t *qbuf, int rw, int lane)
+{
+    const int l16 = lane & 15, dq = (lane >> 4) * (D / 4);
+    const bf16_t *qo = qbuf + (16 * (1 + rw) + l16) * (D + 8) + dq;
+    const bf16_t *qh = qbuf + l16 * (D + 8) + dq;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+        qown.x[t] = *reinterpret_cast<const bf16x8 *>(qo + 8 * t);
+        qhalo.x[t] = *reinterpret_cast<const bf16x8 *>(qh + 8 * t);
     }
 }
 
@@ -401,9 +514,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     const int T = p.T;
     constexpr int CK4 = (CK + 3) / 4;
     constexpr int CKP = CK4 * 4;
-    const int ph = pitch_hl(p.ncb);
+    // 16-wide column blocks of the logit tile (the host passes the same value in p.ncb)
+    constexpr int NCB0 = (BN + CK - 1 + 15) / 16;
+    constexpr int NCB = (MS && NCB0 < 5) ? 5 : NCB0;
+    const int ph = pitch_hl(NCB);
 
-    const Layout lay = layout(D, CH, CQ, CK, p.ncb, p.pitch, MS);
+    const Layout lay = layout(D, CH, CQ, CK, NCB, p.pitch, MS);
     float *sbuf = reinterpret_cast<float *>(smem + lay.s_off);
     const bf16_t *xh = reinterpret_cast<const bf16_t *>(sbuf);
     const bf16_t *xl = xh + EXT_R * ph;
@@ -425,7 +541,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     const bf16_t *Q = reinterpret_cast<const bf16_t *>(p.q) + base0;
     const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + base0;
     const bf16_t *V = reinterpret_cast<const bf16_t *>(p.v) + base0;
-    const int krows = 16 * p.ncb;
+    constexpr int krows = 16 * NCB;
 
     for (int i = tid; i < CH * CQ * CKP; i += NT) {
         const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
@@ -457,32 +573,40 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     store_k<D>(pf, kbuf, krows, tid);
 
     // ------------------------------ pass 1 ---------------------------------
+    // Head-major: all key tiles of head a, then head a+1, so that the head's Q
+    // fragments and kernel fragments stay in registers.
     float m_c[CH], l_c[CH], m_h[CH], l_h[CH];
 #pragma unroll
     for (int a = 0; a < CH; ++a) {
         m_c[a] = NEG_INF; l_c[a] = 0.f; m_h[a] = NEG_INF; l_h[a] = 0.f;
     }
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int j0 = kt * BN;
 #pragma unroll
-        for (int a = 0; a < CH; ++a) {
+    for (int a = 0; a < CH; ++a) {
+        QFrag<D> qown, qhal;
+        ThetaFrags<MS ? CQ : 1> tfr;
+        for (int kt = 0; kt <= qt; ++kt) {
+            const int j0 = kt * BN;
             __syncthreads();
-            if (!KQ_POST && MS)
-                logit_tile_lds<D, RAW, true>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
-            else
-                logit_tile_lds<D, RAW, false>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
-            __syncthreads();
-            // next phase: (kt, a+1), or (kt+1, 0), or pass 2's first phase (0, 0)
-            {
-                const int an = (a + 1 < CH) ? a + 1 : 0;
-                const int ktn = (a + 1 < CH) ? kt : (kt + 1 <= qt ? kt + 1 : 0);
-                load_k<D>(pf, K + an * hstride, ktn * BN, p.hl, krows, T, tid);
-                if (CH > 1) load_q<D>(pf, Q + an * hstride, i0, T, tid);
+            // next phase: (a, kt+1), or (a+1, 0), or pass 2's first phase (head 0,
+            // tile 0); issued early so the loads overlap this whole phase
+            const bool last = kt == qt;
+            const int an = last ? (a + 1 < CH ? a + 1 : 0) : a;
+            const int ktn = last ? 0 : kt + 1;
+            load_k<D>(pf, K + an * hstride, ktn * BN, p.hl, krows, T, tid);
+            if (CH > 1 && last) load_q<D>(pf, Q + an * hstride, i0, T, tid);
+            if (kt == 0) {
+                load_qfrags<D>(qown, qhal, qbuf, rw, lane);
+                if (MS) load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 2 * 64, lane);
             }
+            if (!KQ_POST && MS)
+                logit_tile_regq<D, RAW, true, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+            else
+                logit_tile_regq<D, RAW, false, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+            __syncthreads();
             if (!KQ_POST) {
                 float c[8];
                 if (MS)
-                    stencil_mfma<CQ>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, lane, c);
+                    stencil_mfma_reg<MS ? CQ : 1>(xh, xl, ph, rho, kh, tfr, lane, c);
                 else
                     stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, c);
                 stats_update8(c, j0, ko, qabs, m_c[a], l_c[a]);
@@ -498,7 +622,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 }
             }
             store_k<D>(pf, kbuf, krows, tid);
-            if (CH > 1) store_q<D>(pf, qbuf, tid);
+            if (CH > 1 && last) store_q<D>(pf, qbuf, tid);
         }
     }
 
@@ -561,24 +685,22 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     const int dbase = kh * (D / 2);
 
     // P.V of one head: the A operand (probabilities of 16 rows x 32 keys per
-    // chunk) comes from the exchange buffer, B from the transposed V tile, with
-    // the same key order as the producing lanes.
+    // chunk) comes from the exchange buffer, B from the row-major V tile via
+    // transposing loads, with the same key order as the producing lanes.
     auto pv = [&](int a, f32x4(&ac)[D / 32]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const bf16x8 av = pbuf[((a * 4 + rw) * 2 + c) * 64 + lane];
 #pragma unroll
             for (int nb = 0; nb < D / 32; ++nb) {
-                const bf16_t *vr = vbuf + (dbase + 16 * nb + l16) * VP + 32 * c;
-                bf16x8 bv;
-                if (MS) {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    const bf16x4 u0 = *reinterpret_cast<const bf16x4 *>(vr + 4 * g4);
-                    const bf16x4 u1 = *reinterpret_cast<const bf16x4 *>(vr + 16 + 4 * g4);
-                    bv = bf16x8{u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-                } else {
-                    bv = *reinterpret_cast<const bf16x8 *>(vr + 8 * g4);
-                }
+                // keys of slots 0-3 and 4-7, matching the producing lanes' order
+                const int kb0 = MS ? 32 * c + 4 * g4 : 32 * c + 8 * g4;
+                const int kb1 = MS ? kb0 + 16 : kb0 + 4;
+                const s16x4 u0 = lds_read_tr4(vbuf, vpitch<D>(), kb0, dbase + 16 * nb, l16);
+                const s16x4 u1 = lds_read_tr4(vbuf, vpitch<D>(), kb1, dbase + 16 * nb, l16);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
                 ac[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, ac[nb], 0, 0, 0);
             }
         }
@@ -590,14 +712,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
 #pragma unroll
         for (int a = 0; a < CH; ++a) {
             __syncthreads();
-            if (KQ_POST)
-                logit_tile_lds<D, PROB, MS>(sbuf, ph, qbuf, kbuf, p, i0, j0, st_m + a * EXT_R, st_il + a * EXT_R,
-                                            rw, kh, lane);
-            else
-                logit_tile_lds<D, RAW, MS>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
-            if (kt > 0) pv(a, acc[a]);
-            __syncthreads();
-            // next phase (kt, a+1) or (kt+1, 0): its K, Q and the V tile its P.V reads
+            // next phase (kt, a+1) or (kt+1, 0): its K, Q and the V tile its P.V
+            // reads; issued early so the loads overlap this whole phase
             const int an = (a + 1 < CH) ? a + 1 : 0;
             const int ktn = (a + 1 < CH) ? kt : kt + 1;
             const bool more = ktn <= qt;
@@ -606,6 +722,13 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 if (CH > 1) load_q<D>(pf, Q + an * hstride, i0, T, tid);
             }
             if (ktn >= 1) load_v<D>(pf, V + an * hstride, (ktn - 1) * BN, T, tid);
+            if (KQ_POST)
+                logit_tile_lds<D, PROB, MS, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, st_m + a * EXT_R, st_il + a * EXT_R,
+                                            rw, kh, lane);
+            else
+                logit_tile_lds<D, RAW, MS, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
+            if (kt > 0) pv(a, acc[a]);
+            __syncthreads();
 
             float c[8];
             if (MS)

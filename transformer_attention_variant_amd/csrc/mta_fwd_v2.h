@@ -594,14 +594,18 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             const int ktn = last ? 0 : kt + 1;
             load_k<D>(pf, K + an * hstride, ktn * BN, p.hl, krows, T, tid);
             if (CH > 1 && last) load_q<D>(pf, Q + an * hstride, i0, T, tid);
-            if (kt == 0) {
+            // with the matrix-core stencil the head's Q and kernel fragments stay in
+            // registers; the VALU-stencil variant has no registers to spare for them
+            if (MS && kt == 0) {
                 load_qfrags<D>(qown, qhal, qbuf, rw, lane);
-                if (MS) load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 2 * 64, lane);
+                load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 2 * 64, lane);
             }
             if (!KQ_POST && MS)
                 logit_tile_regq<D, RAW, true, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
-            else
+            else if (MS)
                 logit_tile_regq<D, RAW, false, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+            else
+                logit_tile_lds<D, RAW, false, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
             __syncthreads();
             if (!KQ_POST) {
                 float c[8];

@@ -225,7 +225,8 @@ def cpu_baseline(cfg, inp, args):
     t0 = time.perf_counter()
     oracle.forward(q, k, v, inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q,
                    c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
-                   eps=cfg.gn_eps, depth_scale=cfg.depth_scale, rows=(cfg.T - rows, cfg.T), units=units,
+                   eps=cfg.gn_eps, depth_scale=cfg.depth_scale, gate=inp.get("gate"),
+                   rows=(cfg.T - rows, cfg.T), units=units,
                    chunk=32, threads=threads, lib=lib)
     dt = time.perf_counter() - t0
     full = dt * (U * cfg.T) / (nu * rows)

@@ -108,6 +108,22 @@ int mta_forward(const void *q, const void *k, const void *v,
                 const float *gn_w, const float *gn_b,
                 const mta_config *cfg, void *out, void *stream);
 
+/*
+ * mta_forward_gated — the same forward with the sigmoid-gated GroupNorm of
+ * "Group Normalization with Sigmoid Gating" (page "Multi-Token Attention —
+ * Paper Graph", section 3.4): each head's normalised, affine-transformed output
+ * is multiplied by sigmoid(gate[h]) (and by cfg->depth_scale; pass 1 for the
+ * gate alone).
+ *
+ *  gate        float32 [H] device pointer: one gate logit per head (not NULL;
+ *              MTA_ERR_NULL_ARG otherwise; 4-byte aligned).
+ *  Every other argument and every error code as for mta_forward.
+ */
+int mta_forward_gated(const void *q, const void *k, const void *v,
+                      const float *theta_kq, const float *theta_head,
+                      const float *gn_w, const float *gn_b, const float *gate,
+                      const mta_config *cfg, void *out, void *stream);
+
 /* Host-only check of a configuration against the limits of this build; the
  * same validation mta_forward runs (pointer checks excepted).  Returns MTA_OK
  * or the MTA_ERR_* code mta_forward would return. */

@@ -40,12 +40,12 @@ def build(out: str = LIB, mutant: int = 0, force: bool = True) -> str:
 def _bind(lib):
     D = ctypes.POINTER(ctypes.c_double)
     I = ctypes.c_int
-    lib.mta_oracle_forward.argtypes = [D, D, D, D, D, D, D,
+    lib.mta_oracle_forward.argtypes = [D, D, D, D, D, D, D, D,
                                        I, I, I, I, I, I, I, I, I,
                                        ctypes.c_double, ctypes.c_double,
                                        I, I, ctypes.POINTER(ctypes.c_int), I, I, I, D]
     lib.mta_oracle_forward.restype = I
-    lib.mta_oracle_stages.argtypes = [D, D, D, D, D, D, D,
+    lib.mta_oracle_stages.argtypes = [D, D, D, D, D, D, D, D,
                                       I, I, I, I, I, I, I, I, I,
                                       ctypes.c_double, ctypes.c_double,
                                       I, I, D, D, D, D, D, D, D, D, D]
@@ -89,8 +89,16 @@ def default_threads() -> int:
     return max(1, min(16, n))
 
 
+def _gate(gate, H):
+    if gate is None:
+        return None, None
+    g = _f64(gate)
+    assert g.shape == (H,)
+    return g, _p(g)
+
+
 def forward(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
-            kq_place=0, head_place=1, eps=1e-5, depth_scale=1.0,
+            kq_place=0, head_place=1, eps=1e-5, depth_scale=1.0, gate=None,
             rows: Optional[Sequence[int]] = None, units: Optional[Sequence[int]] = None,
             chunk: int = 64, threads: Optional[int] = None, lib=None) -> np.ndarray:
     """The forward in float64.  q, k, v: [B,H,T,d].  ``rows`` = (begin, end)
@@ -111,7 +119,8 @@ def forward(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
         ua = (ctypes.c_int * len(units))(*[int(u) for u in units])
         up, nu = ua, len(units)
     nt = threads if threads is not None else default_threads()
-    rc = lib.mta_oracle_forward(_p(q), _p(k), _p(v), _p(th), _p(w), _p(gw), _p(gb),
+    ga, gp = _gate(gate, H)
+    rc = lib.mta_oracle_forward(_p(q), _p(k), _p(v), _p(th), _p(w), _p(gw), _p(gb), gp,
                                 B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                                 float(eps), float(depth_scale), r0, r1, up, nu,
                                 int(chunk), int(nt), _p(out))
@@ -121,7 +130,7 @@ def forward(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
 
 
 def stages(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
-           kq_place=0, head_place=1, eps=1e-5, depth_scale=1.0, b=0, g=0,
+           kq_place=0, head_place=1, eps=1e-5, depth_scale=1.0, gate=None, b=0, g=0,
            lib=None) -> Dict[str, np.ndarray]:
     """Every intermediate map of unit (b, g) over all rows: S (logits), C (the
     map entering the softmax before any head mix), Cmix, P (softmax), P2 (after
@@ -134,7 +143,8 @@ def stages(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
     mats = {n: np.full((c_h, T, T), np.nan) for n in ("S", "C", "Cmix", "P", "P2", "P3")}
     vecs = {n: np.full((c_h, T, d), np.nan) for n in ("O", "Y")}
     out = np.full((B, H, T, d), np.nan)
-    rc = lib.mta_oracle_stages(_p(q), _p(k), _p(v), _p(th), _p(w), _p(gw), _p(gb),
+    ga, gp = _gate(gate, H)
+    rc = lib.mta_oracle_stages(_p(q), _p(k), _p(v), _p(th), _p(w), _p(gw), _p(gb), gp,
                                B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                                float(eps), float(depth_scale), int(b), int(g),
                                _p(mats["S"]), _p(mats["C"]), _p(mats["Cmix"]),
@@ -153,11 +163,11 @@ def forward_cfg(cfg, inp: Dict, **kw) -> np.ndarray:
     return forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"],
                    inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
                    kq_place=cfg.kq_place, head_place=cfg.head_place, eps=cfg.gn_eps,
-                   depth_scale=cfg.depth_scale, **kw)
+                   depth_scale=cfg.depth_scale, gate=inp.get("gate"), **kw)
 
 
 def stages_cfg(cfg, inp: Dict, **kw) -> Dict[str, np.ndarray]:
     return stages(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"],
                   inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
                   kq_place=cfg.kq_place, head_place=cfg.head_place, eps=cfg.gn_eps,
-                  depth_scale=cfg.depth_scale, **kw)
+                  depth_scale=cfg.depth_scale, gate=inp.get("gate"), **kw)

@@ -204,9 +204,11 @@ static void step_pv(const double *A, const double *v, int T, int d, int i0, int 
 }
 
 /* Step 7.  GroupNorm with each head's d channels as one group, per-channel
- * affine, then the depth scale ("Group Normalization with Sigmoid Gating":
- * heads are the normalisation groups; the overview page names the scaled
- * variant "Group Normalization with Depth Scaling").  Biased variance. */
+ * affine, then the head's output scale ("Group Normalization with Sigmoid
+ * Gating": heads are the normalisation groups, and each head's normalised
+ * output is multiplied by sigma(g_h) for a learned per-head gate g; the
+ * overview page names the alternative "Group Normalization with Depth
+ * Scaling").  Biased variance.  `depth_scale` is the head's total factor. */
 static void step_groupnorm_scale(const double *O, const double *gw, const double *gb,
                                  int d, int i0, int i1, double eps, double depth_scale,
                                  double *Y)
@@ -238,7 +240,19 @@ static void step_groupnorm_scale(const double *O, const double *gw, const double
 typedef struct {
     int B, H, T, d, c_q, c_k, c_h, kq_place, head_place;
     double eps, depth_scale;
+    const double *gate;  /* [H] per-head gate logits, or NULL (no gate) */
 } oracle_cfg;
+
+/* The sigmoid of the gate ("Group Normalization with Sigmoid Gating"). */
+static double head_scale(const oracle_cfg *cf, int h)
+{
+    if (!cf->gate) return cf->depth_scale;
+#if ORACLE_MUTANT == 8 /* planted: gate used without its sigmoid */
+    return cf->depth_scale * cf->gate[h];
+#else
+    return cf->depth_scale / (1.0 + exp(-cf->gate[h]));
+#endif
+}
 
 /* Stage dump layout for one unit, full rows [0,T) only:
  *   S, C, Cmix, P, P2, P3 : [c_h][T][T] each
@@ -358,7 +372,7 @@ static int unit_rows(const oracle_cfg *cf, const double *q, const double *k, con
         const size_t base = ((size_t)b * H + h) * (size_t)T * d;
         step_pv(A3[a] + off, v + base, T, d, r0, r1, O[a]);
         step_groupnorm_scale(O[a], gn_w + (size_t)h * d, gn_b + (size_t)h * d, d, r0, r1,
-                             cf->eps, cf->depth_scale, out + base + (size_t)r0 * d);
+                             cf->eps, head_scale(cf, h), out + base + (size_t)r0 * d);
         if (st) {
             memcpy(st->O + (size_t)a * T * d, O[a], (size_t)nr * d * sizeof(double));
             memcpy(st->Y + (size_t)a * T * d, out + base + (size_t)r0 * d,
@@ -391,17 +405,19 @@ static int check_cfg(const oracle_cfg *c)
  * run on `n_threads` threads (the arithmetic of an output row does not depend
  * on the chunking).  units == NULL means every unit b*G+g.  Arrays are
  * float64, [B][H][T][d] for q, k, v, out; theta_kq [H][c_q][c_k];
- * theta_head [H/c_h][c_h][c_h]; gn_w, gn_b [H][d].  Only the requested rows of
+ * theta_head [H/c_h][c_h][c_h]; gn_w, gn_b [H][d]; gate [H] or NULL (each
+ * head's output is scaled by depth_scale * sigmoid(gate[h]), or by
+ * depth_scale alone without a gate).  Only the requested rows of
  * the requested units of `out` are written.  Returns 0, or a negative code. */
 int mta_oracle_forward(const double *q, const double *k, const double *v,
                        const double *theta_kq, const double *theta_head,
-                       const double *gn_w, const double *gn_b,
+                       const double *gn_w, const double *gn_b, const double *gate,
                        int B, int H, int T, int d, int c_q, int c_k, int c_h,
                        int kq_place, int head_place, double eps, double depth_scale,
                        int row_begin, int row_end, const int *units, int n_units,
                        int chunk, int n_threads, double *out)
 {
-    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, kq_place, head_place, eps, depth_scale};
+    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, kq_place, head_place, eps, depth_scale, gate};
     int rc = check_cfg(&cf);
     if (rc) return rc;
     if (row_begin < 0 || row_end > T || row_begin > row_end) return -2;
@@ -434,13 +450,13 @@ int mta_oracle_forward(const double *q, const double *k, const double *v,
  * unit's heads of the final result in [B][H][T][d] layout. */
 int mta_oracle_stages(const double *q, const double *k, const double *v,
                       const double *theta_kq, const double *theta_head,
-                      const double *gn_w, const double *gn_b,
+                      const double *gn_w, const double *gn_b, const double *gate,
                       int B, int H, int T, int d, int c_q, int c_k, int c_h,
                       int kq_place, int head_place, double eps, double depth_scale,
                       int b, int g, double *S, double *C, double *Cmix, double *P,
                       double *P2, double *P3, double *O, double *Y, double *out)
 {
-    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, kq_place, head_place, eps, depth_scale};
+    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, kq_place, head_place, eps, depth_scale, gate};
     int rc = check_cfg(&cf);
     if (rc) return rc;
     if (b < 0 || b >= B || g < 0 || g >= H / c_h) return -2;

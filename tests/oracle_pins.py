@@ -83,6 +83,21 @@ def pin_identity_is_causal_attention(lib):
         _close(got, ref.numpy(), 1e-10, f"identity {cfg.short()}")
 
 
+def pin_sigmoid_gate(lib):
+    """Sigmoid-gated GroupNorm ("Group Normalization with Sigmoid Gating"): with
+    identity kernels, head h's output is GroupNorm(SDPA) x sigmoid(g_h) x depth
+    scale, computed with torch.sigmoid and group_norm."""
+    for kq in (I.PRE, I.POST):
+        cfg = I.small(B=2, H=4, T=29, d=8, c_q=3, c_k=5, c_h=2, kq_place=kq, gn_random=True,
+                      gated=True, layer=2, seed=61)
+        inp = _identity_inputs(cfg)
+        got = oracle.forward_cfg(cfg, inp, lib=lib, threads=2)
+        ref = _gn64(_sdpa64(inp["q"], inp["k"], inp["v"]), inp["gn_w"], inp["gn_b"], cfg.gn_eps,
+                    cfg.depth_scale)
+        ref = ref * torch.sigmoid(inp["gate"].double())[None, :, None, None]
+        _close(got, ref.numpy(), 1e-10, f"gate {cfg.short()}")
+
+
 def pin_key_shift_is_shifted_attention(lib):
     """A key-axis delta at j' = +1 reads key j-1: MTA == SDPA with the keys
     shifted down one step (k'_j = k_{j-1}, k'_0 = 0); Mask_0 has no effect
@@ -305,6 +320,7 @@ def pin_brute_force_tiny(lib):
 
 ALL_PINS = [
     pin_identity_is_causal_attention,
+    pin_sigmoid_gate,
     pin_key_shift_is_shifted_attention,
     pin_diff_transformer_special_case,
     pin_pre_softmax_head_mix_is_concat_attention,

@@ -87,6 +87,18 @@ def test_forward_rejects_before_any_device_work(lib):
     assert lib.mta_forward(*a, ctypes.byref(c), good, None) == -5
 
 
+def test_gated_entry_requires_gate(lib):
+    c = cfg()
+    good = 0x10000
+    args = [good] * 7
+    assert lib.mta_forward_gated(*args, None, ctypes.byref(c), good, None) == -1
+    assert lib.mta_forward_gated(*args, good + 2, ctypes.byref(c), good, None) == -5
+    bad = cfg(kq_place=5)
+    assert lib.mta_forward_gated(*args, good, ctypes.byref(bad), good, None) == -3
+    e = cfg(B=0)
+    assert lib.mta_forward_gated(*([None] * 8), ctypes.byref(e), None, None) == 0
+
+
 def test_empty_problem_launches_nothing(lib):
     # B == 0 or T == 0 succeeds without touching pointers (NULL is fine)
     for kw in (dict(B=0), dict(T=0)):

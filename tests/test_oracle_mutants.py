@@ -15,6 +15,7 @@ MUTANTS = {
     5: "kernel key axis reversed",
     6: "head-mix matrix transposed",
     7: "softmax rows not normalised",
+    8: "head gate used without its sigmoid",
 }
 
 

@@ -60,6 +60,13 @@ def _small_cases():
     c.append(I.small("gen_max_16x31", B=1, H=4, T=150, d=64, c_q=16, c_k=31, c_h=4, head_place=P, seed=401))
     c.append(I.small("gen_max_16x31_post", B=1, H=4, T=150, d=64, c_q=16, c_k=31, c_h=1,
                      kq_place=Q, seed=402))
+    # sigmoid-gated GroupNorm, on both kernels and both dtypes
+    for kq in (P, Q):
+        c.append(I.small(f"gated_f32_kq{kq}", B=1, H=4, T=90, d=64, c_q=3, c_k=5, c_h=2, kq_place=kq,
+                         gated=True, gate_std=3.0, gn_random=True, layer=3, seed=700 + kq))
+        c.append(I.small(f"gated_bf16_kq{kq}", B=1, H=4, T=130, d=128, c_q=6, c_k=11, c_h=2, kq_place=kq,
+                         dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True,
+                         seed=710 + kq))
     # tiny sequences: T = 1, T < c_q, exactly one tile, one tile + 1
     for T in (1, 3, 64, 65):
         c.append(I.small(f"f32_T{T}", B=2, H=2, T=T, d=32, c_q=3, c_k=5, c_h=2, seed=500 + T))
@@ -91,7 +98,7 @@ def test_workload_fp32_full(name):
     _say(f"[parity]   max abs err {err:.3e} (tol {tol:.1e})")
 
 
-@pytest.mark.parametrize("name", ["layer2k", "needle4k"] + I.SWEEP)
+@pytest.mark.parametrize("name", ["layer2k", "needle4k", "needle4k_gated"] + I.SWEEP)
 def test_workload_bf16_sampled(name):
     cfg = I.CONFIGS[name]
     _say(f"[parity] sampled {cfg.short()}")

@@ -22,7 +22,8 @@ STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA
           -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
           -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
 # names declared in include/mta.h
-EXPORTS = ("mta_forward", "mta_check_config", "mta_status_string", "mta_abi_version")
+EXPORTS = ("mta_forward", "mta_forward_gated", "mta_check_config", "mta_status_string",
+           "mta_abi_version")
 
 
 class MtaConfig(ctypes.Structure):
@@ -54,6 +55,8 @@ def load(path: Optional[str] = None):
     vp = ctypes.c_void_p
     lib.mta_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MtaConfig), vp, vp]
     lib.mta_forward.restype = ctypes.c_int
+    lib.mta_forward_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MtaConfig), vp, vp]
+    lib.mta_forward_gated.restype = ctypes.c_int
     lib.mta_check_config.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_check_config.restype = ctypes.c_int
     lib.mta_status_string.argtypes = [ctypes.c_int]
@@ -77,9 +80,11 @@ def status_string(code: int) -> str:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.Tensor,
             theta_head: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor, *, c_q: int, c_k: int,
             c_h: int, kq_place: int = I.PRE, head_place: int = I.POST, gn_eps: float = 1e-5,
-            depth_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+            depth_scale: float = 1.0, gate: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None,
             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """MTA forward on the GPU through ``mta_forward``.  q, k, v: [B,H,T,d]
+    """MTA forward on the GPU through ``mta_forward`` (``mta_forward_gated``
+    when a per-head ``gate`` [H] float32 tensor is given).  q, k, v: [B,H,T,d]
     float32 or bfloat16 CUDA tensors; theta_kq [H,c_q,c_k], theta_head
     [H/c_h,c_h,c_h], gn_w/gn_b [H,d] float32.  Asynchronous on ``stream``
     (default: torch's current stream)."""
@@ -101,6 +106,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.T
             raise ValueError(f"{name} must be a CUDA (HIP) tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if gate is not None:
+        if gate.dtype != torch.float32 or not gate.is_cuda or not gate.is_contiguous() \
+                or tuple(gate.shape) != (H,):
+            raise ValueError("gate must be a contiguous float32 CUDA tensor of shape [H]")
     if tuple(theta_kq.shape) != (H, c_q, c_k) or tuple(theta_head.shape) != (H // max(c_h, 1), c_h, c_h) \
             or tuple(gn_w.shape) != (H, d) or tuple(gn_b.shape) != (H, d):
         raise ValueError("parameter shapes do not match (theta_kq [H,c_q,c_k], theta_head [H/c_h,c_h,c_h], "
@@ -112,9 +121,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.T
     cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                       I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    rc = lib.mta_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(),
-                         theta_head.data_ptr(), gn_w.data_ptr(), gn_b.data_ptr(), ctypes.byref(cfg),
-                         out.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if gate is None:
+        rc = lib.mta_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(),
+                             theta_head.data_ptr(), gn_w.data_ptr(), gn_b.data_ptr(), ctypes.byref(cfg),
+                             out.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    else:
+        rc = lib.mta_forward_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(),
+                                   theta_head.data_ptr(), gn_w.data_ptr(), gn_b.data_ptr(),
+                                   gate.data_ptr(), ctypes.byref(cfg), out.data_ptr(),
+                                   ctypes.c_void_p(s.cuda_stream))
     if rc != MTA_OK:
         raise MTAError(rc, status_string(rc))
     return out
@@ -125,4 +140,4 @@ def forward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], out: Optional[to
     return forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"],
                    inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place,
                    head_place=cfg.head_place, gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
-                   out=out, stream=stream)
+                   gate=inp.get("gate"), out=out, stream=stream)

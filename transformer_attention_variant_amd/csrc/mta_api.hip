@@ -72,16 +72,16 @@ const char *mta_status_string(int s)
     }
 }
 
-int mta_forward(const void *q, const void *k, const void *v, const float *theta_kq,
-                const float *theta_head, const float *gn_w, const float *gn_b,
-                const mta_config *cfg, void *out, void *stream)
+static int forward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
+                        const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                        const mta_config *cfg, void *out, void *stream)
 {
     const int vs = validate(cfg);
     if (vs != MTA_OK) return vs;
     if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;  // empty: nothing to do
     if (!q || !k || !v || !theta_kq || !theta_head || !gn_w || !gn_b || !out) return MTA_ERR_NULL_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(theta_kq) ||
-        !aligned4(theta_head) || !aligned4(gn_w) || !aligned4(gn_b))
+        !aligned4(theta_head) || !aligned4(gn_w) || !aligned4(gn_b) || (gate && !aligned4(gate)))
         return MTA_ERR_MISALIGNED;
 
     const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
@@ -90,7 +90,7 @@ int mta_forward(const void *q, const void *k, const void *v, const float *theta_
 
     mta::Params p;
     p.q = q; p.k = k; p.v = v;
-    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b;
+    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b; p.gate = gate;
     p.out = out;
     p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
     p.G = cfg->heads / ch;
@@ -137,6 +137,24 @@ int mta_forward(const void *q, const void *k, const void *v, const float *theta_
     if (!fn || lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
     const hipError_t e = fn(p, grid, lds, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+}
+
+int mta_forward(const void *q, const void *k, const void *v, const float *theta_kq,
+                const float *theta_head, const float *gn_w, const float *gn_b,
+                const mta_config *cfg, void *out, void *stream)
+{
+    return forward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, nullptr, cfg, out, stream);
+}
+
+int mta_forward_gated(const void *q, const void *k, const void *v, const float *theta_kq,
+                      const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                      const mta_config *cfg, void *out, void *stream)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
+    if (!gate) return MTA_ERR_NULL_ARG;
+    return forward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, gate, cfg, out, stream);
 }
 
 }  // extern "C"

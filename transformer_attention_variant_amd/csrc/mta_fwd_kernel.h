@@ -49,6 +49,7 @@ struct Params {
     const float *theta;   // [H][c_q][c_k]
     const float *wmix;    // [H/c_h][c_h][c_h]
     const float *gn_w, *gn_b;
+    const float *gate;    // [H] per-head gate logits, or null
     void *out;
     int H, T, c_q, c_k, G, units, n_qt;
     int head_pre;         // head mix before the softmax
@@ -59,6 +60,14 @@ struct Params {
     float sc;             // log2(e) / sqrt(d)
     float eps, depth_scale;
 };
+
+// Output factor of head h: depth_scale * sigmoid(gate[h]) with a gate
+// ("Group Normalization with Sigmoid Gating"), depth_scale alone without.
+__device__ inline float head_factor(const Params &p, int h)
+{
+    if (!p.gate) return p.depth_scale;
+    return p.depth_scale / (1.0f + __expf(-p.gate[h]));
+}
 
 // ---------------------------------------------------------------------------
 // LDS layout (floats unless noted), sized on the host by lds_bytes():
@@ -664,6 +673,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
         const int h = h0 + a;
         const float *gw = p.gn_w + (size_t)h * D;
         const float *gb = p.gn_b + (size_t)h * D;
+        const float hf = head_factor(p, h);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s = 0.f;
@@ -691,7 +701,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
 #pragma unroll
                 for (int nb = 0; nb < D / 16; ++nb) {
                     const int col = nb * 16 + n;
-                    const float y = ((acc[a][nb][r] - mu) * rstd * gw[col] + gb[col]) * p.depth_scale;
+                    const float y = ((acc[a][nb][r] - mu) * rstd * gw[col] + gb[col]) * hf;
                     dst[col] = cvt_out<DT>(y);
                 }
             }

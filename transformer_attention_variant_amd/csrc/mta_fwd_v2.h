@@ -829,6 +829,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
         const int h = h0 + a;
         const float *gw = p.gn_w + (size_t)h * D;
         const float *gb = p.gn_b + (size_t)h * D;
+        const float hf = head_factor(p, h);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rowt = 16 * rw + 4 * g4 + r;
@@ -840,7 +841,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
 #pragma unroll
                 for (int nb = 0; nb < D / 32; ++nb) {
                     const int col = dbase + 16 * nb + l16;
-                    const float y = ((acc[a][nb][r] - mu[a][r]) * rstd * gw[col] + gb[col]) * p.depth_scale;
+                    const float y = ((acc[a][nb][r] - mu[a][r]) * rstd * gw[col] + gb[col]) * hf;
                     dst[col] = (bf16_t)y;
                 }
             }

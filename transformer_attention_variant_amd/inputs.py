@@ -55,10 +55,12 @@ class MTAConfig:
     seed: int = 0
     gn_eps: float = 1e-5
     gn_random: bool = False
+    gated: bool = False   # per-head sigmoid gate on the GroupNorm output
+    gate_std: float = 1.0  # spread of the gate logits g_h ~ N(0, gate_std^2)
 
     @property
     def depth_scale(self) -> float:
-        # the layer-dependent depth scale: 1 / sqrt(layer)
+        # the layer-dependent depth scale: 1 / sqrt(layer) (1 for layer 1)
         return 1.0 / math.sqrt(self.layer)
 
     @property
@@ -111,6 +113,8 @@ def _configs() -> Dict[str, MTAConfig]:
     c["needle4k"] = MTAConfig("needle4k", B=2, H=16, T=4096, d=128, c_q=6, c_k=11, c_h=2,
                               dtype="bf16", qkv_std=s, theta_std=0.02, head_std=0.02,
                               layer=4, needles=6, seed=1003)
+    # the same layer with the sigmoid-gated GroupNorm (no depth scale)
+    c["needle4k_gated"] = replace(c["needle4k"], name="needle4k_gated", layer=1, gated=True)
     for (cq, ck) in ((4, 9), (6, 11), (8, 15)):
         for ch in (2, 4):
             for kq in (PRE, POST):
@@ -140,7 +144,8 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
 
     Order of draws from ``torch.Generator().manual_seed(cfg.seed)``: Q, K, V,
     key-query kernel noise, head kernel noise, GroupNorm affine (only if
-    ``gn_random``), then the needle positions and directions.  Q, K, V are drawn
+    ``gn_random``), per-head gate logits (only if ``gated``), then the needle
+    positions and directions.  Q, K, V are drawn
     in fp32 and rounded to the run dtype (round to nearest even); kernels and
     GroupNorm parameters stay fp32.
     """
@@ -161,6 +166,11 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
     else:
         gn_w = torch.ones((cfg.H, cfg.d))
         gn_b = torch.zeros((cfg.H, cfg.d))
+
+    gate = None
+    if cfg.gated:
+        # gate logits centred on sigma(g) = 1/2
+        gate = cfg.gate_std * torch.randn((cfg.H,), generator=g)
 
     if cfg.needles:
         # Multi-needle retrieval stand-in: per batch row, `needles` key
@@ -185,6 +195,8 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
         "gn_w": gn_w.float().contiguous(),
         "gn_b": gn_b.float().contiguous(),
     }
+    if gate is not None:
+        out["gate"] = gate.float().contiguous()
     if device != "cpu":
         out = {kk: t.to(device) for kk, t in out.items()}
     return out

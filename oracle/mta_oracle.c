@@ -12,7 +12,8 @@
  * Sentence-Based Technical Breakdown", subsections
  *   - "Standard Multi-Head Attention"       (logits, causal softmax, A·V)
  *   - "Key-Query Convolution"               (Conv2d_theta, Eq. 4, two-pass
- *                                             masking, post-softmax variant)
+ *                                             masking, post-softmax variant,
+ *                                             Eq. 4's exact causal indicator)
  *   - "Head Mixing Convolution"             (Eq. 7 and its pre-softmax form)
  *   - "Putting Everything Together"         (composition order)
  *   - "Group Normalization with Sigmoid Gating" (GroupNorm per head; the
@@ -50,6 +51,7 @@
 
 #define ORACLE_PRE 0
 #define ORACLE_POST 1
+#define ORACLE_PRE_EXACT 2   /* before the softmax, Eq. 4 with its indicator */
 
 /* Optional planted mistakes, used only by the oracle's own mutation test to
  * show that the pins catch them.  The default build has ORACLE_MUTANT == 0. */
@@ -95,15 +97,21 @@ static void step_mask_zero(double *X, int T, int a0, int a1)
 }
 
 /* Step 3.  Conv2d_theta over the (query, key) plane of one head
- * ("Key-Query Convolution", the expanded form Eq. 4 without its indicator,
- * applied to the masked map as the two-pass scheme prescribes):
+ * ("Key-Query Convolution", the expanded form Eq. 4):
  *   Y[i][j] = sum_{i'=0}^{c_q-1} sum_{j'=-floor(c_k/2)}^{ceil(c_k/2)-1}
- *                 theta[i'][j' + floor(c_k/2)] * X[i-i'][j-j']
- * with X = 0 outside [0,T) x [0,T).  X holds rows [x0, x0+nx); the caller
- * passes every row in [0,T) the sum can reach from output rows [i0,i1) (a row
- * it does not hold yields NaN rather than a silent zero). */
+ *                 [indicator] theta[i'][j' + floor(c_k/2)] * X[i-i'][j-j']
+ * with X = 0 outside [0,T) x [0,T).
+ *   indicator == 0: no indicator; the two-pass scheme applies it to the map
+ *                   already masked by Mask_0 (and the post-softmax variant to
+ *                   probabilities, which are 0 in the future);
+ *   indicator == 1: Eq. 4's causal indicator 1{i >= j - j'}: a tap counts only
+ *                   if its key is not in the future of the OUTPUT query i; X is
+ *                   then the unmasked logit map.
+ * X holds rows [x0, x0+nx); the caller passes every row in [0,T) the sum can
+ * reach from output rows [i0,i1) (a row it does not hold yields NaN rather
+ * than a silent zero). */
 static void step_kq_conv(const double *X, int T, int x0, int nx,
-                         const double *theta, int c_q, int c_k,
+                         const double *theta, int c_q, int c_k, int indicator,
                          int i0, int i1, double *Y)
 {
     const int jlo = -(c_k / 2);            /* -floor(c_k/2)      */
@@ -129,6 +137,11 @@ static void step_kq_conv(const double *X, int T, int x0, int nx,
                     const int cidx = j - jp;
 #endif
                     if (cidx < 0 || cidx >= T) continue;  /* zero padding */
+#if ORACLE_MUTANT == 9 /* planted: indicator taken against the input row */
+                    if (indicator && cidx > r) continue;
+#else
+                    if (indicator && cidx > i) continue;  /* 1{i >= j - j'} */
+#endif
 #if ORACLE_MUTANT == 5 /* planted: kernel read transposed in its key axis */
                     const double th = theta[ip * c_k + (c_k - 1 - (jp - jlo))];
 #else
@@ -230,8 +243,9 @@ static void step_groupnorm_scale(const double *O, const double *gw, const double
 /* ------------------------------------------------------------------------ */
 /* Composition for one (batch b, head group g) unit and output rows [r0, r1)
  * ("Putting Everything Together"): logits -> [kq conv pre: Mask_0, Conv2d,
- * then Mask_-inf] -> [head mix pre] -> softmax -> [kq conv post: Conv2d then
- * Mask_0] -> [head mix post] -> A V -> GroupNorm x depth scale.
+ * then Mask_-inf; or, exact form, Conv2d with Eq. 4's indicator on the
+ * unmasked logits, then Mask_-inf] -> [head mix pre] -> softmax -> [kq conv
+ * post: Conv2d then Mask_0] -> [head mix post] -> A V -> GroupNorm x scale.
  *
  * Every stage is an explicit matrix over the extended rows [e0, r1) (the
  * key-query convolution looks c_q-1 query rows back) and all T key columns.
@@ -277,7 +291,7 @@ static int unit_rows(const oracle_cfg *cf, const double *q, const double *k, con
      * key-query convolution before the softmax only the output rows are (the
      * convolution of a halo row would need rows further back); with it after
      * the softmax, the softmax must cover the halo rows too. */
-    const int v0 = (cf->kq_place == ORACLE_PRE) ? r0 : e0;
+    const int v0 = (cf->kq_place == ORACLE_POST) ? e0 : r0;
     const size_t voff = (size_t)(v0 - e0) * T;
     const size_t nv = (size_t)(r1 - v0) * T;
     int rc = 0;
@@ -309,15 +323,19 @@ static int unit_rows(const oracle_cfg *cf, const double *q, const double *k, con
     }
 
     /* A1 <- the map that enters the softmax.
-     *   kq PRE : Conv2d(Mask_0(S)) on rows [r0, r1)
-     *   kq POST: S itself on rows [e0, r1) */
+     *   kq PRE      : Conv2d(Mask_0(S)) on rows [r0, r1)
+     *   kq PRE_EXACT: Conv2d with the indicator, on S itself, rows [r0, r1)
+     *   kq POST     : S itself on rows [e0, r1) */
     for (int a = 0; a < c_h; ++a) {
         const int h = g * c_h + a;
         if (cf->kq_place == ORACLE_PRE) {
             memcpy(A2[a], S[a], ext * sizeof(double));
             step_mask_zero(A2[a], T, e0, r1);
             step_kq_conv(A2[a], T, e0, ne, theta_kq + (size_t)h * cf->c_q * cf->c_k,
-                         cf->c_q, cf->c_k, r0, r1, A1[a] + off);
+                         cf->c_q, cf->c_k, 0, r0, r1, A1[a] + off);
+        } else if (cf->kq_place == ORACLE_PRE_EXACT) {
+            step_kq_conv(S[a], T, e0, ne, theta_kq + (size_t)h * cf->c_q * cf->c_k,
+                         cf->c_q, cf->c_k, 1, r0, r1, A1[a] + off);
         } else {
             memcpy(A1[a], S[a], ext * sizeof(double));
         }
@@ -348,7 +366,7 @@ static int unit_rows(const oracle_cfg *cf, const double *q, const double *k, con
         for (int a = 0; a < c_h; ++a) {
             const int h = g * c_h + a;
             step_kq_conv(A2[a], T, e0, ne, theta_kq + (size_t)h * cf->c_q * cf->c_k,
-                         cf->c_q, cf->c_k, r0, r1, A3[a] + off);
+                         cf->c_q, cf->c_k, 0, r0, r1, A3[a] + off);
             step_mask_zero(A3[a] + off, T, r0, r1);
             memcpy(A2[a] + off, A3[a] + off, (size_t)nr * T * sizeof(double));
         }
@@ -396,7 +414,7 @@ static int check_cfg(const oracle_cfg *c)
 {
     if (c->B < 0 || c->H <= 0 || c->T < 0 || c->d <= 0) return -2;
     if (c->c_q < 1 || c->c_k < 1 || c->c_h < 1 || c->H % c->c_h) return -2;
-    if ((c->kq_place != 0 && c->kq_place != 1) || (c->head_place != 0 && c->head_place != 1)) return -3;
+    if (c->kq_place < 0 || c->kq_place > 2 || (c->head_place != 0 && c->head_place != 1)) return -3;
     return 0;
 }
 

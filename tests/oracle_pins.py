@@ -17,7 +17,9 @@ Facts used (page "Multi-Token Attention — Paper Graph", section 3.4):
   * pre-softmax head mixing is a sum of logits, i.e. one attention over
     concatenated features;
   * Eq. 4 written directly over query/key vectors, with the two-pass mask's
-    indicator (the input position must not be in its own row's future);
+    indicator (the input position must not be in its own row's future), and
+    with Eq. 4's own indicator (the key must not be in the output row's
+    future);
   * softmax rows are distributions over j <= i; causality;
   * hand-derived closed forms in tests/golden/hand_cases.json;
   * brute force at T <= 8 from the definitions.
@@ -73,7 +75,8 @@ def pin_identity_is_causal_attention(lib):
     """Identity kernels: MTA == GroupNorm(SDPA(q,k,v, causal)) x depth scale,
     for every placement of the two convolutions, ragged T and c_h in {1,2,4}."""
     for (kq, hd, ch, T, cq, ck) in [(I.PRE, I.POST, 2, 37, 3, 5), (I.POST, I.POST, 2, 29, 2, 3),
-                                    (I.PRE, I.PRE, 4, 23, 4, 4), (I.POST, I.PRE, 1, 19, 3, 7)]:
+                                    (I.PRE, I.PRE, 4, 23, 4, 4), (I.POST, I.PRE, 1, 19, 3, 7),
+                                    (I.PRE_EXACT, I.POST, 2, 31, 3, 6)]:
         cfg = I.small(B=2, H=4, T=T, d=8, c_q=cq, c_k=ck, c_h=ch, kq_place=kq,
                       head_place=hd, gn_random=True, layer=3, seed=11 + T)
         inp = _identity_inputs(cfg)
@@ -162,6 +165,46 @@ def _eq4_two_pass(q, k, theta, i, j, d):
     return tot
 
 
+def _eq4_exact(q, k, theta, i, j, d):
+    """Eq. 4 summed over vectors with its own indicator 1{i >= j-j'}: tap
+    (i',j') contributes iff both indices are >= 0 and the key is not in the
+    future of the output query i."""
+    c_q, c_k = theta.shape
+    tot = 0.0
+    for ip in range(c_q):
+        for jp in range(-(c_k // 2), (c_k + 1) // 2):
+            a, bb = i - ip, j - jp
+            if a < 0 or bb < 0 or bb > i:
+                continue
+            tot += theta[ip, jp + c_k // 2] * float(np.dot(q[a], k[bb])) / math.sqrt(d)
+    return tot
+
+
+def pin_eq4_exact_indicator(lib):
+    """The exact form: the convolved logit map equals Eq. 4 with its indicator,
+    evaluated on query/key vectors at every causal (i, j); it differs from the
+    two-pass map on the diagonal band and equals it off the band.  Random
+    asymmetric kernel, odd and even c_k, c_q > 1."""
+    for (cq, ck, T) in [(3, 5, 19), (4, 4, 15)]:
+        cfg = I.small(B=1, H=2, T=T, d=4, c_q=cq, c_k=ck, c_h=2, theta_std=0.7, seed=41 + ck,
+                      kq_place=I.PRE_EXACT)
+        inp = I.generate(cfg)
+        C = oracle.stages_cfg(cfg, inp, lib=lib)["C"]
+        C2 = oracle.stages_cfg(I.with_(cfg, kq_place=I.PRE), inp, lib=lib)["C"]
+        q = inp["q"].double().numpy()[0]
+        k = inp["k"].double().numpy()[0]
+        th = inp["theta_kq"].double().numpy()
+        band = cq - 1 + ck // 2
+        for h in range(2):
+            for i in range(T):
+                for j in range(i + 1):
+                    ref = _eq4_exact(q[h], k[h], th[h], i, j, cfg.d)
+                    assert abs(C[h, i, j] - ref) <= 1e-12, ("eq4 exact", cq, ck, h, i, j, C[h, i, j], ref)
+                    if j < i - band + 1:
+                        assert abs(C[h, i, j] - C2[h, i, j]) <= 1e-12, ("off-band", i, j)
+            assert np.max(np.abs(C[h] - C2[h])) > 1e-3, "the two forms must differ on the band"
+
+
 def pin_eq4_vector_form(lib):
     """The convolved logit map (kq pre-softmax) equals Eq. 4 evaluated directly on
     query/key vectors with the two-pass indicator, at every causal (i, j); off
@@ -210,7 +253,8 @@ def pin_softmax_rows_are_distributions(lib):
 
 def pin_causality(lib):
     """Changing q, k, v at positions > t leaves out[..., :t+1, :] bitwise equal."""
-    for (kq, hd) in [(I.PRE, I.POST), (I.POST, I.POST), (I.PRE, I.PRE), (I.POST, I.PRE)]:
+    for (kq, hd) in [(I.PRE, I.POST), (I.POST, I.POST), (I.PRE, I.PRE), (I.POST, I.PRE),
+                     (I.PRE_EXACT, I.POST)]:
         cfg = I.small(B=1, H=4, T=33, d=8, c_q=4, c_k=7, c_h=2, kq_place=kq, head_place=hd, seed=23)
         inp = I.generate(cfg)
         base = oracle.forward_cfg(cfg, inp, lib=lib, threads=2)
@@ -255,12 +299,12 @@ def _brute(q, k, v, th, w, gw, gb, c_q, c_k, c_h, kq, hd, eps, ds):
     out = np.zeros_like(q)
     lo, hi = -(c_k // 2), (c_k + 1) // 2 - 1
 
-    def conv(Xh, h, i, j):
+    def conv(Xh, h, i, j, exact=False):
         s = 0.0
         for ip in range(c_q):
             for jp in range(lo, hi + 1):
                 a, bb = i - ip, j - jp
-                if 0 <= a < T and 0 <= bb < T:
+                if 0 <= a < T and 0 <= bb < T and (bb <= i or not exact):
                     s += th[h, ip, jp - lo] * Xh[a][bb]
         return s
 
@@ -272,6 +316,8 @@ def _brute(q, k, v, th, w, gw, gb, c_q, c_k, c_h, kq, hd, eps, ds):
             if kq == I.PRE:
                 M0 = {h: [[S[h][a][j] if j <= a else 0.0 for j in range(T)] for a in range(T)] for h in hs}
                 L = {h: [[conv(M0[h], h, i, j) for j in range(T)] for i in range(T)] for h in hs}
+            elif kq == I.PRE_EXACT:
+                L = {h: [[conv(S[h], h, i, j, exact=True) for j in range(T)] for i in range(T)] for h in hs}
             else:
                 L = S
             if hd == I.PRE:
@@ -307,7 +353,8 @@ def pin_brute_force_tiny(lib):
     c_q > T, even c_k."""
     for (kq, hd, T, cq, ck, ch) in [(I.PRE, I.POST, 8, 3, 5, 2), (I.POST, I.POST, 7, 2, 3, 2),
                                     (I.PRE, I.PRE, 6, 9, 4, 2), (I.POST, I.PRE, 5, 3, 6, 4),
-                                    (I.PRE, I.POST, 1, 2, 3, 1)]:
+                                    (I.PRE, I.POST, 1, 2, 3, 1), (I.PRE_EXACT, I.POST, 8, 3, 5, 2),
+                                    (I.PRE_EXACT, I.PRE, 6, 9, 4, 2)]:
         cfg = I.small(B=2, H=4, T=T, d=4, c_q=cq, c_k=ck, c_h=ch, kq_place=kq, head_place=hd,
                       theta_std=0.5, head_std=0.5, gn_random=True, layer=2, seed=31 + T)
         inp = I.generate(cfg)
@@ -325,6 +372,7 @@ ALL_PINS = [
     pin_diff_transformer_special_case,
     pin_pre_softmax_head_mix_is_concat_attention,
     pin_eq4_vector_form,
+    pin_eq4_exact_indicator,
     pin_softmax_rows_are_distributions,
     pin_causality,
     pin_hand_cases,

@@ -16,6 +16,7 @@ MUTANTS = {
     6: "head-mix matrix transposed",
     7: "softmax rows not normalised",
     8: "head gate used without its sigmoid",
+    9: "exact indicator taken against the input row",
 }
 
 

@@ -27,6 +27,7 @@ import torch
 
 PRE = 0
 POST = 1
+PRE_EXACT = 2   # key-query convolution before the softmax with Eq. 4's exact indicator
 F32 = 0
 BF16 = 1
 
@@ -92,7 +93,7 @@ class MTAConfig:
         return 4 * self.B * self.H * self.T * self.d * el
 
     def short(self) -> str:
-        kq = "pre" if self.kq_place == PRE else "post"
+        kq = {PRE: "pre", POST: "post", PRE_EXACT: "exact"}[self.kq_place]
         hd = "pre" if self.head_place == PRE else "post"
         return (f"{self.name}:B{self.B}H{self.H}T{self.T}d{self.d}"
                 f"_cq{self.c_q}ck{self.c_k}ch{self.c_h}_kq{kq}_head{hd}_{self.dtype}")

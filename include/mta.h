@@ -7,7 +7,10 @@
  *      Attention");
  *   2. key-query convolution Conv2d_theta over the (query, key) plane of each
  *      head, kernel c_q x c_k, either before the softmax with two-pass masking
- *      Softmax(Mask_-inf(Conv2d(Mask_0(Ahat)))), or after it,
+ *      Softmax(Mask_-inf(Conv2d(Mask_0(Ahat)))), or before it in the exact
+ *      form of Eq. 4, whose indicator 1{i >= j-j'} keeps a tap iff its key is
+ *      not in the future of the output query i (the unmasked logits are
+ *      convolved, then Mask_-inf), or after it,
  *      Mask_0(Conv2d(Softmax(Mask_-inf(Ahat))))     ("Key-Query Convolution",
  *      Eq. 4 and the two-pass / post-softmax forms);
  *   3. head mixing within non-overlapping groups of c_h heads,
@@ -43,9 +46,12 @@
 extern "C" {
 #endif
 
-/* Placement of a convolution relative to the softmax. */
+/* Placement of a convolution relative to the softmax.  MTA_PRE_SOFTMAX_EXACT
+ * is valid for kq_place only: the key-query convolution before the softmax
+ * with Eq. 4's exact causal indicator instead of the two-pass masks. */
 #define MTA_PRE_SOFTMAX 0
 #define MTA_POST_SOFTMAX 1
+#define MTA_PRE_SOFTMAX_EXACT 2
 
 /* Element type of q, k, v and out.  Kernels and GroupNorm parameters are
  * always float32; all intermediate arithmetic is float32 (contractions
@@ -58,7 +64,7 @@ extern "C" {
 #define MTA_OK 0
 #define MTA_ERR_NULL_ARG -1      /* a required pointer is NULL                 */
 #define MTA_ERR_BAD_SHAPE -2     /* B,H,T < 0, H % c_h != 0, kernel size < 1   */
-#define MTA_ERR_BAD_PLACEMENT -3 /* kq_place / head_place not 0 or 1           */
+#define MTA_ERR_BAD_PLACEMENT -3 /* kq_place not 0..2 or head_place not 0..1  */
 #define MTA_ERR_BAD_DTYPE -4     /* dtype not MTA_F32 / MTA_BF16               */
 #define MTA_ERR_MISALIGNED -5    /* a tensor pointer is not 16-byte aligned    */
 #define MTA_ERR_UNSUPPORTED -6   /* valid but outside this build's limits:
@@ -77,7 +83,8 @@ typedef struct mta_config {
     int32_t c_q;        /* key-query kernel size along queries, 1..16         */
     int32_t c_k;        /* key-query kernel size along keys, 1..31            */
     int32_t c_h;        /* heads per mixing group, 1, 2 or 4                   */
-    int32_t kq_place;   /* MTA_PRE_SOFTMAX (two-pass masking) | MTA_POST_SOFTMAX */
+    int32_t kq_place;   /* MTA_PRE_SOFTMAX (two-pass masking) | MTA_POST_SOFTMAX
+                           | MTA_PRE_SOFTMAX_EXACT (Eq. 4's indicator)     */
     int32_t head_place; /* MTA_PRE_SOFTMAX | MTA_POST_SOFTMAX                  */
     int32_t dtype;      /* MTA_F32 | MTA_BF16                                  */
     float gn_eps;       /* GroupNorm epsilon (> 0), e.g. 1e-5                  */

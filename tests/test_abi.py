@@ -53,7 +53,8 @@ def cfg(**kw):
     (dict(B=0), 0), (dict(T=0), 0),
     (dict(B=-1), -2), (dict(T=-5), -2), (dict(H=0), -2), (dict(d=0), -2),
     (dict(c_q=0), -2), (dict(c_k=0), -2), (dict(c_h=0), -2), (dict(H=6, c_h=4), -2),
-    (dict(kq_place=2), -3), (dict(head_place=-1), -3),
+    (dict(kq_place=2), 0), (dict(kq_place=3), -3), (dict(kq_place=-1), -3),
+    (dict(head_place=-1), -3), (dict(head_place=2), -3),
     (dict(dtype=7), -4),
     (dict(gn_eps=0.0), -8), (dict(gn_eps=float("nan")), -8), (dict(depth_scale=float("inf")), -8),
     (dict(d=96), -6), (dict(d=256), -6), (dict(H=8, c_h=8), -6), (dict(H=3, c_h=3), -6),

@@ -67,6 +67,24 @@ def _small_cases():
         c.append(I.small(f"gated_bf16_kq{kq}", B=1, H=4, T=130, d=128, c_q=6, c_k=11, c_h=2, kq_place=kq,
                          dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True,
                          seed=710 + kq))
+    # key-query convolution with Eq. 4's exact indicator: fast and runtime-sized
+    # stencils, odd and even c_k, pre-softmax head mix, c_h = 4, both dtypes
+    E = I.PRE_EXACT
+    c.append(I.small("exact_f32_d32_3x5", B=2, H=4, T=100, d=32, c_q=3, c_k=5, c_h=2, kq_place=E,
+                     theta_std=0.3, seed=801))
+    c.append(I.small("exact_f32_d64_2x9_ch4", B=1, H=4, T=130, d=64, c_q=2, c_k=9, c_h=4, kq_place=E,
+                     theta_std=0.3, seed=802))
+    c.append(I.small("exact_f32_d64_5x4_hpre", B=1, H=4, T=77, d=64, c_q=5, c_k=4, c_h=2, kq_place=E,
+                     head_place=P, theta_std=0.3, seed=803))
+    c.append(I.small("exact_f32_16x31", B=1, H=2, T=150, d=64, c_q=16, c_k=31, c_h=1, kq_place=E,
+                     seed=804))
+    for (cq, ck) in ((6, 11), (4, 9), (8, 15), (1, 1)):
+        c.append(I.small(f"exact_bf16_{cq}x{ck}", B=1, H=4, T=197, d=128, c_q=cq, c_k=ck, c_h=2,
+                         kq_place=E, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05,
+                         seed=810 + cq))
+    c.append(I.small("exact_bf16_5x4_d64", B=2, H=4, T=77, d=64, c_q=5, c_k=4, c_h=2, kq_place=E,
+                     dtype="bf16", seed=820))
+    c.append(I.small("exact_f32_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, kq_place=E, seed=821))
     # tiny sequences: T = 1, T < c_q, exactly one tile, one tile + 1
     for T in (1, 3, 64, 65):
         c.append(I.small(f"f32_T{T}", B=2, H=2, T=T, d=32, c_q=3, c_k=5, c_h=2, seed=500 + T))
@@ -98,7 +116,7 @@ def test_workload_fp32_full(name):
     _say(f"[parity]   max abs err {err:.3e} (tol {tol:.1e})")
 
 
-@pytest.mark.parametrize("name", ["layer2k", "needle4k", "needle4k_gated"] + I.SWEEP)
+@pytest.mark.parametrize("name", ["layer2k", "needle4k", "needle4k_gated", "needle4k_exact"] + I.SWEEP)
 def test_workload_bf16_sampled(name):
     cfg = I.CONFIGS[name]
     _say(f"[parity] sampled {cfg.short()}")
@@ -111,7 +129,7 @@ def test_workload_bf16_sampled(name):
     _say(f"[parity]   rows {ranges} units {units}: max abs err {err:.3e} (tol {tol:.2e})")
 
 
-@pytest.mark.parametrize("name", ["needle4k", "sweep8k_8x15_ch4_post"])
+@pytest.mark.parametrize("name", ["needle4k", "needle4k_exact", "sweep8k_8x15_ch4_post"])
 def test_causality_full_size(name):
     """Perturbing q, k, v after position t leaves out[..., :t+1, :] bitwise equal."""
     cfg = I.CONFIGS[name]

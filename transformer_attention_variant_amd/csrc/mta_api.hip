@@ -17,7 +17,8 @@ int validate(const mta_config *c)
     if (!c) return MTA_ERR_NULL_ARG;
     if (c->batch < 0 || c->heads < 1 || c->seq_len < 0 || c->head_dim < 1) return MTA_ERR_BAD_SHAPE;
     if (c->c_q < 1 || c->c_k < 1 || c->c_h < 1 || c->heads % c->c_h != 0) return MTA_ERR_BAD_SHAPE;
-    if ((c->kq_place != MTA_PRE_SOFTMAX && c->kq_place != MTA_POST_SOFTMAX) ||
+    if ((c->kq_place != MTA_PRE_SOFTMAX && c->kq_place != MTA_POST_SOFTMAX &&
+         c->kq_place != MTA_PRE_SOFTMAX_EXACT) ||
         (c->head_place != MTA_PRE_SOFTMAX && c->head_place != MTA_POST_SOFTMAX))
         return MTA_ERR_BAD_PLACEMENT;
     if (c->dtype != MTA_F32 && c->dtype != MTA_BF16) return MTA_ERR_BAD_DTYPE;
@@ -62,7 +63,7 @@ const char *mta_status_string(int s)
     case MTA_OK: return "ok";
     case MTA_ERR_NULL_ARG: return "a required pointer is NULL";
     case MTA_ERR_BAD_SHAPE: return "invalid shape (B,H,T,d, kernel sizes, or H not a multiple of c_h)";
-    case MTA_ERR_BAD_PLACEMENT: return "convolution placement must be pre- (0) or post-softmax (1)";
+    case MTA_ERR_BAD_PLACEMENT: return "placement must be pre- (0) or post-softmax (1), or exact pre-softmax (2) for kq";
     case MTA_ERR_BAD_DTYPE: return "dtype must be MTA_F32 or MTA_BF16";
     case MTA_ERR_MISALIGNED: return "tensor pointer not aligned (16 bytes for q,k,v,out; 4 for float params)";
     case MTA_ERR_UNSUPPORTED: return "configuration outside this build's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
@@ -86,6 +87,7 @@ static int forward_impl(const void *q, const void *k, const void *v, const float
 
     const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
     const int post = cfg->kq_place == MTA_POST_SOFTMAX;
+    const int exact = cfg->kq_place == MTA_PRE_SOFTMAX_EXACT;
     const int hpre = cfg->head_place == MTA_PRE_SOFTMAX;
 
     mta::Params p;
@@ -97,6 +99,7 @@ static int forward_impl(const void *q, const void *k, const void *v, const float
     p.units = cfg->batch * p.G;
     p.n_qt = (cfg->seq_len + mta::BM - 1) / mta::BM;
     p.head_pre = cfg->head_place == MTA_PRE_SOFTMAX;
+    p.exact = exact;
     p.hl = (ck + 1) / 2 - 1;
     p.ncb = (mta::BN + ck - 1 + 15) / 16;
     p.pitch = p.ncb * 16 + 4;
@@ -118,7 +121,7 @@ static int forward_impl(const void *q, const void *k, const void *v, const float
             // 16-key output block: the tile must span at least 80 columns
             p.ncb = (ms && ncb0 < 5) ? 5 : ncb0;
             p.pitch = p.ncb * 16 + 4;
-            fn = mta::find_launch_v2(d, ch, cq, ck, post, hpre, ms);
+            fn = mta::find_launch_v2(d, ch, cq, ck, post, exact, hpre, ms);
             if (fn) {
                 lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0).total;
                 if (lds > 160 * 1024) fn = nullptr;

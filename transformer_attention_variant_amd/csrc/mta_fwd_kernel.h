@@ -4,6 +4,9 @@
 //   S = Q K^T / sqrt(d)                               ("Standard Multi-Head Attention")
 //   kq PRE : L = Mask_-inf(Conv2d_theta(Mask_0(S)))  (two-pass masking, "Key-Query
 //            Convolution"), P = softmax(L)
+//            or, exact form, L = Mask_-inf(Eq. 4 with its indicator 1{i >= j-j'})
+//            on the unmasked S: a tap counts iff its key is not in the future of
+//            the output query (p.exact)
 //   kq POST: P = Mask_0(Conv2d_theta(softmax(Mask_-inf(S))))   (post-softmax variant)
 //   head mix PRE (logits) or POST (probabilities), Eq. 7, groups of c_h heads
 //   O = P V per head, then GroupNorm over d x depth scale.
@@ -53,6 +56,7 @@ struct Params {
     void *out;
     int H, T, c_q, c_k, G, units, n_qt;
     int head_pre;         // head mix before the softmax
+    int exact;            // kq before the softmax with Eq. 4's exact indicator
     int ncb;              // 16-wide column blocks of the logit tile
     int pitch;            // floats per logit-tile row in LDS
     int hl;               // left key halo = ceil(c_k/2) - 1
@@ -165,19 +169,22 @@ struct FragOf<float, D> {
 // ---------------------------------------------------------------------------
 // Store one 16x16 logit block into the LDS tile.  Tile row rho <-> query
 // i0 - HALO + rho, tile column e <-> key j0 - hl + e.  Mode RAW writes
-// x = S*log2(e)/sqrt(d) where the key is causal for its query (0 <= key <=
-// query < T) and 0 elsewhere (Mask_0 and the zero padding of the convolution).
-// Mode PROB writes the probability exp2(x - m_rho) / l_rho there instead.
+// x = S*log2(e)/sqrt(d) where 0 <= key <= kmax and 0 <= query < T, 0 elsewhere:
+// kmax = query gives Mask_0 and the zero padding of the convolution; with
+// `exact` kmax = T-1 keeps the future logits (Eq. 4's indicator is then applied
+// per output row by the stencil).  Mode PROB writes the probability
+// exp2(x - m_rho) / l_rho where the key is causal instead.
 enum TileMode { RAW = 0, PROB = 1 };
 
 template <int MODE>
 __device__ inline void store_block(float *buf, int pitch, int rb, int cb, f32x4 acc, int i0, int j0,
                                    int hl, int T, float sc, const float *st_m, const float *st_il,
-                                   int lane)
+                                   int exact, int lane)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
     const int qi = i0 - HALO + rho;
+    const int kmax = (MODE == RAW && exact) ? T - 1 : qi;
     float m = 0.f, il = 0.f;
     if (MODE == PROB) {
         m = st_m[rho];
@@ -187,7 +194,7 @@ __device__ inline void store_block(float *buf, int pitch, int rb, int cb, f32x4 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kj = j0 - hl + e0 + r;
-        const bool ok = (kj >= 0) && (kj <= qi) && (qi < T);
+        const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
         float x = acc[r] * sc;
         if (MODE == PROB) x = __builtin_amdgcn_exp2f(x - m) * il;
         o[r] = ok ? x : 0.f;
@@ -210,7 +217,8 @@ __device__ inline void logit_tile(float *buf, const Params &p, const DT *qh, con
     for (int cb = 0; cb < p.ncb; ++cb) {
         load_frag<D>(kf, kh, kcol + cb * 16, p.T, lane);
         const f32x4 acc = qk_mfma<D>(kf, qf);
-        store_block<MODE>(buf, p.pitch, 1 + wave, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+        store_block<MODE>(buf, p.pitch, 1 + wave, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, p.exact,
+                          lane);
     }
     // halo rows, only if the kernel reaches back (c_q > 1)
     if (p.c_q > 1) {
@@ -218,7 +226,8 @@ __device__ inline void logit_tile(float *buf, const Params &p, const DT *qh, con
         for (int cb = wave; cb < p.ncb; cb += 4) {
             load_frag<D>(kf, kh, kcol + cb * 16, p.T, lane);
             const f32x4 acc = qk_mfma<D>(kf, qf);
-            store_block<MODE>(buf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+            store_block<MODE>(buf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, p.exact,
+                              lane);
         }
     }
 }
@@ -229,10 +238,13 @@ __device__ inline void logit_tile(float *buf, const Params &p, const DT *qh, con
 // (tile column jb + o + c_k - 1 - jj holds key j - j' for output key j and
 // j' = jj - floor(c_k/2), since the tile starts hl = ceil(c_k/2)-1 keys left).
 // The kernel weights come from LDS (`th`, rows of `ckp` floats, ckp a multiple
-// of 4), read as broadcast vectors.
+// of 4), read as broadcast vectors.  Window entries t > tlim (tile column
+// jb + t) are taken as 0: with Eq. 4's indicator tlim is the last column whose
+// key is not in the future of this lane's output query; the tile already holds
+// 0 there in the two-pass form, which passes tlim >= the window length.
 template <int CQ, int CK>
 __device__ inline void stencil16(const float *buf, int pitch, int rho, int jb, const float *th,
-                                 int, int, int, float out[16])
+                                 int, int, int, int tlim, float out[16])
 {
     constexpr int NW = 16 + CK - 1;
     constexpr int NW4 = (NW + 3) / 4;
@@ -254,6 +266,10 @@ __device__ inline void stencil16(const float *buf, int pitch, int rho, int jb, c
             win[4 * t + 2] = x[2];
             win[4 * t + 3] = x[3];
         }
+        if (tlim < NW - 1) {
+#pragma unroll
+            for (int t = 0; t < NW; ++t) win[t] = (t <= tlim) ? win[t] : 0.f;
+        }
 #pragma unroll
         for (int t = 0; t < CK4; ++t) {
             const f32x4 x = trow[t];
@@ -273,16 +289,31 @@ __device__ inline void stencil16(const float *buf, int pitch, int rho, int jb, c
 // Runtime-sized variant (any c_q <= 16, c_k <= 31): same sum, read tap by tap.
 template <>
 __device__ inline void stencil16<0, 0>(const float *buf, int pitch, int rho, int jb, const float *th,
-                                       int cq, int ck, int ckp, float out[16])
+                                       int cq, int ck, int ckp, int tlim, float out[16])
 {
 #pragma unroll
     for (int o = 0; o < 16; ++o) out[o] = 0.f;
-    for (int ip = 0; ip < cq; ++ip) {
-        const float *row = buf + (rho - ip) * pitch + jb + ck - 1;
-        for (int jj = 0; jj < ck; ++jj) {
-            const float tv = th[ip * ckp + jj];
+    if (tlim >= 16 + ck - 2) {
+        for (int ip = 0; ip < cq; ++ip) {
+            const float *row = buf + (rho - ip) * pitch + jb + ck - 1;
+            for (int jj = 0; jj < ck; ++jj) {
+                const float tv = th[ip * ckp + jj];
 #pragma unroll
-            for (int o = 0; o < 16; ++o) out[o] = __builtin_fmaf(tv, row[o - jj], out[o]);
+                for (int o = 0; o < 16; ++o) out[o] = __builtin_fmaf(tv, row[o - jj], out[o]);
+            }
+        }
+    } else {
+        // window position of row[o - jj] is ck - 1 + o - jj
+        for (int ip = 0; ip < cq; ++ip) {
+            const float *row = buf + (rho - ip) * pitch + jb + ck - 1;
+            for (int jj = 0; jj < ck; ++jj) {
+                const float tv = th[ip * ckp + jj];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) {
+                    const float x = (ck - 1 + o - jj <= tlim) ? row[o - jj] : 0.f;
+                    out[o] = __builtin_fmaf(tv, x, out[o]);
+                }
+            }
         }
     }
 }
@@ -472,9 +503,12 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
         m_c[a] = NEG_INF; l_c[a] = 0.f; m_h[a] = NEG_INF; l_h[a] = 0.f;
     }
 
+    constexpr int NOLIM = 1 << 30;
     for (int kt = 0; kt <= qt; ++kt) {
         const int j0 = kt * BN;
         const int key0 = j0 + jb;
+        // last window column whose key is not in this row's future (exact form)
+        const int tlim = p.exact ? qabs - (j0 - p.hl + jb) : NOLIM;
         if (!KQ_POST) {
             if (HPRE) {
                 float c[CH][16];
@@ -484,7 +518,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
                     logit_tile<DT, D, RAW>(sbuf, p, Q + base0 + a * hstride, K + base0 + a * hstride,
                                            i0, j0, nullptr, nullptr, wave, lane);
                     __syncthreads();
-                    stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, c[a]);
+                    stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, tlim, c[a]);
                 }
                 head_mix16<CH>(c, w_s);
 #pragma unroll
@@ -497,7 +531,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
                     logit_tile<DT, D, RAW>(sbuf, p, Q + base0 + a * hstride, K + base0 + a * hstride,
                                            i0, j0, nullptr, nullptr, wave, lane);
                     __syncthreads();
-                    stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, c);
+                    stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, tlim, c);
                     stats_update(c, key0, qabs, m_c[a], l_c[a]);
                 }
             }
@@ -582,6 +616,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
     for (int kt = 0; kt <= qt; ++kt) {
         const int j0 = kt * BN;
         const int key0 = j0 + jb;
+        const int tlim = p.exact ? qabs - (j0 - p.hl + jb) : NOLIM;
         float pr[CH][16];
         if (!KQ_POST) {
 #pragma unroll
@@ -590,7 +625,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
                 logit_tile<DT, D, RAW>(sbuf, p, Q + base0 + a * hstride, K + base0 + a * hstride, i0,
                                        j0, nullptr, nullptr, wave, lane);
                 __syncthreads();
-                stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, pr[a]);
+                stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, tlim, pr[a]);
                 if (!HPRE) {
 #pragma unroll
                     for (int o = 0; o < 16; ++o)
@@ -612,7 +647,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
                 logit_tile<DT, D, PROB>(sbuf, p, Q + base0 + a * hstride, K + base0 + a * hstride, i0,
                                         j0, st_m + a * EXT_R, st_il + a * EXT_R, wave, lane);
                 __syncthreads();
-                stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, pr[a]);
+                stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, NOLIM, pr[a]);
 #pragma unroll
                 for (int o = 0; o < 16; ++o) pr[a][o] = (key0 + o <= qabs) ? pr[a][o] : 0.f;  // Mask_0
             }
@@ -645,7 +680,7 @@ __global__ void __launch_bounds__(NT) mta_fwd_kernel(Params p)
 #pragma unroll
             for (int a = 0; a < CH; ++a) {
                 stencil16<CQ, CK>(sbuf + a * EXT_R * p.pitch, p.pitch, rho, jb, th_s + a * cq * ckp, cq,
-                                  ck, ckp, pr[a]);
+                                  ck, ckp, NOLIM, pr[a]);
 #pragma unroll
                 for (int o = 0; o < 16; ++o) pr[a][o] = (key0 + o <= qabs) ? pr[a][o] : 0.f;  // Mask_0
             }

@@ -186,18 +186,21 @@ __device__ inline void split_hl(float x, bf16_t &hi, bf16_t &lo)
 }
 
 // Store a 16x16 logit block as hi/lo bf16 planes (Mask_0 + zero padding
-// applied); MODE PROB stores probabilities exp2(x - m_row) / l_row instead.
+// applied; with `exact` only the zero padding, as in store_block); MODE PROB
+// stores probabilities exp2(x - m_row) / l_row instead.
 template <int MODE>
 __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, int cb, f32x4 acc, int i0,
                                       int j0, int hl, int T, float sc, const float *st_m, const float *st_il,
-                                      int lane)
+                                      int exact, int lane)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
     const int qi = i0 - HALO + rho;
-    // block-uniform classification: every entry causal and inside [0, T), or not
+    const bool ex = MODE == RAW && exact;
+    const int kmax = ex ? T - 1 : qi;
+    // block-uniform classification: every entry kept and inside [0, T), or not
     const int q_lo = i0 - HALO + rb * 16, k_lo = j0 - hl + cb * 16;
-    const bool all_ok = (k_lo >= 0) && (k_lo + 15 <= q_lo) && (q_lo + 15 < T);
+    const bool all_ok = (k_lo >= 0) && (k_lo + 15 <= (ex ? T - 1 : q_lo)) && (q_lo >= 0) && (q_lo + 15 < T);
     float m = 0.f, il = 0.f;
     if (MODE == PROB) {
         m = st_m[rho];
@@ -211,7 +214,7 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
         if (MODE == PROB) x = __builtin_amdgcn_exp2f(x - m) * il;
         if (!all_ok) {
             const int kj = j0 - hl + e0 + r;
-            const bool ok = (kj >= 0) && (kj <= qi) && (qi < T);
+            const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
             x = ok ? x : 0.f;
         }
         bf16_t hh, ll;
@@ -264,9 +267,43 @@ __device__ inline void load_theta_frags(ThetaFrags<CQ> &t, const bf16x8 *tf, int
     }
 }
 
-template <int CQ>
+// Eq. 4's exact indicator on the matrix-core stencil: the B operand of a lane
+// holds tile columns 32kh + 8*(lane/16) + s (+16 for the second block) of the
+// rows above the lane's output query; entries whose key lies in that query's
+// future are cleared.  w[t][q] masks bf16 pair q of block t.
+struct ColMask {
+    uint32_t w[2][4];
+};
+
+// tl: last window column (relative to 32kh + 8*(lane/16)) whose key is not in
+// the future of the lane's output query
+__device__ inline ColMask col_mask(int tl)
+{
+    ColMask m;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 16 * t + 2 * q;
+            m.w[t][q] = (c <= tl ? 0x0000ffffu : 0u) | (c + 1 <= tl ? 0xffff0000u : 0u);
+        }
+    return m;
+}
+
+__device__ inline bf16x8 and_mask(bf16x8 v, const uint32_t (&w)[4])
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u[0] &= w[0];
+    u[1] &= w[1];
+    u[2] &= w[2];
+    u[3] &= w[3];
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int CQ, bool MASK>
 __device__ inline void stencil_mfma_reg(const bf16_t *xh, const bf16_t *xl, int ph, int rho, int kh,
-                                        const ThetaFrags<CQ> &tfr, int lane, float out[8])
+                                        const ThetaFrags<CQ> &tfr, const ColMask &cm, int lane, float out[8])
 {
     const int g4 = lane >> 4;
     // six independent accumulation chains (2 blocks x 3 products), summed at the end
@@ -274,10 +311,16 @@ __device__ inline void stencil_mfma_reg(const bf16_t *xh, const bf16_t *xl, int 
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip) {
         const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
-        const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
-        const bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
-        const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
-        const bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
+        bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
+        bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
+        bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        if (MASK) {
+            h0 = and_mask(h0, cm.w[0]);
+            l0 = and_mask(l0, cm.w[0]);
+            h1 = and_mask(h1, cm.w[1]);
+            l1 = and_mask(l1, cm.w[1]);
+        }
         a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h0, a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h1, a1, 0, 0, 0);
         b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], l0, b0, 0, 0, 0);
@@ -294,9 +337,9 @@ __device__ inline void stencil_mfma_reg(const bf16_t *xh, const bf16_t *xl, int 
 
 // Two 16-key output blocks (keys 32kh + 16t + 4*(lane/16) + r, t = 0,1) of row
 // 16rw + lane%16.  out[4t + r].
-template <int CQ>
+template <int CQ, bool MASK>
 __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, int rho, int kh,
-                                    const bf16x8 *tf, int lane, float out[8])
+                                    const bf16x8 *tf, const ColMask &cm, int lane, float out[8])
 {
     const int g4 = lane >> 4;
     // six independent accumulation chains (2 blocks x 3 products), summed at the end
@@ -306,10 +349,16 @@ __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, 
         const bf16x8 th = tf[(ip * 2 + 0) * 64 + lane];
         const bf16x8 tl = tf[(ip * 2 + 1) * 64 + lane];
         const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
-        const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
-        const bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
-        const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
-        const bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
+        bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
+        bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
+        bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        if (MASK) {
+            h0 = and_mask(h0, cm.w[0]);
+            l0 = and_mask(l0, cm.w[0]);
+            h1 = and_mask(h1, cm.w[1]);
+            l1 = and_mask(l1, cm.w[1]);
+        }
         a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h0, a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h1, a1, 0, 0, 0);
         b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l0, b0, 0, 0, 0);
@@ -328,7 +377,7 @@ __device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, 
 // Logit tile of one head from the Q and K tiles in LDS.  Wave (rw, kh):
 // own-row block 1+rw for column blocks kh, kh+2, ...; the waves with kh == 1
 // also take the HALO block's column blocks rw, rw+4, ... (only if c_q > 1).
-template <int D, int MODE, bool HL, int NCB>
+template <int D, int MODE, bool HL, int NCB, bool EX>
 __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, const bf16_t *kbuf,
                                       const Params &p, int i0, int j0, const float *st_m, const float *st_il,
                                       int rw, int kh, int lane)
@@ -349,9 +398,9 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
         const f32x4 acc = qk_mfma<D>(kf, qf);
         if (HL)
-            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
         else
-            store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+            store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
     }
     if (kh == 1 && p.c_q > 1) {
         const bf16_t *qr = qbuf + l16 * (D + 8) + dq;
@@ -364,16 +413,16 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
             for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
             const f32x4 acc = qk_mfma<D>(kf, qf);
             if (HL)
-                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
             else
-                store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, lane);
+                store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
         }
     }
 }
 
 // Same tile with the wave's Q fragments already in registers (own-row block
 // and, for the waves that take it, the halo block).
-template <int D, int MODE, bool HL, int NCB>
+template <int D, int MODE, bool HL, int NCB, bool EX>
 __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown, const QFrag<D> &qhalo,
                                        const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh,
                                        int lane)
@@ -389,9 +438,9 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
         const f32x4 acc = qk_mfma<D>(kf, qown);
         if (HL)
-            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
         else
-            store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+            store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
     }
     if (kh == 1 && p.c_q > 1) {
 #pragma unroll
@@ -401,9 +450,9 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
             for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
             const f32x4 acc = qk_mfma<D>(kf, qhalo);
             if (HL)
-                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
             else
-                store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, lane);
+                store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
         }
     }
 }
@@ -421,9 +470,11 @@ __device__ inline void load_qfrags(QFrag<D> &qown, QFrag<D> &qhalo, const bf16_t
     }
 }
 
-// Key-query stencil, 8 consecutive outputs of one row (same sum as stencil16).
+// Key-query stencil, 8 consecutive outputs of one row (same sum as stencil16,
+// window entries t > tlim taken as 0).
 template <int CQ, int CK>
-__device__ inline void stencil8(const float *buf, int pitch, int rho, int col0, const float *th, float out[8])
+__device__ inline void stencil8(const float *buf, int pitch, int rho, int col0, const float *th, int tlim,
+                                float out[8])
 {
     constexpr int NWIN = 8 + CK - 1;
     constexpr int NW4 = (NWIN + 3) / 4;
@@ -442,6 +493,10 @@ __device__ inline void stencil8(const float *buf, int pitch, int rho, int col0, 
             win[4 * t + 1] = x[1];
             win[4 * t + 2] = x[2];
             win[4 * t + 3] = x[3];
+        }
+        if (tlim < NWIN - 1) {
+#pragma unroll
+            for (int t = 0; t < NWIN; ++t) win[t] = (t <= tlim) ? win[t] : 0.f;
         }
 #pragma unroll
         for (int t = 0; t < CK4; ++t) {
@@ -499,9 +554,12 @@ __device__ inline void merge_lanes(float &m, float &l)
 // MS: key-query stencil on the matrix cores (bf16 hi/lo, c_k <= 17) instead of
 // the fp32 VALU stencil.  The lane's 8 values are then the keys
 // 32kh + 16t + 4*(lane/16) + r (slot 4t + r) instead of 32kh + 8*(lane/16) + o.
-template <int D, int CH, int CQ, int CK, bool KQ_POST, bool MS>
+// EXACT: the key-query convolution before the softmax with Eq. 4's exact
+// indicator (unmasked logit tile, per-row column limit in the stencil).
+template <int D, int CH, int CQ, int CK, bool KQ_POST, bool MS, bool EXACT>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
 {
+    static_assert(!(EXACT && KQ_POST), "the exact indicator applies before the softmax only");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rw = wave & 3, kh = wave >> 2;
@@ -601,18 +659,26 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 2 * 64, lane);
             }
             if (!KQ_POST && MS)
-                logit_tile_regq<D, RAW, true, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+                logit_tile_regq<D, RAW, true, NCB, EXACT>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
             else if (MS)
-                logit_tile_regq<D, RAW, false, NCB>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+                logit_tile_regq<D, RAW, false, NCB, false>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
             else
-                logit_tile_lds<D, RAW, false, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
+                logit_tile_lds<D, RAW, false, NCB, EXACT>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh,
+                                                          lane);
             __syncthreads();
             if (!KQ_POST) {
                 float c[8];
-                if (MS)
-                    stencil_mfma_reg<MS ? CQ : 1>(xh, xl, ph, rho, kh, tfr, lane, c);
-                else
-                    stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, c);
+                // Eq. 4's indicator: window columns past tl hold keys in this row's future
+                const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
+                if (MS) {
+                    // wave-uniform: can any of the wave's window columns pass its first row?
+                    if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
+                        stencil_mfma_reg<MS ? CQ : 1, true>(xh, xl, ph, rho, kh, tfr, col_mask(tl), lane, c);
+                    else
+                        stencil_mfma_reg<MS ? CQ : 1, false>(xh, xl, ph, rho, kh, tfr, ColMask{}, lane, c);
+                } else {
+                    stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
+                }
                 stats_update8(c, j0, ko, qabs, m_c[a], l_c[a]);
             } else {
                 float x[8];
@@ -727,18 +793,24 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             }
             if (ktn >= 1) load_v<D>(pf, V + an * hstride, (ktn - 1) * BN, T, tid);
             if (KQ_POST)
-                logit_tile_lds<D, PROB, MS, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, st_m + a * EXT_R, st_il + a * EXT_R,
-                                            rw, kh, lane);
+                logit_tile_lds<D, PROB, MS, NCB, false>(sbuf, ph, qbuf, kbuf, p, i0, j0, st_m + a * EXT_R,
+                                                        st_il + a * EXT_R, rw, kh, lane);
             else
-                logit_tile_lds<D, RAW, MS, NCB>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh, lane);
+                logit_tile_lds<D, RAW, MS, NCB, EXACT>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh,
+                                                       lane);
             if (kt > 0) pv(a, acc[a]);
             __syncthreads();
 
             float c[8];
-            if (MS)
-                stencil_mfma<CQ>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, lane, c);
-            else
-                stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, c);
+            const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
+            if (MS) {
+                if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
+                    stencil_mfma<CQ, true>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, col_mask(tl), lane, c);
+                else
+                    stencil_mfma<CQ, false>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, ColMask{}, lane, c);
+            } else {
+                stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
+            }
 #pragma unroll
             for (int o = 0; o < 8; ++o) {
                 const bool causal = j0 + ko[o] <= qabs;
@@ -849,10 +921,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     }
 }
 
-template <int D, int CH, int CQ, int CK, bool POST, bool MS>
+template <int D, int CH, int CQ, int CK, bool POST, bool MS, bool EXACT>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v2<D, CH, CQ, CK, POST, MS>;
+    auto fn = mta_fwd_v2<D, CH, CQ, CK, POST, MS, EXACT>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -27,6 +27,6 @@ hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 LaunchFn find_launch_f32(int d, int ch, int cq, int ck, int post, int hpre);
 LaunchFn find_launch_bf16(int d, int ch, int cq, int ck, int post, int hpre);
 // Pipelined 8-wave bf16 kernels (mta_fwd_v2.h); null when not instantiated.
-LaunchFn find_launch_v2(int d, int ch, int cq, int ck, int post, int hpre, int ms);
+LaunchFn find_launch_v2(int d, int ch, int cq, int ck, int post, int exact, int hpre, int ms);
 
 }  // namespace mta

@@ -116,6 +116,8 @@ def _configs() -> Dict[str, MTAConfig]:
                               layer=4, needles=6, seed=1003)
     # the same layer with the sigmoid-gated GroupNorm (no depth scale)
     c["needle4k_gated"] = replace(c["needle4k"], name="needle4k_gated", layer=1, gated=True)
+    # the same layer with Eq. 4's exact causal indicator instead of two-pass masks
+    c["needle4k_exact"] = replace(c["needle4k"], name="needle4k_exact", kq_place=PRE_EXACT)
     for (cq, ck) in ((4, 9), (6, 11), (8, 15)):
         for ch in (2, 4):
             for kq in (PRE, POST):

@@ -8,11 +8,15 @@ needles (B=2, H=16, T=4096, d=128, c_q=6, c_k=11, c_h=2, bf16).
 Prints one JSON line with tokens/s, effective TFLOP/s, the roofline of the
 kernel (per-launch duration from HIP events recorded on the launch stream
 around every launch of the timed region) and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload.  Also reported: the same kernel with a 1x1
+key-query kernel (the contraction alone; the difference is the convolution
+stage) and the per-launch time when a 512 MiB buffer is written before every
+launch (inputs no longer in the last-level cache).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +32,19 @@ PEAK_VALU_TFLOPS = 157.3   # fp32 vector, 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 PEAK_MFMA_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+FLUSH_MIB = 512
+
+
+def kernel_sources_hash() -> str:
+    """Hash of the HIP sources; traffic counters are valid only for the sources
+    they were taken on."""
+    d = os.path.join(ROOT, "transformer_attention_variant_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip", ".inc")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -37,6 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="needle4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true",
+                    help="skip the 1x1-kernel and cache-flushed timings")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per (batch, head group) unit in the oracle sample, from the end (0 = all)")
     ap.add_argument("--cpu-units", type=int, default=0, help="units in the oracle sample (0 = all)")
@@ -80,7 +99,7 @@ def summarize_pmc(args):
     rd, wr = kf * sf * 1024, kw * sw * 1024
     entry = {"bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
              "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": sf, "write_scale": sw,
-             "dispatches": nk, "copy_mib": copy_kib // 1024}
+             "dispatches": nk, "copy_mib": copy_kib // 1024, "sources": kernel_sources_hash()}
     db = {}
     if os.path.exists(args.traffic_file):
         db = json.load(open(args.traffic_file))
@@ -122,27 +141,31 @@ def main():
     dev = {k: v.cuda() for k, v in inp.items()}
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        binding.forward_cfg(cfg, dev, out=out, stream=stream)
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        binding.forward_cfg(cfg, dev, out=out, stream=stream)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_step = ms_total / K
-    ms_launch = float(np.mean(launch_ms))
+
+    def timed(c, d, flush=None):
+        """(ms per step over the timed region, mean ms per launch) of K calls
+        after the warm-up; with `flush`, that buffer is overwritten before
+        every launch (outside the per-launch events)."""
+        for _ in range(args.warmup):
+            binding.forward_cfg(c, d, out=out, stream=stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(K):
+            if flush is not None:
+                flush.fill_(float(i))
+            ev[i][0].record(stream)
+            binding.forward_cfg(c, d, out=out, stream=stream)
+            ev[i][1].record(stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / K, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_step, ms_launch = timed(cfg, dev)
     tokens = cfg.B * cfg.T
     value = tokens / (ms_step / 1e3)
 
@@ -151,11 +174,13 @@ def main():
     all_flops = fl["contraction"] + fl["stencil"] + fl["mix"]
     t = ms_launch / 1e3
     mfma_peak = PEAK_MFMA_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_MFMA_F32_TFLOPS
+    kname = binding.kernel_name(cfg)
     traffic = None
     if os.path.exists(args.traffic_file):
         try:
-            tr = json.load(open(args.traffic_file))
-            traffic = tr.get(cfg.name, {}).get("bytes_per_launch")
+            tr = json.load(open(args.traffic_file)).get(cfg.name, {})
+            if tr.get("sources") == kernel_sources_hash():
+                traffic = tr.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
     roof = {
@@ -165,7 +190,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(alu_flops / t / 1e12 / PEAK_VALU_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": "mta_fwd_kernel",
+        "kernel": kname,
         "work": "key-query stencil 2*c_q*c_k + head mix 2*c_h FLOP per causal logit",
     }
     mfma = {
@@ -193,7 +218,7 @@ def main():
         "data": "synthetic (seeded; stand-in shapes for the pages' workloads)",
         "config": {"workload": cfg.name, "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.T,
                    "head_dim": cfg.d, "c_q": cfg.c_q, "c_k": cfg.c_k, "c_h": cfg.c_h,
-                   "kq_place": "pre" if cfg.kq_place == I.PRE else "post",
+                   "kq_place": {I.PRE: "pre", I.POST: "post", I.PRE_EXACT: "exact"}[cfg.kq_place],
                    "head_place": "pre" if cfg.head_place == I.PRE else "post",
                    "needles": cfg.needles, "depth_scale": cfg.depth_scale, "global_batch": cfg.B,
                    "parallelism": "single GPU"},
@@ -204,9 +229,45 @@ def main():
         "hbm": hbm,
     }
 
+    if not args.no_stages:
+        res["stages"] = stages(cfg, dev, timed, t, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args)
     print(json.dumps(res), flush=True)
+
+
+def stages(cfg, dev, timed, t, torch):
+    """The convolution stage, read as the difference to the same kernel with a
+    1x1 key-query kernel (the stencil collapses to one tap; same c_h, same
+    placement), and the cache-flushed launch time."""
+    from transformer_attention_variant_amd import binding
+    from transformer_attention_variant_amd import inputs as I
+    c11 = I.with_(cfg, name=cfg.name + "_1x1", c_q=1, c_k=1)
+    d11 = dict(dev)
+    d11["theta_kq"] = torch.ones((cfg.H, 1, 1), dtype=torch.float32, device=dev["q"].device)
+    _, ms11 = timed(c11, d11)
+    t11 = ms11 / 1e3
+    n = float(cfg.causal_logits())
+    st_alg = 2.0 * (cfg.c_q * cfg.c_k - 1) * n  # the taps beyond the single one of the 1x1 run
+    # the difference is the convolution stage only if both runs use the same kernel
+    same = binding.kernel_name(c11) == binding.kernel_name(cfg) and t > t11
+    conv = (t - t11) if same else None
+    flush = torch.empty(FLUSH_MIB * (1 << 18), dtype=torch.float32, device=dev["q"].device)
+    _, msf = timed(cfg, dev, flush)
+    peak_c = PEAK_MFMA_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_MFMA_F32_TFLOPS
+    return {
+        "kernel_1x1": binding.kernel_name(c11),
+        "ms_per_launch_1x1": round(ms11, 4),
+        "contraction_tflops_1x1": round(4 * cfg.d * n / t11 / 1e12, 2),
+        "contraction_frac_1x1": round(4 * cfg.d * n / t11 / 1e12 / peak_c, 4),
+        "conv_stage_ms": round(conv * 1e3, 4) if same else None,
+        "conv_stage_tflops": round(st_alg / conv / 1e12, 2) if same else None,
+        "conv_stage_frac_valu": round(st_alg / conv / 1e12 / PEAK_VALU_TFLOPS, 4) if same else None,
+        "conv_work": "2*(c_q*c_k - 1) FLOP per causal logit (the taps beyond the 1x1 run's one), counted "
+                     "once; null when the 1x1 run selects another kernel",
+        "ms_per_launch_flushed": round(msf, 4),
+        "flush": f"{FLUSH_MIB} MiB written before every launch",
+    }
 
 
 def cpu_baseline(cfg, inp, args):

@@ -131,6 +131,12 @@ int mta_forward_gated(const void *q, const void *k, const void *v,
                       const float *gn_w, const float *gn_b, const float *gate,
                       const mta_config *cfg, void *out, void *stream);
 
+/* Host-only: the name of the kernel mta_forward / mta_forward_gated launch for
+ * this configuration (a static string, e.g. "mta_fwd_v3 (one pass,
+ * matrix-core stencil)"), or NULL if the configuration is invalid or
+ * unsupported.  For profiling and reports; it launches nothing. */
+const char *mta_kernel_name(const mta_config *cfg);
+
 /* Host-only check of a configuration against the limits of this build; the
  * same validation mta_forward runs (pointer checks excepted).  Returns MTA_OK
  * or the MTA_ERR_* code mta_forward would return. */

@@ -34,6 +34,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), f"{n} not exported"
 
 
+@pytest.mark.parametrize("name,expect", [
+    ("needle4k", "mta_fwd_v3"), ("needle4k_exact", "mta_fwd_v3"), ("layer2k", "mta_fwd_v3"),
+    ("sweep8k_6x11_ch2_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
+    ("sweep8k_8x15_ch4_pre", "mta_fwd_v2 (two passes, VALU stencil)"),
+    ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
+])
+def test_kernel_selection(lib, name, expect):
+    """Host-only query of the kernel each workload runs (no launch)."""
+    got = binding.kernel_name(I.CONFIGS[name])
+    assert got is not None and got.startswith(expect), got
+
+
+def test_kernel_name_of_invalid_config(lib):
+    assert lib.mta_kernel_name(None) is None
+    c = cfg(c_h=3, H=6)
+    assert lib.mta_kernel_name(ctypes.byref(c)) is None
+
+
 def test_version_and_status_strings(lib):
     assert lib.mta_abi_version() == 100
     for code in list(binding.STATUS) + [-99]:

@@ -22,8 +22,8 @@ STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA
           -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
           -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
 # names declared in include/mta.h
-EXPORTS = ("mta_forward", "mta_forward_gated", "mta_check_config", "mta_status_string",
-           "mta_abi_version")
+EXPORTS = ("mta_forward", "mta_forward_gated", "mta_check_config", "mta_kernel_name",
+           "mta_status_string", "mta_abi_version")
 
 
 class MtaConfig(ctypes.Structure):
@@ -61,6 +61,8 @@ def load(path: Optional[str] = None):
     lib.mta_check_config.restype = ctypes.c_int
     lib.mta_status_string.argtypes = [ctypes.c_int]
     lib.mta_status_string.restype = ctypes.c_char_p
+    lib.mta_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
+    lib.mta_kernel_name.restype = ctypes.c_char_p
     lib.mta_abi_version.argtypes = []
     lib.mta_abi_version.restype = ctypes.c_int
     if path is None:
@@ -71,6 +73,14 @@ def load(path: Optional[str] = None):
 def make_config(B, H, T, d, c_q, c_k, c_h, kq_place=I.PRE, head_place=I.POST, dtype=I.BF16,
                 gn_eps=1e-5, depth_scale=1.0) -> MtaConfig:
     return MtaConfig(B, H, T, d, c_q, c_k, c_h, kq_place, head_place, dtype, gn_eps, depth_scale)
+
+
+def kernel_name(cfg: I.MTAConfig) -> Optional[str]:
+    """Name of the kernel the library launches for a workload configuration."""
+    c = make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
+                    I.F32 if cfg.dtype == "f32" else I.BF16, cfg.gn_eps, cfg.depth_scale)
+    r = load().mta_kernel_name(ctypes.byref(c))
+    return r.decode() if r else None
 
 
 def status_string(code: int) -> str:

@@ -5,6 +5,7 @@
 
 #include "mta.h"
 #include "mta_fwd_v2.h"
+#include "mta_fwd_v3.h"
 #include "mta_launch.h"
 
 namespace {
@@ -73,6 +74,86 @@ const char *mta_status_string(int s)
     }
 }
 
+// The kernel a valid configuration runs, its launch parameters (shapes and
+// tile geometry; the caller fills in the tensor pointers) and its LDS size.
+struct Plan {
+    mta::LaunchFn fn = nullptr;
+    size_t lds = 0;
+    int grid = 0;
+    const char *name = nullptr;
+    mta::Params p{};
+};
+
+static int make_plan(const mta_config *cfg, Plan &pl)
+{
+    const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
+    const int post = cfg->kq_place == MTA_POST_SOFTMAX;
+    const int exact = cfg->kq_place == MTA_PRE_SOFTMAX_EXACT;
+    const int hpre = cfg->head_place == MTA_PRE_SOFTMAX;
+
+    mta::Params &p = pl.p;
+    p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
+    p.G = cfg->heads / ch;
+    p.units = cfg->batch * p.G;
+    p.n_qt = (cfg->seq_len + mta::BM - 1) / mta::BM;
+    p.head_pre = hpre;
+    p.exact = exact;
+    p.hl = (ck + 1) / 2 - 1;
+    p.ncb = (mta::BN + ck - 1 + 15) / 16;
+    p.pitch = p.ncb * 16 + 4;
+    p.nbuf = (post && hpre) ? ch : 1;
+    p.sc = 1.4426950408889634f / sqrtf((float)d);
+    p.eps = cfg->gn_eps;
+    p.depth_scale = cfg->depth_scale;
+    pl.grid = p.n_qt * p.units;
+
+    constexpr size_t LDS_MAX = 160 * 1024;
+    mta::LaunchFn fn = nullptr;
+    size_t lds = 0;
+    if (cfg->dtype == MTA_BF16) {
+        const int ncb0 = p.ncb, pitch0 = p.pitch;
+        // one pass with online softmax statistics where it applies (key-query
+        // convolution before the softmax, head mix after it, c_h <= 2)
+        fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
+        if (fn) {
+            p.ncb = ncb0 < 5 ? 5 : ncb0;
+            p.pitch = p.ncb * 16 + 4;
+            lds = (size_t)mta::v3::layout(d, ch, cq, ck, p.ncb).total;
+            if (lds > LDS_MAX) fn = nullptr;
+            else pl.name = "mta_fwd_v3 (one pass, matrix-core stencil)";
+        }
+        // else two passes: stencil on the matrix cores first, then the fp32 VALU stencil
+        for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {
+            // the matrix-core stencil reads a 32-column window past each
+            // 16-key output block: the tile must span at least 80 columns
+            p.ncb = (ms && ncb0 < 5) ? 5 : ncb0;
+            p.pitch = p.ncb * 16 + 4;
+            fn = mta::find_launch_v2(d, ch, cq, ck, post, exact, hpre, ms);
+            if (fn) {
+                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0).total;
+                if (lds > LDS_MAX) fn = nullptr;
+                else pl.name = ms ? "mta_fwd_v2 (two passes, matrix-core stencil)"
+                                  : "mta_fwd_v2 (two passes, VALU stencil)";
+            }
+        }
+        if (!fn) {
+            p.ncb = ncb0;
+            p.pitch = pitch0;
+        }
+    }
+    if (!fn) {
+        // the general 4-wave kernel
+        fn = cfg->dtype == MTA_BF16 ? mta::find_launch_bf16(d, ch, cq, ck, post, hpre)
+                                    : mta::find_launch_f32(d, ch, cq, ck, post, hpre);
+        lds = lds_bytes(p, cfg->dtype, d, ch);
+        pl.name = "mta_fwd_kernel (two passes, general)";
+    }
+    if (!fn || lds > LDS_MAX) return MTA_ERR_UNSUPPORTED;
+    pl.fn = fn;
+    pl.lds = lds;
+    return MTA_OK;
+}
+
 static int forward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
                         const mta_config *cfg, void *out, void *stream)
@@ -85,61 +166,22 @@ static int forward_impl(const void *q, const void *k, const void *v, const float
         !aligned4(theta_head) || !aligned4(gn_w) || !aligned4(gn_b) || (gate && !aligned4(gate)))
         return MTA_ERR_MISALIGNED;
 
-    const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
-    const int post = cfg->kq_place == MTA_POST_SOFTMAX;
-    const int exact = cfg->kq_place == MTA_PRE_SOFTMAX_EXACT;
-    const int hpre = cfg->head_place == MTA_PRE_SOFTMAX;
-
-    mta::Params p;
+    Plan pl;
+    const int ps = make_plan(cfg, pl);
+    if (ps != MTA_OK) return ps;
+    mta::Params &p = pl.p;
     p.q = q; p.k = k; p.v = v;
     p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b; p.gate = gate;
     p.out = out;
-    p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
-    p.G = cfg->heads / ch;
-    p.units = cfg->batch * p.G;
-    p.n_qt = (cfg->seq_len + mta::BM - 1) / mta::BM;
-    p.head_pre = cfg->head_place == MTA_PRE_SOFTMAX;
-    p.exact = exact;
-    p.hl = (ck + 1) / 2 - 1;
-    p.ncb = (mta::BN + ck - 1 + 15) / 16;
-    p.pitch = p.ncb * 16 + 4;
-    p.nbuf = (post && p.head_pre) ? ch : 1;
-    p.sc = 1.4426950408889634f / sqrtf((float)d);
-    p.eps = cfg->gn_eps;
-    p.depth_scale = cfg->depth_scale;
-
-    const int grid = p.n_qt * p.units;
-    // the pipelined 8-wave kernel where it is instantiated and fits in LDS,
-    // else the general 4-wave kernel
-    mta::LaunchFn fn = nullptr;
-    size_t lds = 0;
-    if (cfg->dtype == MTA_BF16) {
-        // stencil on the matrix cores first, then the fp32 VALU stencil
-        const int ncb0 = p.ncb, pitch0 = p.pitch;
-        for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {
-            // the matrix-core stencil reads a 32-column window past each
-            // 16-key output block: the tile must span at least 80 columns
-            p.ncb = (ms && ncb0 < 5) ? 5 : ncb0;
-            p.pitch = p.ncb * 16 + 4;
-            fn = mta::find_launch_v2(d, ch, cq, ck, post, exact, hpre, ms);
-            if (fn) {
-                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0).total;
-                if (lds > 160 * 1024) fn = nullptr;
-            }
-        }
-        if (!fn) {
-            p.ncb = ncb0;
-            p.pitch = pitch0;
-        }
-    }
-    if (!fn) {
-        fn = cfg->dtype == MTA_BF16 ? mta::find_launch_bf16(d, ch, cq, ck, post, hpre)
-                                    : mta::find_launch_f32(d, ch, cq, ck, post, hpre);
-        lds = lds_bytes(p, cfg->dtype, d, ch);
-    }
-    if (!fn || lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
-    const hipError_t e = fn(p, grid, lds, reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = pl.fn(p, pl.grid, pl.lds, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+}
+
+const char *mta_kernel_name(const mta_config *cfg)
+{
+    if (validate(cfg) != MTA_OK) return nullptr;
+    Plan pl;
+    return make_plan(cfg, pl) == MTA_OK ? pl.name : nullptr;
 }
 
 int mta_forward(const void *q, const void *k, const void *v, const float *theta_kq,

@@ -10,9 +10,12 @@ namespace mta {
 LaunchFn find_launch_v2_exact(int ch, int cq, int ck, int ms);
 
 namespace {
-#define MTA_V2_L(CH_, CQ_, CK_, MS_)                                    \
+#define MTA_V2_POST(CH_, CQ_, CK_, MS_) \
+    (post ? &v2::launch<128, CH_, CQ_, CK_, true, MS_, false> : nullptr)
+#define MTA_V2_ANY(CH_, CQ_, CK_, MS_)                                  \
     (post ? &v2::launch<128, CH_, CQ_, CK_, true, MS_, false>          \
           : &v2::launch<128, CH_, CQ_, CK_, false, MS_, false>)
+#define MTA_V2_PICK pick_two_pass
 #define MTA_V2_FIND find_two_pass
 #include "mta_inst_v2.inc"
 }  // namespace

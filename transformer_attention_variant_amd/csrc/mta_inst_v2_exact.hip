@@ -7,7 +7,9 @@
 namespace mta {
 
 namespace {
-#define MTA_V2_L(CH_, CQ_, CK_, MS_) (&v2::launch<128, CH_, CQ_, CK_, false, MS_, true>)
+#define MTA_V2_POST(CH_, CQ_, CK_, MS_) (LaunchFn) nullptr
+#define MTA_V2_ANY(CH_, CQ_, CK_, MS_) (&v2::launch<128, CH_, CQ_, CK_, false, MS_, true>)
+#define MTA_V2_PICK pick_exact
 #define MTA_V2_FIND find_exact
 #include "mta_inst_v2.inc"
 }  // namespace

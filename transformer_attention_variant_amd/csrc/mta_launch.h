@@ -28,5 +28,7 @@ LaunchFn find_launch_f32(int d, int ch, int cq, int ck, int post, int hpre);
 LaunchFn find_launch_bf16(int d, int ch, int cq, int ck, int post, int hpre);
 // Pipelined 8-wave bf16 kernels (mta_fwd_v2.h); null when not instantiated.
 LaunchFn find_launch_v2(int d, int ch, int cq, int ck, int post, int exact, int hpre, int ms);
+// One-pass bf16 kernels (mta_fwd_v3.h); null when not instantiated.
+LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 
 }  // namespace mta

@@ -50,6 +50,12 @@ def _bind(lib):
                                       ctypes.c_double, ctypes.c_double,
                                       I, I, D, D, D, D, D, D, D, D, D]
     lib.mta_oracle_stages.restype = I
+    lib.mta_oracle_layer.argtypes = [D] * 12 + [I] * 10 + [ctypes.c_double, ctypes.c_double] + \
+        [I, I, ctypes.POINTER(ctypes.c_int), I, I, I, D]
+    lib.mta_oracle_layer.restype = I
+    lib.mta_oracle_layer_stages.argtypes = [D] * 12 + [I] * 10 + [ctypes.c_double, ctypes.c_double] + \
+        [I, I] + [D] * 10
+    lib.mta_oracle_layer_stages.restype = I
     lib.mta_oracle_max_threads.argtypes = []
     lib.mta_oracle_max_threads.restype = I
     return lib
@@ -158,8 +164,76 @@ def stages(q, k, v, theta_kq, theta_head, gn_w, gn_b, *, c_q, c_k, c_h,
     return res
 
 
+LAYER_KERNELS = ("kq_pre", "head_pre", "conv3d", "head_post", "kq_post", "head_post2")
+
+
+def layer(q, k, v, gn_w, gn_b, *, c_q, c_k, c_h, c_q2=0, c_k2=0, exact=False, eps=1e-5,
+          depth_scale=1.0, gate=None, rows: Optional[Sequence[int]] = None,
+          units: Optional[Sequence[int]] = None, chunk: int = 64, threads: Optional[int] = None,
+          lib=None, **kernels) -> np.ndarray:
+    """The general layer in float64 (``kernels``: any of kq_pre, head_pre,
+    conv3d, head_post, kq_post, head_post2; absent or None = stage absent).
+    Same row/unit selection and result layout as ``forward``."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    gw, gb = _f64(gn_w), _f64(gn_b)
+    B, H, T, d = q.shape
+    ks = {n: (_f64(kernels[n]) if kernels.get(n) is not None else None) for n in LAYER_KERNELS}
+    unknown = set(kernels) - set(LAYER_KERNELS)
+    assert not unknown, unknown
+    r0, r1 = (0, T) if rows is None else (int(rows[0]), int(rows[1]))
+    out = np.full((B, H, T, d), np.nan, dtype=np.float64)
+    if units is None:
+        up, nu = None, 0
+    else:
+        up, nu = (ctypes.c_int * len(units))(*[int(u) for u in units]), len(units)
+    nt = threads if threads is not None else default_threads()
+    ga, gp = _gate(gate, H)
+    ptr = [(_p(ks[n]) if ks[n] is not None else None) for n in LAYER_KERNELS]
+    rc = lib.mta_oracle_layer(_p(q), _p(k), _p(v), *ptr, _p(gw), _p(gb), gp, B, H, T, d, c_q, c_k,
+                              int(c_q2), int(c_k2), c_h, int(bool(exact)), float(eps), float(depth_scale),
+                              r0, r1, up, nu, int(chunk), int(nt), _p(out))
+    if rc != 0:
+        raise ValueError(f"mta_oracle_layer failed with code {rc}")
+    return out
+
+
+def layer_stages(q, k, v, gn_w, gn_b, *, c_q, c_k, c_h, c_q2=0, c_k2=0, exact=False, eps=1e-5,
+                 depth_scale=1.0, gate=None, b=0, g=0, lib=None, **kernels) -> Dict[str, np.ndarray]:
+    """Every intermediate map of the layer for unit (b, g) over all rows: S,
+    Lc (after the pre-softmax convolution), L (entering the softmax), P, Pa
+    (after head_post), P2 (after kq_post and Mask_0), P3 (after head_post2), O, Y."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    gw, gb = _f64(gn_w), _f64(gn_b)
+    B, H, T, d = q.shape
+    ks = {n: (_f64(kernels[n]) if kernels.get(n) is not None else None) for n in LAYER_KERNELS}
+    mats = {n: np.full((c_h, T, T), np.nan) for n in ("S", "Lc", "L", "P", "Pa", "P2", "P3")}
+    vecs = {n: np.full((c_h, T, d), np.nan) for n in ("O", "Y")}
+    out = np.full((B, H, T, d), np.nan)
+    ga, gp = _gate(gate, H)
+    ptr = [(_p(ks[n]) if ks[n] is not None else None) for n in LAYER_KERNELS]
+    rc = lib.mta_oracle_layer_stages(_p(q), _p(k), _p(v), *ptr, _p(gw), _p(gb), gp, B, H, T, d, c_q, c_k,
+                                     int(c_q2), int(c_k2), c_h, int(bool(exact)), float(eps),
+                                     float(depth_scale), int(b), int(g),
+                                     *[_p(mats[n]) for n in ("S", "Lc", "L", "P", "Pa", "P2", "P3")],
+                                     _p(vecs["O"]), _p(vecs["Y"]), _p(out))
+    if rc != 0:
+        raise ValueError(f"mta_oracle_layer_stages failed with code {rc}")
+    res = dict(mats)
+    res.update(vecs)
+    res["out"] = out
+    return res
+
+
 def forward_cfg(cfg, inp: Dict, **kw) -> np.ndarray:
-    """Convenience: run ``forward`` with the fields of an input configuration."""
+    """Convenience: the forward of an input configuration (the general layer
+    for the 3D-convolution and repeated-convolution forms)."""
+    if getattr(cfg, "form", "std") != "std":
+        from transformer_attention_variant_amd.inputs import layer_weights
+        return layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                     c_h=cfg.c_h, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, gate=inp.get("gate"),
+                     **layer_weights(cfg, inp), **kw)
     return forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"],
                    inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
                    kq_place=cfg.kq_place, head_place=cfg.head_place, eps=cfg.gn_eps,

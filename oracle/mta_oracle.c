@@ -482,6 +482,262 @@ int mta_oracle_stages(const double *q, const double *k, const double *v,
     return unit_rows(&cf, q, k, v, theta_kq, theta_head, gn_w, gn_b, b, g, 0, T, out, &st);
 }
 
+/* ======================================================================== */
+/* The general MTA layer ("Putting Everything Together": the key-query and the
+ * head convolution on either side of the softmax, the both-pre-softmax "3D
+ * convolution view", and the repeated MTA convolution after the softmax of
+ * the overall flow).  Every stage is optional:
+ *
+ *   L   = S,  or  Conv2d_theta1(Mask_0(S))  (two-pass; or Eq. 4's indicator on
+ *         S when `exact`),  or the 3D convolution  sum_b Conv2d_theta3[a][b](.)
+ *   L   = head mix w_pre (L)                       (not with the 3D kernel)
+ *   P   = softmax(Mask_-inf(L))
+ *   P   = head mix w_post (P)                      (Eq. 7)
+ *   P   = Mask_0(Conv2d_theta2(P))                  (kq conv after the softmax)
+ *   P   = head mix w_post2 (P)                     (the repeated head conv)
+ *   O   = P V,  GroupNorm x scale.
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+    const double *kq_pre;     /* [H][c_q][c_k] or NULL                                 */
+    const double *head_pre;   /* [G][c_h][c_h] or NULL                                 */
+    const double *conv3d;     /* [G][c_h][c_h][c_q][c_k] or NULL (instead of the two)  */
+    const double *head_post;  /* [G][c_h][c_h] or NULL                                 */
+    const double *kq_post;    /* [H][c_q2][c_k2] or NULL                               */
+    const double *head_post2; /* [G][c_h][c_h] or NULL                                 */
+    int exact;                /* pre-softmax convolution with Eq. 4's indicator        */
+    int c_q2, c_k2;
+} layer_w;
+
+/* Step 3b.  The 3D convolution over (query, key, head) of one group
+ * ("Putting Everything Together", both pre-softmax): output head a sums the
+ * key-query convolutions of every source head b of the group, each with its
+ * own c_q x c_k kernel theta3[a][b]:
+ *   Y^a[i][j] = sum_b sum_{i',j'} theta3[a][b][i'][j'] X^b[i-i'][j-j'].
+ * Each (a, b) term is step 3 (with the same indicator choice). */
+static void step_conv3d(double *const *X, int T, int x0, int nx, const double *th3, int c_h,
+                        int c_q, int c_k, int indicator, int i0, int i1, double *const *Y,
+                        double *tmp)
+{
+    const size_t n = (size_t)(i1 - i0) * T;
+    for (int a = 0; a < c_h; ++a) {
+        for (size_t e = 0; e < n; ++e) Y[a][e] = 0.0;
+        for (int b = 0; b < c_h; ++b) {
+#if ORACLE_MUTANT == 10 /* planted: output and source head swapped in the 3D kernel */
+            const double *th = th3 + ((size_t)b * c_h + a) * c_q * c_k;
+#else
+            const double *th = th3 + ((size_t)a * c_h + b) * c_q * c_k;
+#endif
+            step_kq_conv(X[b], T, x0, nx, th, c_q, c_k, indicator, i0, i1, tmp);
+            for (size_t e = 0; e < n; ++e) Y[a][e] += tmp[e];
+        }
+    }
+}
+
+/* Stage dump layout of the layer for one unit, full rows [0,T) only:
+ *   S, Lc, L, P, Pa, P2, P3 : [c_h][T][T]   (Lc: after the pre-softmax
+ *     convolution, L: entering the softmax, Pa: after w_post, P2: after the
+ *     post-softmax key-query convolution and Mask_0, P3: after w_post2)
+ *   O, Y                    : [c_h][T][d]                                     */
+typedef struct {
+    double *S, *Lc, *L, *P, *Pa, *P2, *P3, *O, *Y;
+} layer_stages;
+
+static int layer_rows(const oracle_cfg *cf, const layer_w *lw, const double *q, const double *k,
+                      const double *v, const double *gn_w, const double *gn_b, int b, int g,
+                      int r0, int r1, double *out, const layer_stages *st)
+{
+    const int T = cf->T, d = cf->d, c_h = cf->c_h, H = cf->H;
+    const int has_pre = lw->kq_pre || lw->conv3d;
+    /* rows of the probabilities the post-softmax convolution reads, and rows of
+     * the logits the pre-softmax convolution reads from those */
+    const int e2 = lw->kq_post ? ((r0 - (lw->c_q2 - 1)) > 0 ? r0 - (lw->c_q2 - 1) : 0) : r0;
+    const int e1 = has_pre ? ((e2 - (cf->c_q - 1)) > 0 ? e2 - (cf->c_q - 1) : 0) : e2;
+    const int ne = r1 - e1, nr = r1 - r0;
+    const size_t ext = (size_t)ne * T;
+    const size_t off2 = (size_t)(e2 - e1) * T;   /* row e2 in an extended buffer */
+    const size_t off = (size_t)(r0 - e1) * T;    /* row r0 */
+    const size_t n2 = (size_t)(r1 - e2) * T;
+    const int G = H / c_h;
+    int rc = 0;
+    (void)G;
+
+    double **S = calloc(c_h, sizeof(double *)), **A = calloc(c_h, sizeof(double *));
+    double **B2 = calloc(c_h, sizeof(double *)), **O = calloc(c_h, sizeof(double *));
+    double **X = calloc(c_h, sizeof(double *)), **Y = calloc(c_h, sizeof(double *));
+    double *tmp = malloc(ext * sizeof(double));
+    if (!S || !A || !B2 || !O || !X || !Y || !tmp) { rc = -1; goto done; }
+    for (int a = 0; a < c_h; ++a) {
+        S[a] = malloc(ext * sizeof(double));
+        A[a] = malloc(ext * sizeof(double));
+        B2[a] = malloc(ext * sizeof(double));
+        O[a] = malloc((size_t)nr * d * sizeof(double));
+        if (!S[a] || !A[a] || !B2[a] || !O[a]) { rc = -1; goto done; }
+        for (size_t e = 0; e < ext; ++e) A[a][e] = B2[a][e] = NAN;
+    }
+#define DUMP(field, buf)                                                               \
+    if (st && st->field)                                                               \
+        for (int a_ = 0; a_ < c_h; ++a_)                                               \
+            memcpy(st->field + (size_t)a_ * T * T, (buf)[a_], ext * sizeof(double));
+
+    for (int a = 0; a < c_h; ++a) {
+        const size_t base = ((size_t)b * H + g * c_h + a) * (size_t)T * d;
+        step_logits(q + base, k + base, T, d, e1, r1, S[a]);
+    }
+    DUMP(S, S)
+
+    /* A <- the pre-softmax convolution on rows [e2, r1) */
+    if (has_pre) {
+        for (int a = 0; a < c_h; ++a) {
+            memcpy(B2[a], S[a], ext * sizeof(double));
+            if (!lw->exact) step_mask_zero(B2[a], T, e1, r1);
+        }
+        if (lw->conv3d) {
+            for (int a = 0; a < c_h; ++a) Y[a] = A[a] + off2;
+            step_conv3d(B2, T, e1, ne, lw->conv3d + (size_t)g * c_h * c_h * cf->c_q * cf->c_k, c_h,
+                        cf->c_q, cf->c_k, lw->exact, e2, r1, Y, tmp);
+        } else {
+            for (int a = 0; a < c_h; ++a)
+                step_kq_conv(B2[a], T, e1, ne, lw->kq_pre + (size_t)(g * c_h + a) * cf->c_q * cf->c_k,
+                             cf->c_q, cf->c_k, lw->exact, e2, r1, A[a] + off2);
+        }
+    } else {
+        for (int a = 0; a < c_h; ++a) memcpy(A[a] + off2, S[a] + off2, n2 * sizeof(double));
+    }
+    DUMP(Lc, A)
+    if (lw->head_pre && !lw->conv3d) {
+        for (int a = 0; a < c_h; ++a) { X[a] = A[a] + off2; Y[a] = B2[a] + off2; }
+        step_head_mix(X, lw->head_pre + (size_t)g * c_h * c_h, c_h, n2, Y);
+        for (int a = 0; a < c_h; ++a) memcpy(A[a] + off2, B2[a] + off2, n2 * sizeof(double));
+    }
+    DUMP(L, A)
+
+    /* softmax on rows [e2, r1) */
+    for (int a = 0; a < c_h; ++a) {
+        step_causal_softmax(A[a] + off2, T, e2, r1, B2[a] + off2);
+        memcpy(A[a] + off2, B2[a] + off2, n2 * sizeof(double));
+    }
+    DUMP(P, A)
+    if (lw->head_post) {
+        for (int a = 0; a < c_h; ++a) { X[a] = A[a] + off2; Y[a] = B2[a] + off2; }
+        step_head_mix(X, lw->head_post + (size_t)g * c_h * c_h, c_h, n2, Y);
+        for (int a = 0; a < c_h; ++a) memcpy(A[a] + off2, B2[a] + off2, n2 * sizeof(double));
+    }
+    DUMP(Pa, A)
+    if (lw->kq_post) {
+        for (int a = 0; a < c_h; ++a) {
+            step_kq_conv(A[a] + off2, T, e2, r1 - e2,
+                         lw->kq_post + (size_t)(g * c_h + a) * lw->c_q2 * lw->c_k2, lw->c_q2, lw->c_k2, 0,
+                         r0, r1, B2[a] + off);
+#if ORACLE_MUTANT != 11 /* planted (11): the Mask_0 after the post-softmax convolution dropped */
+            step_mask_zero(B2[a] + off, T, r0, r1);
+#endif
+        }
+        for (int a = 0; a < c_h; ++a) memcpy(A[a] + off, B2[a] + off, (size_t)nr * T * sizeof(double));
+    }
+    DUMP(P2, A)
+    if (lw->head_post2) {
+        for (int a = 0; a < c_h; ++a) { X[a] = A[a] + off; Y[a] = B2[a] + off; }
+        step_head_mix(X, lw->head_post2 + (size_t)g * c_h * c_h, c_h, (size_t)nr * T, Y);
+        for (int a = 0; a < c_h; ++a) memcpy(A[a] + off, B2[a] + off, (size_t)nr * T * sizeof(double));
+    }
+    DUMP(P3, A)
+#undef DUMP
+
+    for (int a = 0; a < c_h; ++a) {
+        const int h = g * c_h + a;
+        const size_t base = ((size_t)b * H + h) * (size_t)T * d;
+        step_pv(A[a] + off, v + base, T, d, r0, r1, O[a]);
+        step_groupnorm_scale(O[a], gn_w + (size_t)h * d, gn_b + (size_t)h * d, d, r0, r1, cf->eps,
+                             head_scale(cf, h), out + base + (size_t)r0 * d);
+        if (st) {
+            if (st->O) memcpy(st->O + (size_t)a * T * d, O[a], (size_t)nr * d * sizeof(double));
+            if (st->Y)
+                memcpy(st->Y + (size_t)a * T * d, out + base + (size_t)r0 * d, (size_t)nr * d * sizeof(double));
+        }
+    }
+
+done:
+    for (int a = 0; a < c_h; ++a) {
+        if (S) free(S[a]);
+        if (A) free(A[a]);
+        if (B2) free(B2[a]);
+        if (O) free(O[a]);
+    }
+    free(S); free(A); free(B2); free(O); free(X); free(Y); free(tmp);
+    return rc;
+}
+
+static int check_layer(const oracle_cfg *c, const layer_w *lw)
+{
+    if (c->B < 0 || c->H <= 0 || c->T < 0 || c->d <= 0) return -2;
+    if (c->c_q < 1 || c->c_k < 1 || c->c_h < 1 || c->H % c->c_h) return -2;
+    if (lw->conv3d && (lw->kq_pre || lw->head_pre)) return -3;
+    if (lw->kq_post && (lw->c_q2 < 1 || lw->c_k2 < 1)) return -2;
+    return 0;
+}
+
+/* Public entry 3: the general layer over a set of (b, g) units and output rows
+ * [row_begin, row_end), as mta_oracle_forward.  Every kernel pointer may be
+ * NULL (stage absent); conv3d excludes kq_pre and head_pre.  Shapes:
+ * kq_pre [H][c_q][c_k]; head_pre, head_post, head_post2 [H/c_h][c_h][c_h];
+ * conv3d [H/c_h][c_h][c_h][c_q][c_k]; kq_post [H][c_q2][c_k2]. */
+int mta_oracle_layer(const double *q, const double *k, const double *v, const double *kq_pre,
+                     const double *head_pre, const double *conv3d, const double *head_post,
+                     const double *kq_post, const double *head_post2, const double *gn_w,
+                     const double *gn_b, const double *gate, int B, int H, int T, int d, int c_q,
+                     int c_k, int c_q2, int c_k2, int c_h, int exact, double eps, double depth_scale,
+                     int row_begin, int row_end, const int *units, int n_units, int chunk,
+                     int n_threads, double *out)
+{
+    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, 0, 1, eps, depth_scale, gate};
+    layer_w lw = {kq_pre, head_pre, conv3d, head_post, kq_post, head_post2, exact, c_q2, c_k2};
+    int rc = check_layer(&cf, &lw);
+    if (rc) return rc;
+    if (row_begin < 0 || row_end > T || row_begin > row_end) return -2;
+    const int G = H / c_h;
+    const int nu = units ? n_units : B * G;
+    if (chunk <= 0) chunk = row_end - row_begin;
+    if (chunk <= 0) return 0;
+    const int nchunks = (row_end - row_begin + chunk - 1) / chunk;
+    const long ntasks = (long)nu * nchunks;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads < 1) n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads) reduction(| : err)
+#endif
+    for (long t = 0; t < ntasks; ++t) {
+        const int u = units ? units[t / nchunks] : (int)(t / nchunks);
+        const int ck = (int)(t % nchunks);
+        const int b = u / G, g = u % G;
+        if (b < 0 || b >= B) { err |= 1; continue; }
+        const int r0 = row_begin + ck * chunk;
+        const int r1 = (r0 + chunk < row_end) ? r0 + chunk : row_end;
+        if (layer_rows(&cf, &lw, q, k, v, gn_w, gn_b, b, g, r0, r1, out, NULL)) err |= 1;
+    }
+    return err ? -1 : 0;
+}
+
+/* Public entry 4: every stage of the layer for one unit (b, g), all T rows
+ * (tests); any dump pointer may be NULL. */
+int mta_oracle_layer_stages(const double *q, const double *k, const double *v, const double *kq_pre,
+                            const double *head_pre, const double *conv3d, const double *head_post,
+                            const double *kq_post, const double *head_post2, const double *gn_w,
+                            const double *gn_b, const double *gate, int B, int H, int T, int d,
+                            int c_q, int c_k, int c_q2, int c_k2, int c_h, int exact, double eps,
+                            double depth_scale, int b, int g, double *S, double *Lc, double *L,
+                            double *P, double *Pa, double *P2, double *P3, double *O, double *Y,
+                            double *out)
+{
+    oracle_cfg cf = {B, H, T, d, c_q, c_k, c_h, 0, 1, eps, depth_scale, gate};
+    layer_w lw = {kq_pre, head_pre, conv3d, head_post, kq_post, head_post2, exact, c_q2, c_k2};
+    int rc = check_layer(&cf, &lw);
+    if (rc) return rc;
+    if (b < 0 || b >= B || g < 0 || g >= H / c_h) return -2;
+    layer_stages st = {S, Lc, L, P, Pa, P2, P3, O, Y};
+    return layer_rows(&cf, &lw, q, k, v, gn_w, gn_b, b, g, 0, T, out, &st);
+}
+
 int mta_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -22,7 +22,12 @@ Facts used (page "Multi-Token Attention — Paper Graph", section 3.4):
     future);
   * softmax rows are distributions over j <= i; causality;
   * hand-derived closed forms in tests/golden/hand_cases.json;
-  * brute force at T <= 8 from the definitions.
+  * brute force at T <= 8 from the definitions;
+  * the general layer ("Putting Everything Together"): brute force of the 3D
+    and repeated forms, identity kernels give standard attention, a separable
+    3D kernel theta3[a][b] = w_ab theta^b is the key-query convolution followed
+    by the pre-softmax head mix, and the layer reduces to the single
+    placements.
 """
 from __future__ import annotations
 
@@ -365,6 +370,194 @@ def pin_brute_force_tiny(lib):
         _close(got, ref, 1e-10, f"brute {cfg.short()}")
 
 
+def _brute_layer(q, k, v, gw, gb, eps, ds, c_q, c_k, c_h, exact=False, kq_pre=None, head_pre=None,
+                 conv3d=None, head_post=None, kq_post=None, head_post2=None, c_q2=0, c_k2=0):
+    """The general layer, one scalar at a time from the definitions (T <= 8)."""
+    B, H, T, d = q.shape
+    out = np.zeros_like(q)
+
+    def conv(X, th, cq, ck, i, j, ind):
+        lo = -(ck // 2)
+        s = 0.0
+        for ip in range(cq):
+            for jp in range(lo, lo + ck):
+                a, bb = i - ip, j - jp
+                if 0 <= a < T and 0 <= bb < T and (not ind or bb <= i):
+                    s += th[ip, jp - lo] * X[a][bb]
+        return s
+
+    def mix(M, w, rows):
+        return [[[sum(w[x, y] * M[y][i][j] for y in range(c_h)) for j in range(T)] for i in range(T)]
+                for x in range(c_h)]
+
+    for b in range(B):
+        for g in range(H // c_h):
+            hs = list(range(g * c_h, (g + 1) * c_h))
+            S = [[[float(np.dot(q[b, h, i], k[b, h, j])) / math.sqrt(d) for j in range(T)] for i in range(T)]
+                 for h in hs]
+            M0 = [[[S[x][i][j] if (exact or j <= i) else 0.0 for j in range(T)] for i in range(T)]
+                  for x in range(c_h)]
+            if conv3d is not None:
+                L = [[[sum(conv(M0[y], conv3d[g, x, y], c_q, c_k, i, j, exact) for y in range(c_h))
+                       for j in range(T)] for i in range(T)] for x in range(c_h)]
+            elif kq_pre is not None:
+                L = [[[conv(M0[x], kq_pre[hs[x]], c_q, c_k, i, j, exact) for j in range(T)] for i in range(T)]
+                     for x in range(c_h)]
+            else:
+                L = S
+            if head_pre is not None and conv3d is None:
+                L = mix(L, head_pre[g], T)
+            P = []
+            for x in range(c_h):
+                rows = []
+                for i in range(T):
+                    r = [L[x][i][j] for j in range(i + 1)]
+                    m = max(r)
+                    e = [math.exp(t - m) for t in r]
+                    z = sum(e)
+                    rows.append([t / z for t in e] + [0.0] * (T - i - 1))
+                P.append(rows)
+            if head_post is not None:
+                P = mix(P, head_post[g], T)
+            if kq_post is not None:
+                P = [[[conv(P[x], kq_post[hs[x]], c_q2, c_k2, i, j, False) if j <= i else 0.0
+                       for j in range(T)] for i in range(T)] for x in range(c_h)]
+            if head_post2 is not None:
+                P = mix(P, head_post2[g], T)
+            for x, h in enumerate(hs):
+                for i in range(T):
+                    o = [sum(P[x][i][j] * v[b, h, j, c] for j in range(T)) for c in range(d)]
+                    mu = sum(o) / d
+                    var = sum((t - mu) ** 2 for t in o) / d
+                    for c in range(d):
+                        out[b, h, i, c] = ((o[c] - mu) / math.sqrt(var + eps) * gw[h, c] + gb[h, c]) * ds
+    return out
+
+
+def _layer_inputs(cfg):
+    inp = I.generate(cfg)
+    n = {kk: t.double().numpy() for kk, t in inp.items()}
+    w = {kk: (vv.double().numpy() if hasattr(vv, "double") else vv)
+         for kk, vv in I.layer_weights(cfg, inp).items()}
+    return inp, n, w
+
+
+def pin_layer_brute_force(lib):
+    """The 3D-convolution and repeated forms (and a layer with every stage
+    present) against scalar brute force, T <= 8, c_q larger than T, even c_k."""
+    cases = [
+        I.small(B=1, H=4, T=7, d=4, c_q=3, c_k=4, c_h=2, form="3d", head_place=I.PRE, theta_std=0.5,
+                gn_random=True, layer=2, seed=91),
+        I.small(B=1, H=4, T=6, d=4, c_q=2, c_k=3, c_h=4, form="3d", kq_place=I.PRE_EXACT, head_place=I.PRE,
+                theta_std=0.5, seed=92),
+        I.small(B=2, H=4, T=8, d=4, c_q=3, c_k=5, c_h=2, form="repeat", c_q2=2, c_k2=4, theta_std=0.4,
+                head_std=0.4, gn_random=True, seed=93),
+        I.small(B=1, H=2, T=5, d=4, c_q=9, c_k=3, c_h=1, form="repeat", c_q2=3, c_k2=3,
+                kq_place=I.PRE_EXACT, theta_std=0.4, seed=94),
+    ]
+    for cfg in cases:
+        inp, n, w = _layer_inputs(cfg)
+        got = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                           c_h=cfg.c_h, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, lib=lib, threads=1,
+                           **I.layer_weights(cfg, inp))
+        ref = _brute_layer(n["q"], n["k"], n["v"], n["gn_w"], n["gn_b"], cfg.gn_eps, cfg.depth_scale,
+                           cfg.c_q, cfg.c_k, cfg.c_h, **w)
+        _close(got, ref, 1e-10, f"layer brute {cfg.short()}")
+    # every stage at once (3D excluded: it replaces the pre-softmax pair)
+    cfg = I.small(B=1, H=4, T=7, d=4, c_q=2, c_k=3, c_h=2, form="repeat", c_q2=3, c_k2=2, theta_std=0.4,
+                  head_std=0.4, seed=95)
+    inp, n, w = _layer_inputs(cfg)
+    extra = (torch.randn((2, 2, 2), generator=torch.Generator().manual_seed(7)) * 0.4 + torch.eye(2)).double()
+    got = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                       c_h=cfg.c_h, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, lib=lib, threads=1,
+                       head_pre=extra, **I.layer_weights(cfg, inp))
+    ref = _brute_layer(n["q"], n["k"], n["v"], n["gn_w"], n["gn_b"], cfg.gn_eps, cfg.depth_scale,
+                       cfg.c_q, cfg.c_k, cfg.c_h, head_pre=extra.numpy(), **w)
+    _close(got, ref, 1e-10, "layer brute, all stages")
+
+
+def pin_layer_identity_is_attention(lib):
+    """Identity kernels in every stage of the repeated form, and an identity
+    3D kernel, give standard causal attention (library routine)."""
+    for form in ("repeat", "3d"):
+        cfg = I.small(B=2, H=4, T=23, d=8, c_q=3, c_k=5, c_h=2, form=form, c_q2=2, c_k2=3,
+                      head_place=I.PRE if form == "3d" else I.POST, gn_random=True, seed=97)
+        inp = I.generate(cfg)
+        w = I.layer_weights(cfg, inp)
+        for name in ("kq_pre", "kq_post"):
+            if name in w:
+                t = torch.zeros_like(w[name])
+                t[:, 0, t.shape[2] // 2] = 1.0
+                w[name] = t
+        for name in ("head_post", "head_post2"):
+            if name in w:
+                w[name] = torch.eye(cfg.c_h).expand(cfg.groups, cfg.c_h, cfg.c_h).contiguous()
+        if "conv3d" in w:
+            t = torch.zeros_like(w["conv3d"])
+            for a in range(cfg.c_h):
+                t[:, a, a, 0, cfg.c_k // 2] = 1.0
+            w["conv3d"] = t
+        got = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                           c_h=cfg.c_h, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, lib=lib, threads=2, **w)
+        ref = _gn64(_sdpa64(inp["q"], inp["k"], inp["v"]), inp["gn_w"], inp["gn_b"], cfg.gn_eps,
+                    cfg.depth_scale)
+        _close(got, ref.numpy(), 1e-10, f"layer identity {form}")
+
+
+def pin_layer_separable_3d(lib):
+    """A separable 3D kernel theta3[a][b] = w_ab theta^b is the key-query
+    convolution of each head followed by the pre-softmax head mix (linearity),
+    and the layer with one key-query and one head stage equals every single
+    placement of the two convolutions."""
+    cfg = I.small(B=1, H=4, T=19, d=8, c_q=3, c_k=5, c_h=2, kq_place=I.PRE, head_place=I.PRE,
+                  theta_std=0.3, head_std=0.3, seed=98)
+    inp = I.generate(cfg)
+    th, w = inp["theta_kq"].double(), inp["theta_head"].double()
+    G, ch = cfg.groups, cfg.c_h
+    t3 = torch.zeros((G, ch, ch, cfg.c_q, cfg.c_k), dtype=torch.float64)
+    for g in range(G):
+        for a in range(ch):
+            for b in range(ch):
+                t3[g, a, b] = w[g, a, b] * th[g * ch + b]
+    for exact in (False, True):
+        got = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                           c_h=ch, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, conv3d=t3, exact=exact,
+                           lib=lib, threads=2)
+        ref = oracle.forward(inp["q"], inp["k"], inp["v"], th, w, inp["gn_w"], inp["gn_b"], c_q=cfg.c_q,
+                             c_k=cfg.c_k, c_h=ch, kq_place=I.PRE_EXACT if exact else I.PRE,
+                             head_place=I.PRE, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, lib=lib,
+                             threads=2)
+        _close(got, ref, 1e-11, f"separable 3D exact={exact}")
+    for kq in (I.PRE, I.POST, I.PRE_EXACT):
+        for hd in (I.PRE, I.POST):
+            c2 = I.with_(cfg, kq_place=kq, head_place=hd)
+            got = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q,
+                               c_k=cfg.c_k, c_h=ch, eps=cfg.gn_eps, depth_scale=cfg.depth_scale, lib=lib,
+                               threads=2, **I.layer_weights(c2, inp))
+            ref = oracle.forward_cfg(c2, inp, lib=lib, threads=2)
+            _close(got, ref, 1e-12, f"layer = placement {c2.short()}")
+
+
+def pin_layer_causality(lib):
+    """Changing q, k, v after position t leaves the layer's output up to t
+    bitwise unchanged (3D and repeated forms)."""
+    for form in ("3d", "repeat"):
+        cfg = I.small(B=1, H=4, T=29, d=8, c_q=4, c_k=7, c_h=2, form=form, c_q2=3, c_k2=5,
+                      head_place=I.PRE if form == "3d" else I.POST, seed=99)
+        inp = I.generate(cfg)
+        base = oracle.forward_cfg(cfg, inp, lib=lib, threads=2)
+        t = 13
+        gen = torch.Generator().manual_seed(4)
+        for name in ("q", "k", "v"):
+            pert = dict(inp)
+            x = pert[name].clone()
+            x[:, :, t + 1:] += torch.randn(x[:, :, t + 1:].shape, generator=gen) * 5
+            pert[name] = x
+            o2 = oracle.forward_cfg(cfg, pert, lib=lib, threads=2)
+            assert np.array_equal(base[:, :, :t + 1], o2[:, :, :t + 1]), (form, name)
+            assert not np.array_equal(base[:, :, t + 1:], o2[:, :, t + 1:])
+
+
 ALL_PINS = [
     pin_identity_is_causal_attention,
     pin_sigmoid_gate,
@@ -377,4 +570,8 @@ ALL_PINS = [
     pin_causality,
     pin_hand_cases,
     pin_brute_force_tiny,
+    pin_layer_brute_force,
+    pin_layer_identity_is_attention,
+    pin_layer_separable_3d,
+    pin_layer_causality,
 ]

@@ -17,6 +17,8 @@ MUTANTS = {
     7: "softmax rows not normalised",
     8: "head gate used without its sigmoid",
     9: "exact indicator taken against the input row",
+    10: "3D kernel with output and source head swapped",
+    11: "Mask_0 after the post-softmax convolution dropped in the layer",
 }
 
 

@@ -58,6 +58,13 @@ class MTAConfig:
     gn_random: bool = False
     gated: bool = False   # per-head sigmoid gate on the GroupNorm output
     gate_std: float = 1.0  # spread of the gate logits g_h ~ N(0, gate_std^2)
+    # "std": one key-query and one head convolution, placed by kq_place / head_place;
+    # "3d": the both-pre-softmax 3D convolution (kernel [G][c_h][c_h][c_q][c_k]);
+    # "repeat": kq conv before the softmax, head mix after it, then a second
+    #   key-query (c_q2 x c_k2) and head convolution after the softmax
+    form: str = "std"
+    c_q2: int = 0
+    c_k2: int = 0
 
     @property
     def depth_scale(self) -> float:
@@ -81,6 +88,13 @@ class MTAConfig:
         matrix cores (4d), the key-query stencil (2 c_q c_k) and the head mix
         (2 c_h) on the vector ALUs."""
         n = float(self.causal_logits())
+        if self.form == "3d":      # c_h source kernels per output head, no separate mix
+            return {"contraction": n * 4 * self.d, "stencil": n * 2 * self.c_q * self.c_k * self.c_h,
+                    "mix": 0.0}
+        if self.form == "repeat":  # two key-query and two head convolutions
+            return {"contraction": n * 4 * self.d,
+                    "stencil": n * 2 * (self.c_q * self.c_k + self.c_q2 * self.c_k2),
+                    "mix": n * 4 * self.c_h}
         return {
             "contraction": n * 4 * self.d,
             "stencil": n * 2 * self.c_q * self.c_k,
@@ -95,8 +109,10 @@ class MTAConfig:
     def short(self) -> str:
         kq = {PRE: "pre", POST: "post", PRE_EXACT: "exact"}[self.kq_place]
         hd = "pre" if self.head_place == PRE else "post"
+        form = "" if self.form == "std" else f"_{self.form}" + (
+            f"{self.c_q2}x{self.c_k2}" if self.form == "repeat" else "")
         return (f"{self.name}:B{self.B}H{self.H}T{self.T}d{self.d}"
-                f"_cq{self.c_q}ck{self.c_k}ch{self.c_h}_kq{kq}_head{hd}_{self.dtype}")
+                f"_cq{self.c_q}ck{self.c_k}ch{self.c_h}_kq{kq}_head{hd}{form}_{self.dtype}")
 
 
 def _configs() -> Dict[str, MTAConfig]:
@@ -118,6 +134,10 @@ def _configs() -> Dict[str, MTAConfig]:
     c["needle4k_gated"] = replace(c["needle4k"], name="needle4k_gated", layer=1, gated=True)
     # the same layer with Eq. 4's exact causal indicator instead of two-pass masks
     c["needle4k_exact"] = replace(c["needle4k"], name="needle4k_exact", kq_place=PRE_EXACT)
+    # the both-pre-softmax 3D convolution, and the repeated convolution after the
+    # softmax ("Putting Everything Together"), on the same layer
+    c["needle4k_3d"] = replace(c["needle4k"], name="needle4k_3d", form="3d", head_place=PRE)
+    c["needle4k_repeat"] = replace(c["needle4k"], name="needle4k_repeat", form="repeat", c_q2=6, c_k2=11)
     for (cq, ck) in ((4, 9), (6, 11), (8, 15)):
         for ch in (2, 4):
             for kq in (PRE, POST):
@@ -188,6 +208,19 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
                 k[b, h, pos] = 3.0 * u
                 q[b, h, cfg.T - nq:] += u
 
+    # kernels of the 3D and repeated forms, drawn after everything else so that
+    # the other inputs do not depend on the form
+    theta3 = theta2 = w2 = None
+    if cfg.form == "3d":
+        theta3 = torch.randn((cfg.groups, cfg.c_h, cfg.c_h, cfg.c_q, cfg.c_k), generator=g) * cfg.theta_std
+        for a in range(cfg.c_h):
+            theta3[:, a, a, 0, cfg.c_k // 2] += 1.0  # identity: each head's own delta
+    elif cfg.form == "repeat":
+        theta2 = torch.randn((cfg.H, cfg.c_q2, cfg.c_k2), generator=g) * cfg.theta_std
+        theta2[:, 0, cfg.c_k2 // 2] += 1.0
+        w2 = torch.randn((cfg.groups, cfg.c_h, cfg.c_h), generator=g) * cfg.head_std
+        w2 += torch.eye(cfg.c_h).expand(cfg.groups, cfg.c_h, cfg.c_h)
+
     dt = DTYPES[cfg.dtype]
     out = {
         "q": q.to(dt).contiguous(),
@@ -200,9 +233,38 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
     }
     if gate is not None:
         out["gate"] = gate.float().contiguous()
+    if theta3 is not None:
+        out["theta_3d"] = theta3.float().contiguous()
+    if theta2 is not None:
+        out["theta_kq2"] = theta2.float().contiguous()
+        out["theta_head2"] = w2.float().contiguous()
     if device != "cpu":
         out = {kk: t.to(device) for kk, t in out.items()}
     return out
+
+
+def layer_weights(cfg: MTAConfig, inp: Dict[str, torch.Tensor]) -> Dict:
+    """The kernels of a configuration as stages of the general layer (kq_pre,
+    head_pre, conv3d, head_post, kq_post, head_post2; absent stages omitted)
+    plus the flags exact, c_q2, c_k2.  Pure bookkeeping of which tensor fills
+    which stage."""
+    exact = cfg.kq_place == PRE_EXACT
+    if cfg.form == "3d":
+        return {"conv3d": inp["theta_3d"], "exact": exact}
+    if cfg.form == "repeat":
+        return {"kq_pre": inp["theta_kq"], "head_post": inp["theta_head"], "kq_post": inp["theta_kq2"],
+                "head_post2": inp["theta_head2"], "exact": exact, "c_q2": cfg.c_q2, "c_k2": cfg.c_k2}
+    w = {"exact": exact}
+    if cfg.kq_place == POST:
+        w.update(kq_post=inp["theta_kq"], c_q2=cfg.c_q, c_k2=cfg.c_k)
+    else:
+        w["kq_pre"] = inp["theta_kq"]
+    # on the same side of the softmax the key-query convolution comes first
+    if cfg.head_place == PRE:
+        w["head_pre"] = inp["theta_head"]
+    else:
+        w["head_post2" if cfg.kq_place == POST else "head_post"] = inp["theta_head"]
+    return w
 
 
 def with_(cfg: MTAConfig, **kw) -> MTAConfig:

@@ -219,6 +219,7 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.T,
                    "head_dim": cfg.d, "c_q": cfg.c_q, "c_k": cfg.c_k, "c_h": cfg.c_h,
                    "kq_place": {I.PRE: "pre", I.POST: "post", I.PRE_EXACT: "exact"}[cfg.kq_place],
+                   "form": cfg.form, "c_q2": cfg.c_q2, "c_k2": cfg.c_k2,
                    "head_place": "pre" if cfg.head_place == I.PRE else "post",
                    "needles": cfg.needles, "depth_scale": cfg.depth_scale, "global_batch": cfg.B,
                    "parallelism": "single GPU"},
@@ -242,13 +243,23 @@ def stages(cfg, dev, timed, t, torch):
     placement), and the cache-flushed launch time."""
     from transformer_attention_variant_amd import binding
     from transformer_attention_variant_amd import inputs as I
-    c11 = I.with_(cfg, name=cfg.name + "_1x1", c_q=1, c_k=1)
+    dv = dev["q"].device
+    c11 = I.with_(cfg, name=cfg.name + "_1x1", c_q=1, c_k=1, c_q2=1 if cfg.form == "repeat" else cfg.c_q2,
+                  c_k2=1 if cfg.form == "repeat" else cfg.c_k2)
     d11 = dict(dev)
-    d11["theta_kq"] = torch.ones((cfg.H, 1, 1), dtype=torch.float32, device=dev["q"].device)
+    d11["theta_kq"] = torch.ones((cfg.H, 1, 1), dtype=torch.float32, device=dv)
+    if "theta_3d" in dev:  # each output head's own delta
+        d11["theta_3d"] = torch.eye(cfg.c_h, device=dv).expand(cfg.groups, cfg.c_h, cfg.c_h)\
+            .reshape(cfg.groups, cfg.c_h, cfg.c_h, 1, 1).contiguous()
+    if "theta_kq2" in dev:
+        d11["theta_kq2"] = torch.ones((cfg.H, 1, 1), dtype=torch.float32, device=dv)
     _, ms11 = timed(c11, d11)
     t11 = ms11 / 1e3
     n = float(cfg.causal_logits())
-    st_alg = 2.0 * (cfg.c_q * cfg.c_k - 1) * n  # the taps beyond the single one of the 1x1 run
+    # the taps beyond the single one of the 1x1 run (per source head for the 3D kernel)
+    taps = {"3d": cfg.c_h * (cfg.c_q * cfg.c_k - 1),
+            "repeat": cfg.c_q * cfg.c_k - 1 + cfg.c_q2 * cfg.c_k2 - 1}.get(cfg.form, cfg.c_q * cfg.c_k - 1)
+    st_alg = 2.0 * taps * n
     # the difference is the convolution stage only if both runs use the same kernel
     same = binding.kernel_name(c11) == binding.kernel_name(cfg) and t > t11
     conv = (t - t11) if same else None
@@ -263,8 +274,9 @@ def stages(cfg, dev, timed, t, torch):
         "conv_stage_ms": round(conv * 1e3, 4) if same else None,
         "conv_stage_tflops": round(st_alg / conv / 1e12, 2) if same else None,
         "conv_stage_frac_valu": round(st_alg / conv / 1e12 / PEAK_VALU_TFLOPS, 4) if same else None,
-        "conv_work": "2*(c_q*c_k - 1) FLOP per causal logit (the taps beyond the 1x1 run's one), counted "
-                     "once; null when the 1x1 run selects another kernel",
+        "conv_work": "2*(c_q*c_k - 1) FLOP per causal logit and convolution (the taps beyond the 1x1 "
+                     "run's one; per source head for the 3D kernel), counted once; null when the 1x1 run "
+                     "selects another kernel",
         "ms_per_launch_flushed": round(msf, 4),
         "flush": f"{FLUSH_MIB} MiB written before every launch",
     }

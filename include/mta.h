@@ -131,6 +131,61 @@ int mta_forward_gated(const void *q, const void *k, const void *v,
                       const float *gn_w, const float *gn_b, const float *gate,
                       const mta_config *cfg, void *out, void *stream);
 
+/*
+ * The general MTA layer: every stage of "Putting Everything Together" (page
+ * "Multi-Token Attention — Paper Graph", section 3.4), each optional (NULL =
+ * absent), in this order:
+ *   L = S,  or Conv2d_kq_pre(Mask_0(S)) (Eq. 4's indicator when `exact`),  or
+ *       the both-pre-softmax 3D convolution L^a = sum_b Conv2d_conv3d[a][b](.)
+ *   L = head mix head_pre (L)                  (not with conv3d)
+ *   P = softmax(Mask_-inf(L))
+ *   P = head mix head_post (P)                 (Eq. 7)
+ *   P = Mask_0(Conv2d_kq_post(P))              (key-query convolution after it)
+ *   P = head mix head_post2 (P)                (the repeated head convolution)
+ *   O^h = P^h V^h;  GroupNorm over d, times depth_scale (and sigmoid(gate[h])).
+ * The repeated MTA convolution of the overall flow is kq_pre + head_post +
+ * kq_post + head_post2.  A head mix maps source head b to output head a of a
+ * group as in mta_forward; the key-query kernels use mta_forward's layout.
+ */
+typedef struct {
+    const float *kq_pre;     /* [H][c_q][c_k] or NULL                              */
+    const float *head_pre;   /* [H/c_h][c_h][c_h] or NULL                          */
+    const float *conv3d;     /* [H/c_h][c_h][c_h][c_q][c_k] ([g][a][b]) or NULL;    */
+                             /* excludes kq_pre and head_pre                        */
+    const float *head_post;  /* [H/c_h][c_h][c_h] or NULL                          */
+    const float *kq_post;    /* [H][c_q2][c_k2] or NULL                            */
+    const float *head_post2; /* [H/c_h][c_h][c_h] or NULL                          */
+    const float *gn_w, *gn_b;/* [H][d], required                                   */
+    const float *gate;       /* [H] gate logits or NULL                            */
+} mta_layer_weights;
+
+typedef struct {
+    int32_t batch, heads, seq_len, head_dim;
+    int32_t c_q, c_k;        /* kernel size of kq_pre / conv3d (ignored without)   */
+    int32_t c_q2, c_k2;      /* kernel size of kq_post (ignored without)           */
+    int32_t c_h;
+    int32_t exact;           /* 1: the pre-softmax convolution uses Eq. 4's         */
+                             /* indicator instead of the two-pass Mask_0            */
+    int32_t dtype;           /* MTA_F32 | MTA_BF16                                 */
+    float gn_eps, depth_scale;
+} mta_layer_config;
+
+/*
+ * mta_forward_layer — the general layer.  Pointers, layouts, alignment,
+ * asynchrony and error codes as for mta_forward; weights and cfg must be non
+ * NULL, gn_w and gn_b are required; conv3d together with kq_pre or head_pre is
+ * MTA_ERR_BAD_PLACEMENT.  A layer that is one of mta_forward's placements runs
+ * mta_forward's kernels; any other layer runs the general layer kernel, limited
+ * to c_q, c_q2 <= 16, c_k, c_k2 <= 31 and 160 KB of LDS per workgroup
+ * (MTA_ERR_UNSUPPORTED beyond).
+ */
+int mta_forward_layer(const void *q, const void *k, const void *v, const mta_layer_weights *weights,
+                      const mta_layer_config *cfg, void *out, void *stream);
+
+/* Host-only: the kernel mta_forward_layer launches for a layer, or NULL if the
+ * layer is invalid or unsupported (weights' pointers are only tested for NULL). */
+const char *mta_layer_kernel_name(const mta_layer_config *cfg, const mta_layer_weights *weights);
+
 /* Host-only: the name of the kernel mta_forward / mta_forward_gated launch for
  * this configuration (a static string, e.g. "mta_fwd_v3 (one pass,
  * matrix-core stencil)"), or NULL if the configuration is invalid or

@@ -65,12 +65,8 @@ def oracle_sampled(cfg: I.MTAConfig, inp, ranges, units) -> Tuple[np.ndarray, np
     the sampled entries."""
     ref = np.full((cfg.B, cfg.H, cfg.T, cfg.d), np.nan)
     mask = np.zeros(ref.shape, dtype=bool)
-    q, k, v = (oracle._f64(inp[n]) for n in ("q", "k", "v"))
     for (r0, r1) in ranges:
-        o = oracle.forward(q, k, v, inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"],
-                           c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place,
-                           head_place=cfg.head_place, eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
-                           gate=inp.get("gate"), rows=(r0, r1), units=units, chunk=16)
+        o = oracle.forward_cfg(cfg, inp, rows=(r0, r1), units=units, chunk=16)
         for u in units:
             b, g = divmod(u, cfg.groups)
             hs = slice(g * cfg.c_h, (g + 1) * cfg.c_h)

@@ -39,6 +39,7 @@ def test_exports_every_declared_symbol(lib):
     ("sweep8k_6x11_ch2_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
     ("sweep8k_8x15_ch4_pre", "mta_fwd_v2 (two passes, VALU stencil)"),
     ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
+    ("needle4k_3d", "mta_fwd_layer"), ("needle4k_repeat", "mta_fwd_layer"),
 ])
 def test_kernel_selection(lib, name, expect):
     """Host-only query of the kernel each workload runs (no launch)."""
@@ -50,6 +51,54 @@ def test_kernel_name_of_invalid_config(lib):
     assert lib.mta_kernel_name(None) is None
     c = cfg(c_h=3, H=6)
     assert lib.mta_kernel_name(ctypes.byref(c)) is None
+
+
+def _layer(**kw):
+    c = dict(B=2, H=4, T=100, d=128, c_q=6, c_k=11, c_q2=3, c_k2=5, c_h=2, exact=0, dtype=1, gn_eps=1e-5,
+             depth_scale=1.0)
+    c.update({k: v for k, v in kw.items() if k in c})
+    cfg = binding.MtaLayerConfig(c["B"], c["H"], c["T"], c["d"], c["c_q"], c["c_k"], c["c_q2"], c["c_k2"],
+                                 c["c_h"], c["exact"], c["dtype"], c["gn_eps"], c["depth_scale"])
+    ptrs = dict(kq_pre=0x1000, head_post=0x1000, kq_post=0x1000, head_post2=0x1000, gn_w=0x1000, gn_b=0x1000)
+    ptrs.update({k: v for k, v in kw.items() if k in binding.LAYER_KERNELS or k in ("gn_w", "gn_b", "gate")})
+    w = binding.MtaLayerWeights(*[ptrs.get(n) for n in binding.LAYER_KERNELS], ptrs.get("gn_w"),
+                                ptrs.get("gn_b"), ptrs.get("gate"))
+    return cfg, w
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0), (dict(B=0), 0),
+    (dict(H=6, c_h=4), -2), (dict(c_q=0), -2), (dict(c_k2=0), -2),
+    (dict(conv3d=0x1000), -3), (dict(exact=2), -3),
+    (dict(dtype=3), -4), (dict(gn_eps=-1.0), -8),
+    (dict(d=96), -6), (dict(c_q2=17), -6), (dict(c_k=32), -6),
+    (dict(kq_post=None, c_q2=0), 0), (dict(kq_pre=None, c_q=0), 0),
+])
+def test_layer_validation(lib, kw, code):
+    """mta_forward_layer validates on the host before any device work (the
+    tensor pointers here are never dereferenced; B = 0 returns before them)."""
+    cfg, w = _layer(**kw)
+    if code == 0:
+        got = lib.mta_layer_kernel_name(ctypes.byref(cfg), ctypes.byref(w))
+        assert got is not None
+    else:
+        assert lib.mta_forward_layer(0x10000, 0x10000, 0x10000, ctypes.byref(w), ctypes.byref(cfg), 0x10000,
+                                     None) == code
+        assert lib.mta_layer_kernel_name(ctypes.byref(cfg), ctypes.byref(w)) is None
+    assert lib.mta_forward_layer(None, None, None, None, ctypes.byref(cfg), None, None) == -1
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, "mta_fwd_layer"),                                                  # the repeated form
+    (dict(kq_post=None, head_post2=None), "mta_fwd_v3"),                    # kq pre + head post
+    (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v2"),     # kq post + head post
+    (dict(kq_pre=None, head_post2=None), "mta_fwd_layer"),                  # head mix before the kq conv
+    (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000), "mta_fwd_layer"),
+])
+def test_layer_kernel_selection(lib, kw, expect):
+    cfg, w = _layer(**kw)
+    got = lib.mta_layer_kernel_name(ctypes.byref(cfg), ctypes.byref(w))
+    assert got is not None and got.decode().startswith(expect), got
 
 
 def test_version_and_status_strings(lib):

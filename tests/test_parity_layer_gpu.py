@@ -1,0 +1,148 @@
+"""GPU parity of the general MTA layer (mta_forward_layer) against the
+oracle's general layer on the same seeded inputs: the both-pre-softmax 3D
+convolution and the repeated convolution after the softmax ("Putting
+Everything Together"), layers with every stage, without a pre-softmax
+convolution or with head mixes only, and layers that are one of mta_forward's
+placements (which must give bitwise mta_forward's result).  Same tolerances as
+the other parity tests."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import compare, oracle_sampled, run_gpu, sample_plan, to_dev
+from transformer_attention_variant_amd import binding
+from transformer_attention_variant_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cases():
+    P, E = I.PRE, I.PRE_EXACT
+    c = []
+    for (d, dt, ch) in ((32, "f32", 1), (32, "f32", 2), (64, "f32", 4), (128, "bf16", 2), (64, "bf16", 4)):
+        c.append(I.small(f"3d_{dt}_d{d}_ch{ch}", B=1, H=4, T=90, d=d, c_q=3, c_k=5, c_h=ch, form="3d",
+                         head_place=P, dtype=dt, theta_std=0.2, seed=900 + d + ch))
+    c.append(I.small("3d_exact_f32", B=2, H=4, T=70, d=64, c_q=4, c_k=4, c_h=2, form="3d", kq_place=E,
+                     head_place=P, theta_std=0.2, seed=911))
+    c.append(I.small("3d_bf16_6x11", B=1, H=4, T=150, d=128, c_q=6, c_k=11, c_h=2, form="3d", head_place=P,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=912))
+    for (d, dt, ch, cq, ck, cq2, ck2) in ((64, "f32", 2, 3, 5, 2, 4), (32, "f32", 4, 2, 3, 3, 3),
+                                          (128, "bf16", 2, 6, 11, 6, 11), (128, "bf16", 4, 4, 9, 4, 9),
+                                          (64, "f32", 1, 16, 31, 1, 1)):
+        c.append(I.small(f"repeat_{dt}_d{d}_ch{ch}_{cq}x{ck}_{cq2}x{ck2}", B=1, H=4, T=130, d=d, c_q=cq, c_k=ck,
+                         c_h=ch, form="repeat", c_q2=cq2, c_k2=ck2, dtype=dt, theta_std=0.1, head_std=0.1,
+                         seed=920 + cq + ck2))
+    c.append(I.small("repeat_exact_f32", B=2, H=2, T=77, d=32, c_q=3, c_k=6, c_h=2, form="repeat", c_q2=2,
+                     c_k2=5, kq_place=E, theta_std=0.2, head_std=0.2, gn_random=True, seed=931))
+    c.append(I.small("repeat_f32_T3", B=1, H=2, T=3, d=32, c_q=3, c_k=5, c_h=2, form="repeat", c_q2=4, c_k2=3,
+                     seed=932))
+    return c
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_layer_forms(cfg):
+    _say(f"[layer] {cfg.short()}")
+    inp = I.generate(cfg)
+    got = run_gpu(cfg, inp)
+    ref = oracle.forward_cfg(cfg, inp)
+    compare(cfg, got, ref, what="layer")
+
+
+def _extra_mix(cfg, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.eye(cfg.c_h) + 0.2 * torch.randn((cfg.groups, cfg.c_h, cfg.c_h), generator=g)).contiguous()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_layer_stage_combinations(dt):
+    """Every stage at once; no pre-softmax convolution (head mix before the
+    post-softmax one); head mixes only; a gate."""
+    d = 64 if dt == "f32" else 128
+    cfg = I.small("all", B=1, H=4, T=100, d=d, c_q=3, c_k=5, c_h=2, form="repeat", c_q2=3, c_k2=4, dtype=dt,
+                  theta_std=0.15, head_std=0.15, gated=True, seed=940)
+    inp = I.generate(cfg)
+    dev = to_dev(inp)
+    base = I.layer_weights(cfg, inp)
+    exact = base.pop("exact")
+    for c in ("c_q2", "c_k2"):
+        base.pop(c)
+    combos = {
+        "all": dict(base, head_pre=_extra_mix(cfg, 1)),
+        "no_pre": dict(head_post=base["head_post"], kq_post=base["kq_post"], head_post2=base["head_post2"]),
+        "mixes_only": dict(head_pre=_extra_mix(cfg, 2), head_post=base["head_post"]),
+        "pre_only": dict(kq_pre=base["kq_pre"]),
+    }
+    for name, w in combos.items():
+        _say(f"[layer] combination {name} {dt}")
+        got = binding.forward_layer(dev["q"], dev["k"], dev["v"], dev["gn_w"], dev["gn_b"], c_h=cfg.c_h,
+                                    c_q=cfg.c_q, c_k=cfg.c_k, c_q2=cfg.c_q2, c_k2=cfg.c_k2, exact=exact,
+                                    gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale, gate=dev["gate"],
+                                    **{k: v.cuda() for k, v in w.items()})
+        torch.cuda.synchronize()
+        ref = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                           c_h=cfg.c_h, c_q2=cfg.c_q2, c_k2=cfg.c_k2, exact=exact, eps=cfg.gn_eps,
+                           depth_scale=cfg.depth_scale, gate=inp["gate"], **w)
+        compare(cfg, got, ref, what=f"layer {name}")
+
+
+@pytest.mark.parametrize("kq,hd", [(I.PRE, I.POST), (I.POST, I.POST), (I.PRE, I.PRE), (I.POST, I.PRE),
+                                   (I.PRE_EXACT, I.POST)])
+def test_layer_placements_are_mta_forward(kq, hd):
+    """A layer with one key-query and one head convolution runs mta_forward's
+    kernel: bitwise the same output."""
+    cfg = I.small("placement", B=1, H=4, T=140, d=128, c_q=6, c_k=11, c_h=2, kq_place=kq, head_place=hd,
+                  dtype="bf16", qkv_std=0.7071, seed=950 + kq + 3 * hd)
+    inp = I.generate(cfg)
+    dev = to_dev(inp)
+    a = run_gpu(cfg, inp, dev).clone()
+    lcfg = I.with_(cfg, form="layer_view")
+    w = I.layer_weights(cfg, inp)
+    exact = w.pop("exact")
+    c_q2, c_k2 = w.pop("c_q2", 1), w.pop("c_k2", 1)
+    b = binding.forward_layer(dev["q"], dev["k"], dev["v"], dev["gn_w"], dev["gn_b"], c_h=cfg.c_h, c_q=cfg.c_q,
+                              c_k=cfg.c_k, c_q2=c_q2, c_k2=c_k2, exact=exact, gn_eps=cfg.gn_eps,
+                              depth_scale=cfg.depth_scale, **{k: v.cuda() for k, v in w.items()})
+    torch.cuda.synchronize()
+    assert lcfg.form == "layer_view"
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["needle4k_3d", "needle4k_repeat"])
+def test_layer_workloads_sampled(name):
+    cfg = I.CONFIGS[name]
+    _say(f"[layer] sampled {cfg.short()}")
+    inp = I.generate(cfg)
+    got = run_gpu(cfg, inp)
+    ranges, units = sample_plan(cfg)
+    ref, mask = oracle_sampled(cfg, inp, ranges, units)
+    err, tol = compare(cfg, got, ref, mask=mask, what="sampled")
+    assert np.isfinite(got.float().cpu().numpy()).all()
+    _say(f"[layer]   rows {ranges} units {units}: max abs err {err:.3e} (tol {tol:.2e})")
+
+
+def test_layer_causality_full_size():
+    cfg = I.CONFIGS["needle4k_repeat"]
+    _say(f"[layer] causality {cfg.short()}")
+    inp = I.generate(cfg)
+    dev = to_dev(inp)
+    base = run_gpu(cfg, inp, dev).clone()
+    t = cfg.T // 2 + 29
+    g = torch.Generator(device="cpu").manual_seed(6)
+    for name in ("q", "k", "v"):
+        pert = dict(dev)
+        x = pert[name].clone()
+        x[:, :, t + 1:] += torch.randn(x[:, :, t + 1:].shape, generator=g).to(x.dtype).cuda()
+        pert[name] = x
+        o2 = run_gpu(cfg, inp, pert)
+        assert torch.equal(base[:, :, :t + 1], o2[:, :, :t + 1]), name

@@ -22,8 +22,9 @@ STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA
           -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
           -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
 # names declared in include/mta.h
-EXPORTS = ("mta_forward", "mta_forward_gated", "mta_check_config", "mta_kernel_name",
-           "mta_status_string", "mta_abi_version")
+EXPORTS = ("mta_forward", "mta_forward_gated", "mta_forward_layer", "mta_check_config", "mta_kernel_name",
+           "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
+LAYER_KERNELS = ("kq_pre", "head_pre", "conv3d", "head_post", "kq_post", "head_post2")
 
 
 class MtaConfig(ctypes.Structure):
@@ -37,6 +38,19 @@ class MTAError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{STATUS.get(code, code)}: {msg}")
         self.code = code
+
+
+class MtaLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_KERNELS] + \
+        [("gn_w", ctypes.c_void_p), ("gn_b", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
+
+
+class MtaLayerConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("c_q", ctypes.c_int32), ("c_k", ctypes.c_int32),
+                ("c_q2", ctypes.c_int32), ("c_k2", ctypes.c_int32), ("c_h", ctypes.c_int32),
+                ("exact", ctypes.c_int32), ("dtype", ctypes.c_int32), ("gn_eps", ctypes.c_float),
+                ("depth_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -61,6 +75,11 @@ def load(path: Optional[str] = None):
     lib.mta_check_config.restype = ctypes.c_int
     lib.mta_status_string.argtypes = [ctypes.c_int]
     lib.mta_status_string.restype = ctypes.c_char_p
+    lib.mta_forward_layer.argtypes = [vp, vp, vp, ctypes.POINTER(MtaLayerWeights),
+                                      ctypes.POINTER(MtaLayerConfig), vp, vp]
+    lib.mta_forward_layer.restype = ctypes.c_int
+    lib.mta_layer_kernel_name.argtypes = [ctypes.POINTER(MtaLayerConfig), ctypes.POINTER(MtaLayerWeights)]
+    lib.mta_layer_kernel_name.restype = ctypes.c_char_p
     lib.mta_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_kernel_name.restype = ctypes.c_char_p
     lib.mta_abi_version.argtypes = []
@@ -75,12 +94,34 @@ def make_config(B, H, T, d, c_q, c_k, c_h, kq_place=I.PRE, head_place=I.POST, dt
     return MtaConfig(B, H, T, d, c_q, c_k, c_h, kq_place, head_place, dtype, gn_eps, depth_scale)
 
 
+def _layer_structs(B, H, T, d, dtype, c_h, c_q, c_k, c_q2, c_k2, exact, gn_eps, depth_scale, ptrs):
+    cfg = MtaLayerConfig(B, H, T, d, c_q, c_k, c_q2, c_k2, c_h, int(bool(exact)), dtype, gn_eps, depth_scale)
+    w = MtaLayerWeights(*[ptrs.get(n) for n in LAYER_KERNELS], ptrs.get("gn_w"), ptrs.get("gn_b"),
+                        ptrs.get("gate"))
+    return cfg, w
+
+
 def kernel_name(cfg: I.MTAConfig) -> Optional[str]:
     """Name of the kernel the library launches for a workload configuration."""
+    if cfg.form != "std":
+        kinds = {n: 1 for n in LAYER_KERNELS if n in I.layer_weights(cfg, _shape_only(cfg))}
+        kinds.update(gn_w=1, gn_b=1)
+        lc, lw = _layer_structs(cfg.B, cfg.H, cfg.T, cfg.d, I.F32 if cfg.dtype == "f32" else I.BF16, cfg.c_h,
+                                cfg.c_q, cfg.c_k, cfg.c_q2, cfg.c_k2, cfg.kq_place == I.PRE_EXACT, cfg.gn_eps,
+                                cfg.depth_scale, kinds)
+        r = load().mta_layer_kernel_name(ctypes.byref(lc), ctypes.byref(lw))
+        return r.decode() if r else None
     c = make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
                     I.F32 if cfg.dtype == "f32" else I.BF16, cfg.gn_eps, cfg.depth_scale)
     r = load().mta_kernel_name(ctypes.byref(c))
     return r.decode() if r else None
+
+
+def _shape_only(cfg: I.MTAConfig) -> Dict:
+    """Placeholders with the keys generate() would produce for `cfg` (no data)."""
+    keys = ["q", "k", "v", "theta_kq", "theta_head", "gn_w", "gn_b"]
+    keys += {"3d": ["theta_3d"], "repeat": ["theta_kq2", "theta_head2"]}.get(cfg.form, [])
+    return {k: None for k in keys}
 
 
 def status_string(code: int) -> str:
@@ -145,8 +186,60 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.T
     return out
 
 
+def forward_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor,
+                  *, c_h: int, c_q: int = 1, c_k: int = 1, c_q2: int = 1, c_k2: int = 1, exact: bool = False,
+                  gn_eps: float = 1e-5, depth_scale: float = 1.0, gate: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
+                  **kernels) -> torch.Tensor:
+    """The general MTA layer through ``mta_forward_layer``.  ``kernels``: any of
+    kq_pre [H,c_q,c_k], head_pre, head_post, head_post2 [H/c_h,c_h,c_h], conv3d
+    [H/c_h,c_h,c_h,c_q,c_k], kq_post [H,c_q2,c_k2] (float32 CUDA tensors; absent
+    or None = stage absent).  Asynchronous on ``stream``."""
+    lib = load()
+    unknown = set(kernels) - set(LAYER_KERNELS)
+    if unknown:
+        raise ValueError(f"unknown layer stages {sorted(unknown)}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [B, H, T, d] tensors of one dtype")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    B, H, T, d = q.shape
+    G = H // max(c_h, 1)
+    shapes = {"kq_pre": (H, c_q, c_k), "head_pre": (G, c_h, c_h), "conv3d": (G, c_h, c_h, c_q, c_k),
+              "head_post": (G, c_h, c_h), "kq_post": (H, c_q2, c_k2), "head_post2": (G, c_h, c_h),
+              "gn_w": (H, d), "gn_b": (H, d), "gate": (H,)}
+    tens = {n: t for n, t in kernels.items() if t is not None}
+    tens.update(gn_w=gn_w, gn_b=gn_b)
+    if gate is not None:
+        tens["gate"] = gate
+    for name, t in list(tens.items()) + [("q", q), ("k", k), ("v", v)]:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA (HIP) tensor")
+        if name in shapes and (t.dtype != torch.float32 or tuple(t.shape) != shapes[name]):
+            raise ValueError(f"{name} must be float32 of shape {shapes[name]}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous CUDA tensor like q")
+    lc, lw = _layer_structs(B, H, T, d, I.F32 if q.dtype == torch.float32 else I.BF16, c_h, c_q, c_k, c_q2,
+                            c_k2, exact, gn_eps, depth_scale, {n: t.data_ptr() for n, t in tens.items()})
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.mta_forward_layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(lw), ctypes.byref(lc),
+                               out.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != MTA_OK:
+        raise MTAError(rc, status_string(rc))
+    return out
+
+
 def forward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
+    if cfg.form != "std":
+        w = I.layer_weights(cfg, inp)
+        return forward_layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_h=cfg.c_h, c_q=cfg.c_q,
+                             c_k=cfg.c_k, c_q2=max(cfg.c_q2, 1), c_k2=max(cfg.c_k2, 1),
+                             exact=w.pop("exact"), gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
+                             gate=inp.get("gate"), out=out, stream=stream,
+                             **{n: t for n, t in w.items() if n in LAYER_KERNELS})
     return forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"],
                    inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place,
                    head_place=cfg.head_place, gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale,

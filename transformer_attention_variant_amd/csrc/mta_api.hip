@@ -6,6 +6,7 @@
 #include "mta.h"
 #include "mta_fwd_v2.h"
 #include "mta_fwd_v3.h"
+#include "mta_fwd_layer.h"
 #include "mta_launch.h"
 
 namespace {
@@ -200,6 +201,167 @@ int mta_forward_gated(const void *q, const void *k, const void *v, const float *
     if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
     if (!gate) return MTA_ERR_NULL_ARG;
     return forward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, gate, cfg, out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The general layer
+
+static int validate_layer(const mta_layer_config *c, const mta_layer_weights *w)
+{
+    if (!c || !w) return MTA_ERR_NULL_ARG;
+    if (c->batch < 0 || c->heads < 1 || c->seq_len < 0 || c->head_dim < 1 || c->c_h < 1 ||
+        c->heads % c->c_h != 0)
+        return MTA_ERR_BAD_SHAPE;
+    const bool pre = w->kq_pre || w->conv3d;
+    if (pre && (c->c_q < 1 || c->c_k < 1)) return MTA_ERR_BAD_SHAPE;
+    if (w->kq_post && (c->c_q2 < 1 || c->c_k2 < 1)) return MTA_ERR_BAD_SHAPE;
+    if (w->conv3d && (w->kq_pre || w->head_pre)) return MTA_ERR_BAD_PLACEMENT;
+    if (c->exact != 0 && c->exact != 1) return MTA_ERR_BAD_PLACEMENT;
+    if (c->dtype != MTA_F32 && c->dtype != MTA_BF16) return MTA_ERR_BAD_DTYPE;
+    if (!(c->gn_eps > 0.0f) || !isfinite(c->gn_eps) || !isfinite(c->depth_scale)) return MTA_ERR_BAD_VALUE;
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return MTA_ERR_UNSUPPORTED;
+    if (c->c_h != 1 && c->c_h != 2 && c->c_h != 4) return MTA_ERR_UNSUPPORTED;
+    if (pre && (c->c_q > mta::MAX_CQ || c->c_k > mta::MAX_CK)) return MTA_ERR_UNSUPPORTED;
+    if (w->kq_post && (c->c_q2 > mta::MAX_CQ || c->c_k2 > mta::MAX_CK)) return MTA_ERR_UNSUPPORTED;
+    if (c->seq_len > (1 << 24)) return MTA_ERR_UNSUPPORTED;
+    const int64_t n_qt = (c->seq_len + mta::BM - 1) / mta::BM;
+    if (n_qt * (int64_t)c->batch * (c->heads / c->c_h) > INT32_MAX) return MTA_ERR_UNSUPPORTED;
+    return MTA_OK;
+}
+
+// A layer with exactly one key-query and one head convolution in one of
+// mta_forward's placements (the key-query convolution first when both follow
+// the softmax) is that placement.
+static bool as_placement(const mta_layer_config *c, const mta_layer_weights *w, mta_config &sc,
+                         const float *&th_kq, const float *&th_head)
+{
+    if (w->conv3d) return false;
+    const int nkq = (w->kq_pre != nullptr) + (w->kq_post != nullptr);
+    const int nh = (w->head_pre != nullptr) + (w->head_post != nullptr) + (w->head_post2 != nullptr);
+    if (nkq != 1 || nh != 1) return false;
+    if (w->kq_pre) {
+        sc.kq_place = c->exact ? MTA_PRE_SOFTMAX_EXACT : MTA_PRE_SOFTMAX;
+        sc.c_q = c->c_q;
+        sc.c_k = c->c_k;
+        th_kq = w->kq_pre;
+    } else {
+        if (w->head_post) return false;  // a head mix before the post-softmax convolution
+        sc.kq_place = MTA_POST_SOFTMAX;
+        sc.c_q = c->c_q2;
+        sc.c_k = c->c_k2;
+        th_kq = w->kq_post;
+    }
+    if (w->head_pre) {
+        sc.head_place = MTA_PRE_SOFTMAX;
+        th_head = w->head_pre;
+    } else {
+        sc.head_place = MTA_POST_SOFTMAX;
+        th_head = w->head_post ? w->head_post : w->head_post2;
+    }
+    sc.batch = c->batch;
+    sc.heads = c->heads;
+    sc.seq_len = c->seq_len;
+    sc.head_dim = c->head_dim;
+    sc.c_h = c->c_h;
+    sc.dtype = c->dtype;
+    sc.gn_eps = c->gn_eps;
+    sc.depth_scale = c->depth_scale;
+    return true;
+}
+
+struct LayerPlan {
+    mta::layer::LayerFn fn = nullptr;
+    size_t lds = 0;
+    int grid = 0;
+    mta::layer::LParams p{};
+};
+
+static int make_layer_plan(const mta_layer_config *c, const mta_layer_weights *w, LayerPlan &pl)
+{
+    mta::layer::LParams &p = pl.p;
+    const int ch = c->c_h, d = c->head_dim;
+    p.H = c->heads;
+    p.T = c->seq_len;
+    p.G = c->heads / ch;
+    p.units = c->batch * p.G;
+    p.n_qt = (c->seq_len + mta::BM - 1) / mta::BM;
+    p.pre = w->conv3d ? 2 : (w->kq_pre ? 1 : 0);
+    p.exact = p.pre ? c->exact : 0;
+    p.cq1 = p.pre ? c->c_q : 1;
+    p.ck1 = p.pre ? c->c_k : 1;
+    p.cq2 = w->kq_post ? c->c_q2 : 1;
+    p.ck2 = w->kq_post ? c->c_k2 : 1;
+    p.h2 = w->kq_post ? p.cq2 - 1 : 0;
+    p.l2 = w->kq_post ? (p.ck2 + 1) / 2 - 1 : 0;
+    const int r2 = w->kq_post ? p.ck2 / 2 : 0;
+    p.h1 = p.pre ? p.cq1 - 1 : 0;
+    p.l1 = p.pre ? (p.ck1 + 1) / 2 - 1 : 0;
+    p.nLr = mta::BM + p.h2;
+    p.nLc = mta::BN + p.l2 + r2;
+    const int nlcb = (p.nLc + 15) / 16;
+    p.lpitch = nlcb * 16 + 4;
+    p.nSrb = p.pre ? (p.nLr + p.h1 + 15) / 16 : 0;
+    p.nScb = p.pre ? (16 * nlcb + p.ck1 - 1 + 15) / 16 : 0;
+    p.spitch = p.pre ? p.nScb * 16 + 4 : 0;
+    p.ck1p = (p.ck1 + 3) & ~3;
+    p.ck2p = (p.ck2 + 3) & ~3;
+    p.sc = 1.4426950408889634f / sqrtf((float)d);
+    p.eps = c->gn_eps;
+    p.depth_scale = c->depth_scale;
+    pl.grid = p.n_qt * p.units;
+    const int kq1 = p.pre ? p.cq1 : 0, kk1 = p.pre ? p.ck1 : 0;
+    const int kq2 = w->kq_post ? p.cq2 : 0, kk2 = w->kq_post ? p.ck2 : 0;
+    if (c->dtype == MTA_BF16) {
+        pl.fn = mta::find_launch_layer_bf16(d, ch, kq1, kk1, kq2, kk2);
+        pl.lds = d == 32 ? mta::layer::llayout<mta::bf16_t, 32>(p, ch).total
+                 : d == 64 ? mta::layer::llayout<mta::bf16_t, 64>(p, ch).total
+                           : mta::layer::llayout<mta::bf16_t, 128>(p, ch).total;
+    } else {
+        pl.fn = mta::find_launch_layer_f32(d, ch, kq1, kk1, kq2, kk2);
+        pl.lds = d == 32 ? mta::layer::llayout<float, 32>(p, ch).total
+                 : d == 64 ? mta::layer::llayout<float, 64>(p, ch).total
+                           : mta::layer::llayout<float, 128>(p, ch).total;
+    }
+    if (!pl.fn || pl.lds > 160 * 1024) return MTA_ERR_UNSUPPORTED;
+    return MTA_OK;
+}
+
+int mta_forward_layer(const void *q, const void *k, const void *v, const mta_layer_weights *w,
+                      const mta_layer_config *c, void *out, void *stream)
+{
+    const int vs = validate_layer(c, w);
+    if (vs != MTA_OK) return vs;
+    if (c->batch == 0 || c->seq_len == 0) return MTA_OK;
+    mta_config sc;
+    const float *th_kq = nullptr, *th_head = nullptr;
+    if (as_placement(c, w, sc, th_kq, th_head))
+        return forward_impl(q, k, v, th_kq, th_head, w->gn_w, w->gn_b, w->gate, &sc, out, stream);
+    if (!q || !k || !v || !w->gn_w || !w->gn_b || !out) return MTA_ERR_NULL_ARG;
+    const float *ws[] = {w->kq_pre, w->head_pre, w->conv3d, w->head_post, w->kq_post, w->head_post2,
+                         w->gn_w, w->gn_b, w->gate};
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MTA_ERR_MISALIGNED;
+    for (const float *x : ws)
+        if (x && !aligned4(x)) return MTA_ERR_MISALIGNED;
+    LayerPlan pl;
+    const int ps = make_layer_plan(c, w, pl);
+    if (ps != MTA_OK) return ps;
+    mta::layer::LParams &p = pl.p;
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.kq_pre = w->kq_pre; p.head_pre = w->head_pre; p.conv3d = w->conv3d;
+    p.head_post = w->head_post; p.kq_post = w->kq_post; p.head_post2 = w->head_post2;
+    p.gn_w = w->gn_w; p.gn_b = w->gn_b; p.gate = w->gate;
+    const hipError_t e = pl.fn(p, pl.grid, pl.lds, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+}
+
+const char *mta_layer_kernel_name(const mta_layer_config *c, const mta_layer_weights *w)
+{
+    if (validate_layer(c, w) != MTA_OK) return nullptr;
+    mta_config sc;
+    const float *th_kq = nullptr, *th_head = nullptr;
+    if (as_placement(c, w, sc, th_kq, th_head)) return mta_kernel_name(&sc);
+    LayerPlan pl;
+    return make_layer_plan(c, w, pl) == MTA_OK ? "mta_fwd_layer (general layer, two passes)" : nullptr;
 }
 
 }  // extern "C"

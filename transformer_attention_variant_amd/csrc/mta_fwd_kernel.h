@@ -286,33 +286,44 @@ __device__ inline void stencil16(const float *buf, int pitch, int rho, int jb, c
     }
 }
 
-// Runtime-sized variant (any c_q <= 16, c_k <= 31): same sum, read tap by tap.
+// Runtime-sized variant (any c_q <= 16, c_k <= MAX_CK): same sum.  Per query
+// offset the lane loads its window of 16 + c_k - 1 values into registers once;
+// the taps are unrolled to MAX_CK with a uniform guard, walking the window with
+// compile-time register indices (tap m multiplies window entry o + m by the
+// kernel weight of column c_k - 1 - m, read from LDS as a broadcast).
 template <>
 __device__ inline void stencil16<0, 0>(const float *buf, int pitch, int rho, int jb, const float *th,
                                        int cq, int ck, int ckp, int tlim, float out[16])
 {
+    constexpr int NWMAX = 16 + MAX_CK - 1;
+    constexpr int NW4MAX = (NWMAX + 3) / 4;
+    const int nw = 16 + ck - 1;
+    const int nw4 = (nw + 3) / 4;
 #pragma unroll
     for (int o = 0; o < 16; ++o) out[o] = 0.f;
-    if (tlim >= 16 + ck - 2) {
-        for (int ip = 0; ip < cq; ++ip) {
-            const float *row = buf + (rho - ip) * pitch + jb + ck - 1;
-            for (int jj = 0; jj < ck; ++jj) {
-                const float tv = th[ip * ckp + jj];
+    for (int ip = 0; ip < cq; ++ip) {
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(buf + (rho - ip) * pitch + jb);
+        float win[NW4MAX * 4];
 #pragma unroll
-                for (int o = 0; o < 16; ++o) out[o] = __builtin_fmaf(tv, row[o - jj], out[o]);
-            }
+        for (int t = 0; t < NW4MAX; ++t) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (t < nw4) x = row[t];
+            win[4 * t + 0] = x[0];
+            win[4 * t + 1] = x[1];
+            win[4 * t + 2] = x[2];
+            win[4 * t + 3] = x[3];
         }
-    } else {
-        // window position of row[o - jj] is ck - 1 + o - jj
-        for (int ip = 0; ip < cq; ++ip) {
-            const float *row = buf + (rho - ip) * pitch + jb + ck - 1;
-            for (int jj = 0; jj < ck; ++jj) {
-                const float tv = th[ip * ckp + jj];
+        if (tlim < nw - 1) {
 #pragma unroll
-                for (int o = 0; o < 16; ++o) {
-                    const float x = (ck - 1 + o - jj <= tlim) ? row[o - jj] : 0.f;
-                    out[o] = __builtin_fmaf(tv, x, out[o]);
-                }
+            for (int t = 0; t < NWMAX; ++t) win[t] = (t <= tlim) ? win[t] : 0.f;
+        }
+        const float *trow = th + ip * ckp;
+#pragma unroll
+        for (int m = 0; m < MAX_CK; ++m) {
+            if (m < ck) {
+                const float tv = trow[ck - 1 - m];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) out[o] = __builtin_fmaf(tv, win[o + m], out[o]);
             }
         }
     }

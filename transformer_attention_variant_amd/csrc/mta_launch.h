@@ -28,6 +28,14 @@ LaunchFn find_launch_f32(int d, int ch, int cq, int ck, int post, int hpre);
 LaunchFn find_launch_bf16(int d, int ch, int cq, int ck, int post, int hpre);
 // Pipelined 8-wave bf16 kernels (mta_fwd_v2.h); null when not instantiated.
 LaunchFn find_launch_v2(int d, int ch, int cq, int ck, int post, int exact, int hpre, int ms);
+// General-layer kernels (mta_fwd_layer.h) per element type; null when (d, c_h)
+// is not instantiated.
+namespace layer {
+struct LParams;
+typedef hipError_t (*LayerFn)(const LParams &p, int grid, size_t lds, hipStream_t s);
+}  // namespace layer
+layer::LayerFn find_launch_layer_f32(int d, int ch, int cq1, int ck1, int cq2, int ck2);
+layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, int ck2);
 // One-pass bf16 kernels (mta_fwd_v3.h); null when not instantiated.
 LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 

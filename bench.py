@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true",
                     help="skip the 1x1-kernel and cache-flushed timings")
+    ap.add_argument("--no-backward", action="store_true", help="skip the timing of mta_backward")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per (batch, head group) unit in the oracle sample, from the end (0 = all)")
     ap.add_argument("--cpu-units", type=int, default=0, help="units in the oracle sample (0 = all)")
@@ -232,9 +233,65 @@ def main():
 
     if not args.no_stages:
         res["stages"] = stages(cfg, dev, timed, t, torch)
+    if not args.no_backward and cfg.form == "std" and cfg.kq_place != I.POST and cfg.head_place == I.POST \
+            and cfg.c_h <= 2:
+        res["backward"] = backward_timing(cfg, dev, args, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args)
     print(json.dumps(res), flush=True)
+
+
+def backward_timing(cfg, dev, args, torch):
+    """mta_backward (all input gradients) on the same inputs and a seeded dout,
+    timed like the forward (HIP events around every call on the launch stream;
+    the outputs and the workspace are allocated once, outside the timed calls)."""
+    import ctypes
+    from transformer_attention_variant_amd import binding
+    from transformer_attention_variant_amd import inputs as I
+    g = torch.Generator().manual_seed(cfg.seed + 17)
+    dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.d), generator=g).to(dev["q"].dtype).cuda()
+    stream = torch.cuda.current_stream()
+    lib = binding.load()
+    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, I.POST,
+                            I.F32 if cfg.dtype == "f32" else I.BF16, cfg.gn_eps, cfg.depth_scale)
+    f32 = dict(dtype=torch.float32, device=dev["q"].device)
+    outs = [torch.empty(dev["q"].shape, **f32) for _ in range(3)] + \
+        [torch.empty(dev[n].shape, **f32) for n in ("theta_kq", "theta_head", "gn_w", "gn_b")]
+    dgate = torch.empty(dev["gate"].shape, **f32) if "gate" in dev else None
+    nws = int(lib.mta_backward_workspace_size(ctypes.byref(c)))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev["q"].device)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+
+    def call():
+        rc = lib.mta_backward(dev["q"].data_ptr(), dev["k"].data_ptr(), dev["v"].data_ptr(),
+                              dev["theta_kq"].data_ptr(), dev["theta_head"].data_ptr(), dev["gn_w"].data_ptr(),
+                              dev["gn_b"].data_ptr(), ptr(dev.get("gate")), dout.data_ptr(), ctypes.byref(c),
+                              *[o.data_ptr() for o in outs], ptr(dgate), ws.data_ptr(), nws,
+                              ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"mta_backward failed: {binding.status_string(rc)}")
+
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    torch.cuda.synchronize()
+    K = max(3, args.steps // 2)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(sum(a.elapsed_time(b) for a, b in ev) / K)
+    fl = cfg.alg_flops()
+    # algorithmic backward work per causal logit: dP3, dV, dQ, dK (8d), the
+    # transposed convolution and the kernel gradient (4 c_q c_k), the head mix (4 c_h)
+    n = float(cfg.causal_logits())
+    bw = n * (8 * cfg.d + 4 * cfg.c_q * cfg.c_k + 4 * cfg.c_h)
+    return {"ms_per_call": round(ms, 4), "tokens_per_s": round(cfg.B * cfg.T / (ms / 1e3), 1),
+            "alg_tflops": round(bw / (ms / 1e3) / 1e12, 2),
+            "alg_work": "8d + 4 c_q c_k + 4 c_h FLOP per causal logit (dP3, dV, dQ, dK; transposed "
+                        "convolution and kernel gradient; head mix), recomputation not counted",
+            "workspace_bytes": nws, "calls": K}
 
 
 def stages(cfg, dev, timed, t, torch):

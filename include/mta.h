@@ -40,6 +40,7 @@
 #ifndef MTA_H_
 #define MTA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -185,6 +186,34 @@ int mta_forward_layer(const void *q, const void *k, const void *v, const mta_lay
 /* Host-only: the kernel mta_forward_layer launches for a layer, or NULL if the
  * layer is invalid or unsupported (weights' pointers are only tested for NULL). */
 const char *mta_layer_kernel_name(const mta_layer_config *cfg, const mta_layer_weights *weights);
+
+/*
+ * mta_backward — gradients of mta_forward (mta_forward_gated when gate is not
+ * NULL) for the default placement: kq_place MTA_PRE_SOFTMAX or
+ * MTA_PRE_SOFTMAX_EXACT, head_place MTA_POST_SOFTMAX, c_h in {1, 2}
+ * (MTA_ERR_UNSUPPORTED otherwise), d in {32, 64, 128}, either dtype.  Given
+ * dout = dL/dout [B][H][T][d] (input dtype) it writes, in float32:
+ *   dq, dk, dv       [B][H][T][d]
+ *   dtheta_kq        [H][c_q][c_k]
+ *   dtheta_head      [H/c_h][c_h][c_h]
+ *   dgn_w, dgn_b     [H][d]
+ *   dgate            [H] (required if and only if gate is given)
+ * The chain rule of the forward ("Key-Query Convolution" Eq. 4 and its
+ * transpose, the softmax, Eq. 7, A.V, GroupNorm) is applied per tile on the
+ * device; nothing of size T x T is stored.  `workspace` is a device buffer of
+ * at least mta_backward_workspace_size(cfg) bytes, 256-byte aligned, owned by
+ * the caller; its contents are scratch (undefined after the call).  A smaller
+ * workspace_bytes is MTA_ERR_BAD_VALUE.  Asynchronous on `stream`; every
+ * output is overwritten.  Other arguments and error codes as mta_forward.
+ */
+int mta_backward(const void *q, const void *k, const void *v, const float *theta_kq, const float *theta_head,
+                 const float *gn_w, const float *gn_b, const float *gate, const void *dout,
+                 const mta_config *cfg, float *dq, float *dk, float *dv, float *dtheta_kq,
+                 float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace mta_backward needs for cfg (0 if cfg is invalid). */
+size_t mta_backward_workspace_size(const mta_config *cfg);
 
 /* Host-only: the name of the kernel mta_forward / mta_forward_gated launch for
  * this configuration (a static string, e.g. "mta_fwd_v3 (one pass,

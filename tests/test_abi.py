@@ -101,6 +101,32 @@ def test_layer_kernel_selection(lib, kw, expect):
     assert got is not None and got.decode().startswith(expect), got
 
 
+def test_backward_validation(lib):
+    """mta_backward's host checks (no device work on these paths)."""
+    good = 0x10000
+    c = cfg()
+    n = lib.mta_backward_workspace_size(ctypes.byref(c))
+    assert n >= 2 * 4 * 100 * 128 * 2  # dO in bf16 at least
+    args = lambda **kw: dict(dict(q=good, k=good, v=good, th=good, w=good, gw=good, gb=good, gate=None,
+                                  dout=good, dq=good, dk=good, dv=good, dth=good, dw=good, dgw=good, dgb=good,
+                                  dgate=None, ws=good, nws=n), **kw)
+
+    def call(c_, **kw):
+        a_ = args(**kw)
+        return lib.mta_backward(a_["q"], a_["k"], a_["v"], a_["th"], a_["w"], a_["gw"], a_["gb"], a_["gate"],
+                                a_["dout"], ctypes.byref(c_), a_["dq"], a_["dk"], a_["dv"], a_["dth"], a_["dw"],
+                                a_["dgw"], a_["dgb"], a_["dgate"], a_["ws"], a_["nws"], None)
+    assert call(cfg(kq_place=1)) == -6          # post-softmax key-query convolution
+    assert call(cfg(head_place=0)) == -6        # head mix before the softmax
+    assert call(cfg(H=8, c_h=4)) == -6          # c_h = 4
+    assert call(c, dq=None) == -1
+    assert call(c, gate=good, dgate=None) == -1
+    assert call(c, ws=good + 16) == -5          # workspace not 256-byte aligned
+    assert call(c, nws=n - 1) == -8             # workspace too small
+    assert call(cfg(B=0)) == 0
+    assert lib.mta_backward_workspace_size(None) == 0
+
+
 def test_version_and_status_strings(lib):
     assert lib.mta_abi_version() == 100
     for code in list(binding.STATUS) + [-99]:

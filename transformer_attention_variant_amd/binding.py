@@ -22,8 +22,8 @@ STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA
           -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
           -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
 # names declared in include/mta.h
-EXPORTS = ("mta_forward", "mta_forward_gated", "mta_forward_layer", "mta_check_config", "mta_kernel_name",
-           "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
+EXPORTS = ("mta_forward", "mta_forward_gated", "mta_forward_layer", "mta_backward", "mta_backward_workspace_size",
+           "mta_check_config", "mta_kernel_name", "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
 LAYER_KERNELS = ("kq_pre", "head_pre", "conv3d", "head_post", "kq_post", "head_post2")
 
 
@@ -80,6 +80,10 @@ def load(path: Optional[str] = None):
     lib.mta_forward_layer.restype = ctypes.c_int
     lib.mta_layer_kernel_name.argtypes = [ctypes.POINTER(MtaLayerConfig), ctypes.POINTER(MtaLayerWeights)]
     lib.mta_layer_kernel_name.restype = ctypes.c_char_p
+    lib.mta_backward.argtypes = [vp] * 9 + [ctypes.POINTER(MtaConfig)] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.mta_backward.restype = ctypes.c_int
+    lib.mta_backward_workspace_size.argtypes = [ctypes.POINTER(MtaConfig)]
+    lib.mta_backward_workspace_size.restype = ctypes.c_size_t
     lib.mta_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_kernel_name.restype = ctypes.c_char_p
     lib.mta_abi_version.argtypes = []
@@ -184,6 +188,54 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.T
     if rc != MTA_OK:
         raise MTAError(rc, status_string(rc))
     return out
+
+
+GRAD_NAMES = ("q", "k", "v", "theta_kq", "theta_head", "gn_w", "gn_b", "gate")
+
+
+def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: int, c_h: int,
+             kq_place: int = I.PRE, gn_eps: float = 1e-5, depth_scale: float = 1.0,
+             gate: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> Dict:
+    """Gradients of ``forward`` (head mix after the softmax) through
+    ``mta_backward``: returns float32 CUDA tensors keyed q, k, v, theta_kq,
+    theta_head, gn_w, gn_b (and gate).  ``dout`` is dL/dout in the input dtype.
+    Allocates the outputs and the workspace with torch (the library allocates
+    nothing)."""
+    lib = load()
+    B, H, T, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor like q")
+    for name, t in (("theta_kq", theta_kq), ("theta_head", theta_head), ("gn_w", gn_w), ("gn_b", gn_b)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, I.POST,
+                      I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"q": torch.empty(q.shape, **f32), "k": torch.empty(q.shape, **f32), "v": torch.empty(q.shape, **f32),
+         "theta_kq": torch.empty(theta_kq.shape, **f32), "theta_head": torch.empty(theta_head.shape, **f32),
+         "gn_w": torch.empty(gn_w.shape, **f32), "gn_b": torch.empty(gn_b.shape, **f32)}
+    if gate is not None:
+        g["gate"] = torch.empty(gate.shape, **f32)
+    nbytes = int(lib.mta_backward_workspace_size(ctypes.byref(cfg)))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    rc = lib.mta_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(), theta_head.data_ptr(),
+                          gn_w.data_ptr(), gn_b.data_ptr(), ptr(gate), dout.data_ptr(), ctypes.byref(cfg),
+                          g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["theta_kq"].data_ptr(),
+                          g["theta_head"].data_ptr(), g["gn_w"].data_ptr(), g["gn_b"].data_ptr(),
+                          ptr(g.get("gate")), ws.data_ptr(), ws.numel(), ctypes.c_void_p(s.cuda_stream))
+    if rc != MTA_OK:
+        raise MTAError(rc, status_string(rc))
+    return g
+
+
+def backward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], dout: torch.Tensor, stream=None) -> Dict:
+    return backward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"],
+                    dout, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, gn_eps=cfg.gn_eps,
+                    depth_scale=cfg.depth_scale, gate=inp.get("gate"), stream=stream)
 
 
 def forward_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor,

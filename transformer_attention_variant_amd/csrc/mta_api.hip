@@ -7,6 +7,7 @@
 #include "mta_fwd_v2.h"
 #include "mta_fwd_v3.h"
 #include "mta_fwd_layer.h"
+#include "mta_bwd.h"
 #include "mta_launch.h"
 
 namespace {
@@ -362,6 +363,122 @@ const char *mta_layer_kernel_name(const mta_layer_config *c, const mta_layer_wei
     if (as_placement(c, w, sc, th_kq, th_head)) return mta_kernel_name(&sc);
     LayerPlan pl;
     return make_layer_plan(c, w, pl) == MTA_OK ? "mta_fwd_layer (general layer, two passes)" : nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t mta_backward_workspace_size(const mta_config *cfg)
+{
+    if (validate(cfg) != MTA_OK) return 0;
+    const size_t rows = (size_t)cfg->batch * cfg->heads * cfg->seq_len;
+    // bf16: dO as high and low bf16 planes; fp32: one fp32 array
+    const size_t planes = cfg->dtype == MTA_BF16 ? 2 : 1;
+    const size_t el = cfg->dtype == MTA_BF16 ? 2 : 4;
+    return 3 * align256(rows * 4) + planes * align256(rows * cfg->head_dim * el);
+}
+
+int mta_backward(const void *q, const void *k, const void *v, const float *theta_kq, const float *theta_head,
+                 const float *gn_w, const float *gn_b, const float *gate, const void *dout,
+                 const mta_config *cfg, float *dq, float *dk, float *dv, float *dtheta_kq, float *dtheta_head,
+                 float *dgn_w, float *dgn_b, float *dgate, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    if (cfg->kq_place == MTA_POST_SOFTMAX || cfg->head_place != MTA_POST_SOFTMAX || cfg->c_h > 2)
+        return MTA_ERR_UNSUPPORTED;
+    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
+    if (!q || !k || !v || !theta_kq || !theta_head || !gn_w || !gn_b || !dout || !dq || !dk || !dv ||
+        !dtheta_kq || !dtheta_head || !dgn_w || !dgn_b || !workspace || (gate && !dgate))
+        return MTA_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return MTA_ERR_MISALIGNED;
+    const float *fl[] = {theta_kq, theta_head, gn_w, gn_b, gate, dq, dk, dv, dtheta_kq, dtheta_head,
+                         dgn_w, dgn_b, dgate};
+    for (const float *x : fl)
+        if (x && !aligned4(x)) return MTA_ERR_MISALIGNED;
+    if (workspace_bytes < mta_backward_workspace_size(cfg)) return MTA_ERR_BAD_VALUE;
+
+    const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
+    const int bf = cfg->dtype == MTA_BF16;
+    mta::bwd::BwdFn fn = mta::find_launch_bwd(bf, d, ch, cq, ck);
+    if (!fn) return MTA_ERR_UNSUPPORTED;
+
+    mta::bwd::BParams bp{};
+    mta::Params &p = bp.f;
+    p.q = q; p.k = k; p.v = v;
+    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b; p.gate = gate;
+    p.out = nullptr;
+    p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
+    p.G = cfg->heads / ch;
+    p.units = cfg->batch * p.G;
+    p.n_qt = (cfg->seq_len + mta::BM - 1) / mta::BM;
+    p.head_pre = 0;
+    p.exact = cfg->kq_place == MTA_PRE_SOFTMAX_EXACT;
+    p.hl = (ck + 1) / 2 - 1;
+    p.ncb = (mta::BN + ck - 1 + 15) / 16;
+    p.pitch = p.ncb * 16 + 4;
+    p.nbuf = 1;
+    p.sc = 1.4426950408889634f / sqrtf((float)d);
+    p.eps = cfg->gn_eps;
+    p.depth_scale = cfg->depth_scale;
+    bp.dout = dout;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    bp.dtheta = dtheta_kq; bp.dw = dtheta_head; bp.dgn_w = dgn_w; bp.dgn_b = dgn_b; bp.dgate = dgate;
+    const size_t rows = (size_t)cfg->batch * cfg->heads * cfg->seq_len;
+    char *ws = static_cast<char *>(workspace);
+    bp.ws_m = reinterpret_cast<float *>(ws);
+    bp.ws_il = reinterpret_cast<float *>(ws + align256(rows * 4));
+    bp.ws_D = reinterpret_cast<float *>(ws + 2 * align256(rows * 4));
+    bp.ws_dO = ws + 3 * align256(rows * 4);
+    bp.ws_dOl = ws + 3 * align256(rows * 4) + align256(rows * d * (bf ? 2 : 4));
+    bp.hr = ck / 2;
+    bp.nEr = mta::BM + cq - 1;
+    bp.nEc = mta::BN + ck - 1;
+    const int nlcb = (bp.nEc + 15) / 16;
+    bp.epitch = nlcb * 16 + 4;
+    bp.nRrb = (bp.nEr + cq - 1 + 15) / 16;
+    bp.nRcb = (16 * nlcb + ck - 1 + 15) / 16;
+    bp.xpitch = bp.nRcb * 16 + 4;
+    bp.inv_sqrt_d = 1.0f / sqrtf((float)d);
+    bp.inv_log2e = 0.6931471805599453f;
+
+    auto pad4 = [](size_t x) { return (x + 3) & ~(size_t)3; };
+    const size_t ckp = (size_t)((ck + 3) & ~3);
+    const size_t vb = bf ? (d == 32 ? mta::vbuf_bytes<mta::bf16_t, 32>()
+                                    : d == 64 ? mta::vbuf_bytes<mta::bf16_t, 64>()
+                                              : mta::vbuf_bytes<mta::bf16_t, 128>())
+                         : (d == 32 ? mta::vbuf_bytes<float, 32>()
+                                    : d == 64 ? mta::vbuf_bytes<float, 64>() : mta::vbuf_bytes<float, 128>());
+    const size_t lds_a = ((size_t)mta::EXT_R * p.pitch + pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
+                          (size_t)4 * ch * 2 * d + pad4((size_t)4 * ch)) * 4 + vb;
+    const size_t nEr4 = pad4(bp.nEr);
+    const size_t lds_b = ((size_t)bp.nRrb * 16 * bp.xpitch + (size_t)bp.nEr * bp.epitch +
+                          (size_t)ch * bp.nEr * bp.epitch + 2 * pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
+                          (size_t)ch * 3 * nEr4 + pad4((size_t)4 * ch * ch)) * 4 + vb;
+    if (lds_a > 160 * 1024 || lds_b > 160 * 1024) return MTA_ERR_UNSUPPORTED;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    mta::bwd::ZeroList z{};
+    z.p[0] = dq;          z.n[0] = rows * d;
+    z.p[1] = dtheta_kq;   z.n[1] = (size_t)cfg->heads * cq * ck;
+    z.p[2] = dtheta_head; z.n[2] = (size_t)p.G * ch * ch;
+    z.p[3] = dgn_w;       z.n[3] = (size_t)cfg->heads * d;
+    z.p[4] = dgn_b;       z.n[4] = (size_t)cfg->heads * d;
+    z.k = 5;
+    if (dgate) {
+        z.p[5] = dgate;
+        z.n[5] = (size_t)cfg->heads;
+        z.k = 6;
+    }
+    hipError_t e = mta::launch_fill_zero(z, s);
+    if (e != hipSuccess) return MTA_ERR_LAUNCH;
+    const int grid = p.n_qt * p.units;
+    e = fn(bp, grid, lds_a, grid, lds_b, s);
+    return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -1,0 +1,706 @@
+// mta_bwd.h — gradients of the MTA forward on gfx950 for the default placement:
+// key-query convolution before the softmax (two-pass masks, or Eq. 4's exact
+// indicator), head mixing after it (Eq. 7), GroupNorm x depth scale (x optional
+// sigmoid gate) (page "Multi-Token Attention — Paper Graph", section 3.4).
+//
+// Forward, per head (log2-domain quantities as in the forward kernels):
+//   S = Q K^T / sqrt(d);  X = Mask_0(S) (two-pass) or S (exact);
+//   C = Conv2d_theta(X);  P = softmax(Mask_-inf(C));  P3^a = sum_b w_ab P^b;
+//   O^a = P3^a V^a;  Y^a = (GN(O^a) * gamma + beta) * s_a.
+// Backward, given dY:
+//   dO^a from the GroupNorm backward; dV^a = P3^aT dO^a; dP3^a = dO^a V^aT;
+//   dP^b = sum_a w_ab dP3^a;  dw_ab = sum dP3^a . P^b;
+//   dC^b = P^b (dP^b - D^b),  D^b_i = sum_j P^b_ij dP^b_ij = sum_a w_ab dO^a_i . (P^b V^a)_i;
+//   dX^b = Conv2d^T_theta(dC^b);  dtheta^b = corr(dC^b, X^b);  dS = Mask_0(dX) (or dX);
+//   dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
+//
+// Kernel A (one workgroup per (b, head group, 64 query rows), 4 waves): the
+// forward again (statistics pass, then probabilities), accumulating P^b V^a for
+// every (source, output) head pair; the epilogue forms O, the GroupNorm
+// backward (dO, atomics into dgamma, dbeta, dgate) and D^b, and writes the row
+// statistics, D and dO (in the input dtype) to the workspace.
+//
+// Kernel B (one workgroup per (b, head group, 64-key tile), 4 waves) walks the
+// query tiles that reach its keys.  Per query tile it recomputes, on a region
+// extended by the convolution's reach (rows below and keys on both sides of
+// the tile, since the transposed convolution reads dC there), the logits X,
+// the convolved map and P, and dP3 on the matrix cores; forms dC in LDS;
+// accumulates dtheta (LDS atomics), dw, dV and dK (registers), computes dS with
+// the transposed stencil and adds dS K into dQ with global atomics.
+#pragma once
+
+#include "mta_fwd_layer.h"
+
+namespace mta {
+namespace bwd {
+
+constexpr int NT = 256;
+
+struct BParams {
+    Params f;                        // forward geometry and pointers (q, k, v, theta, wmix, gn, gate)
+    const void *dout;                // dY [B][H][T][d] (input dtype)
+    float *dq, *dk, *dv;             // [B][H][T][d] fp32
+    float *dtheta, *dw, *dgn_w, *dgn_b, *dgate;
+    float *ws_m, *ws_il, *ws_D;      // workspace: row statistics (log2 max, 1/sum) and D, [B][H][T]
+    void *ws_dO;                     // workspace: dO [B][H][T][d] in the input dtype (bf16: the high part)
+    void *ws_dOl;                    // workspace, bf16 only: dO - high part, in bf16
+    // kernel B geometry
+    int hr;                          // floor(c_k/2)
+    int nEr, nEc, epitch;            // extended dC region: rows, columns, floats per row
+    int nRrb, nRcb, xpitch;          // logit region: 16-row / 16-column blocks, floats per row
+    float inv_sqrt_d, inv_log2e;
+};
+
+// Buffers cleared before the kernels accumulate into them.
+struct ZeroList {
+    float *p[6];
+    size_t n[6];
+    int k;
+};
+
+typedef hipError_t (*BwdFn)(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t lds_b, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// P.V-shaped product with an fp32 A operand (lane: one row, 16 k values).  With
+// bf16 operands the A values are split into bf16 hi + lo and both are
+// multiplied (the B operand is exact input data), so the product keeps about
+// 16 significant bits of A; fp32 runs one fp32 product.
+template <int D>
+__device__ inline void pv_x(f32x4 (&acc)[D / 16], const float a[16], const bf16_t *buf, int lane)
+{
+    float hi[16], lo[16];
+#pragma unroll
+    for (int o = 0; o < 16; ++o) {
+        hi[o] = (float)(bf16_t)a[o];
+        lo[o] = a[o] - hi[o];
+    }
+    pv_mfma<D>(acc, hi, buf, lane);
+    pv_mfma<D>(acc, lo, buf, lane);
+}
+template <int D>
+__device__ inline void pv_x(f32x4 (&acc)[D / 16], const float a[16], const float *buf, int lane)
+{
+    pv_mfma<D>(acc, a, buf, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel A
+template <typename DT, int D, int CH, int CQ, int CK>
+__global__ void __launch_bounds__(NT) mta_bwd_prep(BParams bp)
+{
+    const Params &p = bp.f;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int L = blockIdx.x;
+    const int unit = L % p.units;
+    const int qt = p.n_qt - 1 - L / p.units;
+    const int b = unit / p.G, g = unit % p.G;
+    const int i0 = qt * BM;
+    const int T = p.T;
+    const int cq = CQ ? CQ : p.c_q;
+    const int ck = CK ? CK : p.c_k;
+    const int ckp = (ck + 3) & ~3;
+
+    float *sbuf = lds;
+    float *th_s = sbuf + EXT_R * p.pitch;                 // [CH][cq][ckp]
+    float *w_s = th_s + ((CH * cq * ckp + 3) & ~3);       // [CH][CH]
+    float *red = w_s + ((CH * CH + 3) & ~3);              // [4 waves][CH][2][D] partial GN sums
+    float *gred = red + 4 * CH * 2 * D;                   // [4 waves][CH] gate partials
+    DT *vbuf = reinterpret_cast<DT *>(gred + ((4 * CH + 3) & ~3));
+
+    const size_t hstride = (size_t)T * D;
+    const DT *Q = reinterpret_cast<const DT *>(p.q);
+    const DT *K = reinterpret_cast<const DT *>(p.k);
+    const DT *V = reinterpret_cast<const DT *>(p.v);
+    const int h0 = g * CH;
+    const size_t base0 = ((size_t)b * p.H + h0) * hstride;
+
+    for (int i = tid; i < CH * cq * ckp; i += NT) {
+        const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
+        th_s[i] = c < ck ? p.theta[((size_t)(h0 + a) * cq + r) * ck + c] : 0.f;
+    }
+    for (int i = tid; i < CH * CH; i += NT) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
+
+    const int io = wave * 16 + (lane & 15);
+    const int jb = 16 * (lane >> 4);
+    const int qabs = i0 + io;
+    const int rho = HALO + io;
+
+    // pass 1: statistics of the convolved logits
+    float m_c[CH], l_c[CH];
+#pragma unroll
+    for (int a = 0; a < CH; ++a) {
+        m_c[a] = NEG_INF;
+        l_c[a] = 0.f;
+    }
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int j0 = kt * BN;
+        const int tlim = p.exact ? qabs - (j0 - p.hl + jb) : (1 << 30);
+#pragma unroll
+        for (int a = 0; a < CH; ++a) {
+            float c[16];
+            __syncthreads();
+            logit_tile<DT, D, RAW>(sbuf, p, Q + base0 + a * hstride, K + base0 + a * hstride, i0, j0, nullptr,
+                                   nullptr, wave, lane);
+            __syncthreads();
+            stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + a * cq * ckp, cq, ck, ckp, tlim, c);
+            stats_update(c, j0 + jb, qabs, m_c[a], l_c[a]);
+        }
+    }
+    float M[CH], IL[CH];
+#pragma unroll
+    for (int a = 0; a < CH; ++a) stats_merge(m_c[a], l_c[a], M[a], IL[a]);
+    if (lane < 16 && qabs < T) {
+#pragma unroll
+        for (int a = 0; a < CH; ++a) {
+            const size_t ri = ((size_t)b * p.H + h0 + a) * T + qabs;
+            bp.ws_m[ri] = M[a];
+            bp.ws_il[ri] = IL[a];
+        }
+    }
+
+    // pass 2: U[s][a] = P^s V^a for every pair
+    f32x4 U[CH][CH][D / 16];
+#pragma unroll
+    for (int s = 0; s < CH; ++s)
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) U[s][a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int j0 = kt * BN;
+        const int tlim = p.exact ? qabs - (j0 - p.hl + jb) : (1 << 30);
+        float pr[CH][16];
+#pragma unroll
+        for (int s = 0; s < CH; ++s) {
+            __syncthreads();
+            logit_tile<DT, D, RAW>(sbuf, p, Q + base0 + s * hstride, K + base0 + s * hstride, i0, j0, nullptr,
+                                   nullptr, wave, lane);
+            __syncthreads();
+            stencil16<CQ, CK>(sbuf, p.pitch, rho, jb, th_s + s * cq * ckp, cq, ck, ckp, tlim, pr[s]);
+#pragma unroll
+            for (int o = 0; o < 16; ++o)
+                pr[s][o] = (j0 + jb + o <= qabs) ? __builtin_amdgcn_exp2f(pr[s][o] - M[s]) * IL[s] : 0.f;
+        }
+#pragma unroll
+        for (int a = 0; a < CH; ++a) {
+            __syncthreads();
+            load_v_tile<D>(vbuf, V + base0 + a * hstride, j0, T, tid);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < CH; ++s) pv_x<D>(U[s][a], pr[s], vbuf, lane);
+        }
+    }
+
+    // epilogue: O, GroupNorm backward, D.  Lane: rows 16*wave + 4*(lane/16) + r,
+    // columns 16*nb + lane%16.
+    const DT *dY = reinterpret_cast<const DT *>(bp.dout);
+    DT *dO_ws = reinterpret_cast<DT *>(bp.ws_dO);
+    DT *dOl_ws = reinterpret_cast<DT *>(bp.ws_dOl);
+    const int n = lane & 15;
+    float dOr[CH][D / 16][4];
+    float gpart[CH];
+#pragma unroll
+    for (int a = 0; a < CH; ++a) {
+        const int h = h0 + a;
+        const float *gw = p.gn_w + (size_t)h * D;
+        const float *gb = p.gn_b + (size_t)h * D;
+        const float sg = p.gate ? 1.0f / (1.0f + __expf(-p.gate[h])) : 1.0f;
+        const float sa = p.depth_scale * sg;
+        float dgw[D / 16], dgb[D / 16];
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) dgw[nb] = dgb[nb] = 0.f;
+        gpart[a] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = i0 + wave * 16 + 4 * (lane >> 4) + r;
+            const bool live = row < T;
+            float x[D / 16];
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+                float o = 0.f;
+#pragma unroll
+                for (int s = 0; s < CH; ++s) o = __builtin_fmaf(w_s[a * CH + s], U[s][a][nb][r], o);
+                x[nb] = o;
+            }
+            float sum = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) sum += x[nb];
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            sum += __shfl_xor(sum, 8);
+            const float mu = sum * (1.0f / D);
+            float v2 = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+                const float dl = x[nb] - mu;
+                v2 = __builtin_fmaf(dl, dl, v2);
+            }
+            v2 += __shfl_xor(v2, 1);
+            v2 += __shfl_xor(v2, 2);
+            v2 += __shfl_xor(v2, 4);
+            v2 += __shfl_xor(v2, 8);
+            const float rstd = 1.0f / __builtin_sqrtf(v2 * (1.0f / D) + p.eps);
+            float xh[D / 16], dxh[D / 16];
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+                const int col = 16 * nb + n;
+                xh[nb] = (x[nb] - mu) * rstd;
+                const float dy = live ? (float)dY[((size_t)b * p.H + h) * hstride + (size_t)row * D + col] : 0.f;
+                const float dys = dy * sa;
+                dgb[nb] += dys;
+                dgw[nb] = __builtin_fmaf(dys, xh[nb], dgw[nb]);
+                gpart[a] = __builtin_fmaf(dy, xh[nb] * gw[col] + gb[col], gpart[a]);
+                dxh[nb] = dys * gw[col];
+                s1 += dxh[nb];
+                s2 = __builtin_fmaf(dxh[nb], xh[nb], s2);
+            }
+            s1 += __shfl_xor(s1, 1);
+            s1 += __shfl_xor(s1, 2);
+            s1 += __shfl_xor(s1, 4);
+            s1 += __shfl_xor(s1, 8);
+            s2 += __shfl_xor(s2, 1);
+            s2 += __shfl_xor(s2, 2);
+            s2 += __shfl_xor(s2, 4);
+            s2 += __shfl_xor(s2, 8);
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+                const float dox = rstd * (dxh[nb] - s1 * (1.0f / D) - xh[nb] * s2 * (1.0f / D));
+                // stored as the input dtype, with the bf16 remainder in a second plane
+                const DT dh = cvt_out<DT>(dox);
+                if (live) {
+                    const size_t at = ((size_t)b * p.H + h) * hstride + (size_t)row * D + 16 * nb + n;
+                    dO_ws[at] = dh;
+                    if (sizeof(DT) == 2) dOl_ws[at] = cvt_out<DT>(dox - (float)dh);
+                }
+                dOr[a][nb][r] = live ? dox : 0.f;
+            }
+        }
+        // dgamma, dbeta: the four lane groups of a column, then the waves via LDS
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+            float u = dgw[nb], t = dgb[nb];
+            u += __shfl_xor(u, 16);
+            u += __shfl_xor(u, 32);
+            t += __shfl_xor(t, 16);
+            t += __shfl_xor(t, 32);
+            if (lane < 16) {
+                red[((wave * CH + a) * 2 + 0) * D + 16 * nb + n] = u;
+                red[((wave * CH + a) * 2 + 1) * D + 16 * nb + n] = t;
+            }
+        }
+        float gsum = gpart[a];
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) gsum += __shfl_xor(gsum, sh);
+        if (lane == 0) gred[wave * CH + a] = gsum * p.depth_scale * sg * (1.0f - sg);
+    }
+    __syncthreads();
+    for (int i = tid; i < CH * 2 * D; i += NT) {
+        const int a = i / (2 * D), which = (i / D) % 2, col = i % D;
+        float t = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) t += red[((w4 * CH + a) * 2 + which) * D + col];
+        atomicAdd((which ? bp.dgn_b : bp.dgn_w) + (size_t)(h0 + a) * D + col, t);
+    }
+    if (p.gate && tid < CH) {
+        float t = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) t += gred[w4 * CH + tid];
+        atomicAdd(bp.dgate + h0 + tid, t);
+    }
+    // D^s_i = sum_a w_as dO^a_i . (P^s V^a)_i
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float t = 0.f;
+#pragma unroll
+            for (int a = 0; a < CH; ++a) {
+                float u = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < D / 16; ++nb) u = __builtin_fmaf(dOr[a][nb][r], U[s][a][nb][r], u);
+                t = __builtin_fmaf(w_s[a * CH + s], u, t);
+            }
+            t += __shfl_xor(t, 1);
+            t += __shfl_xor(t, 2);
+            t += __shfl_xor(t, 4);
+            t += __shfl_xor(t, 8);
+            const int row = i0 + wave * 16 + 4 * (lane >> 4) + r;
+            if (n == 0 && row < T) bp.ws_D[((size_t)b * p.H + h0 + s) * T + row] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B helpers
+
+// Transposed key-query stencil: 16 outputs of one row of dX,
+//   dX[r][c] = sum_{i'} sum_{jj} theta[i'][jj] dC[r + i'][c + jj - floor(c_k/2)],
+// from the extended dC region (its row er + i' holds dC row r + i', its column
+// jb + o + jj holds key c + jj - floor(c_k/2) for output column c = j0 + jb + o).
+// With Eq. 4's indicator the terms of query offset i' count only where
+// c <= r + i', i.e. o <= dlim + i' with dlim = r - j0 - jb.
+template <int CQ, int CK>
+__device__ inline void stencil16_t(const float *ebuf, int pitch, int er, int jb, const float *th, int cq_rt,
+                                   int ck_rt, int ckp, int dlim, float out[16])
+{
+    constexpr int MAXW = CK ? 16 + CK - 1 : 16 + MAX_CK - 1;
+    constexpr int MAXW4 = (MAXW + 3) / 4;
+    constexpr int KMAX = CK ? CK : MAX_CK;
+    const int cq = CQ ? CQ : cq_rt;
+    const int ck = CK ? CK : ck_rt;
+    const int nw4 = (16 + ck - 1 + 3) / 4;
+#pragma unroll
+    for (int o = 0; o < 16; ++o) out[o] = 0.f;
+    for (int ip = 0; ip < cq; ++ip) {
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(ebuf + (er + ip) * pitch + jb);
+        float win[MAXW4 * 4];
+#pragma unroll
+        for (int t = 0; t < MAXW4; ++t) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (CK || t < nw4) x = row[t];
+            win[4 * t + 0] = x[0];
+            win[4 * t + 1] = x[1];
+            win[4 * t + 2] = x[2];
+            win[4 * t + 3] = x[3];
+        }
+        const float *trow = th + ip * ckp;
+        float tmp[16];
+#pragma unroll
+        for (int o = 0; o < 16; ++o) tmp[o] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < KMAX; ++jj) {
+            if (CK || jj < ck) {
+                const float tv = trow[jj];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) tmp[o] = __builtin_fmaf(tv, win[o + jj], tmp[o]);
+            }
+        }
+#pragma unroll
+        for (int o = 0; o < 16; ++o) out[o] += (o <= dlim + ip) ? tmp[o] : 0.f;
+    }
+}
+
+// dtheta[i'][jj] += sum_o g[o] * X[row - i'][col(o) + floor(c_k/2) - jj] for the
+// lane's 16 values g (one row, 16 keys), accumulated into LDS (atomics).  The
+// logit region's row rx0 holds the lane's row minus 0 offsets: window of query
+// offset i' starts at row rx0 - i', column xc0 (the key col(0) - (c_k - 1) +
+// floor(c_k/2)); window entries t > tlim are keys in the future of the row
+// (Eq. 4's indicator) and are skipped.
+template <int CQ, int CK>
+__device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, const float g[16], float *dth,
+                                int cq_rt, int ck_rt, int ckp, int tlim)
+{
+    constexpr int MAXW = CK ? 16 + CK - 1 : 16 + MAX_CK - 1;
+    constexpr int MAXW4 = (MAXW + 3) / 4;
+    constexpr int KMAX = CK ? CK : MAX_CK;
+    const int cq = CQ ? CQ : cq_rt;
+    const int ck = CK ? CK : ck_rt;
+    const int nw = 16 + ck - 1;
+    const int nw4 = (nw + 3) / 4;
+    for (int ip = 0; ip < cq; ++ip) {
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(xbuf + (rx0 - ip) * pitch + xc0);
+        float win[MAXW4 * 4];
+#pragma unroll
+        for (int t = 0; t < MAXW4; ++t) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (CK || t < nw4) x = row[t];
+            win[4 * t + 0] = x[0];
+            win[4 * t + 1] = x[1];
+            win[4 * t + 2] = x[2];
+            win[4 * t + 3] = x[3];
+        }
+        if (tlim < nw - 1) {
+#pragma unroll
+            for (int t = 0; t < MAXW; ++t) win[t] = (t <= tlim) ? win[t] : 0.f;
+        }
+        // tap jj reads window entry o + c_k - 1 - jj; with m = c_k - 1 - jj the
+        // register index o + m is static
+#pragma unroll
+        for (int m = 0; m < KMAX; ++m) {
+            if (CK || m < ck) {
+                float acc = 0.f;
+#pragma unroll
+                for (int o = 0; o < 16; ++o) acc = __builtin_fmaf(g[o], win[o + m], acc);
+                atomicAdd(dth + ip * ckp + (ck - 1 - m), acc);
+            }
+        }
+    }
+}
+
+// dP3 tile: buf[row][col] = dO[r0 + row] . V[c0 + col] over rows < nrows (0
+// outside [0, T)); with SPLIT the product of the low plane of dO is added.
+template <typename DT, int D, bool SPLIT>
+__device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nrows, const DT *dh, const DT *dl,
+                                 const DT *vh, int r0, int c0, int T, int wave, int lane)
+{
+    typedef typename FragOf<DT, D>::type Frag;
+    Frag hf, lf, vf;
+    for (int rb = wave; rb < nrb; rb += 4) {
+        const int qi = r0 + 16 * rb + (lane & 15);
+        load_frag<D>(hf, dh, qi, T, lane);
+        if (SPLIT) load_frag<D>(lf, dl, qi, T, lane);
+        for (int cb = 0; cb < ncb; ++cb) {
+            load_frag<D>(vf, vh, c0 + 16 * cb + (lane & 15), T, lane);
+            f32x4 acc = qk_mfma<D>(vf, hf);
+            if (SPLIT) {
+                const f32x4 a2 = qk_mfma<D>(vf, lf);
+                acc += a2;
+            }
+            if (16 * rb + (lane & 15) < nrows)
+                *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B
+template <typename DT, int D, int CH, int CQ, int CK>
+__global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
+{
+    const Params &p = bp.f;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int L = blockIdx.x;
+    const int unit = L % p.units;
+    const int kt = L / p.units;  // workgroups with the most query tiles first
+    const int b = unit / p.G, g = unit % p.G;
+    const int j0 = kt * BN;
+    const int T = p.T;
+    const int cq = CQ ? CQ : p.c_q;
+    const int ck = CK ? CK : p.c_k;
+    const int ckp = (ck + 3) & ~3;
+    const int hr = bp.hr, hl = p.hl;
+    const int nEr = bp.nEr, nEc = bp.nEc, ep = bp.epitch, xp = bp.xpitch;
+
+    // LDS carve-up
+    float *xbuf = lds;                                            // logits X / later dS core
+    float *ebuf = xbuf + bp.nRrb * 16 * xp;                       // C -> P -> dC (extended region)
+    float *dpb = ebuf + nEr * ep;                                 // dP3^a, [CH][nEr][ep]
+    float *th_s = dpb + CH * nEr * ep;                            // [CH][cq][ckp]
+    float *w_s = th_s + ((CH * cq * ckp + 3) & ~3);
+    float *dth = w_s + ((CH * CH + 3) & ~3);                      // [CH][cq][ckp] accumulated dtheta
+    float *st = dth + ((CH * cq * ckp + 3) & ~3);                 // [CH][3][nEr4]: m, il, D of the region rows
+    const int nEr4 = (nEr + 3) & ~3;
+    float *dwr = st + CH * 3 * nEr4;                              // [4 waves][CH*CH]
+    DT *opbuf = reinterpret_cast<DT *>(dwr + ((4 * CH * CH + 3) & ~3));
+
+    const size_t hstride = (size_t)T * D;
+    const DT *Q = reinterpret_cast<const DT *>(p.q);
+    const DT *K = reinterpret_cast<const DT *>(p.k);
+    const DT *V = reinterpret_cast<const DT *>(p.v);
+    const DT *dO = reinterpret_cast<const DT *>(bp.ws_dO);
+    const DT *dOl = reinterpret_cast<const DT *>(bp.ws_dOl);
+    constexpr bool SPLIT = sizeof(DT) == 2;  // bf16: dO carried as hi + lo planes
+    const int h0 = g * CH;
+    const size_t base0 = ((size_t)b * p.H + h0) * hstride;
+
+    for (int i = tid; i < CH * cq * ckp; i += NT) {
+        const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
+        th_s[i] = c < ck ? p.theta[((size_t)(h0 + a) * cq + r) * ck + c] : 0.f;
+        dth[i] = 0.f;
+    }
+    for (int i = tid; i < CH * CH; i += NT) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
+    float dwp[CH * CH];
+#pragma unroll
+    for (int i = 0; i < CH * CH; ++i) dwp[i] = 0.f;
+
+    const int io = wave * 16 + (lane & 15);  // the lane's row (stencil layout) within a query tile
+    const int jb = 16 * (lane >> 4);         // its first key within the key tile
+    const int km = wave * 16 + (lane & 15);  // its key (transposed operand layout)
+    const int rk = 16 * (lane >> 4);         // its first row (transposed operand layout)
+
+    f32x4 dK[CH][D / 16], dV[CH][D / 16];
+#pragma unroll
+    for (int a = 0; a < CH; ++a)
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+            dK[a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dV[a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int nlcb = (nEc + 15) / 16;
+    const int qt0 = p.exact ? (kt > 0 ? kt - 1 : 0) : kt;
+    for (int qt = qt0; qt < p.n_qt; ++qt) {
+        const int i0 = qt * BM;
+        const int ec0 = j0 - hr;              // key of region column 0
+        const int xr0 = i0 - (cq - 1);        // query of logit row 0
+        const int xc0 = ec0 - hl;             // key of logit column 0
+        __syncthreads();
+        // row statistics and D of the region's rows
+        for (int i = tid; i < CH * nEr; i += NT) {
+            const int a = i / nEr, r = i % nEr;
+            const int row = i0 + r;
+            const size_t ri = ((size_t)b * p.H + h0 + a) * T + row;
+            const bool live = row < T;
+            st[(a * 3 + 0) * nEr4 + r] = live ? bp.ws_m[ri] : 0.f;
+            st[(a * 3 + 1) * nEr4 + r] = live ? bp.ws_il[ri] : 0.f;
+            st[(a * 3 + 2) * nEr4 + r] = live ? bp.ws_D[ri] : 0.f;
+        }
+        // dP3^a over the region: dO^a rows x V^a keys (no scale, no mask; bf16:
+        // high and low planes of dO)
+        for (int a = 0; a < CH; ++a)
+            prod_tile<DT, D, SPLIT>(dpb + a * nEr * ep, ep, (nEr + 15) / 16, nlcb, nEr, dO + base0 + a * hstride,
+                                    dOl + base0 + a * hstride, V + base0 + a * hstride, i0, ec0, T, wave, lane);
+
+#pragma unroll
+        for (int s = 0; s < CH; ++s) {
+            __syncthreads();
+            // X^s over the logit region (log2-scaled; Mask_0 unless exact)
+            layer::s_tile<DT, D>(xbuf, xp, bp.nRrb, bp.nRcb, 16 * bp.nRrb, Q + base0 + s * hstride,
+                                 K + base0 + s * hstride, xr0, xc0, T, p.sc, p.exact != 0, wave, lane);
+            __syncthreads();
+            // C^s over the region -> P^s (in place)
+            for (int t = tid; t < nEr * nlcb; t += NT) {
+                const int r = t / nlcb, cb = t % nlcb;
+                const int qi = i0 + r;
+                const int tlim = p.exact ? qi - (xc0 + 16 * cb) : (1 << 30);
+                float o[16];
+                stencil16<CQ, CK>(xbuf, xp, r + cq - 1, 16 * cb, th_s + s * cq * ckp, cq, ck, ckp, tlim, o);
+                const float m = st[(s * 3 + 0) * nEr4 + r], il = st[(s * 3 + 1) * nEr4 + r];
+                float *dst = ebuf + r * ep + 16 * cb;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int kj = ec0 + 16 * cb + e;
+                    dst[e] = (kj >= 0 && kj <= qi && qi < T) ? __builtin_amdgcn_exp2f(o[e] - m) * il : 0.f;
+                }
+            }
+            __syncthreads();
+            // dV^a += w_as P^sT dO^a (core rows i0.., keys j0..): split P against
+            // dO's high plane, P's high part against dO's low plane
+            for (int a = 0; a < CH; ++a) {
+                __syncthreads();
+                load_v_tile<D>(opbuf, dO + base0 + a * hstride, i0, T, tid);
+                __syncthreads();
+                float at[16];
+                const float wa = w_s[a * CH + s];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) at[o] = wa * ebuf[(rk + o) * ep + hr + km];
+                pv_x<D>(dV[a], at, opbuf, lane);
+                if (SPLIT) {
+                    __syncthreads();
+                    load_v_tile<D>(opbuf, dOl + base0 + a * hstride, i0, T, tid);
+                    __syncthreads();
+                    float ah[16];
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) ah[o] = (float)(bf16_t)at[o];
+                    pv_mfma<D>(dV[a], ah, opbuf, lane);
+                }
+            }
+            __syncthreads();
+            // dC^s = P^s (sum_a w_as dP3^a - D^s) in place; dw partials over the core
+            for (int idx = tid; idx < nEr * nEc; idx += NT) {
+                const int r = idx / nEc, c = idx % nEc;
+                const float pv = ebuf[r * ep + c];
+                float dp = 0.f;
+                const bool core = r < BM && c >= hr && c < hr + BN;
+#pragma unroll
+                for (int a = 0; a < CH; ++a) {
+                    const float x = dpb[(a * nEr + r) * ep + c];
+                    dp = __builtin_fmaf(w_s[a * CH + s], x, dp);
+                    if (core) dwp[a * CH + s] = __builtin_fmaf(x, pv, dwp[a * CH + s]);
+                }
+                ebuf[r * ep + c] = pv * (dp - st[(s * 3 + 2) * nEr4 + r]);
+            }
+            __syncthreads();
+            // dtheta^s += corr(dC core, X^s)
+            {
+                float gc[16];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) gc[o] = ebuf[io * ep + hr + jb + o];
+                const int qi = i0 + io;
+                // window of the lane: logit row (io + cq-1) - i', columns from jb + hr (key j0 + jb - hl)
+                const int tlim = p.exact ? qi - (xc0 + jb + hr) : (1 << 30);
+                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim);
+            }
+            // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil;
+            // with Eq. 4's indicator the terms of offset i' count where key <= r + i'
+            float dsv[16];
+            {
+                const int r = i0 + io;
+                stencil16_t<CQ, CK>(ebuf, ep, io, jb, th_s + s * cq * ckp, cq, ck, ckp,
+                                    p.exact ? r - j0 - jb : (1 << 30), dsv);
+#pragma unroll
+                for (int o = 0; o < 16; ++o) {
+                    const int c = j0 + jb + o;
+                    const bool keep = p.exact ? true : (c <= r);
+                    dsv[o] = (keep && r < T && c < T) ? dsv[o] : 0.f;
+                }
+            }
+            __syncthreads();  // xbuf free (dtheta done), ebuf reads done
+            // dQ^s += dS K^s / sqrt(d)  (global atomics)
+            {
+                load_v_tile<D>(opbuf, K + base0 + s * hstride, j0, T, tid);
+                __syncthreads();
+                f32x4 qa[D / 16];
+#pragma unroll
+                for (int nb = 0; nb < D / 16; ++nb) qa[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pv_x<D>(qa, dsv, opbuf, lane);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int row = i0 + wave * 16 + 4 * (lane >> 4) + r4;
+                    if (row < T) {
+                        float *dst = bp.dq + ((size_t)b * p.H + h0 + s) * hstride + (size_t)row * D;
+#pragma unroll
+                        for (int nb = 0; nb < D / 16; ++nb)
+                            atomicAdd(dst + 16 * nb + (lane & 15), qa[nb][r4] * bp.inv_sqrt_d);
+                    }
+                }
+            }
+            // dS core to LDS (row-major, pitch BN + 4) for the transposed operand of dK
+            float *dsb = xbuf;
+#pragma unroll
+            for (int o = 0; o < 16; ++o) dsb[io * (BN + 4) + jb + o] = dsv[o];
+            __syncthreads();
+            load_v_tile<D>(opbuf, Q + base0 + s * hstride, i0, T, tid);
+            __syncthreads();
+            {
+                float at[16];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) at[o] = dsb[(rk + o) * (BN + 4) + km];
+                pv_x<D>(dK[s], at, opbuf, lane);
+            }
+        }
+    }
+
+    // write dK, dV of the key tile; reduce dtheta and dw into the outputs
+    for (int a = 0; a < CH; ++a) {
+        const size_t hb = ((size_t)b * p.H + h0 + a) * hstride;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int key = j0 + wave * 16 + 4 * (lane >> 4) + r4;
+            if (key < T) {
+#pragma unroll
+                for (int nb = 0; nb < D / 16; ++nb) {
+                    bp.dk[hb + (size_t)key * D + 16 * nb + (lane & 15)] = dK[a][nb][r4] * bp.inv_sqrt_d;
+                    bp.dv[hb + (size_t)key * D + 16 * nb + (lane & 15)] = dV[a][nb][r4];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CH * CH; ++i) {
+        float t = dwp[i];
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) t += __shfl_xor(t, sh);
+        if (lane == 0) dwr[wave * CH * CH + i] = t;
+    }
+    __syncthreads();
+    for (int i = tid; i < CH * CH; i += NT) {
+        const float t = dwr[i] + dwr[CH * CH + i] + dwr[2 * CH * CH + i] + dwr[3 * CH * CH + i];
+        atomicAdd(bp.dw + (size_t)g * CH * CH + i, t);
+    }
+    for (int i = tid; i < CH * cq * ckp; i += NT) {
+        const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
+        if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, dth[i] * bp.inv_log2e);
+    }
+}
+
+}  // namespace bwd
+
+bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck);
+hipError_t launch_fill_zero(const bwd::ZeroList &z, hipStream_t s);
+
+}  // namespace mta

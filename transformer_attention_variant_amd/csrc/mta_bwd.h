@@ -442,13 +442,17 @@ __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nr
         const int qi = r0 + 16 * rb + (lane & 15);
         load_frag<D>(hf, dh, qi, T, lane);
         if (SPLIT) load_frag<D>(lf, dl, qi, T, lane);
+        // the next block's V fragment is requested before this block's products
+        load_frag<D>(vf, vh, c0 + (lane & 15), T, lane);
         for (int cb = 0; cb < ncb; ++cb) {
-            load_frag<D>(vf, vh, c0 + 16 * cb + (lane & 15), T, lane);
+            Frag vn;
+            if (cb + 1 < ncb) load_frag<D>(vn, vh, c0 + 16 * (cb + 1) + (lane & 15), T, lane);
             f32x4 acc = qk_mfma<D>(vf, hf);
             if (SPLIT) {
                 const f32x4 a2 = qk_mfma<D>(vf, lf);
                 acc += a2;
             }
+            vf = vn;
             if (16 * rb + (lane & 15) < nrows)
                 *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
         }
@@ -481,8 +485,10 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     float *dpb = ebuf + nEr * ep;                                 // dP3^a, [CH][nEr][ep]
     float *th_s = dpb + CH * nEr * ep;                            // [CH][cq][ckp]
     float *w_s = th_s + ((CH * cq * ckp + 3) & ~3);
-    float *dth = w_s + ((CH * CH + 3) & ~3);                      // [CH][cq][ckp] accumulated dtheta
-    float *st = dth + ((CH * cq * ckp + 3) & ~3);                 // [CH][3][nEr4]: m, il, D of the region rows
+    // accumulated dtheta, 16 copies [copy][CH][cq][ckp] at an odd stride (banks)
+    const int dstride = ((CH * cq * ckp + 3) & ~3) + 1;
+    float *dth = w_s + ((CH * CH + 3) & ~3);
+    float *st = dth + ((16 * dstride + 3) & ~3);                  // [CH][3][nEr4]: m, il, D of the region rows
     const int nEr4 = (nEr + 3) & ~3;
     float *dwr = st + CH * 3 * nEr4;                              // [4 waves][CH*CH]
     DT *opbuf = reinterpret_cast<DT *>(dwr + ((4 * CH * CH + 3) & ~3));
@@ -500,12 +506,13 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     for (int i = tid; i < CH * cq * ckp; i += NT) {
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
         th_s[i] = c < ck ? p.theta[((size_t)(h0 + a) * cq + r) * ck + c] : 0.f;
-        dth[i] = 0.f;
     }
+    for (int i = tid; i < 16 * dstride; i += NT) dth[i] = 0.f;
     for (int i = tid; i < CH * CH; i += NT) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
     float dwp[CH * CH];
 #pragma unroll
     for (int i = 0; i < CH * CH; ++i) dwp[i] = 0.f;
+
 
     const int io = wave * 16 + (lane & 15);  // the lane's row (stencil layout) within a query tile
     const int jb = 16 * (lane >> 4);         // its first key within the key tile
@@ -613,7 +620,9 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                 const int qi = i0 + io;
                 // window of the lane: logit row (io + cq-1) - i', columns from jb + hr (key j0 + jb - hl)
                 const int tlim = p.exact ? qi - (xc0 + jb + hr) : (1 << 30);
-                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim);
+                // lanes add into one of 16 copies (lane % 16), spreading the atomics
+                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc,
+                                 dth + (lane & 15) * dstride + s * cq * ckp, cq, ck, ckp, tlim);
             }
             // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil;
             // with Eq. 4's indicator the terms of offset i' count where key <= r + i'
@@ -694,7 +703,9 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     }
     for (int i = tid; i < CH * cq * ckp; i += NT) {
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
-        if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, dth[i] * bp.inv_log2e);
+        float t = 0.f;
+        for (int cp = 0; cp < 16; ++cp) t += dth[cp * dstride + i];
+        if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, t * bp.inv_log2e);
     }
 }
 

@@ -28,21 +28,42 @@ namespace v2 {
 
 constexpr int NW = 8;
 constexpr int NT = 64 * NW;
+// LDS pitches (bf16 elements) of the row-major Q, K and V tiles.  A row of
+// D + 16 elements is an even number of 16-byte chunks plus two, so the 16 rows
+// read by one 16-lane group land on distinct bank groups; with frag_base below
+// (lane groups 0/1 and 2/3 an odd number of chunks apart) the 32 lanes served
+// together by one ds_read_b128 never share a bank, and the transposing V reads
+// are conflict-free as well.
 template <int D>
-__host__ __device__ constexpr int vpitch() { return D + 8; }  // bf16 pitch of the row-major V tile
+__host__ __device__ constexpr int kpitch() { return D + 16; }
+template <int D>
+__host__ __device__ constexpr int vpitch() { return D + 16; }
+
+// The logit product of a 16x16 block is a sum over d; lane group g4 supplies
+// the 16-byte chunk fc + 2t (fc = frag_base / 8) of its Q or K row to MFMA
+// step t.  Any assignment that covers every chunk once works when Q and K use
+// the same one.
+template <int D>
+__device__ inline int frag_base(int lane)
+{
+    const int g4 = lane >> 4;
+    return 8 * ((g4 & 1) + (D / 16) * (g4 >> 1));
+}
 
 struct Layout {
     int s_off, k_off, q_off, v_off, p_off, st_off, xs_off, th_off, w_off, gn_off, tf_off, total;
 };
 
-// bf16 pitch of the hi / lo planes of the logit tile (multiple of 8 elements)
-__host__ __device__ inline int pitch_hl(int ncb) { return ncb * 16 + 8; }
+// bf16 pitch of the hi / lo planes of the logit tile: a multiple of 8
+// elements whose 16-byte chunk count is 2 mod 4, so that the stencil's
+// ds_read_b128 (16 rows x 2 adjacent chunks per pass) never shares a bank.
+__host__ __device__ inline int pitch_hl(int ncb) { return (ncb & 1) ? ncb * 16 : ncb * 16 + 16; }
 
 __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb, int pitch, bool ms = false)
 {
     Layout L;
     int o = 0;
-    const int KP = D + 8;
+    const int KP = D + 16;
     const int sb32 = EXT_R * pitch * 4, sbhl = 2 * EXT_R * pitch_hl(ncb) * 2;
     L.s_off = o;  o += sb32 > sbhl ? sb32 : sbhl;           // logit / probability tile (fp32, or bf16 hi+lo)
     L.k_off = o;  o += ncb * 16 * KP * 2;                   // K tile with key halo (bf16)
@@ -100,7 +121,7 @@ __device__ inline void store_k(const Pref<D> &r, bf16_t *kbuf, int nrows, int ti
     for (int it = 0; it < Pref<D>::KL; ++it) {
         const int idx = tid + it * NT;
         const int row = idx / Pref<D>::C8, c8 = idx % Pref<D>::C8;
-        if (row < nrows) *reinterpret_cast<bf16x8 *>(kbuf + row * (D + 8) + 8 * c8) = r.k[it];
+        if (row < nrows) *reinterpret_cast<bf16x8 *>(kbuf + row * kpitch<D>() + 8 * c8) = r.k[it];
     }
 }
 
@@ -126,7 +147,7 @@ __device__ inline void store_q(const Pref<D> &r, bf16_t *qbuf, int tid)
     for (int it = 0; it < Pref<D>::QL; ++it) {
         const int idx = tid + it * NT;
         const int row = idx / Pref<D>::C8, c8 = idx % Pref<D>::C8;
-        if (row < EXT_R) *reinterpret_cast<bf16x8 *>(qbuf + row * (D + 8) + 8 * c8) = r.q[it];
+        if (row < EXT_R) *reinterpret_cast<bf16x8 *>(qbuf + row * kpitch<D>() + 8 * c8) = r.q[it];
     }
 }
 
@@ -222,8 +243,19 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
         h4[r] = hh;
         l4[r] = ll;
     }
-    *reinterpret_cast<bf16x4 *>(xh + rho * ph + e0) = h4;
-    *reinterpret_cast<bf16x4 *>(xl + rho * ph + e0) = l4;
+    // Lane groups 2k and 2k+1 hold keys 8k..8k+3 and 8k+4..8k+7 of the same
+    // row.  One exchange between them (v_permlane16_swap: the odd group's first
+    // operand against the even group's second) leaves the even group with the
+    // 8 hi parts and the odd group with the 8 lo parts, so that every lane
+    // stores 16 contiguous bytes of one plane.
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x2 hw = __builtin_bit_cast(u32x2, h4), lw = __builtin_bit_cast(u32x2, l4);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(hw[0], lw[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(hw[1], lw[1], false, false);
+    const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+    bf16_t *dst = (((lane >> 4) & 1) ? xl : xh) + rho * ph + cb * 16 + 8 * (lane >> 5);
+    *reinterpret_cast<u32x4 *>(dst) = w;
 }
 
 // Banded kernel matrices of the group's heads as MFMA A operands:
@@ -382,20 +414,20 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
                                       const Params &p, int i0, int j0, const float *st_m, const float *st_il,
                                       int rw, int kh, int lane)
 {
-    const int l16 = lane & 15, dq = (lane >> 4) * (D / 4);
+    const int l16 = lane & 15, dq = frag_base<D>(lane);
     bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
     bf16_t *xl = xh + EXT_R * ph;
     QFrag<D> qf, kf;
     {
-        const bf16_t *qr = qbuf + (16 * (1 + rw) + l16) * (D + 8) + dq;
+        const bf16_t *qr = qbuf + (16 * (1 + rw) + l16) * kpitch<D>() + dq;
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 8 * t);
+        for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 16 * t);
     }
 #pragma unroll
     for (int cb = kh; cb < NCB; cb += 2) {
-        const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+        const bf16_t *kr = kbuf + (16 * cb + l16) * kpitch<D>() + dq;
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+        for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qf);
         if (HL)
             store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
@@ -403,14 +435,14 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
             store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
     }
     if (kh == 1 && p.c_q > 1) {
-        const bf16_t *qr = qbuf + l16 * (D + 8) + dq;
+        const bf16_t *qr = qbuf + l16 * kpitch<D>() + dq;
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 8 * t);
+        for (int t = 0; t < D / 32; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + 16 * t);
 #pragma unroll
         for (int cb = rw; cb < NCB; cb += 4) {
-            const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+            const bf16_t *kr = kbuf + (16 * cb + l16) * kpitch<D>() + dq;
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+            for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
             const f32x4 acc = qk_mfma<D>(kf, qf);
             if (HL)
                 store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
@@ -427,15 +459,15 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
                                        const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh,
                                        int lane)
 {
-    const int l16 = lane & 15, dq = (lane >> 4) * (D / 4);
+    const int l16 = lane & 15, dq = frag_base<D>(lane);
     bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
     bf16_t *xl = xh + EXT_R * ph;
     QFrag<D> kf;
 #pragma unroll
     for (int cb = kh; cb < NCB; cb += 2) {
-        const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+        const bf16_t *kr = kbuf + (16 * cb + l16) * kpitch<D>() + dq;
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+        for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qown);
         if (HL)
             store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
@@ -445,9 +477,9 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
     if (kh == 1 && p.c_q > 1) {
 #pragma unroll
         for (int cb = rw; cb < NCB; cb += 4) {
-            const bf16_t *kr = kbuf + (16 * cb + l16) * (D + 8) + dq;
+            const bf16_t *kr = kbuf + (16 * cb + l16) * kpitch<D>() + dq;
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 8 * t);
+            for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
             const f32x4 acc = qk_mfma<D>(kf, qhalo);
             if (HL)
                 store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
@@ -460,13 +492,13 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
 template <int D>
 __device__ inline void load_qfrags(QFrag<D> &qown, QFrag<D> &qhalo, const bf16_t *qbuf, int rw, int lane)
 {
-    const int l16 = lane & 15, dq = (lane >> 4) * (D / 4);
-    const bf16_t *qo = qbuf + (16 * (1 + rw) + l16) * (D + 8) + dq;
-    const bf16_t *qh = qbuf + l16 * (D + 8) + dq;
+    const int l16 = lane & 15, dq = frag_base<D>(lane);
+    const bf16_t *qo = qbuf + (16 * (1 + rw) + l16) * kpitch<D>() + dq;
+    const bf16_t *qh = qbuf + l16 * kpitch<D>() + dq;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-        qown.x[t] = *reinterpret_cast<const bf16x8 *>(qo + 8 * t);
-        qhalo.x[t] = *reinterpret_cast<const bf16x8 *>(qh + 8 * t);
+        qown.x[t] = *reinterpret_cast<const bf16x8 *>(qo + 16 * t);
+        qhalo.x[t] = *reinterpret_cast<const bf16x8 *>(qh + 16 * t);
     }
 }
 

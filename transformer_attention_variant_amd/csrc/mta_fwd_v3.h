@@ -45,7 +45,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
 {
     Layout L;
     int o = 0;
-    const int KP = D + 8;
+    const int KP = D + 16;
     L.s_off = o;  o += 2 * EXT_R * pitch_hl(ncb) * 2;       // logit tile, bf16 hi + lo planes
     L.k_off = o;  o += ncb * 16 * KP * 2;                   // K tile with key halo (bf16)
     L.q_off = o;  o += EXT_R * KP * 2;                      // Q tile with the 16 rows above (bf16)

@@ -31,25 +31,22 @@ namespace mta {
 namespace v3 {
 
 using v2::NT;
-using v2::Pref;
 using v2::ColMask;
 using v2::col_mask;
 using v2::pitch_hl;
-using v2::vpitch;
 
 struct Layout {
-    int s_off, k_off, q_off, v_off, p_off, pm_off, al_off, th_off, w_off, gn_off, tf_off, total;
+    int s_off, k_off, qh_off, v_off, p_off, pm_off, al_off, th_off, w_off, gn_off, tf_off, total;
 };
 
 __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
 {
     Layout L;
     int o = 0;
-    const int KP = D + 16;
     L.s_off = o;  o += 2 * EXT_R * pitch_hl(ncb) * 2;       // logit tile, bf16 hi + lo planes
-    L.k_off = o;  o += ncb * 16 * KP * 2;                   // K tile with key halo (bf16)
-    L.q_off = o;  o += EXT_R * KP * 2;                      // Q tile with the 16 rows above (bf16)
-    L.v_off = o;  o += BN * KP * 2;                         // V tile, row-major (bf16)
+    L.k_off = o;  o += ncb * 16 * D * 2;                    // K tile with key halo (bf16, swizzled rows)
+    L.qh_off = o; o += CH * HALO * D * 2;                   // Q rows above the query tile, every head
+    L.v_off = o;  o += BN * D * 2;                          // V tile (bf16, swizzled rows)
     L.p_off = o;  o += 2 * CH * 4 * 2 * 64 * 16;            // probabilities [parity][b][rw][chunk][lane] x 8 bf16
     L.pm_off = o; o += 2 * BM * 4;                          // partial row maxima [kh][row]
     L.al_off = o; o += CH * BM * 4;                         // rescale factors [b][row]; final 1/l
@@ -61,11 +58,101 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
     return L;
 }
 
+// ---------------------------------------------------------------------------
+// Q, K and V tiles (d = 128: rows of 256 bytes, 16 chunks of 16 bytes) are
+// written by the DMA form of the global load (global_load_lds_dwordx4: lane i
+// of a wave puts its 16 bytes at base + 16 i), so rows carry no padding;
+// instead the chunks of row r are stored in the order c ^ swz(r).  The fragment
+// reads of the logit product (16 rows x 2 lane groups per 512-byte LDS pass)
+// and the transposing V reads (16 rows x 32 bytes per pass) then hit distinct
+// banks.
+typedef __attribute__((address_space(3))) void *lds_void_p;
+typedef __attribute__((address_space(3))) v2::s16x4 *lds_s16x4_p;
+
+__device__ inline int swz_k(int r)
+{
+    const int m = (r >> 1) & 7;
+    return (m & 3) | ((m & 4) << 1);
+}
+__device__ inline int swz_v(int r) { return 2 * ((r >> 1) & 7); }
+
+// Rows [0, nrows) of a tile: global rows key0 + row of the head slice g
+// (clamped into [0, T); the rows outside are masked where they are used).
+// nrows is a multiple of 4; the waves take the 1 KB pieces in turn.
+template <bool VTILE>
+__device__ inline void dma_tile(bf16_t *lds, const bf16_t *g, int key0, int nrows, int T, int wave, int lane)
+{
+    for (int i = wave; i < nrows / 4; i += NT / 64) {
+        const int row = 4 * i + (lane >> 4), pc = lane & 15;
+        const int c = pc ^ (VTILE ? swz_v(row) : swz_k(row));
+        int key = key0 + row;
+        key = key < 0 ? 0 : (key >= T ? T - 1 : key);
+        __builtin_amdgcn_global_load_lds((const void *)(g + (size_t)key * 128 + 8 * c), (lds_void_p)(lds + 512 * i),
+                                         16, 0, 0);
+    }
+}
+
+// wait for this wave's outstanding global loads (the DMA tiles among them)
+__device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Workgroup barrier that publishes LDS writes but lets this wave's DMA tile
+// loads stay in flight (a __syncthreads() fence would wait for them too).
+// Only valid where no wave reads the DMA targets before the next full barrier,
+// which waits for them.
+__device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Logit tile of one head: own-row block 1+rw from the Q fragment in registers,
+// the halo block from the Q rows above the tile in LDS; K fragments from the
+// swizzled K tile.  Work split and stores as in v2::logit_tile_lds.
+template <int NCB, bool EX>
+__device__ inline void logit_tile(bf16_t *xh, bf16_t *xl, int ph, const QFrag<128> &qown, const bf16_t *qhalo,
+                                  const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh, int lane)
+{
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int fk = swz_k(l16);
+    int off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) off[t] = 8 * ((4 * g4 + t) ^ fk);
+    QFrag<128> kf;
+#pragma unroll
+    for (int cb = kh; cb < NCB; cb += 2) {
+        const bf16_t *kr = kbuf + (16 * cb + l16) * 128;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + off[t]);
+        const f32x4 acc = qk_mfma<128>(kf, qown);
+        v2::store_block_hl<RAW>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+    }
+    if (kh == 1 && p.c_q > 1) {
+        QFrag<128> qh;
+        const bf16_t *qr = qhalo + l16 * 128;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qh.x[t] = *reinterpret_cast<const bf16x8 *>(qr + off[t]);
+#pragma unroll
+        for (int cb = rw; cb < NCB; cb += 4) {
+            const bf16_t *kr = kbuf + (16 * cb + l16) * 128;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + off[t]);
+            const f32x4 acc = qk_mfma<128>(kf, qh);
+            v2::store_block_hl<RAW>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+        }
+    }
+}
+
+// Transposing read of 4 keys kb + lane/4 (within the 16-lane group) of the
+// swizzled V tile: element e of lane i is V[kb + e][d0 + i] (see v2::lds_read_tr4).
+__device__ inline v2::s16x4 vread_tr4(const bf16_t *vbuf, int kb, int d0, int j)
+{
+    const int row = kb + (j >> 2), col = d0 + 4 * (j & 3);
+    const bf16_t *a = vbuf + row * 128 + 8 * ((col >> 3) ^ swz_v(row)) + (col & 7);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(a));
+}
+
 template <int D, int CH, int CQ, int CK, bool EXACT>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
 {
     static_assert(CH == 1 || CH == 2, "one accumulator per (source, output) head pair: c_h <= 2");
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
+    static_assert(D == 128, "tile swizzles assume 256-byte rows");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rw = wave & 3, kh = wave >> 2;
@@ -83,10 +170,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
 
     const Layout lay = layout(D, CH, CQ, CK, NCB);
     float *sbuf = reinterpret_cast<float *>(smem + lay.s_off);
-    const bf16_t *xh = reinterpret_cast<const bf16_t *>(sbuf);
-    const bf16_t *xl = xh + EXT_R * ph;
+    bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
+    bf16_t *xl = xh + EXT_R * ph;
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
-    bf16_t *qbuf = reinterpret_cast<bf16_t *>(smem + lay.q_off);
+    bf16_t *qhbuf = reinterpret_cast<bf16_t *>(smem + lay.qh_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
     bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + lay.p_off);
     float *pm = reinterpret_cast<float *>(smem + lay.pm_off);   // [kh][row]
@@ -121,11 +208,22 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
 #pragma unroll
     for (int o = 0; o < 8; ++o) ko[o] = 32 * kh + 16 * (o >> 2) + 4 * g4 + (o & 3);
 
-    Pref<D> pf;
-    v2::load_q<D>(pf, Q, i0, T, tid);
-    v2::load_k<D>(pf, K, 0, p.hl, krows, T, tid);
-    v2::store_q<D>(pf, qbuf, tid);
-    v2::store_k<D>(pf, kbuf, krows, tid);
+    // K of key tile 0 (head 0) and the Q rows above the tile (every head) into
+    // LDS; the wave's own Q rows of every head stay in registers throughout
+    dma_tile<false>(kbuf, K, -p.hl, krows, T, wave, lane);
+#pragma unroll
+    for (int s = 0; s < CH; ++s) dma_tile<false>(qhbuf + s * HALO * D, Q + s * hstride, i0 - HALO, HALO, T, wave, lane);
+    QFrag<D> qown[CH];
+    {
+        int qi = i0 + 16 * rw + l16;
+        qi = qi < T ? qi : T - 1;  // rows past the end: masked in the logit tile
+#pragma unroll
+        for (int s = 0; s < CH; ++s)
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+                qown[s].x[t] = *reinterpret_cast<const bf16x8 *>(Q + s * hstride + (size_t)qi * D + 32 * g4 + 8 * t);
+    }
+    wait_vm();
 
     // U[b][a][nb][r]: rows 16rw + 4g4 + r, d-columns dbase + 16nb + l16
     f32x4 U[CH][CH][D / 32];
@@ -155,8 +253,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
             for (int nb = 0; nb < D / 32; ++nb) {
                 // keys of slots 0-3 and 4-7, in the producing lanes' order
                 const int kb0 = 32 * c + 4 * g4;
-                const v2::s16x4 u0 = v2::lds_read_tr4(vbuf, vpitch<D>(), kb0, dbase + 16 * nb, l16);
-                const v2::s16x4 u1 = v2::lds_read_tr4(vbuf, vpitch<D>(), kb0 + 16, dbase + 16 * nb, l16);
+                const v2::s16x4 u0 = vread_tr4(vbuf, kb0, dbase + 16 * nb, l16);
+                const v2::s16x4 u1 = vread_tr4(vbuf, kb0 + 16, dbase + 16 * nb, l16);
                 typedef short s16x8 __attribute__((ext_vector_type(8)));
                 const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
@@ -186,24 +284,20 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
         const int j0 = kt * BN;
 #pragma unroll
         for (int s = 0; s < CH; ++s) {
-            __syncthreads();  // B1
-            // next phase (kt, s+1) or (kt+1, 0): its K, Q and the V tile its P.V
-            // reads; issued early so the loads overlap the phase
+            __syncthreads();  // B1: K^s(kt) and V^s(kt-1) are in LDS
             const int sn = (s + 1 < CH) ? s + 1 : 0;
             const int ktn = (s + 1 < CH) ? kt : kt + 1;
-            const bool more = ktn <= qt;
-            if (more) {
-                v2::load_k<D>(pf, K + sn * hstride, ktn * BN, p.hl, krows, T, tid);
-                if (CH > 1) v2::load_q<D>(pf, Q + sn * hstride, i0, T, tid);
-            }
-            if (ktn >= 1) v2::load_v<D>(pf, V + sn * hstride, (ktn - 1) * BN, T, tid);
-            v2::logit_tile_lds<D, RAW, true, NCB, EXACT>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw,
-                                                         kh, lane);
+            logit_tile<NCB, EXACT>(xh, xl, ph, qown[s], qhbuf + s * HALO * D,
+                                   kbuf, p, i0, j0, rw, kh, lane);
             if (kt > 0) {
                 if (s == 0) rescale();
                 pv(s, (kt - 1) & 1);
             }
             __syncthreads();  // B2
+            // the next phase (kt, s+1) or (kt+1, 0): its K tile and the V tile
+            // its P.V reads go straight into LDS while this phase convolves
+            if (ktn <= qt) dma_tile<false>(kbuf, K + sn * hstride, ktn * BN - p.hl, krows, T, wave, lane);
+            if (ktn >= 1) dma_tile<true>(vbuf, V + sn * hstride, (ktn - 1) * BN, BN, T, wave, lane);
 
             float c[8];
             const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
@@ -221,7 +315,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             if (g4 == 0) pm[kh * BM + io] = mx;
-            __syncthreads();  // B3
+            barrier_lds();  // B3 (the DMA tiles stay in flight)
             // every row has a causal key in tile 0, so m_new is finite
             const float m_new = fmaxf(m_run[s], fmaxf(mx, pm[(kh ^ 1) * BM + io]));
             const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
@@ -237,24 +331,20 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
             l_run[s] = __builtin_fmaf(l_run[s], alpha, ls);
             if (kh == 0 && g4 == 0) al[s * BM + io] = alpha;
             pbuf[((((kt & 1) * CH + s) * 4 + rw) * 2 + kh) * 64 + lane] = v8;
-
-            if (more) {
-                v2::store_k<D>(pf, kbuf, krows, tid);
-                if (CH > 1) v2::store_q<D>(pf, qbuf, tid);
-            }
-            if (ktn >= 1) v2::store_v<D>(pf, vbuf, tid);
+            wait_vm();
         }
     }
     // P.V of the last key tile, one output head at a time through the V buffer
+    // (V^0 of the last tile arrived with the last phase)
 #pragma unroll
     for (int a = 0; a < CH; ++a) {
         __syncthreads();
         if (a == 0) rescale();
         pv(a, qt & 1);
         if (a + 1 < CH) {
-            v2::load_v<D>(pf, V + (a + 1) * hstride, qt * BN, T, tid);
             __syncthreads();
-            v2::store_v<D>(pf, vbuf, tid);
+            dma_tile<true>(vbuf, V + (a + 1) * hstride, qt * BN, BN, T, wave, lane);
+            wait_vm();
         }
     }
 

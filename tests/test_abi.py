@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 @pytest.mark.parametrize("name,expect", [
-    ("needle4k", "mta_fwd_v3"), ("needle4k_exact", "mta_fwd_v3"), ("layer2k", "mta_fwd_v3"),
+    ("needle4k", "mta_fwd_v4"), ("needle4k_exact", "mta_fwd_v4"), ("layer2k", "mta_fwd_v4"),
+    ("sweep8k_8x15_ch2_pre", "mta_fwd_v4"),
     ("sweep8k_6x11_ch2_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
     ("sweep8k_8x15_ch4_pre", "mta_fwd_v2 (two passes, VALU stencil)"),
     ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
@@ -45,6 +46,14 @@ def test_kernel_selection(lib, name, expect):
     """Host-only query of the kernel each workload runs (no launch)."""
     got = binding.kernel_name(I.CONFIGS[name])
     assert got is not None and got.startswith(expect), got
+
+
+@pytest.mark.parametrize("kq", [I.PRE, I.PRE_EXACT])
+def test_kernel_selection_single_head_groups(lib, kq):
+    """Groups of one head run the key-split one-pass kernel."""
+    cfg = I.small("ch1", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=1, kq_place=kq, dtype="bf16")
+    got = binding.kernel_name(cfg)
+    assert got is not None and got.startswith("mta_fwd_v3"), got
 
 
 def test_kernel_name_of_invalid_config(lib):
@@ -90,7 +99,7 @@ def test_layer_validation(lib, kw, code):
 
 @pytest.mark.parametrize("kw,expect", [
     ({}, "mta_fwd_layer"),                                                  # the repeated form
-    (dict(kq_post=None, head_post2=None), "mta_fwd_v3"),                    # kq pre + head post
+    (dict(kq_post=None, head_post2=None), "mta_fwd_v4"),                    # kq pre + head post
     (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v2"),     # kq post + head post
     (dict(kq_pre=None, head_post2=None), "mta_fwd_layer"),                  # head mix before the kq conv
     (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000), "mta_fwd_layer"),

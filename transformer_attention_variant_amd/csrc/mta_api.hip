@@ -5,7 +5,7 @@
 
 #include "mta.h"
 #include "mta_fwd_v2.h"
-#include "mta_fwd_v3.h"
+#include "mta_fwd_v4.h"
 #include "mta_fwd_layer.h"
 #include "mta_bwd.h"
 #include "mta_launch.h"
@@ -115,9 +115,18 @@ static int make_plan(const mta_config *cfg, Plan &pl)
     if (cfg->dtype == MTA_BF16) {
         const int ncb0 = p.ncb, pitch0 = p.pitch;
         // one pass with online softmax statistics where it applies (key-query
-        // convolution before the softmax, head mix after it, c_h <= 2)
-        fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
+        // convolution before the softmax, head mix after it, c_h <= 2): the
+        // head-split kernel for c_h = 2, else the key-split one
+        fn = mta::find_launch_v4(d, ch, cq, ck, post, exact, hpre);
         if (fn) {
+            p.ncb = 5;
+            p.pitch = p.ncb * 16 + 4;
+            lds = (size_t)mta::v4::layout(cq, ck).total;
+            if (lds > LDS_MAX) fn = nullptr;
+            else pl.name = "mta_fwd_v4 (one pass, head-split waves)";
+        }
+        if (!fn) fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
+        if (fn && !pl.name) {
             p.ncb = ncb0 < 5 ? 5 : ncb0;
             p.pitch = p.ncb * 16 + 4;
             lds = (size_t)mta::v3::layout(d, ch, cq, ck, p.ncb).total;

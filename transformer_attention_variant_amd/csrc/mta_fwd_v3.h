@@ -62,19 +62,17 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
 // Q, K and V tiles (d = 128: rows of 256 bytes, 16 chunks of 16 bytes) are
 // written by the DMA form of the global load (global_load_lds_dwordx4: lane i
 // of a wave puts its 16 bytes at base + 16 i), so rows carry no padding;
-// instead the chunks of row r are stored in the order c ^ swz(r).  The fragment
-// reads of the logit product (16 rows x 2 lane groups per 512-byte LDS pass)
-// and the transposing V reads (16 rows x 32 bytes per pass) then hit distinct
-// banks.
+// instead the chunks of row r are stored in the order c ^ swz(r).  gfx950's
+// LDS has 64 banks of 4 bytes; ds_read_b128 serves a wave in four passes of 16
+// lanes (the pass of lane 0 holds lanes 0-3, 12-15 and 20-27), and the
+// transposing read of a 16-row V block keeps rows r and r + 8 apart.  With the
+// swizzles below every pass of the fragment reads and of the V reads touches
+// each bank once (checked with the bank-conflict counter).
 typedef __attribute__((address_space(3))) void *lds_void_p;
 typedef __attribute__((address_space(3))) v2::s16x4 *lds_s16x4_p;
 
-__device__ inline int swz_k(int r)
-{
-    const int m = (r >> 1) & 7;
-    return (m & 3) | ((m & 4) << 1);
-}
-__device__ inline int swz_v(int r) { return 2 * ((r >> 1) & 7); }
+__device__ inline int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ inline int swz_v(int r) { return 2 * (r & 7); }
 
 // Rows [0, nrows) of a tile: global rows key0 + row of the head slice g
 // (clamped into [0, T); the rows outside are masked where they are used).
@@ -154,7 +152,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     static_assert(D == 128, "tile swizzles assume 256-byte rows");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
     const int rw = wave & 3, kh = wave >> 2;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int L = blockIdx.x;

@@ -1,0 +1,500 @@
+// mta_fwd_v4.h — one-pass MTA forward with head-split waves, for head groups of
+// two (c_h = 2), d = 128, bf16: key-query convolution before the softmax (two-
+// pass masks or Eq. 4's exact indicator), head mixing after it (page "Multi-
+// Token Attention — Paper Graph", section 3.4, "Key-Query Convolution", "Head
+// Mixing Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").
+//
+// Same online-softmax formulation as mta_fwd_v3.h (accumulators
+// U_{b,a} = sum_j exp(C^b_j - m_b) V^a_j, O^a = sum_b w_ab U_{b,a} / l_b), with
+// the work of a key tile split by head instead of by key half:
+//   wave (rw, s), rw = 0..3, s = 0..1, owns query rows 16rw.. of the tile.
+//   In the logit product and the stencil it works on head s only, over all 64
+//   keys of the tile, so the row maxima need no exchange between waves and
+//   the head's banded kernel matrices stay in its registers.  In P.V it owns
+//   the d-columns [64s, 64s + 64) of every (source b, output a) pair.
+// Per key tile there are three barriers, each publishing LDS writes only:
+//   B1 | K tiles of both heads are in LDS; the V tiles of this key tile start
+//        loading (DMA); logit tiles of both heads -> LDS (hi/lo planes)
+//   B2 | the K tiles of the next key tile start loading; stencil, Mask_-inf,
+//        row maximum, rescale factor and probabilities -> LDS
+//   B3 | (V tiles landed) rescale of the accumulators, P.V
+#pragma once
+
+#include "mta_fwd_v3.h"
+
+namespace mta {
+namespace v4 {
+
+using v2::NT;
+using v2::ColMask;
+using v3::swz_k;
+using v3::swz_v;
+using v3::barrier_lds;
+using v3::vread_tr4;
+using v3::lds_void_p;
+
+constexpr int CH = 2;
+constexpr int D = 128;
+constexpr int NCB = 5;          // 16-key column blocks of the logit tile (80 columns)
+constexpr int XP = 16 * NCB;    // bf16 pitch of the hi / lo planes (conflict-free stencil reads)
+constexpr int KROWS = 16 * NCB; // K rows per head (key halo included)
+
+struct Layout {
+    int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, total;
+};
+
+__host__ __device__ inline Layout layout(int cq, int ck)
+{
+    Layout L;
+    int o = 0;
+    L.x_off = o;  o += CH * 2 * EXT_R * XP * 2;   // logit tiles of both heads, bf16 hi + lo planes
+    L.k_off = o;  o += CH * KROWS * D * 2;        // K tiles (swizzled rows)
+    L.v_off = o;  o += CH * BN * D * 2;           // V tiles (swizzled rows)
+    L.qh_off = o; o += CH * HALO * D * 2;         // Q rows above the query tile
+    L.p_off = o;  o += CH * 4 * 2 * 64 * 16;      // probabilities [b][rw][k-step][lane] x 8 bf16
+    L.al_off = o; o += CH * BM * 4;               // rescale factors [b][row]; at the end 1/l
+    L.fl_off = o; o += CH * 4 * 4;                // [b][rw]: some factor of the 16 rows differs from 1
+    L.gn_off = o; o += 2 * CH * BM * 4;           // GroupNorm partial sums [d half][a][row]
+    L.w_off = o;  o += 16;                        // the group's 2x2 mixing matrix
+    L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
+    L.total = o;
+    return L;
+}
+
+// DMA of the same rows of a K or V tile for both heads of the group: piece i
+// (1 KB = 4 rows) of head i / PER; wave w issues pieces w, w + 8, ... so that
+// every wave issues the same number (its vmcnt bookkeeping is uniform).
+template <bool VTILE, int NROWS>
+__device__ inline void dma_pair(bf16_t *lds, const bf16_t *g, size_t hstride, int key0, int T, int wave, int lane)
+{
+    constexpr int PER = NROWS / 4;
+    static_assert((CH * PER) % 8 == 0, "equal share per wave");
+#pragma unroll
+    for (int k = 0; k < CH * PER / 8; ++k) {
+        const int i = wave + 8 * k, h = i / PER, piece = i % PER;
+        const int row = 4 * piece + (lane >> 4), pc = lane & 15;
+        const int c = pc ^ (VTILE ? swz_v(row) : swz_k(row));
+        int key = key0 + row;
+        key = key < 0 ? 0 : (key >= T ? T - 1 : key);
+        __builtin_amdgcn_global_load_lds((const void *)(g + h * hstride + (size_t)key * D + 8 * c),
+                                         (lds_void_p)(lds + h * NROWS * D + 512 * piece), 16, 0, 0);
+    }
+}
+constexpr int K_PIECES = CH * KROWS / 4 / 8;  // per wave
+constexpr int V_PIECES = CH * BN / 4 / 8;
+
+// all of this wave's global loads / only the last K_PIECES may be outstanding
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+__device__ inline void wait_vm_k() { __builtin_amdgcn_s_waitcnt(0x0f70 | K_PIECES); }
+
+// maximum / sum over the four lanes l16 + 16 g4 holding one row
+__device__ inline float row_max4(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float row_sum4(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Eq. 4's indicator for one 16-key output block: the B operand of a lane holds
+// window columns 8*(lane/16) + s of the rows above its output query; entries
+// whose key is in that query's future (window column > tl) are cleared.
+__device__ inline void block_mask(int tl, uint32_t (&w)[4])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w[q] = (2 * q <= tl ? 0x0000ffffu : 0u) | (2 * q + 1 <= tl ? 0xffff0000u : 0u);
+}
+
+// Key-query stencil of the 16 rows of this wave (tile row rho = HALO + 16rw +
+// lane%16) over all 64 keys of the tile: output block t covers keys 16t..16t+15
+// and reads the 32-column window starting at tile column 16t.  Three products
+// (hi*hi, hi*lo, lo*hi) per kernel row on the matrix cores.  out[4t + r] is
+// key 16t + 4*(lane/16) + r.  With MASK, Eq. 4's indicator: tl0 is the last
+// window column of block 0 (relative to 8*(lane/16)) whose key is not in the
+// future of the lane's output query; the blocks are then taken two at a time
+// with their masks built just before use.
+template <int CQ, bool MASK>
+__device__ inline void stencil64(const bf16_t *xh, const bf16_t *xl, int rho, const bf16x8 (&tf)[CQ][2], int tl0,
+                                 int lane, float out[16])
+{
+    const int g4 = lane >> 4;
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // step (ip, t2): the two output blocks t2, t2+1 of kernel row ip
+    bf16x8 h[2], l[2];
+    auto load = [&](int ip, int t2) {
+        const int base = (rho - ip) * XP + 8 * g4;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            h[u] = *reinterpret_cast<const bf16x8 *>(xh + base + 16 * (t2 + u));
+            l[u] = *reinterpret_cast<const bf16x8 *>(xl + base + 16 * (t2 + u));
+        }
+    };
+    auto mma = [&](int ip, int t2, const bf16x8 (&hh)[2], const bf16x8 (&ll)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][0], hh[u], acc[t2 + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][0], ll[u], acc[t2 + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][1], hh[u], acc[t2 + u], 0, 0, 0);
+    };
+    if (MASK) {
+#pragma unroll
+        for (int t2 = 0; t2 < 4; t2 += 2) {
+            uint32_t mk[2][4];
+            block_mask(tl0 - 16 * t2, mk[0]);
+            block_mask(tl0 - 16 * (t2 + 1), mk[1]);
+#pragma unroll
+            for (int ip = 0; ip < CQ; ++ip) {
+                load(ip, t2);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    h[u] = v2::and_mask(h[u], mk[u]);
+                    l[u] = v2::and_mask(l[u], mk[u]);
+                }
+                mma(ip, t2, h, l);
+            }
+        }
+    } else {
+        // two output blocks at a time, so that the operands of one step stay
+        // few next to the resident accumulators
+#pragma unroll
+        for (int ip = 0; ip < CQ; ++ip)
+#pragma unroll
+            for (int t2 = 0; t2 < 4; t2 += 2) {
+                load(ip, t2);
+                mma(ip, t2, h, l);
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[4 * t + r] = acc[t][r];
+}
+
+template <int CQ, int CK, bool EXACT>
+__global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
+{
+    static_assert(CK <= 17, "matrix-core stencil: 32-column window");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
+    const int rw = wave & 3, hs = wave >> 2;  // row block; head (stencil) = d half (P.V)
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int L = blockIdx.x;
+    const int unit = L % p.units;
+    const int qt = p.n_qt - 1 - L / p.units;
+    const int b = unit / p.G, g = unit % p.G;
+    const int i0 = qt * BM;
+    const int T = p.T;
+    constexpr int CKP = ((CK + 3) / 4) * 4;
+
+    const Layout lay = layout(CQ, CK);
+    bf16_t *xbuf = reinterpret_cast<bf16_t *>(smem + lay.x_off);
+    bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
+    bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
+    bf16_t *qhbuf = reinterpret_cast<bf16_t *>(smem + lay.qh_off);
+    bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + lay.p_off);
+    float *al = reinterpret_cast<float *>(smem + lay.al_off);   // [b][row]
+    int *fl = reinterpret_cast<int *>(smem + lay.fl_off);       // [b][rw]
+    float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);  // [half][a][row]
+    float *w_s = reinterpret_cast<float *>(smem + lay.w_off);
+    float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
+
+    const size_t hstride = (size_t)T * D;
+    const int h0 = g * CH;
+    const size_t base0 = ((size_t)b * p.H + h0) * hstride;
+    const bf16_t *Q = reinterpret_cast<const bf16_t *>(p.q) + base0;
+    const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + base0;
+    const bf16_t *V = reinterpret_cast<const bf16_t *>(p.v) + base0;
+
+    // K of key tile 0 and the Q rows above the query tile, both heads; this
+    // wave's Q rows of its head in registers; kernels and mixing matrix
+    dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);
+    dma_pair<false, HALO>(qhbuf, Q, hstride, i0 - HALO, T, wave, lane);
+    // this wave's Q rows of its head (rows past the end: masked in the logit tile)
+    const bf16_t *qrow = Q + hs * hstride + (size_t)((i0 + 16 * rw + l16) < T ? i0 + 16 * rw + l16 : T - 1) * D + 32 * g4;
+    QFrag<D> qown;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) qown.x[t] = *reinterpret_cast<const bf16x8 *>(qrow + 8 * t);
+    for (int i = tid; i < CH * CQ * CKP; i += NT) {
+        const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
+        th_s[i] = c < CK ? p.theta[((size_t)(h0 + a) * CQ + r) * CK + c] : 0.f;
+    }
+    if (tid < CH * CH) w_s[tid] = p.wmix[(size_t)g * CH * CH + tid];
+    wait_vm_all();
+    __syncthreads();
+
+    // banded kernel matrices of head hs (MFMA A operands, hi and lo planes):
+    // row m = lane%16 (output key), columns k = 8*(lane/16) + s of the window
+    bf16x8 tf[CQ][2];
+#pragma unroll
+    for (int ip = 0; ip < CQ; ++ip)
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            const int jj = l16 + CK - 1 - (8 * g4 + s8);
+            const float t = (jj >= 0 && jj < CK) ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
+            bf16_t hh, ll;
+            v2::split_hl(t, hh, ll);
+            tf[ip][0][s8] = hh;
+            tf[ip][1][s8] = ll;
+        }
+
+    const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
+    const int qabs = i0 + io;
+    const int rho = HALO + io;
+    const int dbase = 64 * hs;
+    bf16_t *xh = xbuf + hs * 2 * EXT_R * XP;
+    bf16_t *xl = xh + EXT_R * XP;
+    int koff[4];  // swizzled chunk offsets of the K / Q-halo fragment reads
+#pragma unroll
+    for (int t = 0; t < 4; ++t) koff[t] = 8 * ((4 * g4 + t) ^ swz_k(l16));
+
+    // U[b][a][nb][r]: rows 16rw + 4g4 + r, d-columns dbase + 16nb + l16
+    f32x4 U[CH][CH][4];
+#pragma unroll
+    for (int s = 0; s < CH; ++s)
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) U[s][a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = NEG_INF, l_run = 0.f;  // head hs, row io (l_run: this lane's 16 keys)
+
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int j0 = kt * BN;
+        barrier_lds();  // B1: K tiles of kt are in LDS (each wave waited for its DMA)
+        dma_pair<true, BN>(vbuf, V, hstride, j0, T, wave, lane);
+
+        // logit tiles: own row block of head hs, then a share of the halo blocks
+        {
+            QFrag<D> kf;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const bf16_t *kr = kbuf + hs * KROWS * D + (16 * cb + l16) * D;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
+                const f32x4 acc = qk_mfma<D>(kf, qown);
+                v2::store_block_hl<RAW>(xh, xl, XP, 1 + rw, cb, acc, i0, j0, p.hl, T, p.sc, nullptr, nullptr, EXACT,
+                                        lane);
+            }
+            if (CQ > 1) {
+                for (int q = wave; q < CH * NCB; q += 8) {
+                    const int h = q / NCB, cb = q % NCB;
+                    QFrag<D> qf;
+                    const bf16_t *qr = qhbuf + h * HALO * D + l16 * D;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + koff[t]);
+                    const bf16_t *kr = kbuf + h * KROWS * D + (16 * cb + l16) * D;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
+                    const f32x4 acc = qk_mfma<D>(kf, qf);
+                    bf16_t *hx = xbuf + h * 2 * EXT_R * XP;
+                    v2::store_block_hl<RAW>(hx, hx + EXT_R * XP, XP, 0, cb, acc, i0, j0, p.hl, T, p.sc, nullptr,
+                                            nullptr, EXACT, lane);
+                }
+            }
+        }
+        barrier_lds();  // B2: logit tiles complete; K buffers free
+        const bool more = kt < qt;
+        if (more) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);
+
+        float c[16];
+        if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
+            stencil64<CQ, true>(xh, xl, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
+        else
+            stencil64<CQ, false>(xh, xl, rho, tf, 0, lane, c);
+        // Mask_-inf, the row maximum over the 64 keys, probabilities
+        float mx = NEG_INF;
+#pragma unroll
+        for (int o = 0; o < 16; ++o) {
+            const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
+            c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+            mx = fmaxf(mx, c[o]);
+        }
+        mx = row_max4(mx);
+        // every row has a causal key in tile 0, so m_new is finite
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float ls = 0.f;
+        bf16x8 v8[2];
+#pragma unroll
+        for (int o = 0; o < 16; ++o) {
+            const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
+            ls += e;
+            v8[o >> 3][o & 7] = (bf16_t)e;
+        }
+        l_run = __builtin_fmaf(l_run, alpha, ls);
+        pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
+        pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+        if (g4 == 0) al[hs * BM + io] = alpha;
+        const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+        if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
+        if (more) wait_vm_k();  // this wave's V pieces have landed
+        else wait_vm_all();
+        barrier_lds();  // B3: probabilities, factors and V tiles published
+
+        // bring the accumulators into the frame of the new maxima, then P.V
+#pragma unroll
+        for (int s = 0; s < CH; ++s) {
+            if (kt > 0 && fl[s * 4 + rw]) {
+                float f[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f[r] = al[s * BM + 16 * rw + 4 * g4 + r];
+#pragma unroll
+                for (int a = 0; a < CH; ++a)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) U[s][a][nb][r] *= f[r];
+            }
+        }
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+            bf16x8 av[CH];
+#pragma unroll
+            for (int s = 0; s < CH; ++s) av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
+            const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int a = 0; a < CH; ++a) {
+                    const bf16_t *va = vbuf + a * BN * D;
+                    const v2::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
+                    const v2::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
+                    typedef short s16x8 __attribute__((ext_vector_type(8)));
+                    const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+                    for (int s = 0; s < CH; ++s)
+                        U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
+                }
+        }
+        if (more) wait_vm_all();  // the next K tiles have landed
+    }
+
+    // row sums l_b -> 1/l_b in al (after every wave's last P.V read of al)
+    const float lsum = row_sum4(l_run);
+    __syncthreads();
+    if (g4 == 0) al[hs * BM + io] = 1.0f / lsum;
+    __syncthreads();
+
+    // O^a = sum_b w_ab U_{b,a} / l_b  (rows 16rw + 4g4 + r, d-columns dbase + 16nb + l16)
+    f32x4 acc[CH][4];
+    {
+        float il[CH][4];
+#pragma unroll
+        for (int s = 0; s < CH; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) il[s][r] = al[s * BM + 16 * rw + 4 * g4 + r];
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float o = 0.f;
+#pragma unroll
+                    for (int s = 0; s < CH; ++s) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
+                    acc[a][nb][r] = o;
+                }
+    }
+
+    // ---------------- epilogue: GroupNorm over d, head factor, store -------
+    float mu[CH][4];
+#pragma unroll
+    for (int a = 0; a < CH; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sum = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) sum += acc[a][nb][r];
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            sum += __shfl_xor(sum, 8);
+            if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = sum;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < CH; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rw + 4 * g4 + r;
+            mu[a][r] = (gnx[(0 * CH + a) * BM + row] + gnx[(1 * CH + a) * BM + row]) * (1.0f / D);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < CH; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v2s = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const float dl = acc[a][nb][r] - mu[a][r];
+                v2s = __builtin_fmaf(dl, dl, v2s);
+            }
+            v2s += __shfl_xor(v2s, 1);
+            v2s += __shfl_xor(v2s, 2);
+            v2s += __shfl_xor(v2s, 4);
+            v2s += __shfl_xor(v2s, 8);
+            if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = v2s;
+        }
+    __syncthreads();
+    bf16_t *O = reinterpret_cast<bf16_t *>(p.out);
+#pragma unroll
+    for (int a = 0; a < CH; ++a) {
+        const int h = h0 + a;
+        const float *gw = p.gn_w + (size_t)h * D;
+        const float *gb = p.gn_b + (size_t)h * D;
+        const float hf = head_factor(p, h);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rowt = 16 * rw + 4 * g4 + r;
+            const float var = (gnx[(0 * CH + a) * BM + rowt] + gnx[(1 * CH + a) * BM + rowt]) * (1.0f / D);
+            const float rstd = 1.0f / __builtin_sqrtf(var + p.eps);
+            const int row = i0 + rowt;
+            if (row < T) {
+                bf16_t *dst = O + ((size_t)b * p.H + h) * hstride + (size_t)row * D;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int col = dbase + 16 * nb + l16;
+                    const float y = ((acc[a][nb][r] - mu[a][r]) * rstd * gw[col] + gb[col]) * hf;
+                    dst[col] = (bf16_t)y;
+                }
+            }
+        }
+    }
+}
+
+template <int CQ, int CK, bool EXACT>
+hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
+{
+    auto fn = mta_fwd_v4<CQ, CK, EXACT>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace v4
+}  // namespace mta

@@ -1,5 +1,6 @@
-// One-pass kernels (bf16, d = 128, key-query convolution before the softmax in
-// either form, head mix after it, c_h <= 2) for the kernel sizes of the
+// One-pass key-split kernels (bf16, d = 128, key-query convolution before the
+// softmax in either form, head mix after it) for groups of one head (groups of
+// two run the head-split kernel of mta_fwd_v4.h), for the kernel sizes of the
 // 2K/4K/8K workloads and 1x1.
 #include "mta_fwd_v3.h"
 #include "mta_launch.h"
@@ -10,11 +11,8 @@ namespace mta {
     (exact ? &v3::launch<128, CH_, CQ_, CK_, true> : &v3::launch<128, CH_, CQ_, CK_, false>)
 #define MTA_V3_SIZE(CQ_, CK_)                            \
     if (cq == CQ_ && ck == CK_) {                        \
-        switch (ch) {                                    \
-        case 1: return MTA_V3_L(1, CQ_, CK_);            \
-        case 2: return MTA_V3_L(2, CQ_, CK_);            \
-        default: return nullptr;                         \
-        }                                                \
+        if (ch == 1) return MTA_V3_L(1, CQ_, CK_);       \
+        return nullptr;                                  \
     }
 
 LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre)

@@ -110,6 +110,9 @@ def summarize_pmc(args):
     print(json.dumps({args.config: entry}))
 
 
+RAMP_S = 0.3  # seconds of untimed warm-up before a timed region
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -148,8 +151,15 @@ def main():
         """(ms per step over the timed region, mean ms per launch) of K calls
         after the warm-up; with `flush`, that buffer is overwritten before
         every launch (outside the per-launch events)."""
-        for _ in range(args.warmup):
+        # W warm-up steps, continued (untimed) until the GPU has run the
+        # workload for at least RAMP_S seconds, so that its clock has ramped
+        # before the timed region
+        t0, n = time.time(), 0
+        while n < args.warmup or time.time() - t0 < RAMP_S:
             binding.forward_cfg(c, d, out=out, stream=stream)
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         t_start = torch.cuda.Event(enable_timing=True)

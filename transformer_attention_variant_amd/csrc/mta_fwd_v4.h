@@ -117,6 +117,16 @@ __device__ inline void block_mask(int tl, uint32_t (&w)[4])
         w[q] = (2 * q <= tl ? 0x0000ffffu : 0u) | (2 * q + 1 <= tl ? 0xffff0000u : 0u);
 }
 
+// Q K^T of a 16x16 block over d = 128 in two independent accumulation chains.
+__device__ inline f32x4 qk2(const QFrag<D> &kf, const QFrag<D> &qf)
+{
+    f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[0], qf.x[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[1], qf.x[1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[2], qf.x[2], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[3], qf.x[3], a1, 0, 0, 0);
+    return a0 + a1;
+}
+
 // Key-query stencil of the 16 rows of this wave (tile row rho = HALO + 16rw +
 // lane%16) over all 64 keys of the tile: output block t covers keys 16t..16t+15
 // and reads the 32-column window starting at tile column 16t.  Three products
@@ -289,7 +299,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                 const bf16_t *kr = kbuf + hs * KROWS * D + (16 * cb + l16) * D;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
-                const f32x4 acc = qk_mfma<D>(kf, qown);
+                const f32x4 acc = qk2(kf, qown);
                 v2::store_block_hl<RAW>(xh, xl, XP, 1 + rw, cb, acc, i0, j0, p.hl, T, p.sc, nullptr, nullptr, EXACT,
                                         lane);
             }
@@ -303,7 +313,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                     const bf16_t *kr = kbuf + h * KROWS * D + (16 * cb + l16) * D;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
-                    const f32x4 acc = qk_mfma<D>(kf, qf);
+                    const f32x4 acc = qk2(kf, qf);
                     bf16_t *hx = xbuf + h * 2 * EXT_R * XP;
                     v2::store_block_hl<RAW>(hx, hx + EXT_R * XP, XP, 0, cb, acc, i0, j0, p.hl, T, p.sc, nullptr,
                                             nullptr, EXACT, lane);

@@ -92,11 +92,15 @@ def _small_cases():
     c.append(I.small("exact_bf16_5x4_d64", B=2, H=4, T=77, d=64, c_q=5, c_k=4, c_h=2, kq_place=E,
                      dtype="bf16", seed=820))
     c.append(I.small("exact_f32_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, kq_place=E, seed=821))
-    # tiny sequences: T = 1, T < c_q, exactly one tile, one tile + 1
+    # tiny sequences: T = 1, T < c_q, exactly one tile, one tile + 1 (the
+    # one-pass kernels' diagonal-only and ragged single/double tiles included)
     for T in (1, 3, 64, 65):
         c.append(I.small(f"f32_T{T}", B=2, H=2, T=T, d=32, c_q=3, c_k=5, c_h=2, seed=500 + T))
         c.append(I.small(f"bf16_T{T}_post", B=1, H=2, T=T, d=128, c_q=6, c_k=11, c_h=2, kq_place=Q,
                          dtype="bf16", seed=600 + T))
+        for kq in (P, E):
+            c.append(I.small(f"bf16_T{T}_kq{kq}", B=2, H=4, T=T, d=128, c_q=6, c_k=11, c_h=2, kq_place=kq,
+                             dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=650 + T + kq))
     return c
 
 

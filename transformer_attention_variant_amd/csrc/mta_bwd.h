@@ -383,8 +383,26 @@ __device__ inline void stencil16_t(const float *ebuf, int pitch, int er, int jb,
     }
 }
 
+// Sum of x over the 64 lanes of the wave, in every lane: rotations by 8, 4, 2, 1
+// within each 16-lane row (DPP row_ror), then the rows pairwise
+// (v_permlane16_swap, v_permlane32_swap).
+__device__ inline float wave_sum(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(x);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+}
+
 // dtheta[i'][jj] += sum_o g[o] * X[row - i'][col(o) + floor(c_k/2) - jj] for the
-// lane's 16 values g (one row, 16 keys), accumulated into LDS (atomics).  The
+// lane's 16 values g (one row, 16 keys); each tap's sum over the wave is added
+// into LDS by one lane (atomics between the waves).  The
 // logit region's row rx0 holds the lane's row minus 0 offsets: window of query
 // offset i' starts at row rx0 - i', column xc0 (the key col(0) - (c_k - 1) +
 // floor(c_k/2)); window entries t > tlim are keys in the future of the row
@@ -424,7 +442,8 @@ __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, 
                 float acc = 0.f;
 #pragma unroll
                 for (int o = 0; o < 16; ++o) acc = __builtin_fmaf(g[o], win[o + m], acc);
-                atomicAdd(dth + ip * ckp + (ck - 1 - m), acc);
+                acc = wave_sum(acc);
+                if ((threadIdx.x & 63) == 0) atomicAdd(dth + ip * ckp + (ck - 1 - m), acc);
             }
         }
     }
@@ -485,10 +504,8 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     float *dpb = ebuf + nEr * ep;                                 // dP3^a, [CH][nEr][ep]
     float *th_s = dpb + CH * nEr * ep;                            // [CH][cq][ckp]
     float *w_s = th_s + ((CH * cq * ckp + 3) & ~3);
-    // accumulated dtheta, 16 copies [copy][CH][cq][ckp] at an odd stride (banks)
-    const int dstride = ((CH * cq * ckp + 3) & ~3) + 1;
-    float *dth = w_s + ((CH * CH + 3) & ~3);
-    float *st = dth + ((16 * dstride + 3) & ~3);                  // [CH][3][nEr4]: m, il, D of the region rows
+    float *dth = w_s + ((CH * CH + 3) & ~3);                      // accumulated dtheta [CH][cq][ckp]
+    float *st = dth + ((CH * cq * ckp + 3) & ~3);                 // [CH][3][nEr4]: m, il, D of the region rows
     const int nEr4 = (nEr + 3) & ~3;
     float *dwr = st + CH * 3 * nEr4;                              // [4 waves][CH*CH]
     DT *opbuf = reinterpret_cast<DT *>(dwr + ((4 * CH * CH + 3) & ~3));
@@ -507,7 +524,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
         th_s[i] = c < ck ? p.theta[((size_t)(h0 + a) * cq + r) * ck + c] : 0.f;
     }
-    for (int i = tid; i < 16 * dstride; i += NT) dth[i] = 0.f;
+    for (int i = tid; i < CH * cq * ckp; i += NT) dth[i] = 0.f;
     for (int i = tid; i < CH * CH; i += NT) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
     float dwp[CH * CH];
 #pragma unroll
@@ -620,9 +637,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                 const int qi = i0 + io;
                 // window of the lane: logit row (io + cq-1) - i', columns from jb + hr (key j0 + jb - hl)
                 const int tlim = p.exact ? qi - (xc0 + jb + hr) : (1 << 30);
-                // lanes add into one of 16 copies (lane % 16), spreading the atomics
-                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc,
-                                 dth + (lane & 15) * dstride + s * cq * ckp, cq, ck, ckp, tlim);
+                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim);
             }
             // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil;
             // with Eq. 4's indicator the terms of offset i' count where key <= r + i'
@@ -703,9 +718,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     }
     for (int i = tid; i < CH * cq * ckp; i += NT) {
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
-        float t = 0.f;
-        for (int cp = 0; cp < 16; ++cp) t += dth[cp * dstride + i];
-        if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, t * bp.inv_log2e);
+        if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, dth[i] * bp.inv_log2e);
     }
 }
 

@@ -461,22 +461,84 @@ __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nr
         const int qi = r0 + 16 * rb + (lane & 15);
         load_frag<D>(hf, dh, qi, T, lane);
         if (SPLIT) load_frag<D>(lf, dl, qi, T, lane);
-        // the next block's V fragment is requested before this block's products
+        // the V fragments of the next two blocks are requested before this
+        // block's products (the loads come from L2 / HBM)
+        Frag v1;
         load_frag<D>(vf, vh, c0 + (lane & 15), T, lane);
+        if (ncb > 1) load_frag<D>(v1, vh, c0 + 16 + (lane & 15), T, lane);
         for (int cb = 0; cb < ncb; ++cb) {
-            Frag vn;
-            if (cb + 1 < ncb) load_frag<D>(vn, vh, c0 + 16 * (cb + 1) + (lane & 15), T, lane);
+            Frag v2;
+            if (cb + 2 < ncb) load_frag<D>(v2, vh, c0 + 16 * (cb + 2) + (lane & 15), T, lane);
             f32x4 acc = qk_mfma<D>(vf, hf);
             if (SPLIT) {
                 const f32x4 a2 = qk_mfma<D>(vf, lf);
                 acc += a2;
             }
-            vf = vn;
+            vf = v1;
+            v1 = v2;
             if (16 * rb + (lane & 15) < nrows)
                 *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
         }
     }
 }
+
+// A 64-row tile for the P.V-shaped products of kernel B (layout of
+// load_v_tile), staged in registers: fetch() issues the global loads, put()
+// writes the LDS tile, so that a tile's loads can be in flight while the
+// previous tile is used.
+template <typename DT, int D>
+struct TileStage;
+
+template <int D>
+struct TileStage<bf16_t, D> {
+    bf16x8 x[D / 32];
+    __device__ void fetch(const bf16_t *g, int r0, int T, int tid)
+    {
+        const int key = tid & 63, kj = r0 + key;
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int c0 = ((tid >> 6) + 4 * it) * 8;
+            if (kj < T) {
+                x[it] = *reinterpret_cast<const bf16x8 *>(g + (size_t)kj * D + c0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[it][e] = (bf16_t)0.0f;
+            }
+        }
+    }
+    __device__ void put(bf16_t *vb, int tid) const
+    {
+        const int key = tid & 63;
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int c0 = ((tid >> 6) + 4 * it) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vb[(c0 + e) * VP_BF16 + key] = x[it][e];
+        }
+    }
+};
+
+template <int D>
+struct TileStage<float, D> {
+    static constexpr int C4 = D / 4, N = BN * C4 / NT;
+    f32x4 x[N];
+    __device__ void fetch(const float *g, int r0, int T, int tid)
+    {
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int idx = tid + it * NT, key = idx / C4, c0 = (idx % C4) * 4, kj = r0 + key;
+            x[it] = kj < T ? *reinterpret_cast<const f32x4 *>(g + (size_t)kj * D + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __device__ void put(float *vb, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int idx = tid + it * NT, key = idx / C4, c0 = (idx % C4) * 4;
+            *reinterpret_cast<f32x4 *>(vb + key * (D + 4) + c0) = x[it];
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Kernel B
@@ -547,6 +609,31 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
 
     const int nlcb = (nEc + 15) / 16;
     const int qt0 = p.exact ? (kt > 0 ? kt - 1 : 0) : kt;
+    // The 64-row tiles of one (query tile, head s) step, in order of use:
+    // dO^a (and its low plane) for every output head a, K^s at the key tile,
+    // Q^s at the query tile.  Each is fetched into registers one tile ahead.
+    constexpr int NDO = SPLIT ? 2 * CH : CH;
+    TileStage<DT, D> stg;
+    auto fetch_tile = [&](int qt, int s, int k) {
+        if (qt >= p.n_qt) return;
+        if (k < NDO) {
+            const int a = SPLIT ? k >> 1 : k;
+            const DT *src = (SPLIT && (k & 1)) ? dOl : dO;
+            stg.fetch(src + base0 + a * hstride, qt * BM, T, tid);
+        } else if (k == NDO) {
+            stg.fetch(K + base0 + s * hstride, j0, T, tid);
+        } else {
+            stg.fetch(Q + base0 + s * hstride, qt * BM, T, tid);
+        }
+    };
+    // put tile k of step (qt, s) into LDS, then request the one after it
+    auto put_tile = [&](int qt, int s, int k) {
+        stg.put(opbuf, tid);
+        if (k + 1 <= NDO + 1) fetch_tile(qt, s, k + 1);
+        else if (s + 1 < CH) fetch_tile(qt, s + 1, 0);
+        else fetch_tile(qt + 1, 0, 0);
+    };
+    fetch_tile(qt0, 0, 0);
     for (int qt = qt0; qt < p.n_qt; ++qt) {
         const int i0 = qt * BM;
         const int ec0 = j0 - hr;              // key of region column 0
@@ -596,7 +683,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
             // dO's high plane, P's high part against dO's low plane
             for (int a = 0; a < CH; ++a) {
                 __syncthreads();
-                load_v_tile<D>(opbuf, dO + base0 + a * hstride, i0, T, tid);
+                put_tile(qt, s, SPLIT ? 2 * a : a);
                 __syncthreads();
                 float at[16];
                 const float wa = w_s[a * CH + s];
@@ -605,7 +692,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                 pv_x<D>(dV[a], at, opbuf, lane);
                 if (SPLIT) {
                     __syncthreads();
-                    load_v_tile<D>(opbuf, dOl + base0 + a * hstride, i0, T, tid);
+                    put_tile(qt, s, 2 * a + 1);
                     __syncthreads();
                     float ah[16];
 #pragma unroll
@@ -656,7 +743,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
             __syncthreads();  // xbuf free (dtheta done), ebuf reads done
             // dQ^s += dS K^s / sqrt(d)  (global atomics)
             {
-                load_v_tile<D>(opbuf, K + base0 + s * hstride, j0, T, tid);
+                put_tile(qt, s, NDO);
                 __syncthreads();
                 f32x4 qa[D / 16];
 #pragma unroll
@@ -678,7 +765,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
 #pragma unroll
             for (int o = 0; o < 16; ++o) dsb[io * (BN + 4) + jb + o] = dsv[o];
             __syncthreads();
-            load_v_tile<D>(opbuf, Q + base0 + s * hstride, i0, T, tid);
+            put_tile(qt, s, NDO + 1);
             __syncthreads();
             {
                 float at[16];

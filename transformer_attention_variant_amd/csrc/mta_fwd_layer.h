@@ -89,13 +89,17 @@ __device__ inline void s_tile(float *buf, int pitch, int nrb, int ncb, int nrows
     for (int rb = wave; rb < nrb; rb += 4) {
         load_frag<D>(qf, qh, r0 + 16 * rb + (lane & 15), T, lane);
         const int qi = r0 + 16 * rb + (lane & 15);
-        // the next block's K fragment is requested before this block's product
+        // the K fragments of the next two blocks are requested before this
+        // block's product (the loads come from L2 / HBM)
+        Frag k1;
         load_frag<D>(kf, kh, c0 + (lane & 15), T, lane);
+        if (ncb > 1) load_frag<D>(k1, kh, c0 + 16 + (lane & 15), T, lane);
         for (int cb = 0; cb < ncb; ++cb) {
-            Frag kn;
-            if (cb + 1 < ncb) load_frag<D>(kn, kh, c0 + 16 * (cb + 1) + (lane & 15), T, lane);
+            Frag k2;
+            if (cb + 2 < ncb) load_frag<D>(k2, kh, c0 + 16 * (cb + 2) + (lane & 15), T, lane);
             const f32x4 acc = qk_mfma<D>(kf, qf);
-            kf = kn;
+            kf = k1;
+            k1 = k2;
             const int e0 = 16 * cb + 4 * (lane >> 4);
             f32x4 o;
 #pragma unroll

@@ -435,17 +435,26 @@ __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, 
             for (int t = 0; t < MAXW; ++t) win[t] = (t <= tlim) ? win[t] : 0.f;
         }
         // tap jj reads window entry o + c_k - 1 - jj; with m = c_k - 1 - jj the
-        // register index o + m is static
+        // register index o + m is static.  The taps are independent
+        // accumulators; after the wave sums lane m holds tap m and one LDS
+        // atomic instruction adds them all.
+        float acc[KMAX];
 #pragma unroll
-        for (int m = 0; m < KMAX; ++m) {
+        for (int m = 0; m < KMAX; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int o = 0; o < 16; ++o)
+#pragma unroll
+            for (int m = 0; m < KMAX; ++m)
+                if (CK || m < ck) acc[m] = __builtin_fmaf(g[o], win[o + m], acc[m]);
+        const int lane = threadIdx.x & 63;
+        float v = 0.f;
+#pragma unroll
+        for (int m = 0; m < KMAX; ++m)
             if (CK || m < ck) {
-                float acc = 0.f;
-#pragma unroll
-                for (int o = 0; o < 16; ++o) acc = __builtin_fmaf(g[o], win[o + m], acc);
-                acc = wave_sum(acc);
-                if ((threadIdx.x & 63) == 0) atomicAdd(dth + ip * ckp + (ck - 1 - m), acc);
+                const float t = wave_sum(acc[m]);
+                v = (lane == m) ? t : v;
             }
-        }
+        if (lane < ck) atomicAdd(dth + ip * ckp + (ck - 1 - lane), v);
     }
 }
 

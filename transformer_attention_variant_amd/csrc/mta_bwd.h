@@ -465,19 +465,18 @@ __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nr
                                  const DT *vh, int r0, int c0, int T, int wave, int lane)
 {
     typedef typename FragOf<DT, D>::type Frag;
-    Frag hf, lf, vf;
-    for (int rb = wave; rb < nrb; rb += 4) {
+    // one 16-row block against the column blocks [cb0, ncb) step cstep; the
+    // V fragments of the next two blocks are requested before each product
+    auto row_block = [&](int rb, int cb0, int cstep) {
+        Frag hf, lf, vf, v1;
         const int qi = r0 + 16 * rb + (lane & 15);
         load_frag<D>(hf, dh, qi, T, lane);
         if (SPLIT) load_frag<D>(lf, dl, qi, T, lane);
-        // the V fragments of the next two blocks are requested before this
-        // block's products (the loads come from L2 / HBM)
-        Frag v1;
-        load_frag<D>(vf, vh, c0 + (lane & 15), T, lane);
-        if (ncb > 1) load_frag<D>(v1, vh, c0 + 16 + (lane & 15), T, lane);
-        for (int cb = 0; cb < ncb; ++cb) {
+        load_frag<D>(vf, vh, c0 + 16 * cb0 + (lane & 15), T, lane);
+        if (cb0 + cstep < ncb) load_frag<D>(v1, vh, c0 + 16 * (cb0 + cstep) + (lane & 15), T, lane);
+        for (int cb = cb0; cb < ncb; cb += cstep) {
             Frag v2;
-            if (cb + 2 < ncb) load_frag<D>(v2, vh, c0 + 16 * (cb + 2) + (lane & 15), T, lane);
+            if (cb + 2 * cstep < ncb) load_frag<D>(v2, vh, c0 + 16 * (cb + 2 * cstep) + (lane & 15), T, lane);
             f32x4 acc = qk_mfma<D>(vf, hf);
             if (SPLIT) {
                 const f32x4 a2 = qk_mfma<D>(vf, lf);
@@ -488,7 +487,13 @@ __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nr
             if (16 * rb + (lane & 15) < nrows)
                 *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
         }
-    }
+    };
+    // whole rounds of row blocks: one per wave; the remaining row blocks'
+    // column blocks are dealt to the waves in turn
+    const int full = nrb & ~3;
+    for (int rb = wave; rb < full; rb += 4) row_block(rb, 0, 1);
+    for (int rb = full; rb < nrb; ++rb)
+        if (wave < ncb) row_block(rb, wave, 4);
 }
 
 // A 64-row tile for the P.V-shaped products of kernel B (layout of

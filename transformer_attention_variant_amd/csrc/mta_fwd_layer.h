@@ -85,18 +85,18 @@ __device__ inline void s_tile(float *buf, int pitch, int nrb, int ncb, int nrows
                               int r0, int c0, int T, float sc, bool raw, int wave, int lane)
 {
     typedef typename FragOf<DT, D>::type Frag;
-    Frag qf, kf;
-    for (int rb = wave; rb < nrb; rb += 4) {
-        load_frag<D>(qf, qh, r0 + 16 * rb + (lane & 15), T, lane);
+    // one 16-row block: products with the column blocks [cb0, ncb) step cstep;
+    // the K fragments of the next two blocks are requested before each
+    // product (the loads come from L2 / HBM)
+    auto row_block = [&](int rb, int cb0, int cstep) {
+        Frag qf, kf, k1;
         const int qi = r0 + 16 * rb + (lane & 15);
-        // the K fragments of the next two blocks are requested before this
-        // block's product (the loads come from L2 / HBM)
-        Frag k1;
-        load_frag<D>(kf, kh, c0 + (lane & 15), T, lane);
-        if (ncb > 1) load_frag<D>(k1, kh, c0 + 16 + (lane & 15), T, lane);
-        for (int cb = 0; cb < ncb; ++cb) {
+        load_frag<D>(qf, qh, qi, T, lane);
+        load_frag<D>(kf, kh, c0 + 16 * cb0 + (lane & 15), T, lane);
+        if (cb0 + cstep < ncb) load_frag<D>(k1, kh, c0 + 16 * (cb0 + cstep) + (lane & 15), T, lane);
+        for (int cb = cb0; cb < ncb; cb += cstep) {
             Frag k2;
-            if (cb + 2 < ncb) load_frag<D>(k2, kh, c0 + 16 * (cb + 2) + (lane & 15), T, lane);
+            if (cb + 2 * cstep < ncb) load_frag<D>(k2, kh, c0 + 16 * (cb + 2 * cstep) + (lane & 15), T, lane);
             const f32x4 acc = qk_mfma<D>(kf, qf);
             kf = k1;
             k1 = k2;
@@ -111,7 +111,13 @@ __device__ inline void s_tile(float *buf, int pitch, int nrb, int ncb, int nrows
             if (16 * rb + (lane & 15) < nrows)
                 *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + e0) = o;
         }
-    }
+    };
+    // whole rounds of row blocks: one per wave; the remaining row blocks'
+    // column blocks are dealt to the waves in turn
+    const int full = nrb & ~3;
+    for (int rb = wave; rb < full; rb += 4) row_block(rb, 0, 1);
+    for (int rb = full; rb < nrb; ++rb)
+        if (wave < ncb) row_block(rb, wave, 4);
 }
 
 // CQ1/CK1, CQ2/CK2: compile-time sizes of the pre- and post-softmax key-query

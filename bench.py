@@ -35,15 +35,31 @@ PEAK_HBM_GBS = 8000.0
 FLUSH_MIB = 512
 
 
-def kernel_sources_hash() -> str:
-    """Hash of the HIP sources; traffic counters are valid only for the sources
-    they were taken on."""
+# the HIP sources each forward kernel is built from (its header chain, its
+# instantiation unit and the launch helpers)
+KERNEL_SOURCES = {
+    "mta_fwd_v4": ["mta_fwd_v4.h", "mta_fwd_v3.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v4.hip",
+                   "mta_launch.h"],
+    "mta_fwd_v3": ["mta_fwd_v3.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v3.hip", "mta_launch.h"],
+    "mta_fwd_v2": ["mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v2.hip", "mta_inst_v2.inc",
+                   "mta_inst_v2_exact.hip", "mta_launch.h"],
+    "mta_fwd_kernel": ["mta_fwd_kernel.h", "mta_inst.inc", "mta_inst_bf16.hip", "mta_inst_f32.hip",
+                       "mta_launch.h"],
+}
+
+
+def kernel_sources_hash(kernel: str = "") -> str:
+    """Hash of the HIP sources of a kernel (of all of them when the kernel is
+    not listed); traffic counters are valid only for the sources they were
+    taken on."""
     d = os.path.join(ROOT, "transformer_attention_variant_amd", "csrc")
+    files = next((v for k, v in KERNEL_SOURCES.items() if kernel.startswith(k + " ")), None)
+    if files is None:
+        files = [f for f in sorted(os.listdir(d)) if f.endswith((".h", ".hip", ".inc"))]
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip", ".inc")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(files):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -90,6 +106,8 @@ def summarize_pmc(args):
     """HBM traffic per launch of the MTA kernel.  FETCH_SIZE and WRITE_SIZE are
     read per dispatch; each is scaled by the ratio of the known byte count of a
     plain device copy (--copy-mb) to what the same counter reports for it."""
+    from transformer_attention_variant_amd import binding
+    from transformer_attention_variant_amd import inputs as I
     fdir, wdir, cfdir, cwdir = args.summarize_pmc
     kf, nk = _pmc_avg(fdir, "FETCH_SIZE", "mta_fwd")
     kw, _ = _pmc_avg(wdir, "WRITE_SIZE", "mta_fwd")
@@ -100,7 +118,8 @@ def summarize_pmc(args):
     rd, wr = kf * sf * 1024, kw * sw * 1024
     entry = {"bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
              "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": sf, "write_scale": sw,
-             "dispatches": nk, "copy_mib": copy_kib // 1024, "sources": kernel_sources_hash()}
+             "dispatches": nk, "copy_mib": copy_kib // 1024,
+             "sources": kernel_sources_hash(binding.kernel_name(I.CONFIGS[args.config]) or "")}
     db = {}
     if os.path.exists(args.traffic_file):
         db = json.load(open(args.traffic_file))
@@ -190,7 +209,7 @@ def main():
     if os.path.exists(args.traffic_file):
         try:
             tr = json.load(open(args.traffic_file)).get(cfg.name, {})
-            if tr.get("sources") == kernel_sources_hash():
+            if tr.get("sources") == kernel_sources_hash(kname or ""):
                 traffic = tr.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None

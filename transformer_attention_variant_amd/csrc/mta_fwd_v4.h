@@ -14,10 +14,13 @@
 //   the d-columns [64s, 64s + 64) of every (source b, output a) pair.
 // Per key tile there are three barriers, each publishing LDS writes only:
 //   B1 | K tiles of both heads are in LDS; the V tiles of this key tile start
-//        loading (DMA); logit tiles of both heads -> LDS (hi/lo planes)
+//        loading (DMA); logit tiles of both heads -> LDS (fp16)
 //   B2 | the K tiles of the next key tile start loading; stencil, Mask_-inf,
 //        row maximum, rescale factor and probabilities -> LDS
 //   B3 | (V tiles landed) rescale of the accumulators, P.V
+// The key-query convolution runs on the matrix cores with fp16 operands (the
+// logit tile and the kernel taps rounded to nearest, 11 significant bits) and
+// fp32 accumulation: one product per kernel row and output block.
 #pragma once
 
 #include "mta_fwd_v3.h"
@@ -36,7 +39,7 @@ using v3::lds_void_p;
 constexpr int CH = 2;
 constexpr int D = 128;
 constexpr int NCB = 5;          // 16-key column blocks of the logit tile (80 columns)
-constexpr int XP = 16 * NCB;    // bf16 pitch of the hi / lo planes (conflict-free stencil reads)
+constexpr int XP = 16 * NCB;    // fp16 pitch of the logit tiles (conflict-free stencil reads)
 constexpr int KROWS = 16 * NCB; // K rows per head (key halo included)
 
 struct Layout {
@@ -47,7 +50,7 @@ __host__ __device__ inline Layout layout(int cq, int ck)
 {
     Layout L;
     int o = 0;
-    L.x_off = o;  o += CH * 2 * EXT_R * XP * 2;   // logit tiles of both heads, bf16 hi + lo planes
+    L.x_off = o;  o += CH * EXT_R * XP * 2;       // logit tiles of both heads, fp16
     L.k_off = o;  o += CH * KROWS * D * 2;        // K tiles (swizzled rows)
     L.v_off = o;  o += CH * BN * D * 2;           // V tiles (swizzled rows)
     L.qh_off = o; o += CH * HALO * D * 2;         // Q rows above the query tile
@@ -87,6 +90,52 @@ constexpr int V_PIECES = CH * BN / 4 / 8;
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 __device__ inline void wait_vm_k() { __builtin_amdgcn_s_waitcnt(0x0f70 | K_PIECES); }
 
+typedef _Float16 f16_t;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// fp16 operand of the stencil: magnitudes past the fp16 range are clamped to
+// its largest finite value (never inf, so a zero tap never meets an infinity)
+__device__ inline float f16_range(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
+
+// Store a 16x16 block of raw logits Q K^T (lane: tile row rb*16 + lane%16,
+// columns cb*16 + 4*(lane/16) + r) as fp16 with Mask_0 and the zero padding
+// outside [0, T) applied (with `exact` only the padding).  The convolution
+// being linear, the factor log2(e)/sqrt(d) is applied to the kernel taps.
+__device__ inline void store_block_f16(f16_t *x, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
+                                       bool exact, int lane)
+{
+    const int rho = rb * 16 + (lane & 15);
+    const int e0 = cb * 16 + 4 * (lane >> 4);
+    const int qi = i0 - HALO + rho;
+    const int kmax = exact ? T - 1 : qi;
+    // block-uniform: every entry kept and inside [0, T), or not
+    const int q_lo = i0 - HALO + rb * 16, k_lo = j0 - hl + cb * 16;
+    const bool all_ok = (k_lo >= 0) && (k_lo + 15 <= (exact ? T - 1 : q_lo)) && (q_lo >= 0) && (q_lo + 15 < T);
+    float xv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = f16_range(acc[r]);
+        if (!all_ok) {
+            const int kj = j0 - hl + e0 + r;
+            const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
+            v = ok ? v : 0.f;
+        }
+        xv[r] = v;
+    }
+    const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
+    *reinterpret_cast<f16x4 *>(x + rho * XP + e0) = h;
+}
+
+__device__ inline f16x8 and_mask16(f16x8 v, const uint32_t (&w)[4])
+{
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] &= w[q];
+    return __builtin_bit_cast(f16x8, u);
+}
+
 // maximum / sum over the four lanes l16 + 16 g4 holding one row
 __device__ inline float row_max4(float x)
 {
@@ -117,79 +166,48 @@ __device__ inline void block_mask(int tl, uint32_t (&w)[4])
         w[q] = (2 * q <= tl ? 0x0000ffffu : 0u) | (2 * q + 1 <= tl ? 0xffff0000u : 0u);
 }
 
-// Q K^T of a 16x16 block over d = 128 in two independent accumulation chains.
-__device__ inline f32x4 qk2(const QFrag<D> &kf, const QFrag<D> &qf)
+// Q K^T of a 16x16 block over d = 128 (one accumulation chain).
+__device__ inline f32x4 qk(const QFrag<D> &kf, const QFrag<D> &qf)
 {
-    f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[0], qf.x[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[1], qf.x[1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[2], qf.x[2], a0, 0, 0, 0);
-    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[3], qf.x[3], a1, 0, 0, 0);
-    return a0 + a1;
+    f32x4 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[0], qf.x[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < D / 32; ++t) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.x[t], qf.x[t], a, 0, 0, 0);
+    return a;
 }
 
 // Key-query stencil of the 16 rows of this wave (tile row rho = HALO + 16rw +
 // lane%16) over all 64 keys of the tile: output block t covers keys 16t..16t+15
-// and reads the 32-column window starting at tile column 16t.  Three products
-// (hi*hi, hi*lo, lo*hi) per kernel row on the matrix cores.  out[4t + r] is
+// and reads the 32-column window starting at tile column 16t.  One fp16
+// product per kernel row on the matrix cores.  out[4t + r] is
 // key 16t + 4*(lane/16) + r.  With MASK, Eq. 4's indicator: tl0 is the last
 // window column of block 0 (relative to 8*(lane/16)) whose key is not in the
 // future of the lane's output query; the blocks are then taken two at a time
 // with their masks built just before use.
 template <int CQ, bool MASK>
-__device__ inline void stencil64(const bf16_t *xh, const bf16_t *xl, int rho, const bf16x8 (&tf)[CQ][2], int tl0,
-                                 int lane, float out[16])
+__device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ], int tl0, int lane, float out[16])
 {
     const int g4 = lane >> 4;
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // step (ip, t2): the two output blocks t2, t2+1 of kernel row ip
-    bf16x8 h[2], l[2];
-    auto load = [&](int ip, int t2) {
-        const int base = (rho - ip) * XP + 8 * g4;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            h[u] = *reinterpret_cast<const bf16x8 *>(xh + base + 16 * (t2 + u));
-            l[u] = *reinterpret_cast<const bf16x8 *>(xl + base + 16 * (t2 + u));
-        }
-    };
-    auto mma = [&](int ip, int t2, const bf16x8 (&hh)[2], const bf16x8 (&ll)[2]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][0], hh[u], acc[t2 + u], 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][0], ll[u], acc[t2 + u], 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            acc[t2 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[ip][1], hh[u], acc[t2 + u], 0, 0, 0);
-    };
     if (MASK) {
 #pragma unroll
-        for (int t2 = 0; t2 < 4; t2 += 2) {
-            uint32_t mk[2][4];
-            block_mask(tl0 - 16 * t2, mk[0]);
-            block_mask(tl0 - 16 * (t2 + 1), mk[1]);
+        for (int t = 0; t < 4; ++t) {
+            uint32_t mk[4];
+            block_mask(tl0 - 16 * t, mk);
 #pragma unroll
             for (int ip = 0; ip < CQ; ++ip) {
-                load(ip, t2);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    h[u] = v2::and_mask(h[u], mk[u]);
-                    l[u] = v2::and_mask(l[u], mk[u]);
-                }
-                mma(ip, t2, h, l);
+                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + (rho - ip) * XP + 8 * g4 + 16 * t);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf[ip], and_mask16(xv, mk), acc[t], 0, 0, 0);
             }
         }
     } else {
-        // two output blocks at a time, so that the operands of one step stay
-        // few next to the resident accumulators
 #pragma unroll
         for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
-            for (int t2 = 0; t2 < 4; t2 += 2) {
-                load(ip, t2);
-                mma(ip, t2, h, l);
+            for (int t = 0; t < 4; ++t) {
+                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + (rho - ip) * XP + 8 * g4 + 16 * t);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf[ip], xv, acc[t], 0, 0, 0);
             }
     }
 #pragma unroll
@@ -216,7 +234,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
     constexpr int CKP = ((CK + 3) / 4) * 4;
 
     const Layout lay = layout(CQ, CK);
-    bf16_t *xbuf = reinterpret_cast<bf16_t *>(smem + lay.x_off);
+    f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
     bf16_t *qhbuf = reinterpret_cast<bf16_t *>(smem + lay.qh_off);
@@ -251,27 +269,23 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
     wait_vm_all();
     __syncthreads();
 
-    // banded kernel matrices of head hs (MFMA A operands, hi and lo planes):
+    // banded kernel matrices of head hs (MFMA A operands, fp16):
     // row m = lane%16 (output key), columns k = 8*(lane/16) + s of the window
-    bf16x8 tf[CQ][2];
+    f16x8 tf[CQ];
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
             const int jj = l16 + CK - 1 - (8 * g4 + s8);
             const float t = (jj >= 0 && jj < CK) ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
-            bf16_t hh, ll;
-            v2::split_hl(t, hh, ll);
-            tf[ip][0][s8] = hh;
-            tf[ip][1][s8] = ll;
+            tf[ip][s8] = (f16_t)f16_range(t * p.sc);
         }
 
     const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
     const int qabs = i0 + io;
     const int rho = HALO + io;
     const int dbase = 64 * hs;
-    bf16_t *xh = xbuf + hs * 2 * EXT_R * XP;
-    bf16_t *xl = xh + EXT_R * XP;
+    f16_t *xo = xbuf + hs * EXT_R * XP;
     int koff[4];  // swizzled chunk offsets of the K / Q-halo fragment reads
 #pragma unroll
     for (int t = 0; t < 4; ++t) koff[t] = 8 * ((4 * g4 + t) ^ swz_k(l16));
@@ -291,32 +305,36 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
         barrier_lds();  // B1: K tiles of kt are in LDS (each wave waited for its DMA)
         dma_pair<true, BN>(vbuf, V, hstride, j0, T, wave, lane);
 
-        // logit tiles: own row block of head hs, then a share of the halo blocks
+        // logit tiles: own row block of head hs (five column blocks), then a
+        // share of the halo blocks; the fragments of the next block are read
+        // before the products of the current one
         {
-            QFrag<D> kf;
+            const bf16_t *kh = kbuf + hs * KROWS * D + l16 * D;
+            auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) f.x[t] = *reinterpret_cast<const bf16x8 *>(rows + 16 * cb * D + koff[t]);
+            };
+            QFrag<D> kf[2], hq, hk;
+            kload(kf[0], kh, 0);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const bf16_t *kr = kbuf + hs * KROWS * D + (16 * cb + l16) * D;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
-                const f32x4 acc = qk2(kf, qown);
-                v2::store_block_hl<RAW>(xh, xl, XP, 1 + rw, cb, acc, i0, j0, p.hl, T, p.sc, nullptr, nullptr, EXACT,
-                                        lane);
+                if (cb + 1 < NCB) {
+                    kload(kf[(cb + 1) & 1], kh, cb + 1);
+                } else if (CQ > 1) {
+                    kload(hk, kbuf + (wave / NCB) * KROWS * D + l16 * D, wave % NCB);
+                }
+                store_block_f16(xo, 1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
             }
             if (CQ > 1) {
-                for (int q = wave; q < CH * NCB; q += 8) {
-                    const int h = q / NCB, cb = q % NCB;
-                    QFrag<D> qf;
-                    const bf16_t *qr = qhbuf + h * HALO * D + l16 * D;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) qf.x[t] = *reinterpret_cast<const bf16x8 *>(qr + koff[t]);
-                    const bf16_t *kr = kbuf + h * KROWS * D + (16 * cb + l16) * D;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + koff[t]);
-                    const f32x4 acc = qk2(kf, qf);
-                    bf16_t *hx = xbuf + h * 2 * EXT_R * XP;
-                    v2::store_block_hl<RAW>(hx, hx + EXT_R * XP, XP, 0, cb, acc, i0, j0, p.hl, T, p.sc, nullptr,
-                                            nullptr, EXACT, lane);
+                // halo blocks q = wave and, for waves 0 and 1, q = wave + 8 (q = h * NCB + cb)
+                kload(hq, qhbuf + (wave / NCB) * HALO * D + l16 * D, 0);
+                store_block_f16(xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT,
+                                lane);
+                if (wave + 8 < CH * NCB) {
+                    const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
+                    kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
+                    kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
+                    store_block_f16(xbuf + h * EXT_R * XP, 0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                 }
             }
         }
@@ -326,9 +344,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
 
         float c[16];
         if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
-            stencil64<CQ, true>(xh, xl, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
+            stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
         else
-            stencil64<CQ, false>(xh, xl, rho, tf, 0, lane, c);
+            stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
         // Mask_-inf, the row maximum over the 64 keys, probabilities
         float mx = NEG_INF;
 #pragma unroll

@@ -23,6 +23,8 @@
 // fp32 accumulation: one product per kernel row and output block.
 #pragma once
 
+#include <type_traits>
+
 #include "mta_fwd_v3.h"
 
 namespace mta {
@@ -100,8 +102,11 @@ __device__ inline float f16_range(float x) { return __builtin_amdgcn_fmed3f(x, -
 
 // Store a 16x16 block of raw logits Q K^T (lane: tile row rb*16 + lane%16,
 // columns cb*16 + 4*(lane/16) + r) as fp16 with Mask_0 and the zero padding
-// outside [0, T) applied (with `exact` only the padding).  The convolution
-// being linear, the factor log2(e)/sqrt(d) is applied to the kernel taps.
+// outside [0, T) applied (with `exact` only the padding); MASKED = false
+// when the caller knows that every entry of the block is kept.  The
+// convolution being linear, the factor log2(e)/sqrt(d) is applied to the
+// kernel taps.
+template <bool MASKED>
 __device__ inline void store_block_f16(f16_t *x, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
                                        bool exact, int lane)
 {
@@ -116,7 +121,7 @@ __device__ inline void store_block_f16(f16_t *x, int rb, int cb, f32x4 acc, int 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float v = f16_range(acc[r]);
-        if (!all_ok) {
+        if (MASKED && !all_ok) {
             const int kj = j0 - hl + e0 + r;
             const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
             v = ok ? v : 0.f;
@@ -308,7 +313,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
         // logit tiles: own row block of head hs (five column blocks), then a
         // share of the halo blocks; the fragments of the next block are read
         // before the products of the current one
-        {
+        auto logits = [&](auto masked) {
+            constexpr bool M = decltype(masked)::value;
             const bf16_t *kh = kbuf + hs * KROWS * D + l16 * D;
             auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
 #pragma unroll
@@ -323,21 +329,29 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                 } else if (CQ > 1) {
                     kload(hk, kbuf + (wave / NCB) * KROWS * D + l16 * D, wave % NCB);
                 }
-                store_block_f16(xo, 1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
+                store_block_f16<M>(xo, 1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
             }
             if (CQ > 1) {
                 // halo blocks q = wave and, for waves 0 and 1, q = wave + 8 (q = h * NCB + cb)
                 kload(hq, qhbuf + (wave / NCB) * HALO * D + l16 * D, 0);
-                store_block_f16(xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT,
+                store_block_f16<M>(xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT,
                                 lane);
                 if (wave + 8 < CH * NCB) {
                     const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
                     kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
                     kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
-                    store_block_f16(xbuf + h * EXT_R * XP, 0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                    store_block_f16<M>(xbuf + h * EXT_R * XP, 0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                 }
             }
-        }
+        };
+        // key tiles whose logit blocks (halo rows included) are all inside
+        // [0, T) and, with Mask_0, all in the past of every row: no masks
+        const int kfirst = j0 - p.hl, klast = j0 - p.hl + 16 * NCB - 1;
+        const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
+        if (inner)
+            logits(std::false_type{});
+        else
+            logits(std::true_type{});
         barrier_lds();  // B2: logit tiles complete; K buffers free
         const bool more = kt < qt;
         if (more) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);
@@ -347,14 +361,18 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
             stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
         else
             stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
-        // Mask_-inf, the row maximum over the 64 keys, probabilities
+        // Mask_-inf (only the diagonal tile has keys in the future of its
+        // rows), the row maximum over the 64 keys, probabilities
+        if (kt == qt) {
+#pragma unroll
+            for (int o = 0; o < 16; ++o) {
+                const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
+                c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+            }
+        }
         float mx = NEG_INF;
 #pragma unroll
-        for (int o = 0; o < 16; ++o) {
-            const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
-            c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
-            mx = fmaxf(mx, c[o]);
-        }
+        for (int o = 0; o < 16; ++o) mx = fmaxf(mx, c[o]);
         mx = row_max4(mx);
         // every row has a causal key in tile 0, so m_new is finite
         const float m_new = fmaxf(m_run, mx);

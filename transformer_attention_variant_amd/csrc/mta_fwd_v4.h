@@ -81,8 +81,11 @@ __device__ inline void dma_pair(bf16_t *lds, const bf16_t *g, size_t hstride, in
         const int c = pc ^ (VTILE ? swz_v(row) : swz_k(row));
         int key = key0 + row;
         key = key < 0 ? 0 : (key >= T ? T - 1 : key);
-        __builtin_amdgcn_global_load_lds((const void *)(g + h * hstride + (size_t)key * D + 8 * c),
-                                         (lds_void_p)(lds + h * NROWS * D + 512 * piece), 16, 0, 0);
+        // wave-uniform head base + 32-bit lane offset (scalar-base addressing)
+        const char *gh = reinterpret_cast<const char *>(g + h * hstride);
+        const unsigned off = (unsigned)key * (D * 2) + 16u * (unsigned)c;
+        __builtin_amdgcn_global_load_lds((const void *)(gh + off), (lds_void_p)(lds + h * NROWS * D + 512 * piece),
+                                         16, 0, 0);
     }
 }
 constexpr int K_PIECES = CH * KROWS / 4 / 8;  // per wave

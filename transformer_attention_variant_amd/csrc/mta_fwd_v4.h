@@ -103,15 +103,27 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // its largest finite value (never inf, so a zero tap never meets an infinity)
 __device__ inline float f16_range(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
 
-// Store a 16x16 block of raw logits Q K^T (lane: tile row rb*16 + lane%16,
-// columns cb*16 + 4*(lane/16) + r) as fp16 with Mask_0 and the zero padding
-// outside [0, T) applied (with `exact` only the padding); MASKED = false
-// when the caller knows that every entry of the block is kept.  The
-// convolution being linear, the factor log2(e)/sqrt(d) is applied to the
-// kernel taps.
+// fp16 logit tiles: row rho (0..EXT_R-1) holds 80 columns in ten 16-byte
+// chunks; chunk c of row rho is stored at chunk c ^ ((rho >> 2) & 1).  With the
+// 160-byte row pitch this keeps the stencil's 16-byte reads and the paired
+// 16-byte block stores below free of bank conflicts (ds_write_b128 serves 8
+// consecutive lanes per pass over a 128-byte bank window).
+// With c_q = 8 the kernel keeps the unswizzled layout and stores each block by
+// itself (8 bytes per lane): the pair exchange needs registers that kernel
+// does not have to spare.
+template <int CQ>
+__device__ inline int xchunk(int rho, int c) { return CQ < 8 ? c ^ ((rho >> 2) & 1) : c; }
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// A 16x16 block of raw logits Q K^T (lane: tile row rb*16 + lane%16, columns
+// cb*16 + 4*(lane/16) + r) converted to fp16 with Mask_0 and the zero padding
+// outside [0, T) applied (with `exact` only the padding); MASKED = false when
+// the caller knows that every entry of the block is kept.  The convolution
+// being linear, the factor log2(e)/sqrt(d) is applied to the kernel taps.
 template <bool MASKED>
-__device__ inline void store_block_f16(f16_t *x, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
-                                       bool exact, int lane)
+__device__ inline u32x2 cvt_block(int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T, bool exact, int lane)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
@@ -132,7 +144,34 @@ __device__ inline void store_block_f16(f16_t *x, int rb, int cb, f32x4 acc, int 
         xv[r] = v;
     }
     const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
-    *reinterpret_cast<f16x4 *>(x + rho * XP + e0) = h;
+    return __builtin_bit_cast(u32x2, h);
+}
+
+// Store two converted blocks X and Y (tile bases xX, xY; row blocks, column
+// blocks): lane groups 2k and 2k+1 hold keys 8k..8k+3 and 8k+4..8k+7 of the same
+// row; one exchange between them (v_permlane16_swap) leaves the even group with
+// 8 keys of X and the odd group with 8 keys of Y, and every lane stores 16
+// bytes.  With `one`, Y is absent and the odd groups store nothing.
+template <int CQ>
+__device__ inline void store_pair(f16_t *xX, int rbX, int cbX, u32x2 vX, f16_t *xY, int rbY, int cbY, u32x2 vY,
+                                  int lane, bool one = false)
+{
+    if (CQ >= 8) {
+        // unpaired: each block by itself, 8 bytes per lane
+        const int l16 = lane & 15, g4 = lane >> 4;
+        *reinterpret_cast<u32x2 *>(xX + (rbX * 16 + l16) * XP + 16 * cbX + 4 * g4) = vX;
+        if (!one) *reinterpret_cast<u32x2 *>(xY + (rbY * 16 + l16) * XP + 16 * cbY + 4 * g4) = vY;
+        return;
+    }
+    const auto s0 = __builtin_amdgcn_permlane16_swap(vX[0], vY[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(vX[1], vY[1], false, false);
+    const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+    const int g4 = lane >> 4;
+    const bool odd = g4 & 1;
+    const int rho = (odd ? rbY : rbX) * 16 + (lane & 15);
+    f16_t *x = odd ? xY : xX;
+    const int c = 2 * (odd ? cbY : cbX) + (g4 >> 1);
+    if (!(one && odd)) *reinterpret_cast<u32x4 *>(x + rho * XP + 8 * xchunk<CQ>(rho, c)) = w;
 }
 
 __device__ inline f16x8 and_mask16(f16x8 v, const uint32_t (&w)[4])
@@ -205,7 +244,8 @@ __device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ],
             block_mask(tl0 - 16 * t, mk);
 #pragma unroll
             for (int ip = 0; ip < CQ; ++ip) {
-                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + (rho - ip) * XP + 8 * g4 + 16 * t);
+                const int r = rho - ip;
+                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + r * XP + 8 * xchunk<CQ>(r, g4) + 16 * t);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf[ip], and_mask16(xv, mk), acc[t], 0, 0, 0);
             }
         }
@@ -214,7 +254,8 @@ __device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ],
         for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + (rho - ip) * XP + 8 * g4 + 16 * t);
+                const int r = rho - ip;
+                const f16x8 xv = *reinterpret_cast<const f16x8 *>(x + r * XP + 8 * xchunk<CQ>(r, g4) + 16 * t);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf[ip], xv, acc[t], 0, 0, 0);
             }
     }
@@ -325,6 +366,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
             };
             QFrag<D> kf[2], hq, hk;
             kload(kf[0], kh, 0);
+            u32x2 prev;  // converted block waiting for its store partner
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 if (cb + 1 < NCB) {
@@ -332,19 +374,28 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                 } else if (CQ > 1) {
                     kload(hk, kbuf + (wave / NCB) * KROWS * D + l16 * D, wave % NCB);
                 }
-                store_block_f16<M>(xo, 1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
+                const u32x2 v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
+                if (cb & 1)
+                    store_pair<CQ>(xo, 1 + rw, cb - 1, prev, xo, 1 + rw, cb, v, lane);
+                else
+                    prev = v;
             }
             if (CQ > 1) {
-                // halo blocks q = wave and, for waves 0 and 1, q = wave + 8 (q = h * NCB + cb)
+                // halo blocks q = wave and, for waves 0 and 1, q = wave + 8 (q = h * NCB + cb);
+                // the first one is stored with the last own block
                 kload(hq, qhbuf + (wave / NCB) * HALO * D + l16 * D, 0);
-                store_block_f16<M>(xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT,
-                                lane);
+                const u32x2 v = cvt_block<M>(0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, v, lane);
                 if (wave + 8 < CH * NCB) {
                     const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
                     kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
                     kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
-                    store_block_f16<M>(xbuf + h * EXT_R * XP, 0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                    const u32x2 v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                    f16_t *xh = xbuf + h * EXT_R * XP;
+                    store_pair<CQ>(xh, 0, hc, v2, xh, 0, hc, v2, lane, true);
                 }
+            } else {
+                store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xo, 1 + rw, NCB - 1, prev, lane, true);
             }
         };
         // key tiles whose logit blocks (halo rows included) are all inside

@@ -123,7 +123,7 @@ static int make_plan(const mta_config *cfg, Plan &pl)
             p.pitch = p.ncb * 16 + 4;
             lds = (size_t)mta::v4::layout(cq, ck).total;
             if (lds > LDS_MAX) fn = nullptr;
-            else pl.name = "mta_fwd_v4 (one pass, head-split waves)";
+            else pl.name = "mta_fwd_v4 (one pass, head-split waves, fp16 matrix-core stencil)";
         }
         if (!fn) fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
         if (fn && !pl.name) {

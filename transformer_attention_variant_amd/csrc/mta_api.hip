@@ -141,7 +141,7 @@ static int make_plan(const mta_config *cfg, Plan &pl)
             p.pitch = p.ncb * 16 + 4;
             fn = mta::find_launch_v2(d, ch, cq, ck, post, exact, hpre, ms);
             if (fn) {
-                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0).total;
+                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0, post != 0).total;
                 if (lds > LDS_MAX) fn = nullptr;
                 else pl.name = ms ? "mta_fwd_v2 (two passes, matrix-core stencil)"
                                   : "mta_fwd_v2 (two passes, VALU stencil)";

@@ -54,18 +54,21 @@ struct Layout {
     int s_off, k_off, q_off, v_off, p_off, st_off, xs_off, th_off, w_off, gn_off, tf_off, total;
 };
 
-// bf16 pitch of the hi / lo planes of the logit tile: a multiple of 8
+// fp16 pitch of the logit tile of the matrix-core stencil: a multiple of 8
 // elements whose 16-byte chunk count is 2 mod 4, so that the stencil's
 // ds_read_b128 (16 rows x 2 adjacent chunks per pass) never shares a bank.
 __host__ __device__ inline int pitch_hl(int ncb) { return (ncb & 1) ? ncb * 16 : ncb * 16 + 16; }
 
-__host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb, int pitch, bool ms = false)
+// post: the convolution follows the softmax (pass 1 then keeps raw fp32
+// logits for the statistics, also with the matrix-core stencil)
+__host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb, int pitch, bool ms, bool post)
 {
     Layout L;
     int o = 0;
     const int KP = D + 16;
-    const int sb32 = EXT_R * pitch * 4, sbhl = 2 * EXT_R * pitch_hl(ncb) * 2;
-    L.s_off = o;  o += sb32 > sbhl ? sb32 : sbhl;           // logit / probability tile (fp32, or bf16 hi+lo)
+    const int sb32 = EXT_R * pitch * 4, sb16 = EXT_R * pitch_hl(ncb) * 2;
+    const int sb = (ms && !post) ? sb16 : (sb32 > sb16 ? sb32 : sb16);
+    L.s_off = o;  o += sb;                                  // logit / probability tile (fp32, or fp16)
     L.k_off = o;  o += ncb * 16 * KP * 2;                   // K tile with key halo (bf16)
     L.q_off = o;  o += EXT_R * KP * 2;                      // Q tile with the 16 rows above (bf16)
     L.v_off = o;  o += BN * KP * 2;                         // V tile, row-major (bf16)
@@ -75,7 +78,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb,
     L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
     L.w_off = o;  o += ((CH * CH + 3) & ~3) * 4;
     L.gn_off = o; o += 2 * CH * BM * 4;                     // GroupNorm partial sums per d half
-    L.tf_off = o; o += ms ? CH * cq * 2 * 64 * 16 : 0;      // banded kernel matrices as MFMA A operands
+    L.tf_off = o; o += ms ? CH * cq * 64 * 16 : 0;          // banded kernel matrices as MFMA A operands (fp16)
     L.total = o;
     return L;
 }
@@ -196,23 +199,23 @@ __device__ inline s16x4 lds_read_tr4(const bf16_t *vbuf, int pitch, int kb, int 
 //   C^T[m][n] = sum_{i'} sum_k Theta_{i'}[m][k] * X[row(n) - i'][w0 + k],
 //   Theta_{i'}[m][k] = theta[i'][m + c_k - 1 - k] inside the band, else 0,
 // for output key w0 + m (w0 = first column of the 32-column input window) and
-// query row(n).  Both operands are split into bf16 hi + lo parts and three
-// products (hi*hi, hi*lo, lo*hi) accumulate in fp32 on the matrix cores, which
-// keeps about 16 significant bits of every term.
+// query row(n).  Both operands are rounded to fp16 (11 significant bits,
+// magnitudes clamped to the fp16 range) and one product per kernel row
+// accumulates in fp32 on the matrix cores.
 
-__device__ inline void split_hl(float x, bf16_t &hi, bf16_t &lo)
-{
-    hi = (bf16_t)x;
-    lo = (bf16_t)(x - (float)hi);
-}
+typedef _Float16 f16_t;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// Store a 16x16 logit block as hi/lo bf16 planes (Mask_0 + zero padding
-// applied; with `exact` only the zero padding, as in store_block); MODE PROB
-// stores probabilities exp2(x - m_row) / l_row instead.
+// never inf, so a zero tap never meets an infinity
+__device__ inline float f16_clamp(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
+
+// Store a 16x16 logit block as fp16 (Mask_0 + zero padding applied; with
+// `exact` only the zero padding, as in store_block); MODE PROB stores
+// probabilities exp2(x - m_row) / l_row instead.
 template <int MODE>
-__device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, int cb, f32x4 acc, int i0,
-                                      int j0, int hl, int T, float sc, const float *st_m, const float *st_il,
-                                      int exact, int lane)
+__device__ inline void store_block_x(f16_t *x16, int ph, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
+                                     float sc, const float *st_m, const float *st_il, int exact, int lane)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
@@ -227,8 +230,7 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
         m = st_m[rho];
         il = st_il[rho];
     }
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 h4, l4;
+    float xv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float x = acc[r] * sc;
@@ -238,71 +240,50 @@ __device__ inline void store_block_hl(bf16_t *xh, bf16_t *xl, int ph, int rb, in
             const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
             x = ok ? x : 0.f;
         }
-        bf16_t hh, ll;
-        split_hl(x, hh, ll);
-        h4[r] = hh;
-        l4[r] = ll;
+        xv[r] = f16_clamp(x);
     }
-    // Lane groups 2k and 2k+1 hold keys 8k..8k+3 and 8k+4..8k+7 of the same
-    // row.  One exchange between them (v_permlane16_swap: the odd group's first
-    // operand against the even group's second) leaves the even group with the
-    // 8 hi parts and the odd group with the 8 lo parts, so that every lane
-    // stores 16 contiguous bytes of one plane.
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const u32x2 hw = __builtin_bit_cast(u32x2, h4), lw = __builtin_bit_cast(u32x2, l4);
-    const auto s0 = __builtin_amdgcn_permlane16_swap(hw[0], lw[0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane16_swap(hw[1], lw[1], false, false);
-    const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
-    bf16_t *dst = (((lane >> 4) & 1) ? xl : xh) + rho * ph + cb * 16 + 8 * (lane >> 5);
-    *reinterpret_cast<u32x4 *>(dst) = w;
+    const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
+    *reinterpret_cast<f16x4 *>(x16 + rho * ph + e0) = h;
 }
 
 // Banded kernel matrices of the group's heads as MFMA A operands:
-// tf[((a * c_q + i') * 2 + plane) * 64 + lane] = 8 bf16 of Theta_{i'} (hi or
-// lo plane) for row m = lane%16, columns k = 8*(lane/16) + s.
+// tf[(a * c_q + i') * 64 + lane] = 8 fp16 of Theta_{i'} for row m = lane%16,
+// columns k = 8*(lane/16) + s.
 template <int CQ, int CK>
-__device__ inline void build_theta_frags(bf16x8 *tf, const float *th_s, int CH, int tid, int nt)
+__device__ inline void build_theta_frags(f16x8 *tf, const float *th_s, int CH, int tid, int nt)
 {
     constexpr int CKP = ((CK + 3) / 4) * 4;
     for (int i = tid; i < CH * CQ * 64; i += nt) {
         const int lane = i % 64, ip = (i / 64) % CQ, a = i / (64 * CQ);
         const int m = lane & 15, k0 = 8 * (lane >> 4);
-        bf16x8 h, l;
+        f16x8 h;
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
             const int jj = m + CK - 1 - (k0 + s8);
             const float t = (jj >= 0 && jj < CK) ? th_s[(a * CQ + ip) * CKP + jj] : 0.f;
-            bf16_t hh, ll;
-            split_hl(t, hh, ll);
-            h[s8] = hh;
-            l[s8] = ll;
+            h[s8] = (f16_t)f16_clamp(t);
         }
-        tf[((a * CQ + ip) * 2 + 0) * 64 + lane] = h;
-        tf[((a * CQ + ip) * 2 + 1) * 64 + lane] = l;
+        tf[(a * CQ + ip) * 64 + lane] = h;
     }
 }
 
-// Kernel fragments of one head, resident in registers: th[i'][plane].
+// Kernel fragments of one head, resident in registers: th[i'].
 template <int CQ>
 struct ThetaFrags {
-    bf16x8 f[CQ][2];
+    f16x8 f[CQ];
 };
 
 template <int CQ>
-__device__ inline void load_theta_frags(ThetaFrags<CQ> &t, const bf16x8 *tf, int lane)
+__device__ inline void load_theta_frags(ThetaFrags<CQ> &t, const f16x8 *tf, int lane)
 {
 #pragma unroll
-    for (int ip = 0; ip < CQ; ++ip) {
-        t.f[ip][0] = tf[(ip * 2 + 0) * 64 + lane];
-        t.f[ip][1] = tf[(ip * 2 + 1) * 64 + lane];
-    }
+    for (int ip = 0; ip < CQ; ++ip) t.f[ip] = tf[ip * 64 + lane];
 }
 
 // Eq. 4's exact indicator on the matrix-core stencil: the B operand of a lane
 // holds tile columns 32kh + 8*(lane/16) + s (+16 for the second block) of the
 // rows above the lane's output query; entries whose key lies in that query's
-// future are cleared.  w[t][q] masks bf16 pair q of block t.
+// future are cleared.  w[t][q] masks 16-bit pair q of block t.
 struct ColMask {
     uint32_t w[2][4];
 };
@@ -322,7 +303,7 @@ __device__ inline ColMask col_mask(int tl)
     return m;
 }
 
-__device__ inline bf16x8 and_mask(bf16x8 v, const uint32_t (&w)[4])
+__device__ inline f16x8 and_mask(f16x8 v, const uint32_t (&w)[4])
 {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 u = __builtin_bit_cast(u32x4, v);
@@ -330,79 +311,51 @@ __device__ inline bf16x8 and_mask(bf16x8 v, const uint32_t (&w)[4])
     u[1] &= w[1];
     u[2] &= w[2];
     u[3] &= w[3];
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-template <int CQ, bool MASK>
-__device__ inline void stencil_mfma_reg(const bf16_t *xh, const bf16_t *xl, int ph, int rho, int kh,
-                                        const ThetaFrags<CQ> &tfr, const ColMask &cm, int lane, float out[8])
-{
-    const int g4 = lane >> 4;
-    // six independent accumulation chains (2 blocks x 3 products), summed at the end
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0, c0 = a0, c1 = a0;
-#pragma unroll
-    for (int ip = 0; ip < CQ; ++ip) {
-        const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
-        bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
-        bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
-        bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
-        bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
-        if (MASK) {
-            h0 = and_mask(h0, cm.w[0]);
-            l0 = and_mask(l0, cm.w[0]);
-            h1 = and_mask(h1, cm.w[1]);
-            l1 = and_mask(l1, cm.w[1]);
-        }
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h0, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], h1, a1, 0, 0, 0);
-        b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], l0, b0, 0, 0, 0);
-        b1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][0], l1, b1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][1], h0, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tfr.f[ip][1], h1, c1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        out[r] = (a0[r] + b0[r]) + c0[r];
-        out[4 + r] = (a1[r] + b1[r]) + c1[r];
-    }
+    return __builtin_bit_cast(f16x8, u);
 }
 
 // Two 16-key output blocks (keys 32kh + 16t + 4*(lane/16) + r, t = 0,1) of row
-// 16rw + lane%16.  out[4t + r].
-template <int CQ, bool MASK>
-__device__ inline void stencil_mfma(const bf16_t *xh, const bf16_t *xl, int ph, int rho, int kh,
-                                    const bf16x8 *tf, const ColMask &cm, int lane, float out[8])
+// 16rw + lane%16, kernel fragments th(ip).  out[4t + r].
+template <int CQ, bool MASK, typename TH>
+__device__ inline void stencil_mfma_f(const f16_t *x, int ph, int rho, int kh, TH th, const ColMask &cm, int lane,
+                                      float out[8])
 {
     const int g4 = lane >> 4;
-    // six independent accumulation chains (2 blocks x 3 products), summed at the end
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0, c0 = a0, c1 = a0;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip) {
-        const bf16x8 th = tf[(ip * 2 + 0) * 64 + lane];
-        const bf16x8 tl = tf[(ip * 2 + 1) * 64 + lane];
         const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
-        bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(xh + off);
-        bf16x8 l0 = *reinterpret_cast<const bf16x8 *>(xl + off);
-        bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(xh + off + 16);
-        bf16x8 l1 = *reinterpret_cast<const bf16x8 *>(xl + off + 16);
+        f16x8 x0 = *reinterpret_cast<const f16x8 *>(x + off);
+        f16x8 x1 = *reinterpret_cast<const f16x8 *>(x + off + 16);
         if (MASK) {
-            h0 = and_mask(h0, cm.w[0]);
-            l0 = and_mask(l0, cm.w[0]);
-            h1 = and_mask(h1, cm.w[1]);
-            l1 = and_mask(l1, cm.w[1]);
+            x0 = and_mask(x0, cm.w[0]);
+            x1 = and_mask(x1, cm.w[1]);
         }
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h0, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, h1, a1, 0, 0, 0);
-        b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l0, b0, 0, 0, 0);
-        b1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l1, b1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h0, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, h1, c1, 0, 0, 0);
+        const f16x8 t = th(ip);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(t, x0, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(t, x1, a1, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        out[r] = (a0[r] + b0[r]) + c0[r];
-        out[4 + r] = (a1[r] + b1[r]) + c1[r];
+        out[r] = a0[r];
+        out[4 + r] = a1[r];
     }
+}
+
+// kernel fragments in registers
+template <int CQ, bool MASK>
+__device__ inline void stencil_mfma_reg(const f16_t *x, int ph, int rho, int kh, const ThetaFrags<CQ> &tfr,
+                                        const ColMask &cm, int lane, float out[8])
+{
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tfr.f[ip]; }, cm, lane, out);
+}
+
+// kernel fragments read from LDS (tf of one head)
+template <int CQ, bool MASK>
+__device__ inline void stencil_mfma(const f16_t *x, int ph, int rho, int kh, const f16x8 *tf, const ColMask &cm,
+                                    int lane, float out[8])
+{
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tf[ip * 64 + lane]; }, cm, lane, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -415,8 +368,7 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
                                       int rw, int kh, int lane)
 {
     const int l16 = lane & 15, dq = frag_base<D>(lane);
-    bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
-    bf16_t *xl = xh + EXT_R * ph;
+    f16_t *x16 = reinterpret_cast<f16_t *>(sbuf);
     QFrag<D> qf, kf;
     {
         const bf16_t *qr = qbuf + (16 * (1 + rw) + l16) * kpitch<D>() + dq;
@@ -430,7 +382,7 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qf);
         if (HL)
-            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
+            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
         else
             store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
     }
@@ -445,7 +397,7 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
             for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
             const f32x4 acc = qk_mfma<D>(kf, qf);
             if (HL)
-                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
+                store_block_x<MODE>(x16, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
             else
                 store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
         }
@@ -460,8 +412,7 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
                                        int lane)
 {
     const int l16 = lane & 15, dq = frag_base<D>(lane);
-    bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
-    bf16_t *xl = xh + EXT_R * ph;
+    f16_t *x16 = reinterpret_cast<f16_t *>(sbuf);
     QFrag<D> kf;
 #pragma unroll
     for (int cb = kh; cb < NCB; cb += 2) {
@@ -470,7 +421,7 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qown);
         if (HL)
-            store_block_hl<MODE>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
         else
             store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
     }
@@ -482,7 +433,7 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
             for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
             const f32x4 acc = qk_mfma<D>(kf, qhalo);
             if (HL)
-                store_block_hl<MODE>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+                store_block_x<MODE>(x16, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
             else
                 store_block<MODE>(sbuf, p.pitch, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
         }
@@ -583,7 +534,7 @@ __device__ inline void merge_lanes(float &m, float &l)
 }
 
 // ---------------------------------------------------------------------------
-// MS: key-query stencil on the matrix cores (bf16 hi/lo, c_k <= 17) instead of
+// MS: key-query stencil on the matrix cores (fp16, c_k <= 17) instead of
 // the fp32 VALU stencil.  The lane's 8 values are then the keys
 // 32kh + 16t + 4*(lane/16) + r (slot 4t + r) instead of 32kh + 8*(lane/16) + o.
 // EXACT: the key-query convolution before the softmax with Eq. 4's exact
@@ -609,10 +560,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     constexpr int NCB = (MS && NCB0 < 5) ? 5 : NCB0;
     const int ph = pitch_hl(NCB);
 
-    const Layout lay = layout(D, CH, CQ, CK, NCB, p.pitch, MS);
+    const Layout lay = layout(D, CH, CQ, CK, NCB, p.pitch, MS, KQ_POST);
     float *sbuf = reinterpret_cast<float *>(smem + lay.s_off);
-    const bf16_t *xh = reinterpret_cast<const bf16_t *>(sbuf);
-    const bf16_t *xl = xh + EXT_R * ph;
+    const f16_t *x16 = reinterpret_cast<const f16_t *>(sbuf);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *qbuf = reinterpret_cast<bf16_t *>(smem + lay.q_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -623,7 +573,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
     float *w_s = reinterpret_cast<float *>(smem + lay.w_off);
     float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);  // [kh][a][row]
-    bf16x8 *tf = reinterpret_cast<bf16x8 *>(smem + lay.tf_off);
+    f16x8 *tf = reinterpret_cast<f16x8 *>(smem + lay.tf_off);
 
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
@@ -688,7 +638,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             // registers; the VALU-stencil variant has no registers to spare for them
             if (MS && kt == 0) {
                 load_qfrags<D>(qown, qhal, qbuf, rw, lane);
-                load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 2 * 64, lane);
+                load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 64, lane);
             }
             if (!KQ_POST && MS)
                 logit_tile_regq<D, RAW, true, NCB, EXACT>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
@@ -705,9 +655,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 if (MS) {
                     // wave-uniform: can any of the wave's window columns pass its first row?
                     if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                        stencil_mfma_reg<MS ? CQ : 1, true>(xh, xl, ph, rho, kh, tfr, col_mask(tl), lane, c);
+                        stencil_mfma_reg<MS ? CQ : 1, true>(x16, ph, rho, kh, tfr, col_mask(tl), lane, c);
                     else
-                        stencil_mfma_reg<MS ? CQ : 1, false>(xh, xl, ph, rho, kh, tfr, ColMask{}, lane, c);
+                        stencil_mfma_reg<MS ? CQ : 1, false>(x16, ph, rho, kh, tfr, ColMask{}, lane, c);
                 } else {
                     stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
                 }
@@ -837,9 +787,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
             if (MS) {
                 if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                    stencil_mfma<CQ, true>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, col_mask(tl), lane, c);
+                    stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + a * CQ * 64, col_mask(tl), lane, c);
                 else
-                    stencil_mfma<CQ, false>(xh, xl, ph, rho, kh, tf + a * CQ * 2 * 64, ColMask{}, lane, c);
+                    stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + a * CQ * 64, ColMask{}, lane, c);
             } else {
                 stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
             }

@@ -43,7 +43,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
 {
     Layout L;
     int o = 0;
-    L.s_off = o;  o += 2 * EXT_R * pitch_hl(ncb) * 2;       // logit tile, bf16 hi + lo planes
+    L.s_off = o;  o += EXT_R * pitch_hl(ncb) * 2;           // logit tile (fp16)
     L.k_off = o;  o += ncb * 16 * D * 2;                    // K tile with key halo (bf16, swizzled rows)
     L.qh_off = o; o += CH * HALO * D * 2;                   // Q rows above the query tile, every head
     L.v_off = o;  o += BN * D * 2;                          // V tile (bf16, swizzled rows)
@@ -53,7 +53,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb)
     L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
     L.w_off = o;  o += ((CH * CH + 3) & ~3) * 4;
     L.gn_off = o; o += 2 * CH * BM * 4;                     // GroupNorm partial sums; partial l
-    L.tf_off = o; o += CH * cq * 2 * 64 * 16;               // banded kernel matrices (MFMA A operands)
+    L.tf_off = o; o += CH * cq * 64 * 16;                   // banded kernel matrices (MFMA A operands, fp16)
     L.total = o;
     return L;
 }
@@ -103,7 +103,7 @@ __device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // the halo block from the Q rows above the tile in LDS; K fragments from the
 // swizzled K tile.  Work split and stores as in v2::logit_tile_lds.
 template <int NCB, bool EX>
-__device__ inline void logit_tile(bf16_t *xh, bf16_t *xl, int ph, const QFrag<128> &qown, const bf16_t *qhalo,
+__device__ inline void logit_tile(v2::f16_t *x16, int ph, const QFrag<128> &qown, const bf16_t *qhalo,
                                   const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh, int lane)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -118,7 +118,7 @@ __device__ inline void logit_tile(bf16_t *xh, bf16_t *xl, int ph, const QFrag<12
 #pragma unroll
         for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + off[t]);
         const f32x4 acc = qk_mfma<128>(kf, qown);
-        v2::store_block_hl<RAW>(xh, xl, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+        v2::store_block_x<RAW>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
     }
     if (kh == 1 && p.c_q > 1) {
         QFrag<128> qh;
@@ -131,7 +131,7 @@ __device__ inline void logit_tile(bf16_t *xh, bf16_t *xl, int ph, const QFrag<12
 #pragma unroll
             for (int t = 0; t < 4; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + off[t]);
             const f32x4 acc = qk_mfma<128>(kf, qh);
-            v2::store_block_hl<RAW>(xh, xl, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+            v2::store_block_x<RAW>(x16, ph, 0, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
         }
     }
 }
@@ -169,8 +169,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
 
     const Layout lay = layout(D, CH, CQ, CK, NCB);
     float *sbuf = reinterpret_cast<float *>(smem + lay.s_off);
-    bf16_t *xh = reinterpret_cast<bf16_t *>(sbuf);
-    bf16_t *xl = xh + EXT_R * ph;
+    v2::f16_t *x16 = reinterpret_cast<v2::f16_t *>(sbuf);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *qhbuf = reinterpret_cast<bf16_t *>(smem + lay.qh_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -180,7 +179,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
     float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
     float *w_s = reinterpret_cast<float *>(smem + lay.w_off);
     float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);  // [kh][a][row]
-    bf16x8 *tf = reinterpret_cast<bf16x8 *>(smem + lay.tf_off);
+    v2::f16x8 *tf = reinterpret_cast<v2::f16x8 *>(smem + lay.tf_off);
 
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
@@ -286,7 +285,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
             __syncthreads();  // B1: K^s(kt) and V^s(kt-1) are in LDS
             const int sn = (s + 1 < CH) ? s + 1 : 0;
             const int ktn = (s + 1 < CH) ? kt : kt + 1;
-            logit_tile<NCB, EXACT>(xh, xl, ph, qown[s], qhbuf + s * HALO * D,
+            logit_tile<NCB, EXACT>(x16, ph, qown[s], qhbuf + s * HALO * D,
                                    kbuf, p, i0, j0, rw, kh, lane);
             if (kt > 0) {
                 if (s == 0) rescale();
@@ -301,9 +300,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v3(Params p)
             float c[8];
             const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
             if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                v2::stencil_mfma<CQ, true>(xh, xl, ph, rho, kh, tf + s * CQ * 2 * 64, col_mask(tl), lane, c);
+                v2::stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + s * CQ * 64, col_mask(tl), lane, c);
             else
-                v2::stencil_mfma<CQ, false>(xh, xl, ph, rho, kh, tf + s * CQ * 2 * 64, ColMask{}, lane, c);
+                v2::stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + s * CQ * 64, ColMask{}, lane, c);
             // Mask_-inf, then the maximum over this wave's 32 keys of the row
             float mx = NEG_INF;
 #pragma unroll

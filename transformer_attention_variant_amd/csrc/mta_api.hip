@@ -470,6 +470,17 @@ int mta_backward(const void *q, const void *k, const void *v, const float *theta
                           pad4(ch * cq * ckp) + (size_t)ch * 3 * nEr4 + pad4((size_t)4 * ch * ch)) * 4 + vb;
     if (lds_a > 160 * 1024 || lds_b > 160 * 1024) return MTA_ERR_UNSUPPORTED;
 
+    // bf16, d = 128, c_h = 2: the first kernel's work (row statistics, dO, D,
+    // GroupNorm and gate gradients) is done by the one-pass head-split forward
+    // with that epilogue, where it is instantiated and fits
+    mta::PrepFn pfn = nullptr;
+    size_t lds_v4 = 0;
+    if (bf && d == 128 && ch == 2) {
+        pfn = mta::find_launch_v4_prep(d, ch, cq, ck, p.exact);
+        lds_v4 = (size_t)mta::v4::layout(cq, ck, true).total;
+        if (lds_v4 > 160 * 1024) pfn = nullptr;
+    }
+
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     mta::bwd::ZeroList z{};
     z.p[0] = dq;          z.n[0] = rows * d;
@@ -486,7 +497,19 @@ int mta_backward(const void *q, const void *k, const void *v, const float *theta
     hipError_t e = mta::launch_fill_zero(z, s);
     if (e != hipSuccess) return MTA_ERR_LAUNCH;
     const int grid = p.n_qt * p.units;
-    e = fn(bp, grid, lds_a, grid, lds_b, s);
+    if (pfn) {
+        mta::Params pv = p;
+        pv.ncb = 5;
+        pv.pitch = pv.ncb * 16 + 4;
+        mta::v4::PrepArgs pa{static_cast<const mta::bf16_t *>(dout), bp.ws_m, bp.ws_il, bp.ws_D,
+                             static_cast<mta::bf16_t *>(bp.ws_dO), static_cast<mta::bf16_t *>(bp.ws_dOl),
+                             dgn_w, dgn_b, dgate};
+        e = pfn(pv, pa, grid, lds_v4, s);
+        if (e != hipSuccess) return MTA_ERR_LAUNCH;
+        e = fn(bp, 0, lds_a, grid, lds_b, s);  // the main kernel only
+    } else {
+        e = fn(bp, grid, lds_a, grid, lds_b, s);
+    }
     return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
 }
 

@@ -48,7 +48,9 @@ struct Layout {
     int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, total;
 };
 
-__host__ __device__ inline Layout layout(int cq, int ck)
+// prep: the gradient-preparation variant keeps P as bf16 high part and
+// remainder (a second probability buffer)
+__host__ __device__ inline Layout layout(int cq, int ck, bool prep = false)
 {
     Layout L;
     int o = 0;
@@ -56,7 +58,7 @@ __host__ __device__ inline Layout layout(int cq, int ck)
     L.k_off = o;  o += CH * KROWS * D * 2;        // K tiles (swizzled rows)
     L.v_off = o;  o += CH * BN * D * 2;           // V tiles (swizzled rows)
     L.qh_off = o; o += CH * HALO * D * 2;         // Q rows above the query tile
-    L.p_off = o;  o += CH * 4 * 2 * 64 * 16;      // probabilities [b][rw][k-step][lane] x 8 bf16
+    L.p_off = o;  o += (prep ? 2 : 1) * CH * 4 * 2 * 64 * 16;  // probabilities [plane][b][rw][k-step][lane] x 8 bf16
     L.al_off = o; o += CH * BM * 4;               // rescale factors [b][row]; at the end 1/l
     L.fl_off = o; o += CH * 4 * 4;                // [b][rw]: some factor of the 16 rows differs from 1
     L.gn_off = o; o += 2 * CH * BM * 4;           // GroupNorm partial sums [d half][a][row]
@@ -265,8 +267,22 @@ __device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ],
         for (int r = 0; r < 4; ++r) out[4 * t + r] = acc[t][r];
 }
 
-template <int CQ, int CK, bool EXACT>
-__global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
+// Extra pointers of the gradient-preparation variant (PREP): dY, the
+// workspace of the backward (row statistics, D, dO as bf16 high part and
+// remainder) and the GroupNorm / gate gradients it accumulates into.
+struct PrepArgs {
+    const bf16_t *dout;
+    float *ws_m, *ws_il, *ws_D;
+    bf16_t *ws_dO, *ws_dOl;
+    float *dgn_w, *dgn_b, *dgate;
+};
+
+// PREP: instead of the output, the epilogue writes what the backward's main
+// kernel needs (the same quantities as bwd::mta_bwd_prep: per-row statistics,
+// the GroupNorm backward dO, D^b = sum_a w_ab dO^a . (P^b V^a)) and adds the
+// GroupNorm and gate gradients.
+template <int CQ, int CK, bool EXACT, bool PREP = false>
+__global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -282,7 +298,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
     const int T = p.T;
     constexpr int CKP = ((CK + 3) / 4) * 4;
 
-    const Layout lay = layout(CQ, CK);
+    const Layout lay = layout(CQ, CK, PREP);
     f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -433,16 +449,21 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         float ls = 0.f;
-        bf16x8 v8[2];
+        bf16x8 v8[2], v8l[2];
 #pragma unroll
         for (int o = 0; o < 16; ++o) {
             const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
             ls += e;
             v8[o >> 3][o & 7] = (bf16_t)e;
+            if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
         }
         l_run = __builtin_fmaf(l_run, alpha, ls);
         pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
         pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+        if (PREP) {
+            pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
+            pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
+        }
         if (g4 == 0) al[hs * BM + io] = alpha;
         const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
         if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
@@ -467,9 +488,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
         }
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
-            bf16x8 av[CH];
+            bf16x8 av[CH], avl[CH];
 #pragma unroll
-            for (int s = 0; s < CH; ++s) av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
+            for (int s = 0; s < CH; ++s) {
+                av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
+                if (PREP) avl[s] = pbuf[CH * 4 * 2 * 64 + ((s * 4 + rw) * 2 + cs) * 64 + lane];
+            }
             const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
@@ -482,8 +506,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                     const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
                     const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
-                    for (int s = 0; s < CH; ++s)
+                    for (int s = 0; s < CH; ++s) {
                         U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
+                        // the gradients use P . V with P kept to ~16 bits (high part + remainder)
+                        if (PREP)
+                            U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
+                    }
                 }
         }
         if (more) wait_vm_all();  // the next K tiles have landed
@@ -514,6 +542,198 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p)
                     for (int s = 0; s < CH; ++s) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
                     acc[a][nb][r] = o;
                 }
+    }
+
+    if constexpr (PREP) {
+        // ---------- epilogue of the gradient preparation (instead of the output) ----------
+        // row statistics of head hs for row io: log2-domain maximum and 1/sum
+        if (g4 == 0 && qabs < T) {
+            const size_t ri = ((size_t)b * p.H + h0 + hs) * T + qabs;
+            pa.ws_m[ri] = m_run;
+            pa.ws_il[ri] = 1.0f / lsum;
+        }
+        float *ep = reinterpret_cast<float *>(smem + lay.x_off);  // the logit tiles are free now
+        float *red = ep;                                          // [rw][a][dgamma, dbeta][D]
+        float *sx = red + 4 * CH * 2 * D;                         // [half][a][s1, s2][row]
+        float *gred = sx + 2 * CH * 2 * BM;                       // [wave][a]
+        float *dx = gred + 8 * CH;                                // [half][s][row]
+        auto half_sum = [&](float v) {
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            return v;
+        };
+        // GroupNorm statistics over d (two d halves through LDS)
+        float mu[CH][4], rstd[CH][4];
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float sum = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) sum += acc[a][nb][r];
+                sum = half_sum(sum);
+                if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = sum;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rw + 4 * g4 + r;
+                mu[a][r] = (gnx[(0 * CH + a) * BM + row] + gnx[(1 * CH + a) * BM + row]) * (1.0f / D);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v2s = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const float dl = acc[a][nb][r] - mu[a][r];
+                    v2s = __builtin_fmaf(dl, dl, v2s);
+                }
+                v2s = half_sum(v2s);
+                if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = v2s;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rw + 4 * g4 + r;
+                const float var = (gnx[(0 * CH + a) * BM + row] + gnx[(1 * CH + a) * BM + row]) * (1.0f / D);
+                rstd[a][r] = 1.0f / __builtin_sqrtf(var + p.eps);
+            }
+        // GroupNorm backward: dxh = dY * s_a * gamma; dO = rstd (dxh - mean(dxh) - xh mean(dxh xh))
+        const bf16_t *dY = pa.dout;
+        float dgw[CH][4], dgb[CH][4], gpart[CH], dxh[CH][4][4], xh[CH][4][4];
+#pragma unroll
+        for (int a = 0; a < CH; ++a) {
+            const int h = h0 + a;
+            const float *gw = p.gn_w + (size_t)h * D;
+            const float *gb = p.gn_b + (size_t)h * D;
+            const float sa = head_factor(p, h);
+            gpart[a] = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) dgw[a][nb] = dgb[a][nb] = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = i0 + 16 * rw + 4 * g4 + r;
+                float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int col = dbase + 16 * nb + l16;
+                    xh[a][nb][r] = (acc[a][nb][r] - mu[a][r]) * rstd[a][r];
+                    const float dy = row < T ? (float)dY[((size_t)b * p.H + h) * hstride + (size_t)row * D + col] : 0.f;
+                    const float dys = dy * sa;
+                    dgb[a][nb] += dys;
+                    dgw[a][nb] = __builtin_fmaf(dys, xh[a][nb][r], dgw[a][nb]);
+                    gpart[a] = __builtin_fmaf(dy, xh[a][nb][r] * gw[col] + gb[col], gpart[a]);
+                    dxh[a][nb][r] = dys * gw[col];
+                    s1 += dxh[a][nb][r];
+                    s2 = __builtin_fmaf(dxh[a][nb][r], xh[a][nb][r], s2);
+                }
+                s1 = half_sum(s1);
+                s2 = half_sum(s2);
+                if (l16 == 0) {
+                    sx[((hs * CH + a) * 2 + 0) * BM + 16 * rw + 4 * g4 + r] = s1;
+                    sx[((hs * CH + a) * 2 + 1) * BM + 16 * rw + 4 * g4 + r] = s2;
+                }
+            }
+            // dgamma, dbeta of this wave's 16 rows: the four lane groups, then the waves via LDS
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                float u = dgw[a][nb], t = dgb[a][nb];
+                u += __shfl_xor(u, 16);
+                u += __shfl_xor(u, 32);
+                t += __shfl_xor(t, 16);
+                t += __shfl_xor(t, 32);
+                if (g4 == 0) {
+                    red[((rw * CH + a) * 2 + 0) * D + dbase + 16 * nb + l16] = u;
+                    red[((rw * CH + a) * 2 + 1) * D + dbase + 16 * nb + l16] = t;
+                }
+            }
+            float gsum = gpart[a];
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) gsum += __shfl_xor(gsum, sh);
+            const float sg = p.gate ? 1.0f / (1.0f + __expf(-p.gate[h])) : 1.0f;
+            if (lane == 0) gred[wave * CH + a] = gsum * p.depth_scale * sg * (1.0f - sg);
+        }
+        __syncthreads();
+        for (int i = tid; i < CH * 2 * D; i += NT) {
+            const int a = i / (2 * D), which = (i / D) % 2, col = i % D;
+            float t = 0.f;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) t += red[((w4 * CH + a) * 2 + which) * D + col];
+            atomicAdd((which ? pa.dgn_b : pa.dgn_w) + (size_t)(h0 + a) * D + col, t);
+        }
+        if (p.gate && tid < CH) {
+            float t = 0.f;
+#pragma unroll
+            for (int w8 = 0; w8 < 8; ++w8) t += gred[w8 * CH + tid];
+            atomicAdd(pa.dgate + h0 + tid, t);
+        }
+        // dO (bf16 high part and remainder), then D^s_i = sum_a w_as dO^a_i . (P^s V^a)_i
+        float dOr[CH][4][4];
+#pragma unroll
+        for (int a = 0; a < CH; ++a) {
+            const int h = h0 + a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rowt = 16 * rw + 4 * g4 + r, row = i0 + rowt;
+                const float s1 = (sx[((0 * CH + a) * 2 + 0) * BM + rowt] + sx[((1 * CH + a) * 2 + 0) * BM + rowt]) *
+                                 (1.0f / D);
+                const float s2 = (sx[((0 * CH + a) * 2 + 1) * BM + rowt] + sx[((1 * CH + a) * 2 + 1) * BM + rowt]) *
+                                 (1.0f / D);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const float dox = rstd[a][r] * (dxh[a][nb][r] - s1 - xh[a][nb][r] * s2);
+                    if (row < T) {
+                        const size_t at = ((size_t)b * p.H + h) * hstride + (size_t)row * D + dbase + 16 * nb + l16;
+                        const bf16_t dh = (bf16_t)dox;
+                        pa.ws_dO[at] = dh;
+                        pa.ws_dOl[at] = (bf16_t)(dox - (float)dh);
+                    }
+                    dOr[a][nb][r] = row < T ? dox : 0.f;
+                }
+            }
+        }
+        float il[CH][4];
+#pragma unroll
+        for (int s = 0; s < CH; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) il[s][r] = al[s * BM + 16 * rw + 4 * g4 + r];
+#pragma unroll
+        for (int s = 0; s < CH; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float t = 0.f;
+#pragma unroll
+                for (int a = 0; a < CH; ++a) {
+                    float u = 0.f;
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) u = __builtin_fmaf(dOr[a][nb][r], U[s][a][nb][r], u);
+                    t = __builtin_fmaf(w_s[a * CH + s], u, t);
+                }
+                t = half_sum(t * il[s][r]);
+                if (l16 == 0) dx[(hs * CH + s) * BM + 16 * rw + 4 * g4 + r] = t;
+            }
+        __syncthreads();
+        if (hs == 0 && l16 == 0) {
+#pragma unroll
+            for (int s = 0; s < CH; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rowt = 16 * rw + 4 * g4 + r, row = i0 + rowt;
+                    if (row < T)
+                        pa.ws_D[((size_t)b * p.H + h0 + s) * T + row] =
+                            dx[(0 * CH + s) * BM + rowt] + dx[(1 * CH + s) * BM + rowt];
+                }
+        }
+        return;
     }
 
     // ---------------- epilogue: GroupNorm over d, head factor, store -------
@@ -592,7 +812,18 @@ hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, s, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, s, p, PrepArgs{});
+    return hipGetLastError();
+}
+
+template <int CQ, int CK, bool EXACT>
+hipError_t launch_prep(const Params &p, const PrepArgs &pa, int grid, size_t lds, hipStream_t s)
+{
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, true>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, s, p, pa);
     return hipGetLastError();
 }
 

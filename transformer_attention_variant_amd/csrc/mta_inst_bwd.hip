@@ -6,20 +6,27 @@
 namespace mta {
 namespace bwd {
 
+// grid_a = 0: the first kernel's outputs come from elsewhere (the head-split
+// forward's gradient-preparation variant); only the main kernel runs.
 template <typename DT, int D, int CH, int CQ, int CK>
 hipError_t launch(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t lds_b, hipStream_t s)
 {
     auto fa = mta_bwd_prep<DT, D, CH, CQ, CK>;
     auto fb = mta_bwd_main<DT, D, CH, CQ, CK>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fa),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (grid_a > 0) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(fa), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds_a);
+        if (e != hipSuccess) return e;
+    }
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(fb), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds_b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fa, dim3(grid_a), dim3(NT), lds_a, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (grid_a > 0) {
+        hipLaunchKernelGGL(fa, dim3(grid_a), dim3(NT), lds_a, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(fb, dim3(grid_b), dim3(NT), lds_b, s, p);
     return hipGetLastError();
 }

@@ -40,5 +40,12 @@ layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, 
 LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 // One-pass head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre);
+// Their gradient-preparation variants (key-query convolution before the
+// softmax, head mix after it); null when not instantiated.
+namespace v4 {
+struct PrepArgs;
+}
+typedef hipError_t (*PrepFn)(const Params &p, const v4::PrepArgs &pa, int grid, size_t lds, hipStream_t s);
+PrepFn find_launch_v4_prep(int d, int ch, int cq, int ck, int exact);
 
 }  // namespace mta

@@ -43,7 +43,9 @@ def _cases():
             c.append(I.small(f"bwd_f32_d{d}_ch{ch}_{cq}x{ck}_T{T}_kq{kq}", B=1, H=4, T=T, d=d, c_q=cq, c_k=ck,
                              c_h=ch, kq_place=kq, theta_std=0.2, head_std=0.2, gn_random=True, layer=2,
                              seed=1100 + d + T + kq))
-    for (cq, ck, kq, ch) in ((6, 11, P, 2), (6, 11, E, 2), (4, 9, P, 2), (6, 11, P, 1)):
+    # the compile-time kernel sizes of the bf16 workloads (4x9, 6x11, 8x15) and a
+    # runtime-sized one (c_h = 1)
+    for (cq, ck, kq, ch) in ((6, 11, P, 2), (6, 11, E, 2), (4, 9, P, 2), (8, 15, P, 2), (8, 15, E, 2), (6, 11, P, 1)):
         c.append(I.small(f"bwd_bf16_{cq}x{ck}_ch{ch}_kq{kq}", B=1, H=4, T=150, d=128, c_q=cq, c_k=ck, c_h=ch,
                          kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05,
                          gn_random=True, seed=1200 + cq + kq + ch))

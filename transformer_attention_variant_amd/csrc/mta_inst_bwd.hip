@@ -1,6 +1,6 @@
 // Backward kernels (mta_bwd.h): float32 and bfloat16, d in {32, 64, 128},
-// c_h in {1, 2}; runtime-sized stencils, compile-time 6x11 for the 4K-context
-// layer (bf16, d = 128, c_h = 2).
+// c_h in {1, 2}; runtime-sized stencils, compile-time 4x9, 6x11 and 8x15 for
+// the bf16 workloads (d = 128, c_h = 2).
 #include "mta_bwd.h"
 
 namespace mta {
@@ -36,7 +36,11 @@ hipError_t launch(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t
 bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck)
 {
     using namespace bwd;
-    if (dtype_bf16 && d == 128 && ch == 2 && cq == 6 && ck == 11) return &launch<bf16_t, 128, 2, 6, 11>;
+    if (dtype_bf16 && d == 128 && ch == 2) {
+        if (cq == 6 && ck == 11) return &launch<bf16_t, 128, 2, 6, 11>;
+        if (cq == 4 && ck == 9) return &launch<bf16_t, 128, 2, 4, 9>;
+        if (cq == 8 && ck == 15) return &launch<bf16_t, 128, 2, 8, 15>;
+    }
 #define MTA_BWD_D(T_, D_)                                          \
     if (d == D_) {                                                 \
         if (ch == 1) return &launch<T_, D_, 1, 0, 0>;              \

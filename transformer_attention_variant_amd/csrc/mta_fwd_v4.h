@@ -373,44 +373,58 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         // logit tiles: own row block of head hs (five column blocks), then a
         // share of the halo blocks; the fragments of the next block are read
         // before the products of the current one
-        auto logits = [&](auto masked) {
-            constexpr bool M = decltype(masked)::value;
+        // REUSE (every key tile after the first): column block 0 of the tile
+        // (keys j0 - hl .. j0 - hl + 15) is column block 4 of the previous
+        // tile, copied into place during its P.V; only blocks 1..4 are computed,
+        // and the eight halo blocks (both heads) are one per wave
+        auto logits = [&](auto masked, auto reuse) {
+            constexpr bool M = decltype(masked)::value, R = decltype(reuse)::value;
+            constexpr int CB0 = R ? 1 : 0;
             const bf16_t *kh = kbuf + hs * KROWS * D + l16 * D;
             auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) f.x[t] = *reinterpret_cast<const bf16x8 *>(rows + 16 * cb * D + koff[t]);
             };
+            // the (first) halo block of this wave: head hh, column block hcb
+            const int hh = R ? (wave >> 2) : (wave / NCB);
+            const int hcb = R ? 1 + (wave & 3) : (wave % NCB);
             QFrag<D> kf[2], hq, hk;
-            kload(kf[0], kh, 0);
+            kload(kf[CB0 & 1], kh, CB0);
             u32x2 prev;  // converted block waiting for its store partner
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
+            for (int cb = CB0; cb < NCB; ++cb) {
                 if (cb + 1 < NCB) {
                     kload(kf[(cb + 1) & 1], kh, cb + 1);
                 } else if (CQ > 1) {
-                    kload(hk, kbuf + (wave / NCB) * KROWS * D + l16 * D, wave % NCB);
+                    kload(hk, kbuf + hh * KROWS * D + l16 * D, hcb);
                 }
                 const u32x2 v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
-                if (cb & 1)
+                if ((cb - CB0) & 1)
                     store_pair<CQ>(xo, 1 + rw, cb - 1, prev, xo, 1 + rw, cb, v, lane);
                 else
                     prev = v;
             }
             if (CQ > 1) {
-                // halo blocks q = wave and, for waves 0 and 1, q = wave + 8 (q = h * NCB + cb);
-                // the first one is stored with the last own block
-                kload(hq, qhbuf + (wave / NCB) * HALO * D + l16 * D, 0);
-                const u32x2 v = cvt_block<M>(0, wave % NCB, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
-                store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xbuf + (wave / NCB) * EXT_R * XP, 0, wave % NCB, v, lane);
-                if (wave + 8 < CH * NCB) {
-                    const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
-                    kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
-                    kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
-                    const u32x2 v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
-                    f16_t *xh = xbuf + h * EXT_R * XP;
-                    store_pair<CQ>(xh, 0, hc, v2, xh, 0, hc, v2, lane, true);
+                // halo blocks: with REUSE one per wave; else q = wave and, for waves 0
+                // and 1, q = wave + 8 (q = h * NCB + cb), the first stored with the
+                // last own block
+                kload(hq, qhbuf + hh * HALO * D + l16 * D, 0);
+                const u32x2 v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                f16_t *xhh = xbuf + hh * EXT_R * XP;
+                if (R) {
+                    store_pair<CQ>(xhh, 0, hcb, v, xhh, 0, hcb, v, lane, true);
+                } else {
+                    store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xhh, 0, hcb, v, lane);
+                    if (wave + 8 < CH * NCB) {
+                        const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
+                        kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
+                        kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
+                        const u32x2 v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                        f16_t *xh2 = xbuf + h * EXT_R * XP;
+                        store_pair<CQ>(xh2, 0, hc, v2, xh2, 0, hc, v2, lane, true);
+                    }
                 }
-            } else {
+            } else if (!R) {
                 store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xo, 1 + rw, NCB - 1, prev, lane, true);
             }
         };
@@ -418,10 +432,17 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         // [0, T) and, with Mask_0, all in the past of every row: no masks
         const int kfirst = j0 - p.hl, klast = j0 - p.hl + 16 * NCB - 1;
         const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
-        if (inner)
-            logits(std::false_type{});
-        else
-            logits(std::true_type{});
+        if (kt > 0) {
+            if (inner)
+                logits(std::false_type{}, std::true_type{});
+            else
+                logits(std::true_type{}, std::true_type{});
+        } else {
+            if (inner)
+                logits(std::false_type{}, std::false_type{});
+            else
+                logits(std::true_type{}, std::false_type{});
+        }
         barrier_lds();  // B2: logit tiles complete; K buffers free
         const bool more = kt < qt;
         if (more) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);
@@ -470,6 +491,16 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         if (more) wait_vm_k();  // this wave's V pieces have landed
         else wait_vm_all();
         barrier_lds();  // B3: probabilities, factors and V tiles published
+        if (more) {
+            // column block 4 of this tile becomes column block 0 of the next (the
+            // stencil has read the tile; the next logit blocks write blocks 1..4):
+            // 16-byte chunks 8, 9 -> 0, 1 of every row, which keeps the row swizzle
+            for (int u = tid; u < CH * EXT_R * 2; u += NT) {
+                f16_t *rp = xbuf + (u >> 1) * XP;  // (head, row) = u / 2
+                const int j = u & 1;
+                *reinterpret_cast<u32x4 *>(rp + 8 * j) = *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + j));
+            }
+        }
 
         // bring the accumulators into the frame of the new maxima, then P.V
 #pragma unroll

@@ -12,12 +12,13 @@
 //   keys of the tile, so the row maxima need no exchange between waves and
 //   the head's banded kernel matrices stay in its registers.  In P.V it owns
 //   the d-columns [64s, 64s + 64) of every (source b, output a) pair.
-// Per key tile there are three barriers, each publishing LDS writes only:
-//   B1 | K tiles of both heads are in LDS; the V tiles of this key tile start
-//        loading (DMA); logit tiles of both heads -> LDS (fp16)
-//   B2 | the K tiles of the next key tile start loading; stencil, Mask_-inf,
-//        row maximum, rescale factor and probabilities -> LDS
-//   B3 | (V tiles landed) rescale of the accumulators, P.V
+// Per key tile t there are two barriers, each publishing LDS writes only, and
+// the P.V of a tile runs one phase late, beside the next tile's logit products:
+//   A | K tiles of t, V tiles and probabilities of t - 1 are in LDS: logit
+//     | tiles of both heads -> LDS (fp16); rescale of the accumulators, P.V
+//     | of t - 1
+//   B | the K tiles of t + 1 and the V tiles of t start loading (DMA);
+//     | stencil, Mask_-inf, row maximum, rescale factor, probabilities -> LDS
 // The key-query convolution runs on the matrix cores with fp16 operands (the
 // logit tile and the kernel taps rounded to nearest, 11 significant bits) and
 // fp32 accumulation: one product per kernel row and output block.
@@ -66,6 +67,14 @@ __host__ __device__ inline Layout layout(int cq, int ck, bool prep = false)
     L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
     L.total = o;
     return L;
+}
+
+// An offset the compiler must recompute where it is used: keeps it from holding
+// the four lane addresses of every halo fragment load live across the loop.
+__device__ inline int fresh(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // DMA of the same rows of a K or V tile for both heads of the group: piece i
@@ -365,18 +374,21 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             for (int nb = 0; nb < 4; ++nb) U[s][a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = NEG_INF, l_run = 0.f;  // head hs, row io (l_run: this lane's 16 keys)
 
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int j0 = kt * BN;
-        barrier_lds();  // B1: K tiles of kt are in LDS (each wave waited for its DMA)
-        dma_pair<true, BN>(vbuf, V, hstride, j0, T, wave, lane);
+    // Two phases per key tile t (one more step drains the last P.V):
+    //   A(t) | K(t), V(t-1), P(t-1) in LDS | logit tiles of t; rescale and P.V of t-1
+    //   B(t) | K(t+1), V(t) start loading  | stencil and softmax of t -> P(t)
+    for (int t = 0; t <= qt + 1; ++t) {
+        const int j0 = t * BN;
+        const bool cur = t <= qt;
+        barrier_lds();  // A: K(t), V(t-1) in LDS (each wave waited for its DMA); P(t-1) published
 
         // logit tiles: own row block of head hs (five column blocks), then a
         // share of the halo blocks; the fragments of the next block are read
         // before the products of the current one
         // REUSE (every key tile after the first): column block 0 of the tile
         // (keys j0 - hl .. j0 - hl + 15) is column block 4 of the previous
-        // tile, copied into place during its P.V; only blocks 1..4 are computed,
-        // and the eight halo blocks (both heads) are one per wave
+        // tile, copied into place before the logit products; only blocks 1..4
+        // are computed, and the eight halo blocks (both heads) are one per wave
         auto logits = [&](auto masked, auto reuse) {
             constexpr bool M = decltype(masked)::value, R = decltype(reuse)::value;
             constexpr int CB0 = R ? 1 : 0;
@@ -396,7 +408,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 if (cb + 1 < NCB) {
                     kload(kf[(cb + 1) & 1], kh, cb + 1);
                 } else if (CQ > 1) {
-                    kload(hk, kbuf + hh * KROWS * D + l16 * D, hcb);
+                    kload(hk, kbuf + fresh((hh * KROWS + 16 * hcb + l16) * D), 0);
                 }
                 const u32x2 v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
                 if ((cb - CB0) & 1)
@@ -408,7 +420,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 // halo blocks: with REUSE one per wave; else q = wave and, for waves 0
                 // and 1, q = wave + 8 (q = h * NCB + cb), the first stored with the
                 // last own block
-                kload(hq, qhbuf + hh * HALO * D + l16 * D, 0);
+                kload(hq, qhbuf + fresh((hh * HALO + l16) * D), 0);
                 const u32x2 v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                 f16_t *xhh = xbuf + hh * EXT_R * XP;
                 if (R) {
@@ -417,8 +429,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                     store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xhh, 0, hcb, v, lane);
                     if (wave + 8 < CH * NCB) {
                         const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
-                        kload(hq, qhbuf + h * HALO * D + l16 * D, 0);
-                        kload(hk, kbuf + h * KROWS * D + l16 * D, hc);
+                        kload(hq, qhbuf + fresh((h * HALO + l16) * D), 0);
+                        kload(hk, kbuf + fresh((h * KROWS + 16 * hc + l16) * D), 0);
                         const u32x2 v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                         f16_t *xh2 = xbuf + h * EXT_R * XP;
                         store_pair<CQ>(xh2, 0, hc, v2, xh2, 0, hc, v2, lane, true);
@@ -432,120 +444,128 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         // [0, T) and, with Mask_0, all in the past of every row: no masks
         const int kfirst = j0 - p.hl, klast = j0 - p.hl + 16 * NCB - 1;
         const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
-        if (kt > 0) {
-            if (inner)
-                logits(std::false_type{}, std::true_type{});
-            else
-                logits(std::true_type{}, std::true_type{});
-        } else {
-            if (inner)
-                logits(std::false_type{}, std::false_type{});
-            else
-                logits(std::true_type{}, std::false_type{});
-        }
-        barrier_lds();  // B2: logit tiles complete; K buffers free
-        const bool more = kt < qt;
-        if (more) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);
-
-        float c[16];
-        if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
-            stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
-        else
-            stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
-        // Mask_-inf (only the diagonal tile has keys in the future of its
-        // rows), the row maximum over the 64 keys, probabilities
-        if (kt == qt) {
-#pragma unroll
-            for (int o = 0; o < 16; ++o) {
-                const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
-                c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+        if (cur && t > 0) {
+            // column block 4 of tile t-1 is column block 0 of tile t: 16-byte
+            // chunks 8, 9 -> 0, 1 (which keeps the row swizzle), each wave for the
+            // rows whose block 4 it writes next (own rows; halo rows: the waves of
+            // halo column block 4), so its own program order keeps the read first
+            if (lane < 32) {
+                f16_t *rp = xo + (HALO + 16 * rw + (lane >> 1)) * XP;
+                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
+                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
+            } else if (CQ > 1 && (wave & 3) == 3) {
+                f16_t *rp = xbuf + (wave >> 2) * EXT_R * XP + ((lane - 32) >> 1) * XP;
+                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
+                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
             }
         }
-        float mx = NEG_INF;
-#pragma unroll
-        for (int o = 0; o < 16; ++o) mx = fmaxf(mx, c[o]);
-        mx = row_max4(mx);
-        // every row has a causal key in tile 0, so m_new is finite
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float ls = 0.f;
-        bf16x8 v8[2], v8l[2];
-#pragma unroll
-        for (int o = 0; o < 16; ++o) {
-            const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
-            ls += e;
-            v8[o >> 3][o & 7] = (bf16_t)e;
-            if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
-        }
-        l_run = __builtin_fmaf(l_run, alpha, ls);
-        pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
-        pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
-        if (PREP) {
-            pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
-            pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
-        }
-        if (g4 == 0) al[hs * BM + io] = alpha;
-        const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-        if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
-        if (more) wait_vm_k();  // this wave's V pieces have landed
-        else wait_vm_all();
-        barrier_lds();  // B3: probabilities, factors and V tiles published
-        if (more) {
-            // column block 4 of this tile becomes column block 0 of the next (the
-            // stencil has read the tile; the next logit blocks write blocks 1..4):
-            // 16-byte chunks 8, 9 -> 0, 1 of every row, which keeps the row swizzle
-            for (int u = tid; u < CH * EXT_R * 2; u += NT) {
-                f16_t *rp = xbuf + (u >> 1) * XP;  // (head, row) = u / 2
-                const int j = u & 1;
-                *reinterpret_cast<u32x4 *>(rp + 8 * j) = *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + j));
+        if (cur) {
+            if (t > 0) {
+                if (inner)
+                    logits(std::false_type{}, std::true_type{});
+                else
+                    logits(std::true_type{}, std::true_type{});
+            } else {
+                if (inner)
+                    logits(std::false_type{}, std::false_type{});
+                else
+                    logits(std::true_type{}, std::false_type{});
             }
         }
-
-        // bring the accumulators into the frame of the new maxima, then P.V
-#pragma unroll
-        for (int s = 0; s < CH; ++s) {
-            if (kt > 0 && fl[s * 4 + rw]) {
-                float f[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) f[r] = al[s * BM + 16 * rw + 4 * g4 + r];
-#pragma unroll
-                for (int a = 0; a < CH; ++a)
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) U[s][a][nb][r] *= f[r];
-            }
-        }
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs) {
-            bf16x8 av[CH], avl[CH];
+        if (t >= 1) {
+            // P.V of tile t - 1: bring the accumulators into the frame of its maxima first
+            const int tp = t - 1;
 #pragma unroll
             for (int s = 0; s < CH; ++s) {
-                av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
-                if (PREP) avl[s] = pbuf[CH * 4 * 2 * 64 + ((s * 4 + rw) * 2 + cs) * 64 + lane];
-            }
-            const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
+                if (tp > 0 && fl[s * 4 + rw]) {
+                    float f[4];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+                    for (int r = 0; r < 4; ++r) f[r] = al[s * BM + 16 * rw + 4 * g4 + r];
 #pragma unroll
-                for (int a = 0; a < CH; ++a) {
-                    const bf16_t *va = vbuf + a * BN * D;
-                    const v2::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
-                    const v2::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
-                    typedef short s16x8 __attribute__((ext_vector_type(8)));
-                    const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-                    const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
+                    for (int a = 0; a < CH; ++a)
 #pragma unroll
-                    for (int s = 0; s < CH; ++s) {
-                        U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
-                        // the gradients use P . V with P kept to ~16 bits (high part + remainder)
-                        if (PREP)
-                            U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
-                    }
+                        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) U[s][a][nb][r] *= f[r];
                 }
+            }
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+                bf16x8 av[CH], avl[CH];
+#pragma unroll
+                for (int s = 0; s < CH; ++s) {
+                    av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
+                    if (PREP) avl[s] = pbuf[CH * 4 * 2 * 64 + ((s * 4 + rw) * 2 + cs) * 64 + lane];
+                }
+                const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                    for (int a = 0; a < CH; ++a) {
+                        const bf16_t *va = vbuf + a * BN * D;
+                        const v2::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
+                        const v2::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
+                        typedef short s16x8 __attribute__((ext_vector_type(8)));
+                        const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                        const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+                        for (int s = 0; s < CH; ++s) {
+                            U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
+                            // the gradients use P . V with P kept to ~16 bits (high part + remainder)
+                            if (PREP)
+                                U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
+                        }
+                    }
+            }
         }
-        if (more) wait_vm_all();  // the next K tiles have landed
+        barrier_lds();  // B: logit tiles of t published; K, V and probability buffers free
+        if (t < qt) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);  // K(t+1)
+        if (cur) dma_pair<true, BN>(vbuf, V, hstride, j0, T, wave, lane);                      // V(t)
+
+        if (cur) {
+            float c[16];
+            if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
+                stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
+            else
+                stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
+            // Mask_-inf (only the diagonal tile has keys in the future of its
+            // rows), the row maximum over the 64 keys, probabilities
+            if (t == qt) {
+#pragma unroll
+                for (int o = 0; o < 16; ++o) {
+                    const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
+                    c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+                }
+            }
+            float mx = NEG_INF;
+#pragma unroll
+            for (int o = 0; o < 16; ++o) mx = fmaxf(mx, c[o]);
+            mx = row_max4(mx);
+            // every row has a causal key in tile 0, so m_new is finite
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            float ls = 0.f;
+            bf16x8 v8[2], v8l[2];
+#pragma unroll
+            for (int o = 0; o < 16; ++o) {
+                const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
+                ls += e;
+                v8[o >> 3][o & 7] = (bf16_t)e;
+                if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
+            }
+            l_run = __builtin_fmaf(l_run, alpha, ls);
+            pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
+            pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+            if (PREP) {
+                pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
+                pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
+            }
+            if (g4 == 0) al[hs * BM + io] = alpha;
+            const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+            if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
+            wait_vm_all();  // K(t+1) and V(t) have landed
+        }
     }
 
     // row sums l_b -> 1/l_b in al (after every wave's last P.V read of al)

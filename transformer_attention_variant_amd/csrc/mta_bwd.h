@@ -34,7 +34,9 @@
 namespace mta {
 namespace bwd {
 
-constexpr int NT = 256;
+constexpr int NT = 256;         // kernel A: 4 waves
+constexpr int NTB = 512;        // kernel B: 8 waves, two per SIMD
+constexpr int NWB = NTB / 64;
 
 struct BParams {
     Params f;                        // forward geometry and pointers (q, k, v, theta, wmix, gn, gate)
@@ -81,6 +83,56 @@ template <int D>
 __device__ inline void pv_x(f32x4 (&acc)[D / 16], const float a[16], const float *buf, int lane)
 {
     pv_mfma<D>(acc, a, buf, lane);
+}
+
+// The same products for half of the d-columns: 16-column blocks
+// [nb0, nb0 + D/32) of the B operand (layout of load_v_tile / TileStage).
+template <int D>
+__device__ inline void pv_half(f32x4 (&acc)[D / 32], const float pr[16], const bf16_t *vb, int lane, int nb0)
+{
+    const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (bf16_t)pr[8 * c + e];
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const bf16x8 bv =
+                *reinterpret_cast<const bf16x8 *>(vb + ((nb0 + nb) * 16 + n) * VP_BF16 + kg * 16 + 8 * c);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[nb], 0, 0, 0);
+        }
+    }
+}
+template <int D>
+__device__ inline void pv_half(f32x4 (&acc)[D / 32], const float pr[16], const float *vb, int lane, int nb0)
+{
+    const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+            const float bv = vb[(kg * 16 + t) * (D + 4) + (nb0 + nb) * 16 + n];
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[t], bv, acc[nb], 0, 0, 0);
+        }
+    }
+}
+template <int D>
+__device__ inline void pv_x_half(f32x4 (&acc)[D / 32], const float a[16], const bf16_t *buf, int lane, int nb0)
+{
+    float hi[16], lo[16];
+#pragma unroll
+    for (int o = 0; o < 16; ++o) {
+        hi[o] = (float)(bf16_t)a[o];
+        lo[o] = a[o] - hi[o];
+    }
+    pv_half<D>(acc, hi, buf, lane, nb0);
+    pv_half<D>(acc, lo, buf, lane, nb0);
+}
+template <int D>
+__device__ inline void pv_x_half(f32x4 (&acc)[D / 32], const float a[16], const float *buf, int lane, int nb0)
+{
+    pv_half<D>(acc, a, buf, lane, nb0);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,9 +394,11 @@ __global__ void __launch_bounds__(NT) mta_bwd_prep(BParams bp)
 // jb + o + jj holds key c + jj - floor(c_k/2) for output column c = j0 + jb + o).
 // With Eq. 4's indicator the terms of query offset i' count only where
 // c <= r + i', i.e. o <= dlim + i' with dlim = r - j0 - jb.
+// Only the query offsets i' = ip0, ip0 + 2, ... are summed (the two waves that
+// share a row split them).
 template <int CQ, int CK>
 __device__ inline void stencil16_t(const float *ebuf, int pitch, int er, int jb, const float *th, int cq_rt,
-                                   int ck_rt, int ckp, int dlim, float out[16])
+                                   int ck_rt, int ckp, int dlim, int ip0, float out[16])
 {
     constexpr int MAXW = CK ? 16 + CK - 1 : 16 + MAX_CK - 1;
     constexpr int MAXW4 = (MAXW + 3) / 4;
@@ -354,7 +408,7 @@ __device__ inline void stencil16_t(const float *ebuf, int pitch, int er, int jb,
     const int nw4 = (16 + ck - 1 + 3) / 4;
 #pragma unroll
     for (int o = 0; o < 16; ++o) out[o] = 0.f;
-    for (int ip = 0; ip < cq; ++ip) {
+    for (int ip = ip0; ip < cq; ip += 2) {
         const f32x4 *row = reinterpret_cast<const f32x4 *>(ebuf + (er + ip) * pitch + jb);
         float win[MAXW4 * 4];
 #pragma unroll
@@ -406,10 +460,11 @@ __device__ inline float wave_sum(float x)
 // logit region's row rx0 holds the lane's row minus 0 offsets: window of query
 // offset i' starts at row rx0 - i', column xc0 (the key col(0) - (c_k - 1) +
 // floor(c_k/2)); window entries t > tlim are keys in the future of the row
-// (Eq. 4's indicator) and are skipped.
+// (Eq. 4's indicator) and are skipped.  Only the query offsets i' = ip0,
+// ip0 + 2, ... are done (the two waves that share a row split them).
 template <int CQ, int CK>
 __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, const float g[16], float *dth,
-                                int cq_rt, int ck_rt, int ckp, int tlim)
+                                int cq_rt, int ck_rt, int ckp, int tlim, int ip0)
 {
     constexpr int MAXW = CK ? 16 + CK - 1 : 16 + MAX_CK - 1;
     constexpr int MAXW4 = (MAXW + 3) / 4;
@@ -418,7 +473,7 @@ __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, 
     const int ck = CK ? CK : ck_rt;
     const int nw = 16 + ck - 1;
     const int nw4 = (nw + 3) / 4;
-    for (int ip = 0; ip < cq; ++ip) {
+    for (int ip = ip0; ip < cq; ip += 2) {
         const f32x4 *row = reinterpret_cast<const f32x4 *>(xbuf + (rx0 - ip) * pitch + xc0);
         float win[MAXW4 * 4];
 #pragma unroll
@@ -458,42 +513,70 @@ __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, 
     }
 }
 
+// The nrb x ncb 16x16 blocks of a region product, in row-major order, are dealt
+// to the NWB waves in contiguous runs; a run loads the row fragments again
+// where its row block changes and requests the next column fragments before
+// each product.  f(rb, cb, acc) stores one block (lane: row lane%16, columns
+// 4*(lane/16) .. +3).
+template <typename DT, int D, bool SPLIT, typename F>
+__device__ inline void region_product(int nrb, int ncb, const DT *rh, const DT *rl, int r0, const DT *ch, int c0,
+                                      int T, int wave, int lane, F &&f)
+{
+    typedef typename FragOf<DT, D>::type Frag;
+    const int n = nrb * ncb, t0 = wave * n / NWB, t1 = (wave + 1) * n / NWB;
+    if (t0 >= t1) return;
+    Frag hf, lf, cf, cn;
+    int rcur = -1;
+    load_frag<D>(cf, ch, c0 + 16 * (t0 % ncb) + (lane & 15), T, lane);
+    for (int t = t0; t < t1; ++t) {
+        const int rb = t / ncb, cb = t % ncb;
+        if (rb != rcur) {
+            const int qi = r0 + 16 * rb + (lane & 15);
+            load_frag<D>(hf, rh, qi, T, lane);
+            if (SPLIT) load_frag<D>(lf, rl, qi, T, lane);
+            rcur = rb;
+        }
+        if (t + 1 < t1) load_frag<D>(cn, ch, c0 + 16 * ((t + 1) % ncb) + (lane & 15), T, lane);
+        f32x4 acc = qk_mfma<D>(cf, hf);
+        if (SPLIT) {
+            const f32x4 a2 = qk_mfma<D>(cf, lf);
+            acc += a2;
+        }
+        cf = cn;
+        f(rb, cb, acc);
+    }
+}
+
 // dP3 tile: buf[row][col] = dO[r0 + row] . V[c0 + col] over rows < nrows (0
 // outside [0, T)); with SPLIT the product of the low plane of dO is added.
 template <typename DT, int D, bool SPLIT>
 __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nrows, const DT *dh, const DT *dl,
                                  const DT *vh, int r0, int c0, int T, int wave, int lane)
 {
-    typedef typename FragOf<DT, D>::type Frag;
-    // one 16-row block against the column blocks [cb0, ncb) step cstep; the
-    // V fragments of the next two blocks are requested before each product
-    auto row_block = [&](int rb, int cb0, int cstep) {
-        Frag hf, lf, vf, v1;
+    region_product<DT, D, SPLIT>(nrb, ncb, dh, dl, r0, vh, c0, T, wave, lane, [&](int rb, int cb, const f32x4 &acc) {
+        if (16 * rb + (lane & 15) < nrows)
+            *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
+    });
+}
+
+// Logit region X: buf[row][col] = sc * Q[r0 + row] . K[c0 + col], 0 outside
+// [0, T) and, unless raw, where the key is in the future of the row (Mask_0).
+template <typename DT, int D>
+__device__ inline void x_tile(float *buf, int pitch, int nrb, int ncb, int nrows, const DT *qh, const DT *kh, int r0,
+                              int c0, int T, float sc, bool raw, int wave, int lane)
+{
+    region_product<DT, D, false>(nrb, ncb, qh, qh, r0, kh, c0, T, wave, lane, [&](int rb, int cb, const f32x4 &acc) {
         const int qi = r0 + 16 * rb + (lane & 15);
-        load_frag<D>(hf, dh, qi, T, lane);
-        if (SPLIT) load_frag<D>(lf, dl, qi, T, lane);
-        load_frag<D>(vf, vh, c0 + 16 * cb0 + (lane & 15), T, lane);
-        if (cb0 + cstep < ncb) load_frag<D>(v1, vh, c0 + 16 * (cb0 + cstep) + (lane & 15), T, lane);
-        for (int cb = cb0; cb < ncb; cb += cstep) {
-            Frag v2;
-            if (cb + 2 * cstep < ncb) load_frag<D>(v2, vh, c0 + 16 * (cb + 2 * cstep) + (lane & 15), T, lane);
-            f32x4 acc = qk_mfma<D>(vf, hf);
-            if (SPLIT) {
-                const f32x4 a2 = qk_mfma<D>(vf, lf);
-                acc += a2;
-            }
-            vf = v1;
-            v1 = v2;
-            if (16 * rb + (lane & 15) < nrows)
-                *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + 16 * cb + 4 * (lane >> 4)) = acc;
+        const int e0 = 16 * cb + 4 * (lane >> 4);
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int kj = c0 + e0 + r;
+            const bool ok = qi >= 0 && qi < T && kj >= 0 && kj < T && (raw || kj <= qi);
+            o[r] = ok ? acc[r] * sc : 0.f;
         }
-    };
-    // whole rounds of row blocks: one per wave; the remaining row blocks'
-    // column blocks are dealt to the waves in turn
-    const int full = nrb & ~3;
-    for (int rb = wave; rb < full; rb += 4) row_block(rb, 0, 1);
-    for (int rb = full; rb < nrb; ++rb)
-        if (wave < ncb) row_block(rb, wave, 4);
+        if (16 * rb + (lane & 15) < nrows) *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + e0) = o;
+    });
 }
 
 // A 64-row tile for the P.V-shaped products of kernel B (layout of
@@ -505,15 +588,17 @@ struct TileStage;
 
 template <int D>
 struct TileStage<bf16_t, D> {
-    bf16x8 x[D / 32];
+    // thread -> key tid % 64 and the 8-channel chunks tid / 64 + NWB * it
+    static constexpr int NC = D / 8, IT = (NC + NWB - 1) / NWB;
+    bf16x8 x[IT];
     __device__ void fetch(const bf16_t *g, int r0, int T, int tid)
     {
         const int key = tid & 63, kj = r0 + key;
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int c0 = ((tid >> 6) + 4 * it) * 8;
-            if (kj < T) {
-                x[it] = *reinterpret_cast<const bf16x8 *>(g + (size_t)kj * D + c0);
+        for (int it = 0; it < IT; ++it) {
+            const int ch = (tid >> 6) + NWB * it;
+            if (ch < NC && kj < T) {
+                x[it] = *reinterpret_cast<const bf16x8 *>(g + (size_t)kj * D + 8 * ch);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[it][e] = (bf16_t)0.0f;
@@ -524,23 +609,25 @@ struct TileStage<bf16_t, D> {
     {
         const int key = tid & 63;
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int c0 = ((tid >> 6) + 4 * it) * 8;
+        for (int it = 0; it < IT; ++it) {
+            const int ch = (tid >> 6) + NWB * it;
+            if (ch < NC) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vb[(c0 + e) * VP_BF16 + key] = x[it][e];
+                for (int e = 0; e < 8; ++e) vb[(8 * ch + e) * VP_BF16 + key] = x[it][e];
+            }
         }
     }
 };
 
 template <int D>
 struct TileStage<float, D> {
-    static constexpr int C4 = D / 4, N = BN * C4 / NT;
+    static constexpr int C4 = D / 4, N = BN * C4 / NTB;
     f32x4 x[N];
     __device__ void fetch(const float *g, int r0, int T, int tid)
     {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = tid + it * NT, key = idx / C4, c0 = (idx % C4) * 4, kj = r0 + key;
+            const int idx = tid + it * NTB, key = idx / C4, c0 = (idx % C4) * 4, kj = r0 + key;
             x[it] = kj < T ? *reinterpret_cast<const f32x4 *>(g + (size_t)kj * D + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -548,7 +635,7 @@ struct TileStage<float, D> {
     {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = tid + it * NT, key = idx / C4, c0 = (idx % C4) * 4;
+            const int idx = tid + it * NTB, key = idx / C4, c0 = (idx % C4) * 4;
             *reinterpret_cast<f32x4 *>(vb + key * (D + 4) + c0) = x[it];
         }
     }
@@ -557,7 +644,7 @@ struct TileStage<float, D> {
 // ---------------------------------------------------------------------------
 // Kernel B
 template <typename DT, int D, int CH, int CQ, int CK>
-__global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
+__global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
 {
     const Params &p = bp.f;
     extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -583,8 +670,8 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     float *dth = w_s + ((CH * CH + 3) & ~3);                      // accumulated dtheta [CH][cq][ckp]
     float *st = dth + ((CH * cq * ckp + 3) & ~3);                 // [CH][3][nEr4]: m, il, D of the region rows
     const int nEr4 = (nEr + 3) & ~3;
-    float *dwr = st + CH * 3 * nEr4;                              // [4 waves][CH*CH]
-    DT *opbuf = reinterpret_cast<DT *>(dwr + ((4 * CH * CH + 3) & ~3));
+    float *dwr = st + CH * 3 * nEr4;                              // [NWB waves][CH*CH]
+    DT *opbuf = reinterpret_cast<DT *>(dwr + ((NWB * CH * CH + 3) & ~3));
 
     const size_t hstride = (size_t)T * D;
     const DT *Q = reinterpret_cast<const DT *>(p.q);
@@ -596,27 +683,31 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
     const int h0 = g * CH;
     const size_t base0 = ((size_t)b * p.H + h0) * hstride;
 
-    for (int i = tid; i < CH * cq * ckp; i += NT) {
+    for (int i = tid; i < CH * cq * ckp; i += NTB) {
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
         th_s[i] = c < ck ? p.theta[((size_t)(h0 + a) * cq + r) * ck + c] : 0.f;
     }
-    for (int i = tid; i < CH * cq * ckp; i += NT) dth[i] = 0.f;
-    for (int i = tid; i < CH * CH; i += NT) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
+    for (int i = tid; i < CH * cq * ckp; i += NTB) dth[i] = 0.f;
+    for (int i = tid; i < CH * CH; i += NTB) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
     float dwp[CH * CH];
 #pragma unroll
     for (int i = 0; i < CH * CH; ++i) dwp[i] = 0.f;
 
 
-    const int io = wave * 16 + (lane & 15);  // the lane's row (stencil layout) within a query tile
-    const int jb = 16 * (lane >> 4);         // its first key within the key tile
-    const int km = wave * 16 + (lane & 15);  // its key (transposed operand layout)
-    const int rk = 16 * (lane >> 4);         // its first row (transposed operand layout)
+    // waves w and w + 4 share rows / keys: they split the query offsets of the
+    // stencils and the d-columns of the products (half = w / 4)
+    const int wq = wave & 3, half = wave >> 2;
+    const int nb0 = half * (D / 32);       // first 16-column block of the wave's d-half
+    const int io = wq * 16 + (lane & 15);  // the lane's row (stencil layout) within a query tile
+    const int jb = 16 * (lane >> 4);       // its first key within the key tile
+    const int km = wq * 16 + (lane & 15);  // its key (transposed operand layout)
+    const int rk = 16 * (lane >> 4);       // its first row (transposed operand layout)
 
-    f32x4 dK[CH][D / 16], dV[CH][D / 16];
+    f32x4 dK[CH][D / 32], dV[CH][D / 32];
 #pragma unroll
     for (int a = 0; a < CH; ++a)
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
+        for (int nb = 0; nb < D / 32; ++nb) {
             dK[a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             dV[a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -655,7 +746,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
         const int xc0 = ec0 - hl;             // key of logit column 0
         __syncthreads();
         // row statistics and D of the region's rows
-        for (int i = tid; i < CH * nEr; i += NT) {
+        for (int i = tid; i < CH * nEr; i += NTB) {
             const int a = i / nEr, r = i % nEr;
             const int row = i0 + r;
             const size_t ri = ((size_t)b * p.H + h0 + a) * T + row;
@@ -674,11 +765,11 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
         for (int s = 0; s < CH; ++s) {
             __syncthreads();
             // X^s over the logit region (log2-scaled; Mask_0 unless exact)
-            layer::s_tile<DT, D>(xbuf, xp, bp.nRrb, bp.nRcb, 16 * bp.nRrb, Q + base0 + s * hstride,
-                                 K + base0 + s * hstride, xr0, xc0, T, p.sc, p.exact != 0, wave, lane);
+            x_tile<DT, D>(xbuf, xp, bp.nRrb, bp.nRcb, 16 * bp.nRrb, Q + base0 + s * hstride, K + base0 + s * hstride,
+                          xr0, xc0, T, p.sc, p.exact != 0, wave, lane);
             __syncthreads();
             // C^s over the region -> P^s (in place)
-            for (int t = tid; t < nEr * nlcb; t += NT) {
+            for (int t = tid; t < nEr * nlcb; t += NTB) {
                 const int r = t / nlcb, cb = t % nlcb;
                 const int qi = i0 + r;
                 const int tlim = p.exact ? qi - (xc0 + 16 * cb) : (1 << 30);
@@ -703,7 +794,7 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                 const float wa = w_s[a * CH + s];
 #pragma unroll
                 for (int o = 0; o < 16; ++o) at[o] = wa * ebuf[(rk + o) * ep + hr + km];
-                pv_x<D>(dV[a], at, opbuf, lane);
+                pv_x_half<D>(dV[a], at, opbuf, lane, nb0);
                 if (SPLIT) {
                     __syncthreads();
                     put_tile(qt, s, 2 * a + 1);
@@ -711,12 +802,12 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                     float ah[16];
 #pragma unroll
                     for (int o = 0; o < 16; ++o) ah[o] = (float)(bf16_t)at[o];
-                    pv_mfma<D>(dV[a], ah, opbuf, lane);
+                    pv_half<D>(dV[a], ah, opbuf, lane, nb0);
                 }
             }
             __syncthreads();
             // dC^s = P^s (sum_a w_as dP3^a - D^s) in place; dw partials over the core
-            for (int idx = tid; idx < nEr * nEc; idx += NT) {
+            for (int idx = tid; idx < nEr * nEc; idx += NTB) {
                 const int r = idx / nEc, c = idx % nEc;
                 const float pv = ebuf[r * ep + c];
                 float dp = 0.f;
@@ -738,54 +829,65 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
                 const int qi = i0 + io;
                 // window of the lane: logit row (io + cq-1) - i', columns from jb + hr (key j0 + jb - hl)
                 const int tlim = p.exact ? qi - (xc0 + jb + hr) : (1 << 30);
-                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim);
+                dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim, half);
             }
-            // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil;
-            // with Eq. 4's indicator the terms of offset i' count where key <= r + i'
+            // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil,
+            // this wave's query offsets; with Eq. 4's indicator the terms of offset
+            // i' count where key <= r + i'
             float dsv[16];
-            {
+            stencil16_t<CQ, CK>(ebuf, ep, io, jb, th_s + s * cq * ckp, cq, ck, ckp,
+                                p.exact ? i0 + io - j0 - jb : (1 << 30), half, dsv);
+            __syncthreads();  // xbuf free (dtheta done), ebuf reads done
+            // the second half's partial sums meet the first half's in LDS; the
+            // first half writes dS core row-major (pitch BN + 4) into xbuf
+            float *xch = ebuf + (wq * 64 + lane) * 16;
+            if (half) {
+#pragma unroll
+                for (int o = 0; o < 16; o += 4)
+                    *reinterpret_cast<f32x4 *>(xch + o) = f32x4{dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3]};
+            }
+            put_tile(qt, s, NDO);  // K^s
+            __syncthreads();
+            float *dsb = xbuf;
+            if (!half) {
                 const int r = i0 + io;
-                stencil16_t<CQ, CK>(ebuf, ep, io, jb, th_s + s * cq * ckp, cq, ck, ckp,
-                                    p.exact ? r - j0 - jb : (1 << 30), dsv);
 #pragma unroll
                 for (int o = 0; o < 16; ++o) {
                     const int c = j0 + jb + o;
                     const bool keep = p.exact ? true : (c <= r);
-                    dsv[o] = (keep && r < T && c < T) ? dsv[o] : 0.f;
+                    const float v = dsv[o] + xch[o];
+                    dsb[io * (BN + 4) + jb + o] = (keep && r < T && c < T) ? v : 0.f;
                 }
             }
-            __syncthreads();  // xbuf free (dtheta done), ebuf reads done
-            // dQ^s += dS K^s / sqrt(d)  (global atomics)
+            __syncthreads();
+            // dQ^s += dS K^s / sqrt(d)  (global atomics; this wave's d-half)
             {
-                put_tile(qt, s, NDO);
-                __syncthreads();
-                f32x4 qa[D / 16];
+                float at[16];
 #pragma unroll
-                for (int nb = 0; nb < D / 16; ++nb) qa[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pv_x<D>(qa, dsv, opbuf, lane);
+                for (int o = 0; o < 16; ++o) at[o] = dsb[io * (BN + 4) + jb + o];
+                f32x4 qa[D / 32];
+#pragma unroll
+                for (int nb = 0; nb < D / 32; ++nb) qa[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pv_x_half<D>(qa, at, opbuf, lane, nb0);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int row = i0 + wave * 16 + 4 * (lane >> 4) + r4;
+                    const int row = i0 + wq * 16 + 4 * (lane >> 4) + r4;
                     if (row < T) {
                         float *dst = bp.dq + ((size_t)b * p.H + h0 + s) * hstride + (size_t)row * D;
 #pragma unroll
-                        for (int nb = 0; nb < D / 16; ++nb)
-                            atomicAdd(dst + 16 * nb + (lane & 15), qa[nb][r4] * bp.inv_sqrt_d);
+                        for (int nb = 0; nb < D / 32; ++nb)
+                            atomicAdd(dst + 16 * (nb0 + nb) + (lane & 15), qa[nb][r4] * bp.inv_sqrt_d);
                     }
                 }
             }
-            // dS core to LDS (row-major, pitch BN + 4) for the transposed operand of dK
-            float *dsb = xbuf;
-#pragma unroll
-            for (int o = 0; o < 16; ++o) dsb[io * (BN + 4) + jb + o] = dsv[o];
-            __syncthreads();
-            put_tile(qt, s, NDO + 1);
+            __syncthreads();  // K^s reads done
+            put_tile(qt, s, NDO + 1);  // Q^s
             __syncthreads();
             {
                 float at[16];
 #pragma unroll
                 for (int o = 0; o < 16; ++o) at[o] = dsb[(rk + o) * (BN + 4) + km];
-                pv_x<D>(dK[s], at, opbuf, lane);
+                pv_x_half<D>(dK[s], at, opbuf, lane, nb0);
             }
         }
     }
@@ -795,12 +897,12 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
         const size_t hb = ((size_t)b * p.H + h0 + a) * hstride;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int key = j0 + wave * 16 + 4 * (lane >> 4) + r4;
+            const int key = j0 + wq * 16 + 4 * (lane >> 4) + r4;
             if (key < T) {
 #pragma unroll
-                for (int nb = 0; nb < D / 16; ++nb) {
-                    bp.dk[hb + (size_t)key * D + 16 * nb + (lane & 15)] = dK[a][nb][r4] * bp.inv_sqrt_d;
-                    bp.dv[hb + (size_t)key * D + 16 * nb + (lane & 15)] = dV[a][nb][r4];
+                for (int nb = 0; nb < D / 32; ++nb) {
+                    bp.dk[hb + (size_t)key * D + 16 * (nb0 + nb) + (lane & 15)] = dK[a][nb][r4] * bp.inv_sqrt_d;
+                    bp.dv[hb + (size_t)key * D + 16 * (nb0 + nb) + (lane & 15)] = dV[a][nb][r4];
                 }
             }
         }
@@ -813,11 +915,13 @@ __global__ void __launch_bounds__(NT) mta_bwd_main(BParams bp)
         if (lane == 0) dwr[wave * CH * CH + i] = t;
     }
     __syncthreads();
-    for (int i = tid; i < CH * CH; i += NT) {
-        const float t = dwr[i] + dwr[CH * CH + i] + dwr[2 * CH * CH + i] + dwr[3 * CH * CH + i];
+    for (int i = tid; i < CH * CH; i += NTB) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWB; ++w) t += dwr[w * CH * CH + i];
         atomicAdd(bp.dw + (size_t)g * CH * CH + i, t);
     }
-    for (int i = tid; i < CH * cq * ckp; i += NT) {
+    for (int i = tid; i < CH * cq * ckp; i += NTB) {
         const int a = i / (cq * ckp), r = (i / ckp) % cq, c = i % ckp;
         if (c < ck) atomicAdd(bp.dtheta + ((size_t)(h0 + a) * cq + r) * ck + c, dth[i] * bp.inv_log2e);
     }

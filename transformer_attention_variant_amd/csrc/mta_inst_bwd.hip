@@ -27,7 +27,7 @@ hipError_t launch(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fb, dim3(grid_b), dim3(NT), lds_b, s, p);
+    hipLaunchKernelGGL(fb, dim3(grid_b), dim3(NTB), lds_b, s, p);
     return hipGetLastError();
 }
 

@@ -99,12 +99,8 @@ __device__ inline void dma_pair(bf16_t *lds, const bf16_t *g, size_t hstride, in
                                          16, 0, 0);
     }
 }
-constexpr int K_PIECES = CH * KROWS / 4 / 8;  // per wave
-constexpr int V_PIECES = CH * BN / 4 / 8;
-
-// all of this wave's global loads / only the last K_PIECES may be outstanding
+// all of this wave's global loads (its DMA pieces included) have landed
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-__device__ inline void wait_vm_k() { __builtin_amdgcn_s_waitcnt(0x0f70 | K_PIECES); }
 
 typedef _Float16 f16_t;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));

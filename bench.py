@@ -140,7 +140,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the MTA "
-              "forward here is a single-GPU kernel; multi-GPU sharding is not part of this build.",
+              "forward here is a single-GPU kernel; sharding over several GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 

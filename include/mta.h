@@ -68,7 +68,7 @@ extern "C" {
 #define MTA_ERR_BAD_PLACEMENT -3 /* kq_place not 0..2 or head_place not 0..1  */
 #define MTA_ERR_BAD_DTYPE -4     /* dtype not MTA_F32 / MTA_BF16               */
 #define MTA_ERR_MISALIGNED -5    /* a tensor pointer is not 16-byte aligned    */
-#define MTA_ERR_UNSUPPORTED -6   /* valid but outside this build's limits:
+#define MTA_ERR_UNSUPPORTED -6   /* valid but outside the library's limits:
                                     head_dim not in {32,64,128}, c_h not in
                                     {1,2,4}, c_q > 16, c_k > 31, T > 2^24      */
 #define MTA_ERR_LAUNCH -7        /* the kernel launch reported an error        */
@@ -221,7 +221,7 @@ size_t mta_backward_workspace_size(const mta_config *cfg);
  * unsupported.  For profiling and reports; it launches nothing. */
 const char *mta_kernel_name(const mta_config *cfg);
 
-/* Host-only check of a configuration against the limits of this build; the
+/* Host-only check of a configuration against the library's limits; the
  * same validation mta_forward runs (pointer checks excepted).  Returns MTA_OK
  * or the MTA_ERR_* code mta_forward would return. */
 int mta_check_config(const mta_config *cfg);

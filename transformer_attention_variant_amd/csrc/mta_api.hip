@@ -69,7 +69,7 @@ const char *mta_status_string(int s)
     case MTA_ERR_BAD_PLACEMENT: return "placement must be pre- (0) or post-softmax (1), or exact pre-softmax (2) for kq";
     case MTA_ERR_BAD_DTYPE: return "dtype must be MTA_F32 or MTA_BF16";
     case MTA_ERR_MISALIGNED: return "tensor pointer not aligned (16 bytes for q,k,v,out; 4 for float params)";
-    case MTA_ERR_UNSUPPORTED: return "configuration outside this build's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
+    case MTA_ERR_UNSUPPORTED: return "configuration outside the library's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
     case MTA_ERR_LAUNCH: return "kernel launch failed";
     case MTA_ERR_BAD_VALUE: return "gn_eps must be finite and > 0, depth_scale finite";
     default: return "unknown status";

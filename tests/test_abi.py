@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 @pytest.mark.parametrize("name,expect", [
     ("needle4k", "mta_fwd_v4"), ("needle4k_exact", "mta_fwd_v4"), ("layer2k", "mta_fwd_v4"),
     ("sweep8k_8x15_ch2_pre", "mta_fwd_v4"),
-    ("sweep8k_6x11_ch2_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
+    ("sweep8k_6x11_ch2_post", "mta_fwd_v4 (two passes"), ("sweep8k_4x9_ch2_post", "mta_fwd_v4 (two passes"),
     # c_h = 4: the fp16 matrix-core stencil fits in LDS except for 8x15 after the softmax
     ("sweep8k_8x15_ch4_pre", "mta_fwd_v2 (two passes, matrix-core stencil)"),
     ("sweep8k_6x11_ch4_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
@@ -103,7 +103,7 @@ def test_layer_validation(lib, kw, code):
 @pytest.mark.parametrize("kw,expect", [
     ({}, "mta_fwd_layer"),                                                  # the repeated form
     (dict(kq_post=None, head_post2=None), "mta_fwd_v4"),                    # kq pre + head post
-    (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v2"),     # kq post + head post
+    (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v4 (two passes"),  # kq post + head post
     (dict(kq_pre=None, head_post2=None), "mta_fwd_layer"),                  # head mix before the kq conv
     (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000), "mta_fwd_layer"),
 ])

@@ -140,7 +140,7 @@ def test_workload_bf16_sampled(name):
     _say(f"[parity]   rows {ranges} units {units}: max abs err {err:.3e} (tol {tol:.2e})")
 
 
-@pytest.mark.parametrize("name", ["needle4k", "needle4k_exact", "sweep8k_8x15_ch4_post"])
+@pytest.mark.parametrize("name", ["needle4k", "needle4k_exact", "sweep8k_8x15_ch4_post", "sweep8k_4x9_ch2_post"])
 def test_causality_full_size(name):
     """Perturbing q, k, v after position t leaves out[..., :t+1, :] bitwise equal."""
     cfg = I.CONFIGS[name]

@@ -114,16 +114,18 @@ static int make_plan(const mta_config *cfg, Plan &pl)
     size_t lds = 0;
     if (cfg->dtype == MTA_BF16) {
         const int ncb0 = p.ncb, pitch0 = p.pitch;
-        // one pass with online softmax statistics where it applies (key-query
-        // convolution before the softmax, head mix after it, c_h <= 2): the
-        // head-split kernel for c_h = 2, else the key-split one
+        // the head-split kernel for c_h = 2 with the head mix after the softmax
+        // (one pass with online softmax statistics when the key-query
+        // convolution comes before the softmax, two passes when after), else one
+        // pass with the key-split kernel (c_h = 1, convolution before the softmax)
         fn = mta::find_launch_v4(d, ch, cq, ck, post, exact, hpre);
         if (fn) {
             p.ncb = 5;
             p.pitch = p.ncb * 16 + 4;
-            lds = (size_t)mta::v4::layout(cq, ck).total;
+            lds = (size_t)mta::v4::layout(cq, ck, false, post != 0).total;
             if (lds > LDS_MAX) fn = nullptr;
-            else pl.name = "mta_fwd_v4 (one pass, head-split waves, fp16 matrix-core stencil)";
+            else pl.name = post ? "mta_fwd_v4 (two passes, head-split waves, fp16 matrix-core stencil)"
+                                : "mta_fwd_v4 (one pass, head-split waves, fp16 matrix-core stencil)";
         }
         if (!fn) fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
         if (fn && !pl.name) {

@@ -46,12 +46,12 @@ constexpr int XP = 16 * NCB;    // fp16 pitch of the logit tiles (conflict-free 
 constexpr int KROWS = 16 * NCB; // K rows per head (key halo included)
 
 struct Layout {
-    int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, total;
+    int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, st_off, total;
 };
 
 // prep: the gradient-preparation variant keeps P as bf16 high part and
 // remainder (a second probability buffer)
-__host__ __device__ inline Layout layout(int cq, int ck, bool prep = false)
+__host__ __device__ inline Layout layout(int cq, int ck, bool prep = false, bool post = false)
 {
     Layout L;
     int o = 0;
@@ -65,6 +65,10 @@ __host__ __device__ inline Layout layout(int cq, int ck, bool prep = false)
     L.gn_off = o; o += 2 * CH * BM * 4;           // GroupNorm partial sums [d half][a][row]
     L.w_off = o;  o += 16;                        // the group's 2x2 mixing matrix
     L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
+    // post: softmax statistics of the tile rows and the rows above them
+    // (maximum, 1/sum: [h][row]) and the halo rows' partial statistics
+    // ([h][key block][row][maximum, sum])
+    L.st_off = o; o += post ? (2 * CH * EXT_R + CH * 4 * 16 * 2) * 4 : 0;
     L.total = o;
     return L;
 }
@@ -146,6 +150,35 @@ __device__ inline u32x2 cvt_block(int rb, int cb, f32x4 acc, int i0, int j0, int
         if (MASKED && !all_ok) {
             const int kj = j0 - hl + e0 + r;
             const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
+            v = ok ? v : 0.f;
+        }
+        xv[r] = v;
+    }
+    const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
+    return __builtin_bit_cast(u32x2, h);
+}
+
+// The same block as probabilities of the softmax before a post-softmax
+// convolution: exp2(sc * S - m) * il with the row's statistics (m: maximum of
+// sc * S over its causal keys, il: 1 / sum), 0 for keys in the row's future and
+// outside [0, T) (entries whose exp2 may be out of range are selected away,
+// never multiplied).
+template <bool MASKED>
+__device__ inline u32x2 cvt_prob(int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T, float m, float il,
+                                 float sc, int lane)
+{
+    const int rho = rb * 16 + (lane & 15);
+    const int e0 = cb * 16 + 4 * (lane >> 4);
+    const int qi = i0 - HALO + rho;
+    const int q_lo = i0 - HALO + rb * 16, k_lo = j0 - hl + cb * 16;
+    const bool all_ok = (k_lo >= 0) && (k_lo + 15 <= q_lo) && (q_lo >= 0) && (q_lo + 15 < T);
+    float xv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], sc, -m)) * il;
+        if (MASKED && !all_ok) {
+            const int kj = j0 - hl + e0 + r;
+            const bool ok = (kj >= 0) && (kj <= qi) && (qi >= 0) && (qi < T);
             v = ok ? v : 0.f;
         }
         xv[r] = v;
@@ -286,10 +319,15 @@ struct PrepArgs {
 // kernel needs (the same quantities as bwd::mta_bwd_prep: per-row statistics,
 // the GroupNorm backward dO, D^b = sum_a w_ab dO^a . (P^b V^a)) and adds the
 // GroupNorm and gate gradients.
-template <int CQ, int CK, bool EXACT, bool PREP = false>
+// POST: the key-query convolution after the softmax (then Mask_0), in two
+// passes over the key tiles: the softmax statistics of the tile's rows and of
+// the 16 rows above it first, then the probabilities of the extended tile ->
+// fp16 stencil -> Mask_0 -> P.V; the head mix stays in the epilogue.
+template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
+    static_assert(!(POST && (EXACT || PREP)), "post-softmax form: two-pass masks, forward only");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
@@ -303,7 +341,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     const int T = p.T;
     constexpr int CKP = ((CK + 3) / 4) * 4;
 
-    const Layout lay = layout(CQ, CK, PREP);
+    const Layout lay = layout(CQ, CK, PREP, POST);
     f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -314,6 +352,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);  // [half][a][row]
     float *w_s = reinterpret_cast<float *>(smem + lay.w_off);
     float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
+    float *stm = reinterpret_cast<float *>(smem + lay.st_off);  // POST: [h][row] maximum (log2 domain)
+    float *stil = stm + CH * EXT_R;                             // POST: [h][row] 1 / sum
 
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
@@ -322,9 +362,13 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + base0;
     const bf16_t *V = reinterpret_cast<const bf16_t *>(p.v) + base0;
 
-    // K of key tile 0 and the Q rows above the query tile, both heads; this
-    // wave's Q rows of its head in registers; kernels and mixing matrix
-    dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);
+    // K of key tile 0 (POST: the statistics pass's 64 keys) and the Q rows above
+    // the query tile, both heads; this wave's Q rows of its head in registers;
+    // kernels and mixing matrix
+    if constexpr (POST)
+        dma_pair<false, BN>(kbuf, K, hstride, 0, T, wave, lane);
+    else
+        dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);
     dma_pair<false, HALO>(qhbuf, Q, hstride, i0 - HALO, T, wave, lane);
     // this wave's Q rows of its head (rows past the end: masked in the logit tile)
     const bf16_t *qrow = Q + hs * hstride + (size_t)((i0 + 16 * rw + l16) < T ? i0 + 16 * rw + l16 : T - 1) * D + 32 * g4;
@@ -348,7 +392,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         for (int s8 = 0; s8 < 8; ++s8) {
             const int jj = l16 + CK - 1 - (8 * g4 + s8);
             const float t = (jj >= 0 && jj < CK) ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
-            tf[ip][s8] = (f16_t)f16_range(t * p.sc);
+            tf[ip][s8] = (f16_t)f16_range(POST ? t : t * p.sc);  // POST: on probabilities, unscaled
         }
 
     const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
@@ -359,6 +403,92 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     int koff[4];  // swizzled chunk offsets of the K / Q-halo fragment reads
 #pragma unroll
     for (int t = 0; t < 4; ++t) koff[t] = 8 * ((4 * g4 + t) ^ swz_k(l16));
+
+    // POST, pass 1: running maximum and sum of sc * S over the causal keys, per
+    // lane (its 16 keys of a tile) for row io of head hs and for halo row l16 of
+    // head wave / 4 (key block wave % 4 of every tile); merged over the lanes
+    // and the four halo waves at the end.  K tiles of 64 keys, double-buffered
+    // in the K and V buffers (free in this pass).
+    float pm_o = 0.f, pil_o = 0.f, pm_h = 0.f, pil_h = 0.f;
+    if constexpr (POST) {
+        const int hh = wave >> 2, hcb = wave & 3;
+        constexpr float FLOOR = -1e30f;  // finite: a lane with no causal key yet keeps l = 0
+        float m1 = FLOOR, l1 = 0.f, m2 = FLOOR, l2 = 0.f;
+        auto update = [](float &m, float &l, const float *v, int n) {
+            float mx = m;
+            for (int o = 0; o < n; ++o) mx = fmaxf(mx, v[o]);
+            float sum = 0.f;
+            for (int o = 0; o < n; ++o) sum += __builtin_amdgcn_exp2f(v[o] - mx);  // exp2(-inf) = 0
+            l = __builtin_fmaf(l, __builtin_amdgcn_exp2f(m - mx), sum);
+            m = mx;
+        };
+        auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.x[t] = *reinterpret_cast<const bf16x8 *>(rows + 16 * cb * D + koff[t]);
+        };
+        QFrag<D> hq;
+        kload(hq, qhbuf + (hh * HALO + l16) * D, 0);
+        const int qh = i0 - HALO + l16;  // the lane's halo row
+        for (int t = 0; t <= qt; ++t) {
+            const int j0 = t * BN;
+            bf16_t *kb = (t & 1) ? vbuf : kbuf;
+            wait_vm_all();
+            __syncthreads();  // K(t) in LDS; every wave is done with the other buffer
+            if (t < qt) dma_pair<false, BN>((t & 1) ? kbuf : vbuf, K, hstride, j0 + BN, T, wave, lane);
+            float v[16];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                QFrag<D> kf;
+                kload(kf, kb + (hs * BN + l16) * D, cb);
+                const f32x4 acc = qk(kf, qown);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[4 * cb + r] = (j0 + 16 * cb + 4 * g4 + r <= qabs) ? acc[r] * p.sc : NEG_INF;
+            }
+            update(m1, l1, v, 16);
+            {
+                QFrag<D> kf;
+                kload(kf, kb + (hh * BN + l16) * D, hcb);
+                const f32x4 acc = qk(kf, hq);
+                float w[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = (j0 + 16 * hcb + 4 * g4 + r <= qh) ? acc[r] * p.sc : NEG_INF;
+                update(m2, l2, w, 4);
+            }
+        }
+        // merge the four lanes of each row (keys 4 * (lane / 16) + ...)
+        const float mo = row_max4(m1), lo = row_sum4(l1 * __builtin_amdgcn_exp2f(m1 - mo));
+        const float mh = row_max4(m2), lh = row_sum4(l2 * __builtin_amdgcn_exp2f(m2 - mh));
+        float *hpart = stil + CH * EXT_R;  // [h][key block][row][maximum, sum]
+        if (g4 == 0) {
+            stm[hs * EXT_R + rho] = mo;
+            stil[hs * EXT_R + rho] = lo > 0.f ? 1.0f / lo : 0.f;
+            hpart[((hh * 4 + hcb) * 16 + l16) * 2 + 0] = mh;
+            hpart[((hh * 4 + hcb) * 16 + l16) * 2 + 1] = lh;
+        }
+        __syncthreads();  // pass-1 reads of the K buffers and the partial statistics are done
+        dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);  // pass 2's first K tiles
+        if (tid < CH * 16) {
+            // halo rows: the four key blocks of each
+            const int h = tid >> 4, r = tid & 15;
+            float mr = FLOOR;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mr = fmaxf(mr, hpart[((h * 4 + k) * 16 + r) * 2]);
+            float lr = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                lr = __builtin_fmaf(hpart[((h * 4 + k) * 16 + r) * 2 + 1],
+                                    __builtin_amdgcn_exp2f(hpart[((h * 4 + k) * 16 + r) * 2] - mr), lr);
+            stm[h * EXT_R + r] = mr;
+            stil[h * EXT_R + r] = lr > 0.f ? 1.0f / lr : 0.f;
+        }
+        wait_vm_all();
+        __syncthreads();
+        pm_o = stm[hs * EXT_R + rho];
+        pil_o = stil[hs * EXT_R + rho];
+        pm_h = stm[hh * EXT_R + l16];
+        pil_h = stil[hh * EXT_R + l16];
+    }
 
     // U[b][a][nb][r]: rows 16rw + 4g4 + r, d-columns dbase + 16nb + l16
     f32x4 U[CH][CH][4];
@@ -406,7 +536,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 } else if (CQ > 1) {
                     kload(hk, kbuf + fresh((hh * KROWS + 16 * hcb + l16) * D), 0);
                 }
-                const u32x2 v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
+                // raw logits, or (POST) probabilities with the row's statistics
+                u32x2 v;
+                if constexpr (POST)
+                    v = cvt_prob<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, pm_o, pil_o, p.sc, lane);
+                else
+                    v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
                 if ((cb - CB0) & 1)
                     store_pair<CQ>(xo, 1 + rw, cb - 1, prev, xo, 1 + rw, cb, v, lane);
                 else
@@ -417,7 +552,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 // and 1, q = wave + 8 (q = h * NCB + cb), the first stored with the
                 // last own block
                 kload(hq, qhbuf + fresh((hh * HALO + l16) * D), 0);
-                const u32x2 v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                u32x2 v;
+                if constexpr (POST)
+                    v = cvt_prob<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, R ? pm_h : stm[hh * EXT_R + l16],
+                                    R ? pil_h : stil[hh * EXT_R + l16], p.sc, lane);
+                else
+                    v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                 f16_t *xhh = xbuf + hh * EXT_R * XP;
                 if (R) {
                     store_pair<CQ>(xhh, 0, hcb, v, xhh, 0, hcb, v, lane, true);
@@ -427,7 +567,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                         const int h = (wave + 8) / NCB, hc = (wave + 8) % NCB;
                         kload(hq, qhbuf + fresh((h * HALO + l16) * D), 0);
                         kload(hk, kbuf + fresh((h * KROWS + 16 * hc + l16) * D), 0);
-                        const u32x2 v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                        u32x2 v2;
+                        if constexpr (POST)
+                            v2 = cvt_prob<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, stm[h * EXT_R + l16],
+                                             stil[h * EXT_R + l16], p.sc, lane);
+                        else
+                            v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
                         f16_t *xh2 = xbuf + h * EXT_R * XP;
                         store_pair<CQ>(xh2, 0, hc, v2, xh2, 0, hc, v2, lane, true);
                     }
@@ -524,50 +669,69 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
             else
                 stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
-            // Mask_-inf (only the diagonal tile has keys in the future of its
-            // rows), the row maximum over the 64 keys, probabilities
-            if (t == qt) {
+            if constexpr (POST) {
+                // Mask_0 after the convolution (only the diagonal tile has keys in
+                // the future of its rows); no renormalisation
+                if (t == qt) {
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) {
+                        const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
+                        c[o] = (j0 + key <= qabs) ? c[o] : 0.f;
+                    }
+                }
+                bf16x8 v8[2];
+#pragma unroll
+                for (int o = 0; o < 16; ++o) v8[o >> 3][o & 7] = (bf16_t)c[o];
+                pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
+                pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+                if (lane == 0) fl[hs * 4 + rw] = 0;  // no rescale
+            } else {
+                // Mask_-inf (only the diagonal tile has keys in the future of its
+                // rows), the row maximum over the 64 keys, probabilities
+                if (t == qt) {
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) {
+                        const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
+                        c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+                    }
+                }
+                float mx = NEG_INF;
+#pragma unroll
+                for (int o = 0; o < 16; ++o) mx = fmaxf(mx, c[o]);
+                mx = row_max4(mx);
+                // every row has a causal key in tile 0, so m_new is finite
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                float ls = 0.f;
+                bf16x8 v8[2], v8l[2];
 #pragma unroll
                 for (int o = 0; o < 16; ++o) {
-                    const int key = 16 * (o >> 2) + 4 * g4 + (o & 3);
-                    c[o] = (j0 + key <= qabs) ? c[o] : NEG_INF;
+                    const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
+                    ls += e;
+                    v8[o >> 3][o & 7] = (bf16_t)e;
+                    if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
                 }
+                l_run = __builtin_fmaf(l_run, alpha, ls);
+                pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
+                pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+                if (PREP) {
+                    pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
+                    pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
+                }
+                if (g4 == 0) al[hs * BM + io] = alpha;
+                const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+                if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
             }
-            float mx = NEG_INF;
-#pragma unroll
-            for (int o = 0; o < 16; ++o) mx = fmaxf(mx, c[o]);
-            mx = row_max4(mx);
-            // every row has a causal key in tile 0, so m_new is finite
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float ls = 0.f;
-            bf16x8 v8[2], v8l[2];
-#pragma unroll
-            for (int o = 0; o < 16; ++o) {
-                const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
-                ls += e;
-                v8[o >> 3][o & 7] = (bf16_t)e;
-                if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
-            }
-            l_run = __builtin_fmaf(l_run, alpha, ls);
-            pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
-            pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
-            if (PREP) {
-                pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
-                pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
-            }
-            if (g4 == 0) al[hs * BM + io] = alpha;
-            const bool moved = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-            if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
             wait_vm_all();  // K(t+1) and V(t) have landed
         }
     }
 
-    // row sums l_b -> 1/l_b in al (after every wave's last P.V read of al)
+    // row sums l_b -> 1/l_b in al (after every wave's last P.V read of al);
+    // POST: the probabilities were normalised before the convolution
     const float lsum = row_sum4(l_run);
     __syncthreads();
-    if (g4 == 0) al[hs * BM + io] = 1.0f / lsum;
+    if (g4 == 0) al[hs * BM + io] = POST ? 1.0f : 1.0f / lsum;
     __syncthreads();
 
     // O^a = sum_b w_ab U_{b,a} / l_b  (rows 16rw + 4g4 + r, d-columns dbase + 16nb + l16)
@@ -850,10 +1014,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     }
 }
 
-template <int CQ, int CK, bool EXACT>
+template <int CQ, int CK, bool EXACT, bool POST = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

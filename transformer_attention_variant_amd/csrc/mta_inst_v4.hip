@@ -1,17 +1,20 @@
-// One-pass head-split kernels (bf16, d = 128, c_h = 2, key-query convolution
-// before the softmax in either form, head mix after it) for the kernel sizes
-// of the 2K/4K/8K workloads and 1x1.
+// Head-split kernels (bf16, d = 128, c_h = 2, head mix after the softmax) for
+// the kernel sizes of the 2K/4K/8K workloads and 1x1: one pass with the
+// key-query convolution before the softmax (either form), two passes with it
+// after the softmax.
 #include "mta_fwd_v4.h"
 #include "mta_launch.h"
 
 namespace mta {
 
-#define MTA_V4_SIZE(CQ_, CK_) \
-    if (cq == CQ_ && ck == CK_) return exact ? &v4::launch<CQ_, CK_, true> : &v4::launch<CQ_, CK_, false>;
+#define MTA_V4_SIZE(CQ_, CK_)                                                                          \
+    if (cq == CQ_ && ck == CK_)                                                                        \
+        return post ? &v4::launch<CQ_, CK_, false, true>                                              \
+                    : (exact ? &v4::launch<CQ_, CK_, true> : &v4::launch<CQ_, CK_, false>);
 
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre)
 {
-    if (d != 128 || ch != 2 || post || hpre) return nullptr;
+    if (d != 128 || ch != 2 || hpre || (post && exact)) return nullptr;
     MTA_V4_SIZE(1, 1)
     MTA_V4_SIZE(4, 9)
     MTA_V4_SIZE(6, 11)

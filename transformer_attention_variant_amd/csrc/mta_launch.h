@@ -38,7 +38,7 @@ layer::LayerFn find_launch_layer_f32(int d, int ch, int cq1, int ck1, int cq2, i
 layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, int ck2);
 // One-pass bf16 kernels (mta_fwd_v3.h); null when not instantiated.
 LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
-// One-pass head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
+// Head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 // Their gradient-preparation variants (key-query convolution before the
 // softmax, head mix after it); null when not instantiated.

@@ -1,8 +1,9 @@
-// mta_fwd_v4.h — one-pass MTA forward with head-split waves, for head groups of
-// two (c_h = 2), d = 128, bf16: key-query convolution before the softmax (two-
-// pass masks or Eq. 4's exact indicator), head mixing after it (page "Multi-
-// Token Attention — Paper Graph", section 3.4, "Key-Query Convolution", "Head
-// Mixing Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").
+// mta_fwd_v4.h — MTA forward with head-split waves, for head groups of two
+// (c_h = 2), d = 128, bf16, head mixing after the softmax: one pass with the
+// key-query convolution before the softmax (two-pass masks or Eq. 4's exact
+// indicator), two passes with it after the softmax (POST) (page "Multi-Token
+// Attention — Paper Graph", section 3.4, "Key-Query Convolution", "Head Mixing
+// Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").
 //
 // Same online-softmax formulation as mta_fwd_v3.h (accumulators
 // U_{b,a} = sum_j exp(C^b_j - m_b) V^a_j, O^a = sum_b w_ab U_{b,a} / l_b), with

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
     ("sweep8k_6x11_ch4_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
     ("sweep8k_8x15_ch4_post", "mta_fwd_v2 (two passes, VALU stencil)"),
     ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
-    ("needle4k_3d", "mta_fwd_layer"), ("needle4k_repeat", "mta_fwd_layer"),
+    ("needle4k_3d", "mta_fwd_v4 (one pass, head-split waves, 3D"), ("needle4k_repeat", "mta_fwd_layer"),
 ])
 def test_kernel_selection(lib, name, expect):
     """Host-only query of the kernel each workload runs (no launch)."""
@@ -105,7 +105,10 @@ def test_layer_validation(lib, kw, code):
     (dict(kq_post=None, head_post2=None), "mta_fwd_v4"),                    # kq pre + head post
     (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v4 (two passes"),  # kq post + head post
     (dict(kq_pre=None, head_post2=None), "mta_fwd_layer"),                  # head mix before the kq conv
-    (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000), "mta_fwd_layer"),
+    (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000), "mta_fwd_v4 (one pass, head-split waves, 3D"),
+    (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000, exact=1), "mta_fwd_layer"),
+    (dict(kq_pre=None, head_post=None, head_post2=None, kq_post=None, conv3d=0x1000, c_q=3, c_k=5), "mta_fwd_layer"),
+    (dict(kq_pre=None, kq_post=None, head_post2=None, conv3d=0x1000), "mta_fwd_layer"),   # 3D then a head mix
 ])
 def test_layer_kernel_selection(lib, kw, expect):
     cfg, w = _layer(**kw)

@@ -34,6 +34,10 @@ def _cases():
                      head_place=P, theta_std=0.2, seed=911))
     c.append(I.small("3d_bf16_6x11", B=1, H=4, T=150, d=128, c_q=6, c_k=11, c_h=2, form="3d", head_place=P,
                      dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=912))
+    # the head-split kernel's 3D form: one tile + 1, a single partial tile, several batches
+    for (T, B) in ((65, 2), (3, 1), (200, 3)):
+        c.append(I.small(f"3d_bf16_6x11_T{T}", B=B, H=4, T=T, d=128, c_q=6, c_k=11, c_h=2, form="3d",
+                         head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=913 + T))
     for (d, dt, ch, cq, ck, cq2, ck2) in ((64, "f32", 2, 3, 5, 2, 4), (32, "f32", 4, 2, 3, 3, 3),
                                           (128, "bf16", 2, 6, 11, 6, 11), (128, "bf16", 4, 4, 9, 4, 9),
                                           (64, "f32", 1, 16, 31, 1, 1)):
@@ -131,8 +135,9 @@ def test_layer_workloads_sampled(name):
     _say(f"[layer]   rows {ranges} units {units}: max abs err {err:.3e} (tol {tol:.2e})")
 
 
-def test_layer_causality_full_size():
-    cfg = I.CONFIGS["needle4k_repeat"]
+@pytest.mark.parametrize("name", ["needle4k_repeat", "needle4k_3d"])
+def test_layer_causality_full_size(name):
+    cfg = I.CONFIGS[name]
     _say(f"[layer] causality {cfg.short()}")
     inp = I.generate(cfg)
     dev = to_dev(inp)

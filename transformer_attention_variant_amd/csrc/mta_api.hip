@@ -2,6 +2,7 @@
 // kernel selection and the asynchronous launch on the caller's stream.
 #include <math.h>
 #include <stdint.h>
+#include <cstring>
 
 #include "mta.h"
 #include "mta_fwd_v2.h"
@@ -338,6 +339,31 @@ static int make_layer_plan(const mta_layer_config *c, const mta_layer_weights *w
     return MTA_OK;
 }
 
+// A layer whose only convolution is the both-pre-softmax 3D kernel (two-pass
+// masks) runs the head-split kernel's 3D form where it is instantiated (bf16,
+// d = 128, c_h = 2): the geometry of the default placement's plan, the 3D
+// kernel in place of the per-head one and no head mix.
+static bool as_v4_3d(const mta_layer_config *c, const mta_layer_weights *w, Plan &pl)
+{
+    if (!w->conv3d || w->kq_pre || w->head_pre || w->head_post || w->kq_post || w->head_post2) return false;
+    if (c->dtype != MTA_BF16 || c->exact) return false;
+    const mta::LaunchFn fn = mta::find_launch_v4_3d(c->head_dim, c->c_h, c->c_q, c->c_k);
+    if (!fn) return false;
+    mta_config sc{};
+    sc.batch = c->batch; sc.heads = c->heads; sc.seq_len = c->seq_len; sc.head_dim = c->head_dim;
+    sc.c_q = c->c_q; sc.c_k = c->c_k; sc.c_h = c->c_h;
+    sc.kq_place = MTA_PRE_SOFTMAX; sc.head_place = MTA_POST_SOFTMAX;
+    sc.dtype = c->dtype; sc.gn_eps = c->gn_eps; sc.depth_scale = c->depth_scale;
+    if (validate(&sc) != MTA_OK || make_plan(&sc, pl) != MTA_OK) return false;
+    if (!pl.name || std::strncmp(pl.name, "mta_fwd_v4", 10) != 0) return false;
+    const size_t lds = (size_t)mta::v4::layout(c->c_q, c->c_k, false, false, true).total;
+    if (lds > 160 * 1024) return false;
+    pl.fn = fn;
+    pl.lds = lds;
+    pl.name = "mta_fwd_v4 (one pass, head-split waves, 3D convolution, fp16 matrix-core stencil)";
+    return true;
+}
+
 int mta_forward_layer(const void *q, const void *k, const void *v, const mta_layer_weights *w,
                       const mta_layer_config *c, void *out, void *stream)
 {
@@ -354,6 +380,15 @@ int mta_forward_layer(const void *q, const void *k, const void *v, const mta_lay
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MTA_ERR_MISALIGNED;
     for (const float *x : ws)
         if (x && !aligned4(x)) return MTA_ERR_MISALIGNED;
+    Plan p3;
+    if (as_v4_3d(c, w, p3)) {
+        mta::Params &p = p3.p;
+        p.q = q; p.k = k; p.v = v;
+        p.theta = w->conv3d; p.wmix = nullptr; p.gn_w = w->gn_w; p.gn_b = w->gn_b; p.gate = w->gate;
+        p.out = out;
+        const hipError_t e = p3.fn(p, p3.grid, p3.lds, reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+    }
     LayerPlan pl;
     const int ps = make_layer_plan(c, w, pl);
     if (ps != MTA_OK) return ps;
@@ -372,6 +407,8 @@ const char *mta_layer_kernel_name(const mta_layer_config *c, const mta_layer_wei
     mta_config sc;
     const float *th_kq = nullptr, *th_head = nullptr;
     if (as_placement(c, w, sc, th_kq, th_head)) return mta_kernel_name(&sc);
+    Plan p3;
+    if (as_v4_3d(c, w, p3)) return p3.name;
     LayerPlan pl;
     return make_layer_plan(c, w, pl) == MTA_OK ? "mta_fwd_layer (general layer, two passes)" : nullptr;
 }

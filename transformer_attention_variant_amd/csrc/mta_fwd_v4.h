@@ -52,7 +52,7 @@ struct Layout {
 
 // prep: the gradient-preparation variant keeps P as bf16 high part and
 // remainder (a second probability buffer)
-__host__ __device__ inline Layout layout(int cq, int ck, bool prep = false, bool post = false)
+__host__ __device__ inline Layout layout(int cq, int ck, bool prep = false, bool post = false, bool c3d = false)
 {
     Layout L;
     int o = 0;
@@ -65,7 +65,7 @@ __host__ __device__ inline Layout layout(int cq, int ck, bool prep = false, bool
     L.fl_off = o; o += CH * 4 * 4;                // [b][rw]: some factor of the 16 rows differs from 1
     L.gn_off = o; o += 2 * CH * BM * 4;           // GroupNorm partial sums [d half][a][row]
     L.w_off = o;  o += 16;                        // the group's 2x2 mixing matrix
-    L.th_off = o; o += ((CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;
+    L.th_off = o; o += (((c3d ? CH : 1) * CH * cq * ((ck + 3) & ~3) + 3) & ~3) * 4;  // [a][(b)][row][col]
     // post: softmax statistics of the tile rows and the rows above them
     // (maximum, 1/sum: [h][row]) and the halo rows' partial statistics
     // ([h][key block][row][maximum, sum])
@@ -306,6 +306,32 @@ __device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ],
         for (int r = 0; r < 4; ++r) out[4 * t + r] = acc[t][r];
 }
 
+// The 3D form's stencil (two-pass masks): both heads' logit tiles x and x2,
+// each through its own banded kernel matrices, accumulated into one output.
+template <int CQ>
+__device__ inline void stencil64_pair(const f16_t *x, const f16_t *x2, int rho, const f16x8 (&tf)[CQ],
+                                      const f16x8 (&tf2)[CQ], int lane, float out[16])
+{
+    const int g4 = lane >> 4;
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ip = 0; ip < CQ; ++ip)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = rho - ip, off = r * XP + 8 * xchunk<CQ>(r, g4) + 16 * t;
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf[ip], *reinterpret_cast<const f16x8 *>(x + off), acc[t],
+                                                            0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tf2[ip], *reinterpret_cast<const f16x8 *>(x2 + off),
+                                                            acc[t], 0, 0, 0);
+        }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[4 * t + r] = acc[t][r];
+}
+
 // Extra pointers of the gradient-preparation variant (PREP): dY, the
 // workspace of the backward (row statistics, D, dO as bf16 high part and
 // remainder) and the GroupNorm / gate gradients it accumulates into.
@@ -324,11 +350,16 @@ struct PrepArgs {
 // passes over the key tiles: the softmax statistics of the tile's rows and of
 // the 16 rows above it first, then the probabilities of the extended tile ->
 // fp16 stencil -> Mask_0 -> P.V; the head mix stays in the epilogue.
-template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false>
+// C3D: the both-pre-softmax 3D convolution (kernel theta[g][a][b][i'][j'], p.theta)
+// in place of the per-head one, with no head mix: output head a's stencil sums
+// over the logit tiles of both heads b, and only the P.V products of head a's
+// probabilities with V^a are formed.
+template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     static_assert(!(POST && (EXACT || PREP)), "post-softmax form: two-pass masks, forward only");
+    static_assert(!(C3D && (EXACT || PREP || POST)), "3D form: two-pass masks, forward only");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
@@ -342,7 +373,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     const int T = p.T;
     constexpr int CKP = ((CK + 3) / 4) * 4;
 
-    const Layout lay = layout(CQ, CK, PREP, POST);
+    const Layout lay = layout(CQ, CK, PREP, POST, C3D);
     f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -376,24 +407,41 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     QFrag<D> qown;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) qown.x[t] = *reinterpret_cast<const bf16x8 *>(qrow + 8 * t);
-    for (int i = tid; i < CH * CQ * CKP; i += NT) {
-        const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
-        th_s[i] = c < CK ? p.theta[((size_t)(h0 + a) * CQ + r) * CK + c] : 0.f;
+    if constexpr (C3D) {
+        for (int i = tid; i < CH * CH * CQ * CKP; i += NT) {
+            const int ab = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
+            th_s[i] = c < CK ? p.theta[(((size_t)g * CH * CH + ab) * CQ + r) * CK + c] : 0.f;
+        }
+        if (tid < CH * CH) w_s[tid] = (tid / CH == tid % CH) ? 1.f : 0.f;  // no head mix
+    } else {
+        for (int i = tid; i < CH * CQ * CKP; i += NT) {
+            const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
+            th_s[i] = c < CK ? p.theta[((size_t)(h0 + a) * CQ + r) * CK + c] : 0.f;
+        }
+        if (tid < CH * CH) w_s[tid] = p.wmix[(size_t)g * CH * CH + tid];
     }
-    if (tid < CH * CH) w_s[tid] = p.wmix[(size_t)g * CH * CH + tid];
     wait_vm_all();
     __syncthreads();
 
     // banded kernel matrices of head hs (MFMA A operands, fp16):
     // row m = lane%16 (output key), columns k = 8*(lane/16) + s of the window
-    f16x8 tf[CQ];
+    // (C3D: tf from source head hs, tfo from the other head, both into head hs)
+    f16x8 tf[CQ], tfo[C3D ? CQ : 1];
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
             const int jj = l16 + CK - 1 - (8 * g4 + s8);
-            const float t = (jj >= 0 && jj < CK) ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
-            tf[ip][s8] = (f16_t)f16_range(POST ? t : t * p.sc);  // POST: on probabilities, unscaled
+            const bool in = jj >= 0 && jj < CK;
+            if constexpr (C3D) {
+                const float t = in ? th_s[((hs * CH + hs) * CQ + ip) * CKP + jj] : 0.f;
+                const float u = in ? th_s[((hs * CH + (1 - hs)) * CQ + ip) * CKP + jj] : 0.f;
+                tf[ip][s8] = (f16_t)f16_range(t * p.sc);
+                tfo[ip][s8] = (f16_t)f16_range(u * p.sc);
+            } else {
+                const float t = in ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
+                tf[ip][s8] = (f16_t)f16_range(POST ? t : t * p.sc);  // POST: on probabilities, unscaled
+            }
         }
 
     const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
@@ -624,11 +672,13 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) f[r] = al[s * BM + 16 * rw + 4 * g4 + r];
 #pragma unroll
-                    for (int a = 0; a < CH; ++a)
+                    for (int a = 0; a < CH; ++a) {
+                        if (C3D && a != s) continue;  // no head mix: only U[a][a]
 #pragma unroll
                         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                             for (int r = 0; r < 4; ++r) U[s][a][nb][r] *= f[r];
+                    }
                 }
             }
 #pragma unroll
@@ -652,6 +702,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
                         for (int s = 0; s < CH; ++s) {
+                            if (C3D && s != a) continue;
                             U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
                             // the gradients use P . V with P kept to ~16 bits (high part + remainder)
                             if (PREP)
@@ -666,7 +717,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 
         if (cur) {
             float c[16];
-            if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
+            if constexpr (C3D)
+                stencil64_pair<CQ>(xo, xbuf + (1 - hs) * EXT_R * XP, rho, tf, tfo, lane, c);
+            else if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
                 stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
             else
                 stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
@@ -751,7 +804,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 for (int r = 0; r < 4; ++r) {
                     float o = 0.f;
 #pragma unroll
-                    for (int s = 0; s < CH; ++s) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
+                    for (int s = 0; s < CH; ++s)
+                        if (!C3D || s == a) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
                     acc[a][nb][r] = o;
                 }
     }
@@ -1015,10 +1069,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     }
 }
 
-template <int CQ, int CK, bool EXACT, bool POST = false>
+template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -22,4 +22,12 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
     return nullptr;
 }
 
+// The 3D form (both-pre-softmax 3D convolution, no head mix) at the 4K
+// workload's kernel size.
+LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
+{
+    if (d == 128 && ch == 2 && cq == 6 && ck == 11) return &v4::launch<6, 11, false, false, true>;
+    return nullptr;
+}
+
 }  // namespace mta

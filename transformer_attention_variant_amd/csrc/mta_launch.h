@@ -40,6 +40,8 @@ layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, 
 LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 // Head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre);
+// Its 3D-convolution form (two-pass masks, no head mix); null when not instantiated.
+LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
 // Their gradient-preparation variants (key-query convolution before the
 // softmax, head mix after it); null when not instantiated.
 namespace v4 {

@@ -23,10 +23,12 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
 }
 
 // The 3D form (both-pre-softmax 3D convolution, no head mix) at the 4K
-// workload's kernel size.
+// workload's kernel size and 1x1.
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
 {
-    if (d == 128 && ch == 2 && cq == 6 && ck == 11) return &v4::launch<6, 11, false, false, true>;
+    if (d != 128 || ch != 2) return nullptr;
+    if (cq == 6 && ck == 11) return &v4::launch<6, 11, false, false, true>;
+    if (cq == 1 && ck == 1) return &v4::launch<1, 1, false, false, true>;
     return nullptr;
 }
 

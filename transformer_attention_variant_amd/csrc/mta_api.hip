@@ -506,7 +506,8 @@ int mta_backward(const void *q, const void *k, const void *v, const float *theta
     const size_t nEr4 = pad4(bp.nEr);
     const size_t lds_b = ((size_t)bp.nRrb * 16 * bp.xpitch + (size_t)bp.nEr * bp.epitch +
                           (size_t)ch * bp.nEr * bp.epitch + pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
-                          pad4(ch * cq * ckp) + (size_t)ch * 3 * nEr4 + pad4((size_t)mta::bwd::NWB * ch * ch)) * 4 + vb;
+                          pad4(ch * cq * ckp) + (size_t)ch * 3 * nEr4 + pad4((size_t)mta::bwd::NWB * ch * ch)) * 4 + vb +
+                          mta::bwd::ms_bytes(mta::bwd_fixed_sizes(bf, d, ch, cq, ck), bp.nRrb, ch, cq);
     if (lds_a > 160 * 1024 || lds_b > 160 * 1024) return MTA_ERR_UNSUPPORTED;
 
     // bf16, d = 128, c_h = 2: the first kernel's work (row statistics, dO, D,

@@ -38,6 +38,25 @@ constexpr int NT = 256;         // kernel A: 4 waves
 constexpr int NTB = 512;        // kernel B: 8 waves, two per SIMD
 constexpr int NWB = NTB / 64;
 
+typedef _Float16 h16_t;
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+// fp16 copy of the logit region for the matrix-core stencil: halves per row
+constexpr int X16P = 104;
+
+// Kernels with compile-time stencil sizes (bf16, d = 128) recompute the
+// convolved map on the matrix cores, as the head-split forward does: fp16
+// operands (the logit region and the banded kernel matrices), fp32 sums.
+template <typename DT, int D, int CQ, int CK>
+constexpr bool stencil_on_mfma() { return sizeof(DT) == 2 && D == 128 && CQ > 0 && CK > 0 && CK <= 17; }
+
+// bytes of the fp16 logit region and of both heads' banded kernel matrices
+// (0 for the kernels that keep the VALU stencil)
+__host__ __device__ constexpr int ms_bytes(bool on, int nrrb, int ch, int cq)
+{
+    return on ? nrrb * 16 * X16P * 2 + ch * cq * 64 * 16 : 0;
+}
+
 struct BParams {
     Params f;                        // forward geometry and pointers (q, k, v, theta, wmix, gn, gate)
     const void *dout;                // dY [B][H][T][d] (input dtype)
@@ -561,9 +580,10 @@ __device__ inline void prod_tile(float *buf, int pitch, int nrb, int ncb, int nr
 
 // Logit region X: buf[row][col] = sc * Q[r0 + row] . K[c0 + col], 0 outside
 // [0, T) and, unless raw, where the key is in the future of the row (Mask_0).
+// With x16, the same values also go to an fp16 copy (pitch X16P).
 template <typename DT, int D>
 __device__ inline void x_tile(float *buf, int pitch, int nrb, int ncb, int nrows, const DT *qh, const DT *kh, int r0,
-                              int c0, int T, float sc, bool raw, int wave, int lane)
+                              int c0, int T, float sc, bool raw, int wave, int lane, h16_t *x16 = nullptr)
 {
     region_product<DT, D, false>(nrb, ncb, qh, qh, r0, kh, c0, T, wave, lane, [&](int rb, int cb, const f32x4 &acc) {
         const int qi = r0 + 16 * rb + (lane & 15);
@@ -576,6 +596,10 @@ __device__ inline void x_tile(float *buf, int pitch, int nrb, int ncb, int nrows
             o[r] = ok ? acc[r] * sc : 0.f;
         }
         if (16 * rb + (lane & 15) < nrows) *reinterpret_cast<f32x4 *>(buf + (16 * rb + (lane & 15)) * pitch + e0) = o;
+        if (x16) {
+            const h16x4 h = {(h16_t)o[0], (h16_t)o[1], (h16_t)o[2], (h16_t)o[3]};
+            *reinterpret_cast<h16x4 *>(x16 + (16 * rb + (lane & 15)) * X16P + e0) = h;
+        }
     });
 }
 
@@ -672,6 +696,10 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
     const int nEr4 = (nEr + 3) & ~3;
     float *dwr = st + CH * 3 * nEr4;                              // [NWB waves][CH*CH]
     DT *opbuf = reinterpret_cast<DT *>(dwr + ((NWB * CH * CH + 3) & ~3));
+    constexpr bool MS = stencil_on_mfma<DT, D, CQ, CK>();
+    // MS: fp16 copy of the logit region, then both heads' banded kernel matrices
+    h16_t *x16 = reinterpret_cast<h16_t *>(reinterpret_cast<char *>(opbuf) + vbuf_bytes<DT, D>());
+    h16x8 *tfl = reinterpret_cast<h16x8 *>(x16 + bp.nRrb * 16 * X16P);  // [s][i'][lane]
 
     const size_t hstride = (size_t)T * D;
     const DT *Q = reinterpret_cast<const DT *>(p.q);
@@ -689,6 +717,22 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
     }
     for (int i = tid; i < CH * cq * ckp; i += NTB) dth[i] = 0.f;
     for (int i = tid; i < CH * CH; i += NTB) w_s[i] = p.wmix[(size_t)g * CH * CH + i];
+    if constexpr (MS) {
+        // banded kernel matrices (MFMA A operands): lane row m = lane%16 (output
+        // key), columns k = 8*(lane/16) + e of the 32-column window, tap
+        // j' = m + c_k - 1 - k
+        __syncthreads();
+        for (int i = tid; i < CH * CQ * 64; i += NTB) {
+            const int sh = i / (CQ * 64), ip = (i / 64) % CQ, ln = i % 64;
+            h16x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = (ln & 15) + CK - 1 - (8 * (ln >> 4) + e);
+                f[e] = (h16_t)((jj >= 0 && jj < CK) ? th_s[(sh * CQ + ip) * ckp + jj] : 0.f);
+            }
+            tfl[i] = f;
+        }
+    }
     float dwp[CH * CH];
 #pragma unroll
     for (int i = 0; i < CH * CH; ++i) dwp[i] = 0.f;
@@ -766,9 +810,39 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
             __syncthreads();
             // X^s over the logit region (log2-scaled; Mask_0 unless exact)
             x_tile<DT, D>(xbuf, xp, bp.nRrb, bp.nRcb, 16 * bp.nRrb, Q + base0 + s * hstride, K + base0 + s * hstride,
-                          xr0, xc0, T, p.sc, p.exact != 0, wave, lane);
+                          xr0, xc0, T, p.sc, p.exact != 0, wave, lane, (MS && !p.exact) ? x16 : nullptr);
             __syncthreads();
             // C^s over the region -> P^s (in place)
+            if (MS && !p.exact) {
+                // on the matrix cores (two-pass masks; Eq. 4's indicator keeps the
+                // VALU stencil): 16x16 blocks (region rows 16rb.., columns 16cb..)
+                // dealt to the waves; lane: row 16rb + lane%16, columns 16cb + 4*(lane/16) + r
+                const h16x8 *tfs = tfl + s * CQ * 64;
+                const int nrb = (nEr + 15) / 16, nxr = 16 * bp.nRrb;
+                for (int tsk = wave; tsk < nrb * nlcb; tsk += NWB) {
+                    const int rb = tsk / nlcb, cb = tsk % nlcb;
+                    const int r = 16 * rb + (lane & 15);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ip = 0; ip < CQ; ++ip) {
+                        int xr = r + CQ - 1 - ip;
+                        xr = xr < nxr ? xr : nxr - 1;  // rows past the region: results unused
+                        const h16x8 xv = *reinterpret_cast<const h16x8 *>(x16 + xr * X16P + 16 * cb + 8 * (lane >> 4));
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(tfs[ip * 64 + lane], xv, acc, 0, 0, 0);
+                    }
+                    if (r < nEr) {
+                        const int qi = i0 + r;
+                        const float m = st[(s * 3 + 0) * nEr4 + r], il = st[(s * 3 + 1) * nEr4 + r];
+                        f32x4 o;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int kj = ec0 + 16 * cb + 4 * (lane >> 4) + q;
+                            o[q] = (kj >= 0 && kj <= qi && qi < T) ? __builtin_amdgcn_exp2f(acc[q] - m) * il : 0.f;
+                        }
+                        *reinterpret_cast<f32x4 *>(ebuf + r * ep + 16 * cb + 4 * (lane >> 4)) = o;
+                    }
+                }
+            } else
             for (int t = tid; t < nEr * nlcb; t += NTB) {
                 const int r = t / nlcb, cb = t % nlcb;
                 const int qi = i0 + r;
@@ -930,6 +1004,9 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
 }  // namespace bwd
 
 bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck);
+// find_launch_bwd picks a main kernel with compile-time stencil sizes (whose
+// convolved-map recompute runs on the matrix cores)
+bool bwd_fixed_sizes(int dtype_bf16, int d, int ch, int cq, int ck);
 hipError_t launch_fill_zero(const bwd::ZeroList &z, hipStream_t s);
 
 }  // namespace mta

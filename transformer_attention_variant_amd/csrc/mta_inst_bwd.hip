@@ -33,13 +33,18 @@ hipError_t launch(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t
 
 }  // namespace bwd
 
+bool bwd_fixed_sizes(int dtype_bf16, int d, int ch, int cq, int ck)
+{
+    return dtype_bf16 && d == 128 && ch == 2 && ((cq == 6 && ck == 11) || (cq == 4 && ck == 9) || (cq == 8 && ck == 15));
+}
+
 bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck)
 {
     using namespace bwd;
-    if (dtype_bf16 && d == 128 && ch == 2) {
-        if (cq == 6 && ck == 11) return &launch<bf16_t, 128, 2, 6, 11>;
-        if (cq == 4 && ck == 9) return &launch<bf16_t, 128, 2, 4, 9>;
-        if (cq == 8 && ck == 15) return &launch<bf16_t, 128, 2, 8, 15>;
+    if (bwd_fixed_sizes(dtype_bf16, d, ch, cq, ck)) {
+        if (cq == 6) return &launch<bf16_t, 128, 2, 6, 11>;
+        if (cq == 4) return &launch<bf16_t, 128, 2, 4, 9>;
+        return &launch<bf16_t, 128, 2, 8, 15>;
     }
 #define MTA_BWD_D(T_, D_)                                          \
     if (d == D_) {                                                 \

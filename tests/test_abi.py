@@ -51,6 +51,17 @@ def test_kernel_selection(lib, name, expect):
     assert got is not None and got.startswith(expect), got
 
 
+@pytest.mark.parametrize("kq,expect", [(I.PRE, "mta_fwd_v4 (one pass, head-split waves, pre-softmax head mix"),
+                                       (I.PRE_EXACT, "mta_fwd_kernel"), (I.POST, "mta_fwd_kernel")])
+def test_kernel_selection_head_mix_before_softmax(lib, kq, expect):
+    """c_h = 2 with the head mix before the softmax: the head-split kernel's 3D form
+    for the two-pass masks at an instantiated size, else the general kernel."""
+    cfg = I.small("hpre", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=2, kq_place=kq, head_place=I.PRE,
+                  dtype="bf16")
+    got = binding.kernel_name(cfg)
+    assert got is not None and got.startswith(expect), got
+
+
 @pytest.mark.parametrize("kq", [I.PRE, I.PRE_EXACT])
 def test_kernel_selection_single_head_groups(lib, kq):
     """Groups of one head run the key-split one-pass kernel."""

@@ -50,6 +50,12 @@ def _small_cases():
                 c.append(I.small(f"bf16_{cq}x{ck}_kq{kq}_ch{ch}", B=1, H=4, T=197, d=128, c_q=cq, c_k=ck,
                                  c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05,
                                  head_std=0.05, seed=200 + cq * 10 + ck + kq + ch))
+    # head mix before the softmax at c_h = 2 (the head-split kernel's 3D form with
+    # the kernel w_ab theta_b): the instantiated sizes, ragged T, one tile + 1
+    for (cq, ck, T) in ((6, 11, 197), (1, 1, 197), (6, 11, 65)):
+        c.append(I.small(f"bf16_{cq}x{ck}_hpre_T{T}", B=2, H=4, T=T, d=128, c_q=cq, c_k=ck, c_h=2, kq_place=P,
+                         head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.3,
+                         seed=260 + cq + T))
     # one head per group (the one-pass kernel with a single accumulator pair)
     for kq in (P, I.PRE_EXACT):
         c.append(I.small(f"bf16_6x11_ch1_kq{kq}", B=2, H=2, T=150, d=128, c_q=6, c_k=11, c_h=1, kq_place=kq,

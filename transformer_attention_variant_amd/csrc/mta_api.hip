@@ -128,6 +128,18 @@ static int make_plan(const mta_config *cfg, Plan &pl)
             else pl.name = post ? "mta_fwd_v4 (two passes, head-split waves, fp16 matrix-core stencil)"
                                 : "mta_fwd_v4 (one pass, head-split waves, fp16 matrix-core stencil)";
         }
+        if (!fn && hpre && !post && !exact) {
+            // head mix before the softmax: by linearity the 3D convolution with
+            // kernel w[g][a][b] * theta[b], built in the kernel from both
+            fn = mta::find_launch_v4_3d(d, ch, cq, ck);
+            if (fn) {
+                p.ncb = 5;
+                p.pitch = p.ncb * 16 + 4;
+                lds = (size_t)mta::v4::layout(cq, ck, false, false, true).total;
+                if (lds > LDS_MAX) fn = nullptr;
+                else pl.name = "mta_fwd_v4 (one pass, head-split waves, pre-softmax head mix as a 3D convolution, fp16 matrix-core stencil)";
+            }
+        }
         if (!fn) fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
         if (fn && !pl.name) {
             p.ncb = ncb0 < 5 ? 5 : ncb0;

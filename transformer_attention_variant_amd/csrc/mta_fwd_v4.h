@@ -351,9 +351,10 @@ struct PrepArgs {
 // the 16 rows above it first, then the probabilities of the extended tile ->
 // fp16 stencil -> Mask_0 -> P.V; the head mix stays in the epilogue.
 // C3D: the both-pre-softmax 3D convolution (kernel theta[g][a][b][i'][j'], p.theta)
-// in place of the per-head one, with no head mix: output head a's stencil sums
-// over the logit tiles of both heads b, and only the P.V products of head a's
-// probabilities with V^a are formed.
+// in place of the per-head one, with no head mix after the softmax: output head
+// a's stencil sums over the logit tiles of both heads b, and only the P.V
+// products of head a's probabilities with V^a are formed.  With p.head_pre the
+// kernel is built from the per-head kernels and the pre-softmax head mix.
 template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
@@ -408,11 +409,18 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) qown.x[t] = *reinterpret_cast<const bf16x8 *>(qrow + 8 * t);
     if constexpr (C3D) {
+        // p.head_pre: the per-head kernels followed by the head mix before the
+        // softmax, which by linearity is the 3D kernel w[g][a][b] * theta[h0 + b]
         for (int i = tid; i < CH * CH * CQ * CKP; i += NT) {
             const int ab = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
-            th_s[i] = c < CK ? p.theta[(((size_t)g * CH * CH + ab) * CQ + r) * CK + c] : 0.f;
+            float v = 0.f;
+            if (c < CK)
+                v = p.head_pre ? p.wmix[(size_t)g * CH * CH + ab] *
+                                     p.theta[((size_t)(h0 + ab % CH) * CQ + r) * CK + c]
+                               : p.theta[(((size_t)g * CH * CH + ab) * CQ + r) * CK + c];
+            th_s[i] = v;
         }
-        if (tid < CH * CH) w_s[tid] = (tid / CH == tid % CH) ? 1.f : 0.f;  // no head mix
+        if (tid < CH * CH) w_s[tid] = (tid / CH == tid % CH) ? 1.f : 0.f;  // no mix after the softmax
     } else {
         for (int i = tid; i < CH * CQ * CKP; i += NT) {
             const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;

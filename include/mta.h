@@ -176,9 +176,11 @@ typedef struct {
  * asynchrony and error codes as for mta_forward; weights and cfg must be non
  * NULL, gn_w and gn_b are required; conv3d together with kq_pre or head_pre is
  * MTA_ERR_BAD_PLACEMENT.  A layer that is one of mta_forward's placements runs
- * mta_forward's kernels; any other layer runs the general layer kernel, limited
- * to c_q, c_q2 <= 16, c_k, c_k2 <= 31 and 160 KB of LDS per workgroup
- * (MTA_ERR_UNSUPPORTED beyond).
+ * mta_forward's kernels; a layer whose only convolution is conv3d (two-pass
+ * masks) runs the head-split kernel's 3D form where it is built (bf16,
+ * head_dim 128, c_h 2, 6x11 or 1x1); any other layer runs the general layer
+ * kernel, limited to c_q, c_q2 <= 16, c_k, c_k2 <= 31 and 160 KB of LDS per
+ * workgroup (MTA_ERR_UNSUPPORTED beyond).
  */
 int mta_forward_layer(const void *q, const void *k, const void *v, const mta_layer_weights *weights,
                       const mta_layer_config *cfg, void *out, void *stream);

@@ -63,6 +63,12 @@ def kernel_sources_hash(kernel: str = "") -> str:
     return h.hexdigest()[:16]
 
 
+def stencil_on_matrix_cores(kname) -> bool:
+    """Whether the named kernel runs the key-query stencil on the matrix cores
+    (fp16 operands) rather than on the fp32 vector ALUs."""
+    return kname is not None and ("mta_fwd_v4" in kname or "matrix-core" in kname)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,16 +223,9 @@ def main():
     # the matrix-core stencil run all the algorithmic work but the head mix
     # (a few VALU FLOP per logit) on the matrix cores, so everything is priced
     # against the 16-bit matrix-core peak; kernels with the fp32 VALU stencil
-    # are bound by the vector ALUs and priced against their fp32 peak.
-    on_mc = kname is not None and ("mta_fwd_v4" in kname or "matrix-core" in kname)
-    alu_view = {
-        "bound": "alu",
-        "achieved": round(alu_flops / t / 1e12, 3),
-        "peak": PEAK_VALU_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(alu_flops / t / 1e12 / PEAK_VALU_TFLOPS, 4),
-        "work": "key-query stencil 2*c_q*c_k + head mix 2*c_h FLOP per causal logit",
-    }
+    # are bound by the vector ALUs and priced against their fp32 peak (the
+    # stencil and the head mix, the work that runs there).
+    on_mc = stencil_on_matrix_cores(kname)
     if on_mc:
         roof = {
             "bound": "mfma",
@@ -237,8 +236,14 @@ def main():
             "work": "4*d (QK^T, PV) + 2*c_q*c_k (stencil) + 2*c_h (head mix) FLOP per causal logit",
         }
     else:
-        roof = dict(alu_view)
-    roof.update(traffic=traffic, kernel=kname)
+        roof = {
+            "bound": "alu",
+            "achieved": round(alu_flops / t / 1e12, 3),
+            "peak": PEAK_VALU_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alu_flops / t / 1e12 / PEAK_VALU_TFLOPS, 4),
+            "work": "key-query stencil 2*c_q*c_k + head mix 2*c_h FLOP per causal logit",
+        }
     mfma = {
         "achieved": round(fl["contraction"] / t / 1e12, 2),
         "peak": mfma_peak,
@@ -272,7 +277,6 @@ def main():
         "eff_tflops": round(all_flops / t / 1e12, 2),
         "ms_per_launch": round(ms_launch, 4),
         "roofline": roof,
-        "alu_view": alu_view,
         "mfma": mfma,
         "hbm": hbm,
     }
@@ -369,6 +373,10 @@ def stages(cfg, dev, timed, t, torch):
     flush = torch.empty(FLUSH_MIB * (1 << 18), dtype=torch.float32, device=dev["q"].device)
     _, msf = timed(cfg, dev, flush)
     peak_c = PEAK_MFMA_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_MFMA_F32_TFLOPS
+    # the convolution stage against the peak of the unit that runs it: the
+    # 16-bit matrix cores (fp16 operands) or the fp32 vector ALUs
+    on_mc = stencil_on_matrix_cores(binding.kernel_name(cfg))
+    conv_peak = PEAK_MFMA_BF16_TFLOPS if on_mc else PEAK_VALU_TFLOPS
     return {
         "kernel_1x1": binding.kernel_name(c11),
         "ms_per_launch_1x1": round(ms11, 4),
@@ -376,13 +384,27 @@ def stages(cfg, dev, timed, t, torch):
         "contraction_frac_1x1": round(4 * cfg.d * n / t11 / 1e12 / peak_c, 4),
         "conv_stage_ms": round(conv * 1e3, 4) if same else None,
         "conv_stage_tflops": round(st_alg / conv / 1e12, 2) if same else None,
-        "conv_stage_frac_valu": round(st_alg / conv / 1e12 / PEAK_VALU_TFLOPS, 4) if same else None,
+        "conv_stage_unit": "fp16 matrix cores" if on_mc else "fp32 VALU",
+        "conv_stage_peak": conv_peak,
+        "conv_stage_frac": round(st_alg / conv / 1e12 / conv_peak, 4) if same else None,
         "conv_work": "2*(c_q*c_k - 1) FLOP per causal logit and convolution (the taps beyond the 1x1 "
                      "run's one; per source head for the 3D kernel), counted once; null when the 1x1 run "
                      "selects another kernel",
         "ms_per_launch_flushed": round(msf, 4),
         "flush": f"{FLUSH_MIB} MiB written before every launch",
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(cfg, inp, args):
@@ -407,7 +429,7 @@ def cpu_baseline(cfg, inp, args):
     dt = time.perf_counter() - t0
     full = dt * (U * cfg.T) / (nu * rows)
     return {"value": round(cfg.B * cfg.T / full, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "threads": threads, "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{nu} of {U} (batch, head group) units x last {rows} of {cfg.T} rows "
                       f"({nu * rows * cfg.c_h} row-heads) in {dt:.2f} s; scaled by rows to the full "
                       f"workload ({full:.1f} s)"}

@@ -55,9 +55,18 @@ extern "C" {
 #define MTA_PRE_SOFTMAX_EXACT 2
 
 /* Element type of q, k, v and out.  Kernels and GroupNorm parameters are
- * always float32; all intermediate arithmetic is float32 (contractions
- * accumulate in float32 on the matrix cores; with MTA_BF16 the probabilities
- * enter the A·V product as bf16). */
+ * always float32.  Intermediate arithmetic is float32 (contractions accumulate
+ * in float32 on the matrix cores; with MTA_BF16 the probabilities enter the A·V
+ * product as bf16), with one exception: for MTA_BF16 the key-query convolution
+ * of the head-split and two-pass bf16 kernels runs on the matrix cores with
+ * fp16 operands (the logits or probabilities and the taps rounded to nearest,
+ * 11 significant bits; magnitudes beyond 65504 clamped to 65504, which only
+ * logits past ~5800 in natural units reach) and float32 accumulation.  In the
+ * head-split kernels (head groups of two) the centre tap (query offset 0, key
+ * offset 0) before the softmax is applied to the float32 logits, so a kernel
+ * near the identity keeps float32 accuracy at large logits; the other kernels
+ * round it like the other taps (2^-11 relative to the logit).  mta_kernel_name
+ * tells which kernel a configuration runs. */
 #define MTA_F32 0
 #define MTA_BF16 1
 
@@ -223,9 +232,10 @@ size_t mta_backward_workspace_size(const mta_config *cfg);
  * unsupported.  For profiling and reports; it launches nothing. */
 const char *mta_kernel_name(const mta_config *cfg);
 
-/* Host-only check of a configuration against the library's limits; the
- * same validation mta_forward runs (pointer checks excepted).  Returns MTA_OK
- * or the MTA_ERR_* code mta_forward would return. */
+/* Host-only check of a configuration against the library's limits: the same
+ * validation and kernel selection (LDS fit included) that mta_forward runs,
+ * pointer checks excepted.  Returns MTA_OK or the MTA_ERR_* code mta_forward
+ * would return. */
 int mta_check_config(const mta_config *cfg);
 
 /* Static description of a status code (never NULL). */

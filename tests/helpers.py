@@ -12,10 +12,16 @@ import oracle
 from transformer_attention_variant_amd import binding
 from transformer_attention_variant_amd import inputs as I
 
-# Tolerances (max-abs error of the output): 1e-4 in float32; in bfloat16
-# 2e-2 times the RMS of the oracle's output.
+# Tolerances, element by element: 1e-4 in float32; in bfloat16 2e-2 times the
+# RMS of the oracle's output, plus the bf16 unit roundoff (2^-8) times the
+# element's own magnitude.  The second term is the rounding of the result to the
+# output format, which the float64 oracle does not have: near 4-5 x RMS one
+# bf16 step is already as large as 2e-2 x RMS, so without it the bar would
+# measure the output format rather than the computation.  One rule for every
+# bf16 case.
 F32_TOL = 1e-4
 BF16_REL_TOL = 2e-2
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
 
 
 def to_dev(inp: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
@@ -29,11 +35,18 @@ def run_gpu(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], dev=None) -> torch.T
     return out
 
 
-def tolerance(cfg: I.MTAConfig, ref: np.ndarray) -> float:
+def tolerance(cfg: I.MTAConfig, ref: np.ndarray):
+    """The bar of each compared element (a scalar in float32, an array like
+    ``ref`` in bfloat16)."""
     if cfg.dtype == "f32":
         return F32_TOL
-    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
-    return BF16_REL_TOL * rms
+    return bf16_tolerance(ref)
+
+
+def bf16_tolerance(ref: np.ndarray) -> np.ndarray:
+    ref = ref.astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    return BF16_REL_TOL * rms + BF16_UNIT_ROUNDOFF * np.abs(ref)
 
 
 def compare(cfg: I.MTAConfig, got: torch.Tensor, ref: np.ndarray, mask: Optional[np.ndarray] = None,
@@ -43,10 +56,17 @@ def compare(cfg: I.MTAConfig, got: torch.Tensor, ref: np.ndarray, mask: Optional
         g, ref = g[mask], ref[mask]
     assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
     assert np.isfinite(ref).all(), f"{what}: non-finite oracle output"
-    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
-    tol = tolerance(cfg, ref)
-    assert err <= tol, f"{what} {cfg.short()}: max abs err {err:.3e} > tol {tol:.3e}"
-    return err, tol
+    if not g.size:
+        return 0.0, 0.0
+    diff = np.abs(g - ref)
+    tol = np.broadcast_to(tolerance(cfg, ref), diff.shape)
+    worst = int(np.argmax(diff - tol))
+    err = float(diff.flat[worst])
+    assert diff.flat[worst] <= tol.flat[worst], \
+        f"{what} {cfg.short()}: abs err {err:.3e} > tol {float(tol.flat[worst]):.3e} at flat index {worst} " \
+        f"(max abs err {float(diff.max()):.3e})"
+    # the margin of the closest element: its error and its bar
+    return err, float(tol.flat[worst])
 
 
 def sample_plan(cfg: I.MTAConfig, n_units: int = 2, rows: int = 64) -> Tuple[Sequence[Tuple[int, int]], Sequence[int]]:

@@ -185,6 +185,17 @@ def test_check_config(lib, kw, code):
     assert lib.mta_check_config(ctypes.byref(c)) == code
 
 
+def test_check_config_includes_the_lds_fit(lib):
+    # valid shape, but its kernel's LDS (fp32, d = 128, c_h = 4, 16x31, key-query
+    # convolution after the softmax with the head mix before it) exceeds 160 KB:
+    # mta_check_config returns what mta_forward would, and no kernel is named
+    c = cfg(d=128, dtype=0, c_h=4, c_q=16, c_k=31, kq_place=1, head_place=0)
+    assert lib.mta_check_config(ctypes.byref(c)) == -6
+    assert lib.mta_kernel_name(ctypes.byref(c)) is None
+    good = 0x10000  # never dereferenced: the call returns during planning
+    assert lib.mta_forward(*([good] * 7), ctypes.byref(c), good, None) == -6
+
+
 def test_forward_rejects_before_any_device_work(lib):
     c = cfg()
     good = 0x10000  # never dereferenced: every call below returns during validation

@@ -37,12 +37,15 @@ def _cases():
     # the head-split kernel's 3D form: one tile + 1, a single partial tile, several batches
     c.append(I.small("3d_bf16_1x1", B=1, H=4, T=150, d=128, c_q=1, c_k=1, c_h=2, form="3d", head_place=P,
                      dtype="bf16", qkv_std=0.7071, theta_std=0.3, seed=920))
-    # the gate through the layer entry point on the 3D form; as in the forward's
-    # gated bf16 case the bar is 2e-2 x the RMS over all heads, so the GroupNorm
-    # affine stays at its identity (random affine weights together with the gates
-    # put the largest channel's output rounding alone near the bar)
+    # the gate through the layer entry point on the 3D form, with a random
+    # GroupNorm affine
     c.append(I.small("3d_bf16_6x11_gated", B=1, H=4, T=130, d=128, c_q=6, c_k=11, c_h=2, form="3d", head_place=P,
-                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, gated=True, gate_std=0.5, seed=921))
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, gated=True, gate_std=1.0, gn_random=True,
+                     seed=921))
+    # large competing logits (needle keys 9u on top of their own draw) through the 3D form
+    c.append(I.small("3d_bf16_6x11_hot", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=2, form="3d", head_place=P,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.02, layer=4, needles=6, needle_scale=9.0,
+                     needle_on_key=True, seed=922))
     for (T, B) in ((65, 2), (3, 1), (200, 3)):
         c.append(I.small(f"3d_bf16_6x11_T{T}", B=B, H=4, T=T, d=128, c_q=6, c_k=11, c_h=2, form="3d",
                          head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=913 + T))

@@ -128,6 +128,17 @@ def _shape_only(cfg: I.MTAConfig) -> Dict:
     return {k: None for k in keys}
 
 
+def _launch_stream(device, stream: Optional[torch.cuda.Stream]) -> torch.cuda.Stream:
+    """The stream a call launches on: ``stream``, or torch's current stream.  A
+    side stream first waits for the work already queued on the current stream
+    (the inputs may still be in flight there)."""
+    cur = torch.cuda.current_stream(device)
+    if stream is None or stream.cuda_stream == cur.cuda_stream:
+        return cur
+    stream.wait_stream(cur)
+    return stream
+
+
 def status_string(code: int) -> str:
     return load().mta_status_string(int(code)).decode()
 
@@ -169,13 +180,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, theta_kq: torch.T
             or tuple(gn_w.shape) != (H, d) or tuple(gn_b.shape) != (H, d):
         raise ValueError("parameter shapes do not match (theta_kq [H,c_q,c_k], theta_head [H/c_h,c_h,c_h], "
                          "gn_w/gn_b [H,d])")
+    s = _launch_stream(q.device, stream)
     if out is None:
-        out = torch.empty_like(q)
+        # allocated on the launch stream: the caching allocator then never hands
+        # its memory to other work while the kernel may still write it
+        with torch.cuda.stream(s):
+            out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous CUDA tensor like q")
     cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                       I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
     if gate is None:
         rc = lib.mta_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(),
                              theta_head.data_ptr(), gn_w.data_ptr(), gn_b.data_ptr(), ctypes.byref(cfg),
@@ -213,14 +227,19 @@ def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: 
                       I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
-    g = {"q": torch.empty(q.shape, **f32), "k": torch.empty(q.shape, **f32), "v": torch.empty(q.shape, **f32),
-         "theta_kq": torch.empty(theta_kq.shape, **f32), "theta_head": torch.empty(theta_head.shape, **f32),
-         "gn_w": torch.empty(gn_w.shape, **f32), "gn_b": torch.empty(gn_b.shape, **f32)}
-    if gate is not None:
-        g["gate"] = torch.empty(gate.shape, **f32)
+    s = _launch_stream(dev, stream)
     nbytes = int(lib.mta_backward_workspace_size(ctypes.byref(cfg)))
-    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    # outputs and workspace are allocated on the launch stream, so that the
+    # caching allocator does not reuse the workspace (freed on return) for other
+    # work while the kernels on that stream may still use it
+    with torch.cuda.stream(s):
+        g = {"q": torch.empty(q.shape, **f32), "k": torch.empty(q.shape, **f32),
+             "v": torch.empty(q.shape, **f32), "theta_kq": torch.empty(theta_kq.shape, **f32),
+             "theta_head": torch.empty(theta_head.shape, **f32), "gn_w": torch.empty(gn_w.shape, **f32),
+             "gn_b": torch.empty(gn_b.shape, **f32)}
+        if gate is not None:
+            g["gate"] = torch.empty(gate.shape, **f32)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     ptr = lambda t: t.data_ptr() if t is not None else None
     rc = lib.mta_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(), theta_head.data_ptr(),
                           gn_w.data_ptr(), gn_b.data_ptr(), ptr(gate), dout.data_ptr(), ctypes.byref(cfg),
@@ -269,13 +288,14 @@ def forward_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gn_w: torch
             raise ValueError(f"{name} must be a contiguous CUDA (HIP) tensor")
         if name in shapes and (t.dtype != torch.float32 or tuple(t.shape) != shapes[name]):
             raise ValueError(f"{name} must be float32 of shape {shapes[name]}")
+    s = _launch_stream(q.device, stream)
     if out is None:
-        out = torch.empty_like(q)
+        with torch.cuda.stream(s):
+            out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous CUDA tensor like q")
     lc, lw = _layer_structs(B, H, T, d, I.F32 if q.dtype == torch.float32 else I.BF16, c_h, c_q, c_k, c_q2,
                             c_k2, exact, gn_eps, depth_scale, {n: t.data_ptr() for n, t in tens.items()})
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
     rc = lib.mta_forward_layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(lw), ctypes.byref(lc),
                                out.data_ptr(), ctypes.c_void_p(s.cuda_stream))
     if rc != MTA_OK:

@@ -59,8 +59,6 @@ extern "C" {
 
 int mta_abi_version(void) { return 100; }
 
-int mta_check_config(const mta_config *cfg) { return validate(cfg); }
-
 const char *mta_status_string(int s)
 {
     switch (s) {
@@ -201,6 +199,15 @@ static int forward_impl(const void *q, const void *k, const void *v, const float
     p.out = out;
     const hipError_t e = pl.fn(p, pl.grid, pl.lds, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+}
+
+int mta_check_config(const mta_config *cfg)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    // kernel selection and its LDS fit, exactly as mta_forward decides them
+    Plan pl;
+    return make_plan(cfg, pl);
 }
 
 const char *mta_kernel_name(const mta_config *cfg)

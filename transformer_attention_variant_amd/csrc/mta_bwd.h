@@ -817,12 +817,25 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
                 // on the matrix cores (two-pass masks; Eq. 4's indicator keeps the
                 // VALU stencil): 16x16 blocks (region rows 16rb.., columns 16cb..)
                 // dealt to the waves; lane: row 16rb + lane%16, columns 16cb + 4*(lane/16) + r
+                // The centre tap is exact: the accumulators start from
+                // theta_00 x - fp16(theta_00) fp16(x) at the output positions (x
+                // from the fp32 region), as the forward that produced the
+                // statistics makes it exact.
                 const h16x8 *tfs = tfl + s * CQ * 64;
+                const float t00 = th_s[s * cq * ckp + CK / 2], t00h = (float)(h16_t)t00;
                 const int nrb = (nEr + 15) / 16, nxr = 16 * bp.nRrb;
                 for (int tsk = wave; tsk < nrb * nlcb; tsk += NWB) {
                     const int rb = tsk / nlcb, cb = tsk % nlcb;
                     const int r = 16 * rb + (lane & 15);
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 acc;
+                    {
+                        int xr = r + CQ - 1;
+                        xr = xr < nxr ? xr : nxr - 1;  // rows past the region: results unused
+                        const int xc = 16 * cb + 4 * (lane >> 4) + p.hl;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[q] = __builtin_fmaf(t00, xbuf[xr * xp + xc + q], -t00h * (float)x16[xr * X16P + xc + q]);
+                    }
 #pragma unroll
                     for (int ip = 0; ip < CQ; ++ip) {
                         int xr = r + CQ - 1 - ip;

@@ -22,7 +22,11 @@
 //     | stencil, Mask_-inf, row maximum, rescale factor, probabilities -> LDS
 // The key-query convolution runs on the matrix cores with fp16 operands (the
 // logit tile and the kernel taps rounded to nearest, 11 significant bits) and
-// fp32 accumulation: one product per kernel row and output block.
+// fp32 accumulation: one product per kernel row and output block.  Before the
+// softmax the centre tap (the largest one of a kernel near the identity) is
+// exact: the logit phase also writes the logits at the output positions to a
+// centre-tap plane in LDS, and the stencil's accumulators start from the
+// centre tap times those logits in fp32.
 #pragma once
 
 #include <type_traits>
@@ -45,9 +49,20 @@ constexpr int D = 128;
 constexpr int NCB = 5;          // 16-key column blocks of the logit tile (80 columns)
 constexpr int XP = 16 * NCB;    // fp16 pitch of the logit tiles (conflict-free stencil reads)
 constexpr int KROWS = 16 * NCB; // K rows per head (key halo included)
+// Tile column 0 is key j0 - XL (XL >= the convolution's left reach, c_k <= 17):
+// the 16-key output blocks then sit at 16-byte-aligned tile columns 16t + XL,
+// and the shared logit column block of consecutive key tiles still lines up.
+constexpr int XL = 8;
+// Centre-tap plane (before the softmax): row io of the query tile, output key o
+// of the key tile at column o (o >= 8), keys 0..7 at columns 0..7 or 64..71 by
+// key-tile parity (they are produced one key tile early).  The forward keeps
+// the logits there in fp32; the gradient-preparation variant, short of LDS,
+// keeps the fp16 rounding residuals and reads the rounded part from the
+// logit tile.
+constexpr int CRP = 72;
 
 struct Layout {
-    int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, st_off, total;
+    int x_off, k_off, v_off, qh_off, p_off, al_off, fl_off, gn_off, w_off, th_off, st_off, cr_off, total;
 };
 
 // prep: the gradient-preparation variant keeps P as bf16 high part and
@@ -70,6 +85,8 @@ __host__ __device__ inline Layout layout(int cq, int ck, bool prep = false, bool
     // (maximum, 1/sum: [h][row]) and the halo rows' partial statistics
     // ([h][key block][row][maximum, sum])
     L.st_off = o; o += post ? (2 * CH * EXT_R + CH * 4 * 16 * 2) * 4 : 0;
+    // before the softmax: the centre-tap plane (fp32 logits; prep: fp16 residuals)
+    L.cr_off = o; o += post ? 0 : CH * BM * CRP * (prep ? 2 : 4);
     L.total = o;
     return L;
 }
@@ -134,8 +151,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // outside [0, T) applied (with `exact` only the padding); MASKED = false when
 // the caller knows that every entry of the block is kept.  The convolution
 // being linear, the factor log2(e)/sqrt(d) is applied to the kernel taps.
+// `xs` receives the masked logits in fp32 (for the centre-tap plane).
 template <bool MASKED>
-__device__ inline u32x2 cvt_block(int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T, bool exact, int lane)
+__device__ inline u32x2 cvt_block(int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T, bool exact, int lane,
+                                  f32x4 &xs)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
@@ -147,16 +166,47 @@ __device__ inline u32x2 cvt_block(int rb, int cb, f32x4 acc, int i0, int j0, int
     float xv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float v = f16_range(acc[r]);
+        float v = acc[r];
         if (MASKED && !all_ok) {
             const int kj = j0 - hl + e0 + r;
             const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
             v = ok ? v : 0.f;
         }
-        xv[r] = v;
+        xs[r] = v;
+        xv[r] = f16_range(v);
     }
     const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
     return __builtin_bit_cast(u32x2, h);
+}
+
+// Centre-tap plane write of an own-row logit block (tile columns 16cb +
+// 4(lane/16) + r hold output keys 16cb + 4(lane/16) - XL + r): keys 0..7 go to
+// the region of this tile's parity, keys 64..71 (the next tile's 0..7) to the
+// other parity's region, and keys -8..-1 (only in the first tile, whose block 0
+// is computed; nobody reads them) to the other region too, before block 4's
+// writes land there in the same wave's program order.  The column is plain
+// arithmetic on the lane half (no per-lane masks to keep live).  F32: the
+// logits xs; else the fp16 residuals of their rounding h.
+template <int CB, bool F32>
+__device__ inline void store_centre(void *crow, f32x4 xs, u32x2 h, int t, int lane)
+{
+    const int g4 = lane >> 4, hi = g4 >> 1, q = 4 * (g4 & 1);
+    const int cur = (t & 1) ? 64 : 0, other = 64 - cur;
+    int col;
+    if constexpr (CB == 0)
+        col = q + other + hi * (cur - other);
+    else if constexpr (CB == NCB - 1)
+        col = q + 56 + hi * (other - 56);
+    else
+        col = 16 * CB + 4 * g4 - XL;
+    if constexpr (F32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(crow) + col) = xs;
+    } else {
+        const f16x4 hh = __builtin_bit_cast(f16x4, h);
+        const f16x4 e = {(f16_t)(f16_range(xs[0]) - (float)hh[0]), (f16_t)(f16_range(xs[1]) - (float)hh[1]),
+                         (f16_t)(f16_range(xs[2]) - (float)hh[2]), (f16_t)(f16_range(xs[3]) - (float)hh[3])};
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<f16_t *>(crow) + col) = __builtin_bit_cast(u32x2, e);
+    }
 }
 
 // The same block as probabilities of the softmax before a post-softmax
@@ -263,21 +313,52 @@ __device__ inline f32x4 qk(const QFrag<D> &kf, const QFrag<D> &qf)
     return a;
 }
 
+// Accumulator start of the stencil's output block t for the lane (keys
+// 16t + 4*(lane/16) + r of its row): the centre tap (query offset 0, key
+// offset 0) times the logit itself, in fp32; the banded matrices leave that tap
+// out.  CORR = 1: the logits from the fp32 plane; CORR = 2: the fp16 logit
+// tile's value plus its fp16 residual.  par: the column of keys 0..7 of this
+// key tile (0 or 64).
+template <int CQ, int CORR>
+__device__ inline f32x4 centre_init(const f16_t *x, int rho, const void *crow, int t, int par, float c00, int lane)
+{
+    const int g4 = lane >> 4, o = 16 * t + 4 * g4;
+    // keys 0..7 (block 0, lanes 0..31) sit at the tile parity's column
+    const int col = t == 0 ? o + (1 - (g4 >> 1)) * par : o;
+    if constexpr (CORR == 1) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(crow) + col);
+        return f32x4{c00 * v[0], c00 * v[1], c00 * v[2], c00 * v[3]};
+    } else {
+        const f16x4 e = __builtin_bit_cast(f16x4, *reinterpret_cast<const u32x2 *>(
+                                                      reinterpret_cast<const f16_t *>(crow) + col));
+        // tile column o + XL: 16-byte chunk (o + XL) / 8, half (o + XL) % 8 = 4 (g4 & 1)
+        const f16x4 h = *reinterpret_cast<const f16x4 *>(x + rho * XP + 8 * xchunk<CQ>(rho, (o + XL) >> 3) +
+                                                         4 * (g4 & 1));
+        f32x4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = c00 * ((float)h[k] + (float)e[k]);
+        return r;
+    }
+}
+
 // Key-query stencil of the 16 rows of this wave (tile row rho = HALO + 16rw +
 // lane%16) over all 64 keys of the tile: output block t covers keys 16t..16t+15
-// and reads the 32-column window starting at tile column 16t.  One fp16
-// product per kernel row on the matrix cores.  out[4t + r] is
-// key 16t + 4*(lane/16) + r.  With MASK, Eq. 4's indicator: tl0 is the last
-// window column of block 0 (relative to 8*(lane/16)) whose key is not in the
-// future of the lane's output query; the blocks are then taken two at a time
-// with their masks built just before use.
-template <int CQ, bool MASK>
-__device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ], int tl0, int lane, float out[16])
+// and reads the 32-column window starting at tile column 16t (keys j0 - XL +
+// 16t ...).  One fp16 product per kernel row on the matrix cores.  out[4t + r]
+// is key 16t + 4*(lane/16) + r.  With CORR the accumulators start from the
+// centre tap's term (centre_init).  With MASK, Eq. 4's indicator: tl0
+// is the last window column of block 0 (relative to 8*(lane/16)) whose key is
+// not in the future of the lane's output query; the blocks are then taken two
+// at a time with their masks built just before use.
+template <int CQ, bool MASK, int CORR>
+__device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ], int tl0, const void *crow,
+                                 int par, float c00, int lane, float out[16])
 {
     const int g4 = lane >> 4;
     f32x4 acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t)
+        acc[t] = CORR ? centre_init<CQ, CORR>(x, rho, crow, t, par, c00, lane) : f32x4{0.f, 0.f, 0.f, 0.f};
     if (MASK) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -307,15 +388,17 @@ __device__ inline void stencil64(const f16_t *x, int rho, const f16x8 (&tf)[CQ],
 }
 
 // The 3D form's stencil (two-pass masks): both heads' logit tiles x and x2,
-// each through its own banded kernel matrices, accumulated into one output.
+// each through its own banded kernel matrices, accumulated into one output
+// that starts from the own head's (x) centre-tap term (fp32 plane).
 template <int CQ>
 __device__ inline void stencil64_pair(const f16_t *x, const f16_t *x2, int rho, const f16x8 (&tf)[CQ],
-                                      const f16x8 (&tf2)[CQ], int lane, float out[16])
+                                      const f16x8 (&tf2)[CQ], const void *crow, int par, float c00, int lane,
+                                      float out[16])
 {
     const int g4 = lane >> 4;
     f32x4 acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[t] = centre_init<CQ, 1>(x, rho, crow, t, par, c00, lane);
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
@@ -387,6 +470,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
     float *stm = reinterpret_cast<float *>(smem + lay.st_off);  // POST: [h][row] maximum (log2 domain)
     float *stil = stm + CH * EXT_R;                             // POST: [h][row] 1 / sum
+    // before the softmax: the centre-tap plane [h][row][CRP] (fp32; PREP: fp16)
+    unsigned char *crbuf = smem + lay.cr_off;
+    constexpr int CORR = POST ? 0 : (PREP ? 2 : 1);
 
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
@@ -401,7 +487,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     if constexpr (POST)
         dma_pair<false, BN>(kbuf, K, hstride, 0, T, wave, lane);
     else
-        dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);
+        dma_pair<false, KROWS>(kbuf, K, hstride, -XL, T, wave, lane);
     dma_pair<false, HALO>(qhbuf, Q, hstride, i0 - HALO, T, wave, lane);
     // this wave's Q rows of its head (rows past the end: masked in the logit tile)
     const bf16_t *qrow = Q + hs * hstride + (size_t)((i0 + 16 * rw + l16) < T ? i0 + 16 * rw + l16 : T - 1) * D + 32 * g4;
@@ -431,28 +517,41 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     wait_vm_all();
     __syncthreads();
 
+    // Before the softmax the centre tap (i' = 0, j' = 0) of head hs's own
+    // kernel is applied in fp32 to the logit itself (centre_init); the banded
+    // matrices leave it out.  After the softmax the taps act on probabilities,
+    // unscaled.
+    const float c00 =
+        POST ? 0.f : th_s[(C3D ? (hs * CH + hs) : hs) * CQ * CKP + CK / 2] * p.sc;
+    const float kap = POST ? 1.f : p.sc;
+
     // banded kernel matrices of head hs (MFMA A operands, fp16):
-    // row m = lane%16 (output key), columns k = 8*(lane/16) + s of the window
-    // (C3D: tf from source head hs, tfo from the other head, both into head hs)
+    // row m = lane%16 (output key j0 + 16t + m), columns k = 8*(lane/16) + s of
+    // the window (key j0 - XL + 16t + k), so j' = m + XL - k
+    // (C3D: tf from source head hs, tfo from the other head, both into head hs;
+    // the own centre tap is left out before the softmax)
     f16x8 tf[CQ], tfo[C3D ? CQ : 1];
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
-            const int jj = l16 + CK - 1 - (8 * g4 + s8);
-            const bool in = jj >= 0 && jj < CK;
+            const int jj = l16 + XL - (8 * g4 + s8) + CK / 2;
+            const bool in = jj >= 0 && jj < CK && (POST || ip != 0 || jj != CK / 2);
             if constexpr (C3D) {
                 const float t = in ? th_s[((hs * CH + hs) * CQ + ip) * CKP + jj] : 0.f;
-                const float u = in ? th_s[((hs * CH + (1 - hs)) * CQ + ip) * CKP + jj] : 0.f;
-                tf[ip][s8] = (f16_t)f16_range(t * p.sc);
-                tfo[ip][s8] = (f16_t)f16_range(u * p.sc);
+                const bool in2 = jj >= 0 && jj < CK;  // the other head's centre tap stays
+                const float u = in2 ? th_s[((hs * CH + (1 - hs)) * CQ + ip) * CKP + jj] : 0.f;
+                tf[ip][s8] = (f16_t)f16_range(t * kap);
+                tfo[ip][s8] = (f16_t)f16_range(u * kap);
             } else {
                 const float t = in ? th_s[(hs * CQ + ip) * CKP + jj] : 0.f;
-                tf[ip][s8] = (f16_t)f16_range(POST ? t : t * p.sc);  // POST: on probabilities, unscaled
+                tf[ip][s8] = (f16_t)f16_range(t * kap);
             }
         }
 
     const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
+    // its row of the centre-tap plane (before the softmax)
+    void *crow = crbuf + (size_t)(hs * BM + io) * CRP * (PREP ? 2 : 4);
     const int qabs = i0 + io;
     const int rho = HALO + io;
     const int dbase = 64 * hs;
@@ -524,7 +623,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             hpart[((hh * 4 + hcb) * 16 + l16) * 2 + 1] = lh;
         }
         __syncthreads();  // pass-1 reads of the K buffers and the partial statistics are done
-        dma_pair<false, KROWS>(kbuf, K, hstride, -p.hl, T, wave, lane);  // pass 2's first K tiles
+        dma_pair<false, KROWS>(kbuf, K, hstride, -XL, T, wave, lane);  // pass 2's first K tiles
         if (tid < CH * 16) {
             // halo rows: the four key blocks of each
             const int h = tid >> 4, r = tid & 15;
@@ -560,7 +659,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     // Two phases per key tile t (one more step drains the last P.V):
     //   A(t) | K(t), V(t-1), P(t-1) in LDS | logit tiles of t; rescale and P.V of t-1
     //   B(t) | K(t+1), V(t) start loading  | stencil and softmax of t -> P(t)
-    for (int t = 0; t <= qt + 1; ++t) {
+    // The first key tile (no shared column block, no P.V yet) is its own copy
+    // of the step, so that the loop holds only the steady-state forms.
+    auto step = [&](const int t, auto first_t) {
+        constexpr bool FIRST = decltype(first_t)::value;
         const int j0 = t * BN;
         const bool cur = t <= qt;
         barrier_lds();  // A: K(t), V(t-1) in LDS (each wave waited for its DMA); P(t-1) published
@@ -569,7 +671,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         // share of the halo blocks; the fragments of the next block are read
         // before the products of the current one
         // REUSE (every key tile after the first): column block 0 of the tile
-        // (keys j0 - hl .. j0 - hl + 15) is column block 4 of the previous
+        // (keys j0 - XL .. j0 - XL + 15) is column block 4 of the previous
         // tile, copied into place before the logit products; only blocks 1..4
         // are computed, and the eight halo blocks (both heads) are one per wave
         auto logits = [&](auto masked, auto reuse) {
@@ -595,10 +697,19 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 }
                 // raw logits, or (POST) probabilities with the row's statistics
                 u32x2 v;
-                if constexpr (POST)
-                    v = cvt_prob<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, pm_o, pil_o, p.sc, lane);
-                else
-                    v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, p.hl, T, EXACT, lane);
+                if constexpr (POST) {
+                    v = cvt_prob<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, XL, T, pm_o, pil_o, p.sc, lane);
+                } else {
+                    f32x4 xs;
+                    v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, XL, T, EXACT, lane, xs);
+                    if (cb == 0)
+                        store_centre<0, !PREP>(crow, xs, v, t, lane);
+                    else if (cb == NCB - 1)
+                        store_centre<NCB - 1, !PREP>(crow, xs, v, t, lane);
+                    else
+                        store_centre<1, !PREP>(reinterpret_cast<unsigned char *>(crow) + 16 * (cb - 1) * (PREP ? 2 : 4),
+                                               xs, v, t, lane);
+                }
                 if ((cb - CB0) & 1)
                     store_pair<CQ>(xo, 1 + rw, cb - 1, prev, xo, 1 + rw, cb, v, lane);
                 else
@@ -610,11 +721,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                 // last own block
                 kload(hq, qhbuf + fresh((hh * HALO + l16) * D), 0);
                 u32x2 v;
+                f32x4 nores;  // halo rows: not in the centre-tap plane
                 if constexpr (POST)
-                    v = cvt_prob<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, R ? pm_h : stm[hh * EXT_R + l16],
+                    v = cvt_prob<M>(0, hcb, qk(hk, hq), i0, j0, XL, T, R ? pm_h : stm[hh * EXT_R + l16],
                                     R ? pil_h : stil[hh * EXT_R + l16], p.sc, lane);
                 else
-                    v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                    v = cvt_block<M>(0, hcb, qk(hk, hq), i0, j0, XL, T, EXACT, lane, nores);
                 f16_t *xhh = xbuf + hh * EXT_R * XP;
                 if (R) {
                     store_pair<CQ>(xhh, 0, hcb, v, xhh, 0, hcb, v, lane, true);
@@ -626,10 +738,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                         kload(hk, kbuf + fresh((h * KROWS + 16 * hc + l16) * D), 0);
                         u32x2 v2;
                         if constexpr (POST)
-                            v2 = cvt_prob<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, stm[h * EXT_R + l16],
+                            v2 = cvt_prob<M>(0, hc, qk(hk, hq), i0, j0, XL, T, stm[h * EXT_R + l16],
                                              stil[h * EXT_R + l16], p.sc, lane);
                         else
-                            v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, p.hl, T, EXACT, lane);
+                            v2 = cvt_block<M>(0, hc, qk(hk, hq), i0, j0, XL, T, EXACT, lane, nores);
                         f16_t *xh2 = xbuf + h * EXT_R * XP;
                         store_pair<CQ>(xh2, 0, hc, v2, xh2, 0, hc, v2, lane, true);
                     }
@@ -640,9 +752,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         };
         // key tiles whose logit blocks (halo rows included) are all inside
         // [0, T) and, with Mask_0, all in the past of every row: no masks
-        const int kfirst = j0 - p.hl, klast = j0 - p.hl + 16 * NCB - 1;
+        const int kfirst = j0 - XL, klast = j0 - XL + 16 * NCB - 1;
         const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
-        if (cur && t > 0) {
+        if (!FIRST && cur) {
             // column block 4 of tile t-1 is column block 0 of tile t: 16-byte
             // chunks 8, 9 -> 0, 1 (which keeps the row swizzle), each wave for the
             // rows whose block 4 it writes next (own rows; halo rows: the waves of
@@ -658,7 +770,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             }
         }
         if (cur) {
-            if (t > 0) {
+            if constexpr (!FIRST) {
                 if (inner)
                     logits(std::false_type{}, std::true_type{});
                 else
@@ -670,7 +782,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                     logits(std::true_type{}, std::false_type{});
             }
         }
-        if (t >= 1) {
+        if constexpr (!FIRST) {
             // P.V of tile t - 1: bring the accumulators into the frame of its maxima first
             const int tp = t - 1;
 #pragma unroll
@@ -720,17 +832,18 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             }
         }
         barrier_lds();  // B: logit tiles of t published; K, V and probability buffers free
-        if (t < qt) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - p.hl, T, wave, lane);  // K(t+1)
+        if (t < qt) dma_pair<false, KROWS>(kbuf, K, hstride, j0 + BN - XL, T, wave, lane);  // K(t+1)
         if (cur) dma_pair<true, BN>(vbuf, V, hstride, j0, T, wave, lane);                      // V(t)
 
         if (cur) {
             float c[16];
+            const int par = (t & 1) ? 64 : 0;  // this key tile's column of keys 0..7 in the centre-tap plane
             if constexpr (C3D)
-                stencil64_pair<CQ>(xo, xbuf + (1 - hs) * EXT_R * XP, rho, tf, tfo, lane, c);
-            else if (EXACT && j0 - p.hl + 79 > i0 + 16 * rw)
-                stencil64<CQ, true>(xo, rho, tf, qabs - (j0 - p.hl + 8 * g4), lane, c);
+                stencil64_pair<CQ>(xo, xbuf + (1 - hs) * EXT_R * XP, rho, tf, tfo, crow, par, c00, lane, c);
+            else if (EXACT && j0 - XL + 79 > i0 + 16 * rw)
+                stencil64<CQ, true, CORR>(xo, rho, tf, qabs - (j0 - XL + 8 * g4), crow, par, c00, lane, c);
             else
-                stencil64<CQ, false>(xo, rho, tf, 0, lane, c);
+                stencil64<CQ, false, CORR>(xo, rho, tf, 0, crow, par, c00, lane, c);
             if constexpr (POST) {
                 // Mask_0 after the convolution (only the diagonal tile has keys in
                 // the future of its rows); no renormalisation
@@ -787,7 +900,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             }
             wait_vm_all();  // K(t+1) and V(t) have landed
         }
-    }
+        };
+    step(0, std::true_type{});
+    for (int t = 1; t <= qt + 1; ++t) step(t, std::false_type{});
 
     // row sums l_b -> 1/l_b in al (after every wave's last P.V read of al);
     // POST: the probabilities were normalised before the convolution

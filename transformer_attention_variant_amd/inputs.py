@@ -53,6 +53,11 @@ class MTAConfig:
     layer: int = 1
     needles: int = 0
     needle_queries: int = 32
+    needle_scale: float = 3.0  # needle keys are needle_scale x the direction u
+    # False: a needle key is replaced by needle_scale * u (all needles of a row
+    # give the same logit); True: needle_scale * u is added to the key's own
+    # draw, so the needles of a row compete with logits a few units apart
+    needle_on_key: bool = False
     seed: int = 0
     gn_eps: float = 1e-5
     gn_random: bool = False
@@ -197,15 +202,19 @@ def generate(cfg: MTAConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
 
     if cfg.needles:
         # Multi-needle retrieval stand-in: per batch row, `needles` key
-        # positions (uniform without replacement, in random order) carry 3x a
-        # per-head direction u, and the last `needle_queries` queries carry u.
+        # positions (uniform without replacement, in random order) carry
+        # needle_scale (3 in the workloads) times a per-head direction u, and
+        # the last `needle_queries` queries carry u.
         nq = min(cfg.needle_queries, cfg.T)
         span = max(cfg.T - nq, cfg.needles)
         for b in range(cfg.B):
             pos = torch.randperm(span, generator=g)[: cfg.needles]
             for h in range(cfg.H):
                 u = torch.randn((cfg.d,), generator=g) * cfg.qkv_std
-                k[b, h, pos] = 3.0 * u
+                if cfg.needle_on_key:
+                    k[b, h, pos] += cfg.needle_scale * u
+                else:
+                    k[b, h, pos] = cfg.needle_scale * u
                 q[b, h, cfg.T - nq:] += u
 
     # kernels of the 3D and repeated forms, drawn after everything else so that

@@ -83,6 +83,9 @@ extern "C" {
 #define MTA_ERR_LAUNCH -7        /* the kernel launch reported an error        */
 #define MTA_ERR_BAD_VALUE -8     /* gn_eps <= 0 or not finite, depth_scale not
                                     finite                                      */
+#define MTA_ERR_SCRATCH -9       /* mta_backward_noalloc: the problem needs more
+                                    workspace than the device scratch array
+                                    holds (mta_backward_scratch_bytes)          */
 
 /* Problem description (all fields read synchronously). */
 typedef struct mta_config {
@@ -225,6 +228,30 @@ int mta_backward(const void *q, const void *k, const void *v, const float *theta
 
 /* Bytes of workspace mta_backward needs for cfg (0 if cfg is invalid). */
 size_t mta_backward_workspace_size(const mta_config *cfg);
+
+/*
+ * mta_backward_noalloc — mta_backward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving or training loops,
+ * harnesses that forbid hipMalloc): the same computation and arguments without
+ * `workspace` / `workspace_bytes`.  Its workspace is a device array inside the
+ * library, mta_backward_scratch_bytes() bytes (72 MiB: the 4K-context
+ * workload's 65.5 MiB fits), one per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  A problem
+ * whose mta_backward_workspace_size exceeds the array returns MTA_ERR_SCRATCH
+ * before any device work.  Every call on a GPU uses that GPU's one array:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs clearing between
+ * calls (the kernels write every workspace entry before reading it).
+ */
+int mta_backward_noalloc(const void *q, const void *k, const void *v, const float *theta_kq,
+                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
+                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
+                         void *stream);
+
+/* Size in bytes of mta_backward_noalloc's device scratch array. */
+size_t mta_backward_scratch_bytes(void);
 
 /* Host-only: the name of the kernel mta_forward / mta_forward_gated launch for
  * this configuration (a static string, e.g. "mta_fwd_v3 (one pass,

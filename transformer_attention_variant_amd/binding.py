@@ -20,10 +20,11 @@ LIB_PATH = os.path.join(HERE, "libmta.so")
 MTA_OK = 0
 STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA_ERR_BAD_PLACEMENT",
           -4: "MTA_ERR_BAD_DTYPE", -5: "MTA_ERR_MISALIGNED", -6: "MTA_ERR_UNSUPPORTED",
-          -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE"}
+          -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE", -9: "MTA_ERR_SCRATCH"}
 # names declared in include/mta.h
 EXPORTS = ("mta_forward", "mta_forward_gated", "mta_forward_layer", "mta_backward", "mta_backward_workspace_size",
-           "mta_check_config", "mta_kernel_name", "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
+           "mta_backward_noalloc", "mta_backward_scratch_bytes", "mta_check_config", "mta_kernel_name",
+           "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
 LAYER_KERNELS = ("kq_pre", "head_pre", "conv3d", "head_post", "kq_post", "head_post2")
 
 
@@ -84,6 +85,10 @@ def load(path: Optional[str] = None):
     lib.mta_backward.restype = ctypes.c_int
     lib.mta_backward_workspace_size.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_backward_workspace_size.restype = ctypes.c_size_t
+    lib.mta_backward_noalloc.argtypes = [vp] * 9 + [ctypes.POINTER(MtaConfig)] + [vp] * 9
+    lib.mta_backward_noalloc.restype = ctypes.c_int
+    lib.mta_backward_scratch_bytes.argtypes = []
+    lib.mta_backward_scratch_bytes.restype = ctypes.c_size_t
     lib.mta_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_kernel_name.restype = ctypes.c_char_p
     lib.mta_abi_version.argtypes = []
@@ -209,12 +214,14 @@ GRAD_NAMES = ("q", "k", "v", "theta_kq", "theta_head", "gn_w", "gn_b", "gate")
 
 def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: int, c_h: int,
              kq_place: int = I.PRE, gn_eps: float = 1e-5, depth_scale: float = 1.0,
-             gate: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> Dict:
+             gate: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
+             noalloc: bool = False) -> Dict:
     """Gradients of ``forward`` (head mix after the softmax) through
     ``mta_backward``: returns float32 CUDA tensors keyed q, k, v, theta_kq,
     theta_head, gn_w, gn_b (and gate).  ``dout`` is dL/dout in the input dtype.
     Allocates the outputs and the workspace with torch (the library allocates
-    nothing)."""
+    nothing).  With ``noalloc`` the call goes to ``mta_backward_noalloc``, whose
+    workspace is the library's own device scratch array (no workspace tensor)."""
     lib = load()
     B, H, T, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
@@ -239,22 +246,26 @@ def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: 
              "gn_b": torch.empty(gn_b.shape, **f32)}
         if gate is not None:
             g["gate"] = torch.empty(gate.shape, **f32)
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        ws = None if noalloc else torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     ptr = lambda t: t.data_ptr() if t is not None else None
-    rc = lib.mta_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(), theta_head.data_ptr(),
-                          gn_w.data_ptr(), gn_b.data_ptr(), ptr(gate), dout.data_ptr(), ctypes.byref(cfg),
-                          g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["theta_kq"].data_ptr(),
-                          g["theta_head"].data_ptr(), g["gn_w"].data_ptr(), g["gn_b"].data_ptr(),
-                          ptr(g.get("gate")), ws.data_ptr(), ws.numel(), ctypes.c_void_p(s.cuda_stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), theta_kq.data_ptr(), theta_head.data_ptr(),
+            gn_w.data_ptr(), gn_b.data_ptr(), ptr(gate), dout.data_ptr(), ctypes.byref(cfg),
+            g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["theta_kq"].data_ptr(),
+            g["theta_head"].data_ptr(), g["gn_w"].data_ptr(), g["gn_b"].data_ptr(), ptr(g.get("gate")))
+    if noalloc:
+        rc = lib.mta_backward_noalloc(*args, ctypes.c_void_p(s.cuda_stream))
+    else:
+        rc = lib.mta_backward(*args, ws.data_ptr(), ws.numel(), ctypes.c_void_p(s.cuda_stream))
     if rc != MTA_OK:
         raise MTAError(rc, status_string(rc))
     return g
 
 
-def backward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], dout: torch.Tensor, stream=None) -> Dict:
+def backward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], dout: torch.Tensor, stream=None,
+                 noalloc: bool = False) -> Dict:
     return backward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"],
                     dout, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, gn_eps=cfg.gn_eps,
-                    depth_scale=cfg.depth_scale, gate=inp.get("gate"), stream=stream)
+                    depth_scale=cfg.depth_scale, gate=inp.get("gate"), stream=stream, noalloc=noalloc)
 
 
 def forward_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor,

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <cstring>
+#include <mutex>
 
 #include "mta.h"
 #include "mta_fwd_v2.h"
@@ -71,6 +72,7 @@ const char *mta_status_string(int s)
     case MTA_ERR_UNSUPPORTED: return "configuration outside the library's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
     case MTA_ERR_LAUNCH: return "kernel launch failed";
     case MTA_ERR_BAD_VALUE: return "gn_eps must be finite and > 0, depth_scale finite";
+    case MTA_ERR_SCRATCH: return "the problem needs more workspace than the library's device scratch array holds";
     default: return "unknown status";
     }
 }
@@ -447,10 +449,83 @@ size_t mta_backward_workspace_size(const mta_config *cfg)
     return 3 * align256(rows * 4) + planes * align256(rows * cfg->head_dim * el);
 }
 
+static int backward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
+                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
+                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 int mta_backward(const void *q, const void *k, const void *v, const float *theta_kq, const float *theta_head,
                  const float *gn_w, const float *gn_b, const float *gate, const void *dout,
                  const mta_config *cfg, float *dq, float *dk, float *dv, float *dtheta_kq, float *dtheta_head,
                  float *dgn_w, float *dgn_b, float *dgate, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return backward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, gate, dout, cfg, dq, dk, dv, dtheta_kq,
+                         dtheta_head, dgn_w, dgn_b, dgate, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The backward without a caller workspace: the workspace is a file-scope device
+// array, one per GPU the library runs on, held until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address): its address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+
+namespace {
+
+constexpr size_t SCRATCH_BYTES = (size_t)72 << 20;
+__device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[MAX_DEVICES] = {};
+
+// The scratch array's device address on the current device (NULL on failure).
+void *scratch_on_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mta_backward_scratch_bytes(void) { return SCRATCH_BYTES; }
+
+int mta_backward_noalloc(const void *q, const void *k, const void *v, const float *theta_kq,
+                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
+                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
+                         void *stream)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    if (mta_backward_workspace_size(cfg) > SCRATCH_BYTES) return MTA_ERR_SCRATCH;
+    void *ws = scratch_on_current_device();
+    if (!ws) return MTA_ERR_LAUNCH;
+    return backward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, gate, dout, cfg, dq, dk, dv, dtheta_kq,
+                         dtheta_head, dgn_w, dgn_b, dgate, ws, SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+static int backward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
+                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
+                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
+                         void *workspace, size_t workspace_bytes, void *stream)
 {
     const int vs = validate(cfg);
     if (vs != MTA_OK) return vs;

@@ -38,9 +38,8 @@ FLUSH_MIB = 512
 # the HIP sources each forward kernel is built from (its header chain, its
 # instantiation unit and the launch helpers)
 KERNEL_SOURCES = {
-    "mta_fwd_v4": ["mta_fwd_v4.h", "mta_fwd_v3.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v4.hip",
+    "mta_fwd_v4": ["mta_fwd_v4.h", "mta_tiles.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v4.hip",
                    "mta_launch.h"],
-    "mta_fwd_v3": ["mta_fwd_v3.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v3.hip", "mta_launch.h"],
     "mta_fwd_v2": ["mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v2.hip", "mta_inst_v2.inc",
                    "mta_inst_v2_exact.hip", "mta_launch.h"],
     "mta_fwd_kernel": ["mta_fwd_kernel.h", "mta_inst.inc", "mta_inst_bf16.hip", "mta_inst_f32.hip",
@@ -244,6 +243,7 @@ def main():
             "frac": round(alu_flops / t / 1e12 / PEAK_VALU_TFLOPS, 4),
             "work": "key-query stencil 2*c_q*c_k + head mix 2*c_h FLOP per causal logit",
         }
+    roof.update(traffic=traffic, kernel=kname)
     mfma = {
         "achieved": round(fl["contraction"] / t / 1e12, 2),
         "peak": mfma_peak,

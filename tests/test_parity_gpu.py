@@ -89,6 +89,12 @@ def _small_cases():
                              kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02,
                              layer=4, needles=6, needle_scale=9.0, needle_on_key=True,
                              seed=730 + cq + T + kq))
+        # the same through single-head groups (head pairs; odd H: the general
+        # kernel) and groups of four (the two-pass kernel)
+        for (ch, H, cq, ck) in ((1, 2, 6, 11), (1, 3, 6, 11), (4, 4, 6, 11), (4, 4, 8, 15)):
+            c.append(I.small(f"hot_bf16_ch{ch}_H{H}_{cq}x{ck}_kq{kq}", B=1, H=H, T=256, d=128, c_q=cq, c_k=ck,
+                             c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02,
+                             layer=4, needles=6, needle_scale=9.0, needle_on_key=True, seed=760 + ch + H + kq))
     # key-query convolution with Eq. 4's exact indicator: fast and runtime-sized
     # stencils, odd and even c_k, pre-softmax head mix, c_h = 4, both dtypes
     E = I.PRE_EXACT

@@ -140,13 +140,25 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 else pl.name = "mta_fwd_v4 (one pass, head-split waves, pre-softmax head mix as a 3D convolution, fp16 matrix-core stencil)";
             }
         }
-        if (!fn) fn = mta::find_launch_v3(d, ch, cq, ck, post, exact, hpre);
-        if (fn && !pl.name) {
-            p.ncb = ncb0 < 5 ? 5 : ncb0;
-            p.pitch = p.ncb * 16 + 4;
-            lds = (size_t)mta::v3::layout(d, ch, cq, ck, p.ncb).total;
-            if (lds > LDS_MAX) fn = nullptr;
-            else pl.name = "mta_fwd_v3 (one pass, matrix-core stencil)";
+        if (!fn && ch == 1 && !post && cfg->heads % 2 == 0) {
+            // single-head groups, two per workgroup: the head-split kernel with
+            // the 1x1 mix of each head (the grid counts head pairs)
+            fn = mta::find_launch_v4_pairs(d, cq, ck, exact);
+            if (fn) {
+                p.ncb = 5;
+                p.pitch = p.ncb * 16 + 4;
+                p.G = cfg->heads / 2;
+                p.units = cfg->batch * p.G;
+                pl.grid = p.n_qt * p.units;
+                lds = (size_t)mta::v4::layout(cq, ck, false, false).total;
+                if (lds > LDS_MAX) fn = nullptr;
+                else pl.name = "mta_fwd_v4 (one pass, head-split waves, head pairs of single-head groups, fp16 matrix-core stencil)";
+            }
+            if (!fn) {
+                p.G = cfg->heads / ch;
+                p.units = cfg->batch * p.G;
+                pl.grid = p.n_qt * p.units;
+            }
         }
         // else two passes: stencil on the matrix cores first, then the fp32 VALU stencil
         for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {

@@ -51,8 +51,13 @@ __device__ inline int frag_base(int lane)
 }
 
 struct Layout {
-    int s_off, k_off, q_off, v_off, p_off, st_off, xs_off, th_off, w_off, gn_off, tf_off, total;
+    int s_off, k_off, q_off, v_off, p_off, st_off, xs_off, th_off, w_off, gn_off, tf_off, cr_off, total;
 };
+
+// Centre-tap correction plane of the matrix-core stencil before the softmax:
+// fp16 [row of the query tile][key of the key tile], pitch CRP2 (34 banks per
+// row: the stencil's 8-byte reads of 16 rows never share a bank).
+constexpr int CRP2 = 68;
 
 // fp16 pitch of the logit tile of the matrix-core stencil: a multiple of 8
 // elements whose 16-byte chunk count is 2 mod 4, so that the stencil's
@@ -79,6 +84,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb,
     L.w_off = o;  o += ((CH * CH + 3) & ~3) * 4;
     L.gn_off = o; o += 2 * CH * BM * 4;                     // GroupNorm partial sums per d half
     L.tf_off = o; o += ms ? CH * cq * 64 * 16 : 0;          // banded kernel matrices as MFMA A operands (fp16)
+    L.cr_off = o; o += (ms && !post) ? BM * CRP2 * 2 : 0;   // centre-tap corrections (fp16)
     L.total = o;
     return L;
 }
@@ -213,9 +219,14 @@ __device__ inline float f16_clamp(float x) { return __builtin_amdgcn_fmed3f(x, -
 // Store a 16x16 logit block as fp16 (Mask_0 + zero padding applied; with
 // `exact` only the zero padding, as in store_block); MODE PROB stores
 // probabilities exp2(x - m_row) / l_row instead.
+// With `cr` (before the softmax, own rows only): the centre tap's correction
+// c00 x - c00h fp16(x) of each stored logit (c00: the centre tap, c00h: its
+// fp16 value in the banded matrices) goes to the correction plane at its
+// output key, so that the stencil's centre product becomes exact.
 template <int MODE>
 __device__ inline void store_block_x(f16_t *x16, int ph, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
-                                     float sc, const float *st_m, const float *st_il, int exact, int lane)
+                                     float sc, const float *st_m, const float *st_il, int exact, int lane,
+                                     f16_t *cr = nullptr, float c00 = 0.f, float c00h = 0.f)
 {
     const int rho = rb * 16 + (lane & 15);
     const int e0 = cb * 16 + 4 * (lane >> 4);
@@ -240,10 +251,19 @@ __device__ inline void store_block_x(f16_t *x16, int ph, int rb, int cb, f32x4 a
             const bool ok = (kj >= 0) && (kj <= kmax) && (qi >= 0) && (qi < T);
             x = ok ? x : 0.f;
         }
-        xv[r] = f16_clamp(x);
+        xv[r] = x;
     }
-    const f16x4 h = {(f16_t)xv[0], (f16_t)xv[1], (f16_t)xv[2], (f16_t)xv[3]};
+    const f16x4 h = {(f16_t)f16_clamp(xv[0]), (f16_t)f16_clamp(xv[1]), (f16_t)f16_clamp(xv[2]),
+                     (f16_t)f16_clamp(xv[3])};
     *reinterpret_cast<f16x4 *>(x16 + rho * ph + e0) = h;
+    if (MODE == RAW && cr && rb > 0) {
+        f16_t *crow = cr + (rho - HALO) * CRP2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = e0 + r - hl;  // output key of the entry
+            if (o >= 0 && o < BN) crow[o] = (f16_t)__builtin_fmaf(c00, xv[r], -c00h * (float)h[r]);
+        }
+    }
 }
 
 // Banded kernel matrices of the group's heads as MFMA A operands:
@@ -316,12 +336,21 @@ __device__ inline f16x8 and_mask(f16x8 v, const uint32_t (&w)[4])
 
 // Two 16-key output blocks (keys 32kh + 16t + 4*(lane/16) + r, t = 0,1) of row
 // 16rw + lane%16, kernel fragments th(ip).  out[4t + r].
+// With `cr`, the accumulators start from the centre-tap corrections of the
+// lane's row (centre product exact; see store_block_x).
 template <int CQ, bool MASK, typename TH>
 __device__ inline void stencil_mfma_f(const f16_t *x, int ph, int rho, int kh, TH th, const ColMask &cm, int lane,
-                                      float out[8])
+                                      float out[8], const f16_t *cr = nullptr)
 {
     const int g4 = lane >> 4;
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    if (cr) {
+        const f16_t *crow = cr + (rho - HALO) * CRP2 + 32 * kh + 4 * g4;
+        const f16x4 c0 = *reinterpret_cast<const f16x4 *>(crow);
+        const f16x4 c1 = *reinterpret_cast<const f16x4 *>(crow + 16);
+        a0 = f32x4{(float)c0[0], (float)c0[1], (float)c0[2], (float)c0[3]};
+        a1 = f32x4{(float)c1[0], (float)c1[1], (float)c1[2], (float)c1[3]};
+    }
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip) {
         const int off = (rho - ip) * ph + 32 * kh + 8 * g4;
@@ -345,17 +374,17 @@ __device__ inline void stencil_mfma_f(const f16_t *x, int ph, int rho, int kh, T
 // kernel fragments in registers
 template <int CQ, bool MASK>
 __device__ inline void stencil_mfma_reg(const f16_t *x, int ph, int rho, int kh, const ThetaFrags<CQ> &tfr,
-                                        const ColMask &cm, int lane, float out[8])
+                                        const ColMask &cm, int lane, float out[8], const f16_t *cr = nullptr)
 {
-    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tfr.f[ip]; }, cm, lane, out);
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tfr.f[ip]; }, cm, lane, out, cr);
 }
 
 // kernel fragments read from LDS (tf of one head)
 template <int CQ, bool MASK>
 __device__ inline void stencil_mfma(const f16_t *x, int ph, int rho, int kh, const f16x8 *tf, const ColMask &cm,
-                                    int lane, float out[8])
+                                    int lane, float out[8], const f16_t *cr = nullptr)
 {
-    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tf[ip * 64 + lane]; }, cm, lane, out);
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tf[ip * 64 + lane]; }, cm, lane, out, cr);
 }
 
 // ---------------------------------------------------------------------------
@@ -365,7 +394,8 @@ __device__ inline void stencil_mfma(const f16_t *x, int ph, int rho, int kh, con
 template <int D, int MODE, bool HL, int NCB, bool EX>
 __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, const bf16_t *kbuf,
                                       const Params &p, int i0, int j0, const float *st_m, const float *st_il,
-                                      int rw, int kh, int lane)
+                                      int rw, int kh, int lane, f16_t *cr = nullptr, float c00 = 0.f,
+                                      float c00h = 0.f)
 {
     const int l16 = lane & 15, dq = frag_base<D>(lane);
     f16_t *x16 = reinterpret_cast<f16_t *>(sbuf);
@@ -382,7 +412,8 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qf);
         if (HL)
-            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
+            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane, cr, c00,
+                                c00h);
         else
             store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, st_m, st_il, EX, lane);
     }
@@ -409,7 +440,7 @@ __device__ inline void logit_tile_lds(float *sbuf, int ph, const bf16_t *qbuf, c
 template <int D, int MODE, bool HL, int NCB, bool EX>
 __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown, const QFrag<D> &qhalo,
                                        const bf16_t *kbuf, const Params &p, int i0, int j0, int rw, int kh,
-                                       int lane)
+                                       int lane, f16_t *cr = nullptr, float c00 = 0.f, float c00h = 0.f)
 {
     const int l16 = lane & 15, dq = frag_base<D>(lane);
     f16_t *x16 = reinterpret_cast<f16_t *>(sbuf);
@@ -421,7 +452,8 @@ __device__ inline void logit_tile_regq(float *sbuf, int ph, const QFrag<D> &qown
         for (int t = 0; t < D / 32; ++t) kf.x[t] = *reinterpret_cast<const bf16x8 *>(kr + 16 * t);
         const f32x4 acc = qk_mfma<D>(kf, qown);
         if (HL)
-            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
+            store_block_x<MODE>(x16, ph, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane, cr,
+                                c00, c00h);
         else
             store_block<MODE>(sbuf, p.pitch, 1 + rw, cb, acc, i0, j0, p.hl, p.T, p.sc, nullptr, nullptr, EX, lane);
     }
@@ -574,6 +606,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
     float *w_s = reinterpret_cast<float *>(smem + lay.w_off);
     float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);  // [kh][a][row]
     f16x8 *tf = reinterpret_cast<f16x8 *>(smem + lay.tf_off);
+    // before the softmax with the matrix-core stencil: centre-tap corrections
+    f16_t *cr = (MS && !KQ_POST) ? reinterpret_cast<f16_t *>(smem + lay.cr_off) : nullptr;
 
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
@@ -641,7 +675,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 load_theta_frags<MS ? CQ : 1>(tfr, tf + a * CQ * 64, lane);
             }
             if (!KQ_POST && MS)
-                logit_tile_regq<D, RAW, true, NCB, EXACT>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
+                logit_tile_regq<D, RAW, true, NCB, EXACT>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane, cr,
+                                                          th_s[a * CQ * CKP + CK / 2],
+                                                          (float)(f16_t)f16_clamp(th_s[a * CQ * CKP + CK / 2]));
             else if (MS)
                 logit_tile_regq<D, RAW, false, NCB, false>(sbuf, ph, qown, qhal, kbuf, p, i0, j0, rw, kh, lane);
             else
@@ -655,9 +691,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 if (MS) {
                     // wave-uniform: can any of the wave's window columns pass its first row?
                     if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                        stencil_mfma_reg<MS ? CQ : 1, true>(x16, ph, rho, kh, tfr, col_mask(tl), lane, c);
+                        stencil_mfma_reg<MS ? CQ : 1, true>(x16, ph, rho, kh, tfr, col_mask(tl), lane, c, cr);
                     else
-                        stencil_mfma_reg<MS ? CQ : 1, false>(x16, ph, rho, kh, tfr, ColMask{}, lane, c);
+                        stencil_mfma_reg<MS ? CQ : 1, false>(x16, ph, rho, kh, tfr, ColMask{}, lane, c, cr);
                 } else {
                     stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
                 }
@@ -779,7 +815,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                                                         st_il + a * EXT_R, rw, kh, lane);
             else
                 logit_tile_lds<D, RAW, MS, NCB, EXACT>(sbuf, ph, qbuf, kbuf, p, i0, j0, nullptr, nullptr, rw, kh,
-                                                       lane);
+                                                       lane, cr, th_s[a * CQ * CKP + CK / 2],
+                                                       (float)(f16_t)f16_clamp(th_s[a * CQ * CKP + CK / 2]));
             if (kt > 0) pv(a, acc[a]);
             __syncthreads();
 
@@ -787,9 +824,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
             if (MS) {
                 if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                    stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + a * CQ * 64, col_mask(tl), lane, c);
+                    stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + a * CQ * 64, col_mask(tl), lane, c, cr);
                 else
-                    stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + a * CQ * 64, ColMask{}, lane, c);
+                    stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + a * CQ * 64, ColMask{}, lane, c, cr);
             } else {
                 stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
             }

@@ -5,9 +5,15 @@
 // Attention — Paper Graph", section 3.4, "Key-Query Convolution", "Head Mixing
 // Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").
 //
-// Same online-softmax formulation as mta_fwd_v3.h (accumulators
-// U_{b,a} = sum_j exp(C^b_j - m_b) V^a_j, O^a = sum_b w_ab U_{b,a} / l_b), with
-// the work of a key tile split by head instead of by key half:
+// The two-pass kernels walk the key tiles twice: once for each row's softmax
+// statistics, once for the probabilities.  Here the statistics are kept online
+// instead.  Post-softmax mixing combines NORMALISED maps of different heads,
+// O^a = sum_b w_ab P^b V^a with P^b = exp(C^b - m_b) / l_b, and l_b is only
+// known at the end, so the kernel keeps one accumulator per (source head b,
+// output head a), U_{b,a} = sum_j exp(C^b_j - m_b) V^a_j (rescaled when m_b
+// grows), and forms O^a = sum_b w_ab U_{b,a} / l_b in the epilogue: c_h^2
+// accumulators and c_h times the P.V work instead of a whole first pass.  The
+// work of a key tile is split by head:
 //   wave (rw, s), rw = 0..3, s = 0..1, owns query rows 16rw.. of the tile.
 //   In the logit product and the stencil it works on head s only, over all 64
 //   keys of the tile, so the row maxima need no exchange between waves and
@@ -31,18 +37,18 @@
 
 #include <type_traits>
 
-#include "mta_fwd_v3.h"
+#include "mta_tiles.h"
 
 namespace mta {
 namespace v4 {
 
 using v2::NT;
 using v2::ColMask;
-using v3::swz_k;
-using v3::swz_v;
-using v3::barrier_lds;
-using v3::vread_tr4;
-using v3::lds_void_p;
+using tile::swz_k;
+using tile::swz_v;
+using tile::barrier_lds;
+using tile::vread_tr4;
+using tile::lds_void_p;
 
 constexpr int CH = 2;
 constexpr int D = 128;
@@ -438,12 +444,18 @@ struct PrepArgs {
 // a's stencil sums over the logit tiles of both heads b, and only the P.V
 // products of head a's probabilities with V^a are formed.  With p.head_pre the
 // kernel is built from the per-head kernels and the pre-softmax head mix.
-template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false>
+// NOMIX: head groups of one head (c_h = 1), taken two at a time: the two
+// heads of the workgroup are neighbouring single-head groups, so only the
+// U[a][a] products are formed and each output head is its own head's mixed map
+// (the 1x1 mixing weight w_h, p.wmix[h]).  p.G and p.units count head pairs.
+template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false, bool NOMIX = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     static_assert(!(POST && (EXACT || PREP)), "post-softmax form: two-pass masks, forward only");
     static_assert(!(C3D && (EXACT || PREP || POST)), "3D form: two-pass masks, forward only");
+    static_assert(!(NOMIX && (C3D || PREP)), "single-head groups: the forward of the per-head kernels");
+    constexpr bool DIAG = C3D || NOMIX;  // output head a uses only source head a
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
@@ -512,7 +524,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
             const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
             th_s[i] = c < CK ? p.theta[((size_t)(h0 + a) * CQ + r) * CK + c] : 0.f;
         }
-        if (tid < CH * CH) w_s[tid] = p.wmix[(size_t)g * CH * CH + tid];
+        if (tid < CH * CH)
+            w_s[tid] = NOMIX ? ((tid / CH == tid % CH) ? p.wmix[h0 + tid / CH] : 0.f)
+                             : p.wmix[(size_t)g * CH * CH + tid];
     }
     wait_vm_all();
     __syncthreads();
@@ -793,7 +807,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                     for (int r = 0; r < 4; ++r) f[r] = al[s * BM + 16 * rw + 4 * g4 + r];
 #pragma unroll
                     for (int a = 0; a < CH; ++a) {
-                        if (C3D && a != s) continue;  // no head mix: only U[a][a]
+                        if (DIAG && a != s) continue;  // no head mix: only U[a][a]
 #pragma unroll
                         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -822,7 +836,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
                         for (int s = 0; s < CH; ++s) {
-                            if (C3D && s != a) continue;
+                            if (DIAG && s != a) continue;
                             U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
                             // the gradients use P . V with P kept to ~16 bits (high part + remainder)
                             if (PREP)
@@ -928,7 +942,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
                     float o = 0.f;
 #pragma unroll
                     for (int s = 0; s < CH; ++s)
-                        if (!C3D || s == a) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
+                        if (!DIAG || s == a) o = __builtin_fmaf(w_s[a * CH + s] * il[s][r], U[s][a][nb][r], o);
                     acc[a][nb][r] = o;
                 }
     }
@@ -1192,10 +1206,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     }
 }
 
-template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false>
+template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -36,10 +36,11 @@ typedef hipError_t (*LayerFn)(const LParams &p, int grid, size_t lds, hipStream_
 }  // namespace layer
 layer::LayerFn find_launch_layer_f32(int d, int ch, int cq1, int ck1, int cq2, int ck2);
 layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, int ck2);
-// One-pass bf16 kernels (mta_fwd_v3.h); null when not instantiated.
-LaunchFn find_launch_v3(int d, int ch, int cq, int ck, int post, int exact, int hpre);
 // Head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre);
+// Its form for head groups of one head, two groups per workgroup (key-query
+// convolution before the softmax); null when not instantiated.
+LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int exact);
 // Its 3D-convolution form (two-pass masks, no head mix); null when not instantiated.
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
 // Their gradient-preparation variants (key-query convolution before the

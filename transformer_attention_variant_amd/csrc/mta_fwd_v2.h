@@ -56,8 +56,11 @@ struct Layout {
 
 // Centre-tap correction plane of the matrix-core stencil before the softmax:
 // fp16 [row of the query tile][key of the key tile], pitch CRP2 (34 banks per
-// row: the stencil's 8-byte reads of 16 rows never share a bank).
+// row: the stencil's 8-byte reads of 16 rows never share a bank), followed by
+// one flag per own-row logit block, [row block][column block] (CRF column
+// blocks), saying whether the block wrote corrections.
 constexpr int CRP2 = 68;
+constexpr int CRF = 8;
 
 // fp16 pitch of the logit tile of the matrix-core stencil: a multiple of 8
 // elements whose 16-byte chunk count is 2 mod 4, so that the stencil's
@@ -84,7 +87,7 @@ __host__ __device__ inline Layout layout(int D, int CH, int cq, int ck, int ncb,
     L.w_off = o;  o += ((CH * CH + 3) & ~3) * 4;
     L.gn_off = o; o += 2 * CH * BM * 4;                     // GroupNorm partial sums per d half
     L.tf_off = o; o += ms ? CH * cq * 64 * 16 : 0;          // banded kernel matrices as MFMA A operands (fp16)
-    L.cr_off = o; o += (ms && !post) ? BM * CRP2 * 2 : 0;   // centre-tap corrections (fp16)
+    L.cr_off = o; o += (ms && !post) ? BM * CRP2 * 2 + 4 * CRF * 4 : 0;  // centre-tap corrections, flags
     L.total = o;
     return L;
 }
@@ -219,10 +222,13 @@ __device__ inline float f16_clamp(float x) { return __builtin_amdgcn_fmed3f(x, -
 // Store a 16x16 logit block as fp16 (Mask_0 + zero padding applied; with
 // `exact` only the zero padding, as in store_block); MODE PROB stores
 // probabilities exp2(x - m_row) / l_row instead.
-// With `cr` (before the softmax, own rows only): the centre tap's correction
-// c00 x - c00h fp16(x) of each stored logit (c00: the centre tap, c00h: its
-// fp16 value in the banded matrices) goes to the correction plane at its
-// output key, so that the stencil's centre product becomes exact.
+// With `cr` (before the softmax, own rows only): for a block holding a logit
+// above 8 / |c00| in magnitude (log2 units; below it the fp16 rounding of the
+// centre product stays under the bf16 rounding of the probabilities) the
+// centre tap's correction c00 x - c00h fp16(x) of each stored logit (c00: the
+// centre tap, c00h: its fp16 value in the banded matrices) goes to the
+// correction plane at its output key, so that the stencil's centre product
+// becomes exact there; the block's flag says whether it did.
 template <int MODE>
 __device__ inline void store_block_x(f16_t *x16, int ph, int rb, int cb, f32x4 acc, int i0, int j0, int hl, int T,
                                      float sc, const float *st_m, const float *st_il, int exact, int lane,
@@ -257,12 +263,17 @@ __device__ inline void store_block_x(f16_t *x16, int ph, int rb, int cb, f32x4 a
                      (f16_t)f16_clamp(xv[3])};
     *reinterpret_cast<f16x4 *>(x16 + rho * ph + e0) = h;
     if (MODE == RAW && cr && rb > 0) {
-        f16_t *crow = cr + (rho - HALO) * CRP2;
+        const float big = fmaxf(fmaxf(fabsf(xv[0]), fabsf(xv[1])), fmaxf(fabsf(xv[2]), fabsf(xv[3])));
+        const bool any = __builtin_amdgcn_ballot_w64(big * fabsf(c00) > 8.0f) != 0;  // wave-uniform
+        if (any) {
+            f16_t *crow = cr + (rho - HALO) * CRP2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int o = e0 + r - hl;  // output key of the entry
-            if (o >= 0 && o < BN) crow[o] = (f16_t)__builtin_fmaf(c00, xv[r], -c00h * (float)h[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int o = e0 + r - hl;  // output key of the entry
+                if (o >= 0 && o < BN) crow[o] = (f16_t)__builtin_fmaf(c00, xv[r], -c00h * (float)h[r]);
+            }
         }
+        if ((lane & 63) == 0) reinterpret_cast<int *>(cr + BM * CRP2)[(rb - 1) * CRF + cb] = any ? 1 : 0;
     }
 }
 
@@ -337,19 +348,34 @@ __device__ inline f16x8 and_mask(f16x8 v, const uint32_t (&w)[4])
 // Two 16-key output blocks (keys 32kh + 16t + 4*(lane/16) + r, t = 0,1) of row
 // 16rw + lane%16, kernel fragments th(ip).  out[4t + r].
 // With `cr`, the accumulators start from the centre-tap corrections of the
-// lane's row (centre product exact; see store_block_x).
+// lane's row where the producing logit block wrote them (centre product
+// exact; see store_block_x).  hl: tile column of key 0 of the key tile.
 template <int CQ, bool MASK, typename TH>
 __device__ inline void stencil_mfma_f(const f16_t *x, int ph, int rho, int kh, TH th, const ColMask &cm, int lane,
-                                      float out[8], const f16_t *cr = nullptr)
+                                      float out[8], const f16_t *cr = nullptr, int hl = 0)
 {
     const int g4 = lane >> 4;
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
     if (cr) {
-        const f16_t *crow = cr + (rho - HALO) * CRP2 + 32 * kh + 4 * g4;
-        const f16x4 c0 = *reinterpret_cast<const f16x4 *>(crow);
-        const f16x4 c1 = *reinterpret_cast<const f16x4 *>(crow + 16);
-        a0 = f32x4{(float)c0[0], (float)c0[1], (float)c0[2], (float)c0[3]};
-        a1 = f32x4{(float)c1[0], (float)c1[1], (float)c1[2], (float)c1[3]};
+        // flags of the logit blocks holding the wave's output keys (tile
+        // columns 32kh + hl ..., hl = tile column of key 0 of the key tile)
+        const int rb = (rho - HALO) >> 4;
+        const int *fl = reinterpret_cast<const int *>(cr + BM * CRP2) + rb * CRF;
+        const int c_lo = (32 * kh + hl) >> 4;
+        unsigned bits = 0;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) bits |= (fl[c_lo + q] ? 1u : 0u) << q;
+        if (bits) {
+            const f16_t *crow = cr + (rho - HALO) * CRP2 + 32 * kh + 4 * g4;
+            const f16x4 c0 = *reinterpret_cast<const f16x4 *>(crow);
+            const f16x4 c1 = *reinterpret_cast<const f16x4 *>(crow + 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k0 = ((32 * kh + 4 * g4 + r + hl) >> 4) - c_lo;
+                a0[r] = ((bits >> k0) & 1u) ? (float)c0[r] : 0.f;
+                a1[r] = ((bits >> (k0 + 1)) & 1u) ? (float)c1[r] : 0.f;
+            }
+        }
     }
 #pragma unroll
     for (int ip = 0; ip < CQ; ++ip) {
@@ -374,17 +400,18 @@ __device__ inline void stencil_mfma_f(const f16_t *x, int ph, int rho, int kh, T
 // kernel fragments in registers
 template <int CQ, bool MASK>
 __device__ inline void stencil_mfma_reg(const f16_t *x, int ph, int rho, int kh, const ThetaFrags<CQ> &tfr,
-                                        const ColMask &cm, int lane, float out[8], const f16_t *cr = nullptr)
+                                        const ColMask &cm, int lane, float out[8], const f16_t *cr = nullptr,
+                                        int hl = 0)
 {
-    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tfr.f[ip]; }, cm, lane, out, cr);
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tfr.f[ip]; }, cm, lane, out, cr, hl);
 }
 
 // kernel fragments read from LDS (tf of one head)
 template <int CQ, bool MASK>
 __device__ inline void stencil_mfma(const f16_t *x, int ph, int rho, int kh, const f16x8 *tf, const ColMask &cm,
-                                    int lane, float out[8], const f16_t *cr = nullptr)
+                                    int lane, float out[8], const f16_t *cr = nullptr, int hl = 0)
 {
-    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tf[ip * 64 + lane]; }, cm, lane, out, cr);
+    stencil_mfma_f<CQ, MASK>(x, ph, rho, kh, [&](int ip) { return tf[ip * 64 + lane]; }, cm, lane, out, cr, hl);
 }
 
 // ---------------------------------------------------------------------------
@@ -691,9 +718,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
                 if (MS) {
                     // wave-uniform: can any of the wave's window columns pass its first row?
                     if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                        stencil_mfma_reg<MS ? CQ : 1, true>(x16, ph, rho, kh, tfr, col_mask(tl), lane, c, cr);
+                        stencil_mfma_reg<MS ? CQ : 1, true>(x16, ph, rho, kh, tfr, col_mask(tl), lane, c, cr, p.hl);
                     else
-                        stencil_mfma_reg<MS ? CQ : 1, false>(x16, ph, rho, kh, tfr, ColMask{}, lane, c, cr);
+                        stencil_mfma_reg<MS ? CQ : 1, false>(x16, ph, rho, kh, tfr, ColMask{}, lane, c, cr, p.hl);
                 } else {
                     stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
                 }
@@ -824,9 +851,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v2(Params p)
             const int tl = EXACT ? qabs - (j0 - p.hl + col0) : (1 << 30);
             if (MS) {
                 if (EXACT && j0 - p.hl + 32 * kh + 47 > i0 + 16 * rw)
-                    stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + a * CQ * 64, col_mask(tl), lane, c, cr);
+                    stencil_mfma<CQ, true>(x16, ph, rho, kh, tf + a * CQ * 64, col_mask(tl), lane, c, cr, p.hl);
                 else
-                    stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + a * CQ * 64, ColMask{}, lane, c, cr);
+                    stencil_mfma<CQ, false>(x16, ph, rho, kh, tf + a * CQ * 64, ColMask{}, lane, c, cr, p.hl);
             } else {
                 stencil8<CQ, CK>(sbuf, p.pitch, rho, col0, th_s + a * CQ * CKP, tl, c);
             }

@@ -18,6 +18,20 @@ CASES = [
             gated=True, seed=72),
     I.small(B=1, H=4, T=8, d=4, c_q=4, c_k=3, c_h=2, kq_place=I.PRE_EXACT, theta_std=0.4, head_std=0.3,
             gated=True, layer=2, seed=73),
+    # the key-query convolution after the softmax, head mix after it
+    I.small(B=1, H=4, T=9, d=4, c_q=3, c_k=4, c_h=2, kq_place=I.POST, theta_std=0.4, head_std=0.3,
+            gn_random=True, layer=3, seed=74),
+    # four-head groups
+    I.small(B=1, H=4, T=8, d=4, c_q=2, c_k=3, c_h=4, theta_std=0.4, head_std=0.3, gn_random=True, gated=True,
+            seed=75),
+    I.small(B=1, H=4, T=7, d=4, c_q=3, c_k=5, c_h=4, kq_place=I.POST, theta_std=0.4, head_std=0.3, seed=76),
+    # head mix before the softmax, with each key-query placement
+    I.small(B=1, H=4, T=8, d=4, c_q=3, c_k=3, c_h=2, head_place=I.PRE, theta_std=0.4, head_std=0.3,
+            gn_random=True, seed=77),
+    I.small(B=1, H=4, T=7, d=4, c_q=2, c_k=4, c_h=4, kq_place=I.PRE_EXACT, head_place=I.PRE, theta_std=0.4,
+            head_std=0.3, seed=78),
+    I.small(B=2, H=2, T=7, d=4, c_q=3, c_k=5, c_h=2, kq_place=I.POST, head_place=I.PRE, theta_std=0.4,
+            head_std=0.3, gated=True, seed=79),
 ]
 
 
@@ -34,8 +48,8 @@ def _c_oracle(cfg, inp):
 def test_forward_matches_c_oracle(cfg):
     inp = _inputs(cfg)
     got = mta_grad.forward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"],
-                           inp["gn_b"], c_h=cfg.c_h, exact=cfg.kq_place == I.PRE_EXACT, eps=cfg.gn_eps,
-                           depth_scale=cfg.depth_scale, gate=inp.get("gate"))
+                           inp["gn_b"], c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
+                           eps=cfg.gn_eps, depth_scale=cfg.depth_scale, gate=inp.get("gate"))
     ref = _c_oracle(cfg, inp)
     assert float((got - ref).abs().max()) <= 1e-12
 
@@ -45,8 +59,8 @@ def test_gradients_match_finite_differences(cfg):
     inp = _inputs(cfg)
     g = torch.Generator().manual_seed(5)
     dout = torch.randn(inp["q"].shape, generator=g, dtype=torch.float64)
-    grads = mta_grad.gradients(inp, dout, c_h=cfg.c_h, exact=cfg.kq_place == I.PRE_EXACT, eps=cfg.gn_eps,
-                               depth_scale=cfg.depth_scale)
+    grads = mta_grad.gradients(inp, dout, c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
+                               eps=cfg.gn_eps, depth_scale=cfg.depth_scale)
     assert set(grads) == {n for n in mta_grad.NAMES if n in inp}
     h = 1e-5
     for name, gr in grads.items():
@@ -58,3 +72,19 @@ def test_gradients_match_finite_differences(cfg):
             fd = float(((_c_oracle(cfg, plus) - _c_oracle(cfg, minus)) * dout).sum()) / (2 * h)
             an = float((gr * u).sum())
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, trial, fd, an)
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.short())
+def test_term_scales_bound_the_kernel_gradients(cfg):
+    """The term scales are sums of magnitudes of the terms of the kernel
+    gradients, so each bounds its gradient, element by element; and they are
+    positive wherever a tap or head pair touches the map."""
+    inp = _inputs(cfg)
+    dout = torch.randn(inp["q"].shape, generator=torch.Generator().manual_seed(9), dtype=torch.float64)
+    g = mta_grad.gradients(inp, dout, c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
+                           eps=cfg.gn_eps, depth_scale=cfg.depth_scale, term_scales=True)
+    for name in ("theta_kq", "theta_head"):
+        sc = g["scale_" + name]
+        assert sc.shape == g[name].shape
+        assert bool((g[name].abs() <= sc * (1 + 1e-12) + 1e-300).all()), name
+        assert float(sc.min()) > 0.0, name

@@ -283,8 +283,7 @@ def main():
 
     if not args.no_stages:
         res["stages"] = stages(cfg, dev, timed, t, torch)
-    if not args.no_backward and cfg.form == "std" and cfg.kq_place != I.POST and cfg.head_place == I.POST \
-            and cfg.c_h <= 2:
+    if not args.no_backward and cfg.form == "std":
         res["backward"] = backward_timing(cfg, dev, args, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args)
@@ -302,7 +301,7 @@ def backward_timing(cfg, dev, args, torch):
     dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.d), generator=g).to(dev["q"].dtype).cuda()
     stream = torch.cuda.current_stream()
     lib = binding.load()
-    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, I.POST,
+    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
                             I.F32 if cfg.dtype == "f32" else I.BF16, cfg.gn_eps, cfg.depth_scale)
     f32 = dict(dtype=torch.float32, device=dev["q"].device)
     outs = [torch.empty(dev["q"].shape, **f32) for _ in range(3)] + \
@@ -337,7 +336,8 @@ def backward_timing(cfg, dev, args, torch):
     # transposed convolution and the kernel gradient (4 c_q c_k), the head mix (4 c_h)
     n = float(cfg.causal_logits())
     bw = n * (8 * cfg.d + 4 * cfg.c_q * cfg.c_k + 4 * cfg.c_h)
-    return {"ms_per_call": round(ms, 4), "tokens_per_s": round(cfg.B * cfg.T / (ms / 1e3), 1),
+    return {"kernel": binding.backward_kernel_name(cfg),
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(cfg.B * cfg.T / (ms / 1e3), 1),
             "alg_tflops": round(bw / (ms / 1e3) / 1e12, 2),
             "alg_work": "8d + 4 c_q c_k + 4 c_h FLOP per causal logit (dP3, dV, dQ, dK; transposed "
                         "convolution and kernel gradient; head mix), recomputation not counted",

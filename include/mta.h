@@ -203,22 +203,32 @@ const char *mta_layer_kernel_name(const mta_layer_config *cfg, const mta_layer_w
 
 /*
  * mta_backward — gradients of mta_forward (mta_forward_gated when gate is not
- * NULL) for the default placement: kq_place MTA_PRE_SOFTMAX or
- * MTA_PRE_SOFTMAX_EXACT, head_place MTA_POST_SOFTMAX, c_h in {1, 2}
- * (MTA_ERR_UNSUPPORTED otherwise), d in {32, 64, 128}, either dtype.  Given
+ * NULL) for every placement of the two convolutions (kq_place, head_place),
+ * c_h in {1, 2, 4}, d in {32, 64, 128}, either dtype: the chain rule of the
+ * forward of page "Multi-Token Attention — Paper Graph", section 3.4 ("Key-Query
+ * Convolution" Eq. 4 and its transpose, the softmax, "Head Mixing Convolution"
+ * Eq. 7, A.V, "Group Normalization with Sigmoid Gating").  Given
  * dout = dL/dout [B][H][T][d] (input dtype) it writes, in float32:
  *   dq, dk, dv       [B][H][T][d]
  *   dtheta_kq        [H][c_q][c_k]
  *   dtheta_head      [H/c_h][c_h][c_h]
  *   dgn_w, dgn_b     [H][d]
  *   dgate            [H] (required if and only if gate is given)
- * The chain rule of the forward ("Key-Query Convolution" Eq. 4 and its
- * transpose, the softmax, Eq. 7, A.V, GroupNorm) is applied per tile on the
- * device; nothing of size T x T is stored.  `workspace` is a device buffer of
- * at least mta_backward_workspace_size(cfg) bytes, 256-byte aligned, owned by
- * the caller; its contents are scratch (undefined after the call).  A smaller
- * workspace_bytes is MTA_ERR_BAD_VALUE.  Asynchronous on `stream`; every
- * output is overwritten.  Other arguments and error codes as mta_forward.
+ * Two implementations (mta_backward_kernel_name tells which one a
+ * configuration runs):
+ *   - the default placement (kq_place MTA_PRE_SOFTMAX or MTA_PRE_SOFTMAX_EXACT,
+ *     head_place MTA_POST_SOFTMAX) with c_h <= 2 is fused per tile: nothing of
+ *     size T x T is stored; the workspace holds row statistics and dO;
+ *   - every other configuration keeps each head's T x T maps (float32, the
+ *     causal band of 64 x 64 tiles) in the workspace and computes in float32
+ *     throughout; T <= 32768 (MTA_ERR_UNSUPPORTED beyond).  Head groups are
+ *     processed in as many chunks as the workspace needs.
+ * `workspace` is a device buffer, 256-byte aligned, owned by the caller, of
+ * mta_backward_workspace_size(cfg) bytes (the fused form needs exactly that;
+ * the map form accepts less, down to one head group's maps, and then runs more
+ * chunks); its contents are scratch (undefined after the call).  Too small a
+ * workspace is MTA_ERR_BAD_VALUE.  Asynchronous on `stream`; every output is
+ * overwritten.  Other arguments and error codes as mta_forward.
  */
 int mta_backward(const void *q, const void *k, const void *v, const float *theta_kq, const float *theta_head,
                  const float *gn_w, const float *gn_b, const float *gate, const void *dout,
@@ -226,8 +236,14 @@ int mta_backward(const void *q, const void *k, const void *v, const float *theta
                  float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate, void *workspace,
                  size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace mta_backward needs for cfg (0 if cfg is invalid). */
+/* Bytes of workspace mta_backward asks for cfg: the fused form's need, or the
+ * map form's maps for all head groups at once, capped at 16 GiB (at least one
+ * head group).  0 if cfg is invalid or unsupported. */
 size_t mta_backward_workspace_size(const mta_config *cfg);
+
+/* Host-only: which backward mta_backward runs for cfg (a static string), or
+ * NULL if cfg is invalid or unsupported. */
+const char *mta_backward_kernel_name(const mta_config *cfg);
 
 /*
  * mta_backward_noalloc — mta_backward for callers that cannot allocate device
@@ -238,8 +254,9 @@ size_t mta_backward_workspace_size(const mta_config *cfg);
  * workload's 65.5 MiB fits), one per GPU, reserved when the library's code is
  * loaded on that GPU and held until the process ends.  The call allocates
  * nothing (no hipMalloc, hipFree or allocating library routine).  A problem
- * whose mta_backward_workspace_size exceeds the array returns MTA_ERR_SCRATCH
- * before any device work.  Every call on a GPU uses that GPU's one array:
+ * whose least workspace exceeds the array (the fused form's
+ * mta_backward_workspace_size, or one head group's maps) returns
+ * MTA_ERR_SCRATCH before any device work.  Every call on a GPU uses that GPU's one array:
  * calls that overlap on one GPU (other streams, other host threads) race and
  * must be ordered by the caller.  Nothing in the array needs clearing between
  * calls (the kernels write every workspace entry before reading it).

@@ -53,6 +53,8 @@ static void sweep_configs(void)
                                            "check_config %d but kernel_name %s", rc, name ? name : "(null)");
                                     if (name) EXPECT(strlen(name) > 8, "short kernel name");
                                     const size_t ws = mta_backward_workspace_size(&c);
+                                    const char *bname = mta_backward_kernel_name(&c);
+                                    EXPECT((rc == MTA_OK) <= (bname != NULL), "backward name for a valid config");
                                     EXPECT((ws == 0) == (rc != MTA_OK && rc != MTA_ERR_UNSUPPORTED) ||
                                                rc == MTA_ERR_UNSUPPORTED,
                                            "workspace %zu for status %d", ws, rc);
@@ -128,10 +130,23 @@ static void scalar_checks(void)
     EXPECT(mta_backward(fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, NULL, fbuf, &c, fbuf, fbuf, fbuf, fbuf, fbuf,
                         fbuf, fbuf, NULL, fbuf, need - 1, NULL) == MTA_ERR_BAD_VALUE,
            "workspace too small");
+    /* every placement has a backward; the one with the maps in the workspace
+     * takes T <= 32768 and accepts down to one head group's maps */
     c.kq_place = MTA_POST_SOFTMAX;
+    c.c_h = 4;
+    EXPECT(mta_backward_kernel_name(&c) && strstr(mta_backward_kernel_name(&c), "mta_bwd_gen"),
+           "post-softmax backward name");
     EXPECT(mta_backward(fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, NULL, fbuf, &c, fbuf, fbuf, fbuf, fbuf, fbuf,
-                        fbuf, fbuf, NULL, fbuf, need, NULL) == MTA_ERR_UNSUPPORTED,
-           "post-softmax backward");
+                        fbuf, fbuf, NULL, fbuf, 4096, NULL) == MTA_ERR_BAD_VALUE,
+           "post-softmax backward, workspace too small");
+    c.seq_len = 40000;
+    EXPECT(mta_backward_kernel_name(&c) == NULL, "map form beyond T = 32768");
+    EXPECT(mta_backward_workspace_size(&c) == 0, "map form workspace beyond T = 32768");
+    EXPECT(mta_backward(fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, fbuf, NULL, fbuf, &c, fbuf, fbuf, fbuf, fbuf, fbuf,
+                        fbuf, fbuf, NULL, fbuf, sizeof fbuf, NULL) == MTA_ERR_UNSUPPORTED,
+           "map form beyond T = 32768");
+    c = base();
+    EXPECT(mta_backward_kernel_name(&c) && strstr(mta_backward_kernel_name(&c), "fused"), "fused backward name");
     /* a problem beyond the device scratch array is refused before any GPU call */
     c = base();
     c.batch = 64;

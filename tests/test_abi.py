@@ -146,9 +146,16 @@ def test_backward_validation(lib):
         return lib.mta_backward(a_["q"], a_["k"], a_["v"], a_["th"], a_["w"], a_["gw"], a_["gb"], a_["gate"],
                                 a_["dout"], ctypes.byref(c_), a_["dq"], a_["dk"], a_["dv"], a_["dth"], a_["dw"],
                                 a_["dgw"], a_["dgb"], a_["dgate"], a_["ws"], a_["nws"], None)
-    assert call(cfg(kq_place=1)) == -6          # post-softmax key-query convolution
-    assert call(cfg(head_place=0)) == -6        # head mix before the softmax
-    assert call(cfg(H=8, c_h=4)) == -6          # c_h = 4
+    # every other placement runs the backward with its maps in the workspace:
+    # a workspace below one head group's maps is refused, so is T > 32768
+    for other in (cfg(kq_place=1), cfg(head_place=0), cfg(H=8, c_h=4)):
+        name = lib.mta_backward_kernel_name(ctypes.byref(other))
+        assert name is not None and name.decode().startswith("mta_bwd_gen"), name
+        assert lib.mta_backward_workspace_size(ctypes.byref(other)) > 4096
+        assert call(other, nws=4096) == -8
+        assert call(cfg(kq_place=other.kq_place, head_place=other.head_place, H=other.heads, c_h=other.c_h,
+                        T=40000)) == -6
+    assert lib.mta_backward_kernel_name(ctypes.byref(c)).decode().startswith("mta_bwd (fused")
     assert call(c, dq=None) == -1
     assert call(c, gate=good, dgate=None) == -1
     assert call(c, ws=good + 16) == -5          # workspace not 256-byte aligned

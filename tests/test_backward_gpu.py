@@ -14,6 +14,7 @@ tol x the sum of the magnitudes of the terms (the oracle's term scales), the
 error model of a floating-point sum.  A gradient that vanishes identically
 (T = 1: a softmax over one key depends on neither q nor k) is bounded by
 tol x RMS(dv) instead of its own (zero) RMS."""
+import ctypes
 import sys
 
 import numpy as np
@@ -57,6 +58,32 @@ def _cases():
                      gn_random=True, theta_std=0.2, seed=1301))
     c.append(I.small("bwd_f32_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, seed=1302))
     c.append(I.small("bwd_bf16_T1", B=2, H=2, T=1, d=128, c_q=6, c_k=11, c_h=2, dtype="bf16", seed=1303))
+    # every other placement (the backward with the maps in the workspace): the
+    # 8K sweep's kernel sizes after the softmax and with four-head groups, the
+    # head mix before the softmax with each key-query placement, ragged T over
+    # several tiles, the exact indicator, the largest kernel, a gate
+    Q = I.POST
+    for (cq, ck, kq, ch) in ((4, 9, Q, 2), (6, 11, Q, 2), (8, 15, Q, 2), (4, 9, P, 4), (6, 11, P, 4), (8, 15, P, 4),
+                             (4, 9, Q, 4), (6, 11, Q, 4), (8, 15, Q, 4), (6, 11, E, 4)):
+        c.append(I.small(f"gen_bf16_{cq}x{ck}_ch{ch}_kq{kq}", B=1, H=4, T=150, d=128, c_q=cq, c_k=ck, c_h=ch,
+                         kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05,
+                         gn_random=True, seed=1500 + cq + 10 * kq + ch))
+    for (kq, ch, d, T, dt) in ((P, 2, 64, 100, "f32"), (E, 4, 32, 77, "f32"), (Q, 2, 128, 130, "bf16"),
+                               (P, 4, 128, 150, "bf16")):
+        c.append(I.small(f"gen_{dt}_headpre_kq{kq}_ch{ch}_d{d}_T{T}", B=1, H=4, T=T, d=d, c_q=3, c_k=5, c_h=ch,
+                         kq_place=kq, head_place=P, dtype=dt, theta_std=0.2, head_std=0.2, gn_random=True,
+                         seed=1600 + kq + ch + d))
+    c.append(I.small("gen_f32_post_ch4_d64_T200", B=2, H=4, T=200, d=64, c_q=4, c_k=7, c_h=4, kq_place=Q,
+                     theta_std=0.2, head_std=0.2, gn_random=True, gated=True, gate_std=1.0, layer=3, seed=1701))
+    c.append(I.small("gen_f32_post_ch1_d32_T77", B=1, H=3, T=77, d=32, c_q=2, c_k=4, c_h=1, kq_place=Q,
+                     theta_std=0.3, gated=True, seed=1702))
+    c.append(I.small("gen_f32_16x31_ch2", B=1, H=2, T=140, d=32, c_q=16, c_k=31, c_h=2, kq_place=E,
+                     theta_std=0.1, head_std=0.2, seed=1703))
+    c.append(I.small("gen_bf16_post_T1", B=2, H=4, T=1, d=128, c_q=6, c_k=11, c_h=4, kq_place=Q, dtype="bf16",
+                     seed=1704))
+    c.append(I.small("gen_f32_post_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, kq_place=Q, seed=1705))
+    c.append(I.small("gen_bf16_6x11_ch4_T600", B=1, H=4, T=600, d=128, c_q=6, c_k=11, c_h=4, kq_place=Q,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=1706))
     return c
 
 
@@ -68,20 +95,30 @@ def _dout(cfg):
     return torch.randn((cfg.B, cfg.H, cfg.T, cfg.d), generator=g).to(I.DTYPES[cfg.dtype])
 
 
+def _reference(cfg, inp, dout):
+    return mta_grad.gradients({k: v.double() for k, v in inp.items()}, dout.double(), c_h=cfg.c_h,
+                              kq_place=cfg.kq_place, head_place=cfg.head_place, eps=cfg.gn_eps,
+                              depth_scale=cfg.depth_scale, term_scales=True)
+
+
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 def test_backward_matches_oracle(cfg):
     _say(f"[bwd] {cfg.short()}")
     inp = I.generate(cfg)
     dout = _dout(cfg)
     dev = to_dev(inp)
+    kname = binding.backward_kernel_name(cfg)
+    _say(f"[bwd]   {kname}")
     got = binding.backward_cfg(cfg, dev, dout.cuda())
     torch.cuda.synchronize()
-    ref = mta_grad.gradients({k: v.double() for k, v in inp.items()}, dout.double(), c_h=cfg.c_h,
-                             exact=cfg.kq_place == I.PRE_EXACT, eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
-                             term_scales=True)
+    ref = _reference(cfg, inp, dout)
     scales = {n[len("scale_"):]: ref.pop(n).numpy() for n in list(ref) if n.startswith("scale_")}
     assert set(got) == set(ref)
-    tol = TOL[cfg.dtype]
+    # the map form computes in float32 throughout (bf16 inputs are exact in
+    # float32), so it is held to the float32 bar for both dtypes
+    tol = TOL["f32"] if kname.startswith("mta_bwd_gen") else TOL[cfg.dtype]
+    if cfg.name.startswith("gen_"):
+        assert kname.startswith("mta_bwd_gen"), kname
     for name in ref:
         g = got[name].double().cpu().numpy()
         r = ref[name].numpy()
@@ -113,3 +150,32 @@ def test_backward_is_deterministic_up_to_atomics():
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
     for n in a:
         assert torch.allclose(a[n], b[n], rtol=1e-5, atol=1e-6 * float(a[n].abs().max())), n
+
+
+def test_general_backward_on_a_side_stream_and_in_small_chunks():
+    """The map form on a side stream (outputs and workspace allocated on it), and
+    with a workspace of one head group (four chunks): both equal the default call
+    on the current stream to rounding (atomics in dtheta, dw and the GroupNorm
+    gradients; dq, dk, dv come from the same products in the same order)."""
+    cfg = I.small("gen_side", B=2, H=4, T=130, d=64, c_q=4, c_k=9, c_h=2, kq_place=I.POST, dtype="bf16",
+                  theta_std=0.1, head_std=0.1, gn_random=True, seed=1801)
+    inp = I.generate(cfg)
+    dev = to_dev(inp)
+    dout = _dout(cfg).cuda()
+    a = binding.backward_cfg(cfg, dev, dout)
+    s = torch.cuda.Stream()
+    b = binding.backward_cfg(cfg, dev, dout, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    lib = binding.load()
+    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
+                            I.BF16, cfg.gn_eps, cfg.depth_scale)
+    full = int(lib.mta_backward_workspace_size(ctypes.byref(c)))
+    units = cfg.B * cfg.H // cfg.c_h
+    small = binding.backward_cfg(cfg, dev, dout, workspace_bytes=full // units)
+    torch.cuda.synchronize()
+    for got in (b, small):
+        assert set(got) == set(a)
+        for n in a:
+            assert torch.equal(a[n], got[n]) if n in ("q", "k", "v") else \
+                torch.allclose(a[n], got[n], rtol=1e-5, atol=1e-6 * float(a[n].abs().max())), n

@@ -46,11 +46,14 @@ def test_noalloc_matches_workspace_entry_point():
     cases = [I.small("noalloc_big", B=2, H=4, T=300, d=128, c_q=6, c_k=11, c_h=2, dtype="bf16", qkv_std=0.7071,
                      theta_std=0.05, head_std=0.05, gated=True, gn_random=True, seed=1501),
              I.small("noalloc_small", B=1, H=2, T=97, d=128, c_q=4, c_k=9, c_h=2, kq_place=I.PRE_EXACT,
-                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=1502)]
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=1502),
+             # the backward that keeps its maps in the workspace (convolution after the softmax, c_h = 4)
+             I.small("noalloc_maps", B=1, H=4, T=130, d=64, c_q=4, c_k=9, c_h=4, kq_place=I.POST, dtype="bf16",
+                     theta_std=0.1, head_std=0.1, gn_random=True, seed=1503)]
     for cfg in cases:
         _say(f"[noalloc] {cfg.short()}")
-        c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, I.POST,
-                                I.BF16, cfg.gn_eps, cfg.depth_scale)
+        c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place,
+                                cfg.head_place, I.BF16, cfg.gn_eps, cfg.depth_scale)
         assert lib.mta_backward_workspace_size(ctypes.byref(c)) <= lib.mta_backward_scratch_bytes()
         inp = I.generate(cfg)
         dev = to_dev(inp)
@@ -61,10 +64,11 @@ def test_noalloc_matches_workspace_entry_point():
         _check_same(cfg, got, ref)
 
 
-def test_noalloc_refuses_problems_beyond_its_scratch():
+@pytest.mark.parametrize("name", ["sweep8k_6x11_ch2_pre", "sweep8k_6x11_ch4_post"])
+def test_noalloc_refuses_problems_beyond_its_scratch(name):
     lib = binding.load()
-    cfg = I.CONFIGS["sweep8k_6x11_ch2_pre"]
-    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, I.POST,
+    cfg = I.CONFIGS[name]
+    c = binding.make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
                             I.BF16, cfg.gn_eps, cfg.depth_scale)
     assert lib.mta_backward_workspace_size(ctypes.byref(c)) > lib.mta_backward_scratch_bytes()
     good = 0x10000  # never dereferenced: the call returns during validation

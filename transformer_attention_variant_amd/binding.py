@@ -23,8 +23,8 @@ STATUS = {0: "MTA_OK", -1: "MTA_ERR_NULL_ARG", -2: "MTA_ERR_BAD_SHAPE", -3: "MTA
           -7: "MTA_ERR_LAUNCH", -8: "MTA_ERR_BAD_VALUE", -9: "MTA_ERR_SCRATCH"}
 # names declared in include/mta.h
 EXPORTS = ("mta_forward", "mta_forward_gated", "mta_forward_layer", "mta_backward", "mta_backward_workspace_size",
-           "mta_backward_noalloc", "mta_backward_scratch_bytes", "mta_check_config", "mta_kernel_name",
-           "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
+           "mta_backward_noalloc", "mta_backward_scratch_bytes", "mta_backward_kernel_name", "mta_check_config",
+           "mta_kernel_name", "mta_layer_kernel_name", "mta_status_string", "mta_abi_version")
 LAYER_KERNELS = ("kq_pre", "head_pre", "conv3d", "head_post", "kq_post", "head_post2")
 
 
@@ -91,6 +91,8 @@ def load(path: Optional[str] = None):
     lib.mta_backward_scratch_bytes.restype = ctypes.c_size_t
     lib.mta_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
     lib.mta_kernel_name.restype = ctypes.c_char_p
+    lib.mta_backward_kernel_name.argtypes = [ctypes.POINTER(MtaConfig)]
+    lib.mta_backward_kernel_name.restype = ctypes.c_char_p
     lib.mta_abi_version.argtypes = []
     lib.mta_abi_version.restype = ctypes.c_int
     if path is None:
@@ -213,15 +215,17 @@ GRAD_NAMES = ("q", "k", "v", "theta_kq", "theta_head", "gn_w", "gn_b", "gate")
 
 
 def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: int, c_h: int,
-             kq_place: int = I.PRE, gn_eps: float = 1e-5, depth_scale: float = 1.0,
+             kq_place: int = I.PRE, head_place: int = I.POST, gn_eps: float = 1e-5, depth_scale: float = 1.0,
              gate: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
-             noalloc: bool = False) -> Dict:
-    """Gradients of ``forward`` (head mix after the softmax) through
+             noalloc: bool = False, workspace_bytes: Optional[int] = None) -> Dict:
+    """Gradients of ``forward`` (any placement) through
     ``mta_backward``: returns float32 CUDA tensors keyed q, k, v, theta_kq,
     theta_head, gn_w, gn_b (and gate).  ``dout`` is dL/dout in the input dtype.
     Allocates the outputs and the workspace with torch (the library allocates
     nothing).  With ``noalloc`` the call goes to ``mta_backward_noalloc``, whose
-    workspace is the library's own device scratch array (no workspace tensor)."""
+    workspace is the library's own device scratch array (no workspace tensor).
+    ``workspace_bytes`` overrides the workspace size the library asks for (the
+    map form accepts less and runs more chunks)."""
     lib = load()
     B, H, T, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
@@ -230,12 +234,12 @@ def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: 
     for name, t in (("theta_kq", theta_kq), ("theta_head", theta_head), ("gn_w", gn_w), ("gn_b", gn_b)):
         if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
-    cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, I.POST,
+    cfg = make_config(B, H, T, d, c_q, c_k, c_h, kq_place, head_place,
                       I.F32 if q.dtype == torch.float32 else I.BF16, gn_eps, depth_scale)
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
     s = _launch_stream(dev, stream)
-    nbytes = int(lib.mta_backward_workspace_size(ctypes.byref(cfg)))
+    nbytes = int(lib.mta_backward_workspace_size(ctypes.byref(cfg))) if workspace_bytes is None else workspace_bytes
     # outputs and workspace are allocated on the launch stream, so that the
     # caching allocator does not reuse the workspace (freed on return) for other
     # work while the kernels on that stream may still use it
@@ -262,10 +266,19 @@ def backward(q, k, v, theta_kq, theta_head, gn_w, gn_b, dout, *, c_q: int, c_k: 
 
 
 def backward_cfg(cfg: I.MTAConfig, inp: Dict[str, torch.Tensor], dout: torch.Tensor, stream=None,
-                 noalloc: bool = False) -> Dict:
+                 noalloc: bool = False, workspace_bytes: Optional[int] = None) -> Dict:
     return backward(inp["q"], inp["k"], inp["v"], inp["theta_kq"], inp["theta_head"], inp["gn_w"], inp["gn_b"],
-                    dout, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, gn_eps=cfg.gn_eps,
-                    depth_scale=cfg.depth_scale, gate=inp.get("gate"), stream=stream, noalloc=noalloc)
+                    dout, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq_place=cfg.kq_place, head_place=cfg.head_place,
+                    gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale, gate=inp.get("gate"), stream=stream,
+                    noalloc=noalloc, workspace_bytes=workspace_bytes)
+
+
+def backward_kernel_name(cfg: I.MTAConfig) -> Optional[str]:
+    """Which backward ``mta_backward`` runs for a workload configuration."""
+    c = make_config(cfg.B, cfg.H, cfg.T, cfg.d, cfg.c_q, cfg.c_k, cfg.c_h, cfg.kq_place, cfg.head_place,
+                    I.F32 if cfg.dtype == "f32" else I.BF16, cfg.gn_eps, cfg.depth_scale)
+    r = load().mta_backward_kernel_name(ctypes.byref(c))
+    return r.decode() if r else None
 
 
 def forward_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gn_w: torch.Tensor, gn_b: torch.Tensor,

@@ -10,6 +10,7 @@
 #include "mta_fwd_v4.h"
 #include "mta_fwd_layer.h"
 #include "mta_bwd.h"
+#include "mta_bwd_gen_api.h"
 #include "mta_launch.h"
 
 namespace {
@@ -451,14 +452,60 @@ const char *mta_layer_kernel_name(const mta_layer_config *c, const mta_layer_wei
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The fused backward (mta_bwd.h): the default placement (key-query
+// convolution before the softmax, head mix after it) with c_h <= 2, where its
+// kernels are instantiated and fit in LDS.  Fills the shape fields of bp and
+// the LDS sizes.
+static bool fused_plan(const mta_config *cfg, mta::bwd::BParams &bp, size_t &lds_a, size_t &lds_b,
+                       mta::bwd::BwdFn &fn);
+
+static bool use_fused(const mta_config *cfg)
+{
+    mta::bwd::BParams bp{};
+    size_t la, lb;
+    mta::bwd::BwdFn fn;
+    return fused_plan(cfg, bp, la, lb, fn);
+}
+
 size_t mta_backward_workspace_size(const mta_config *cfg)
 {
     if (validate(cfg) != MTA_OK) return 0;
+    if (!use_fused(cfg)) {
+        if (cfg->seq_len > mta::gen::MAX_T) return 0;
+        if (cfg->batch == 0 || cfg->seq_len == 0) return 0;
+        return mta::gen::workspace_bytes(cfg->batch, cfg->heads, cfg->seq_len, cfg->head_dim, cfg->c_h,
+                                         cfg->kq_place, cfg->head_place);
+    }
     const size_t rows = (size_t)cfg->batch * cfg->heads * cfg->seq_len;
     // bf16: dO as high and low bf16 planes; fp32: one fp32 array
     const size_t planes = cfg->dtype == MTA_BF16 ? 2 : 1;
     const size_t el = cfg->dtype == MTA_BF16 ? 2 : 4;
     return 3 * align256(rows * 4) + planes * align256(rows * cfg->head_dim * el);
+}
+
+const char *mta_backward_kernel_name(const mta_config *cfg)
+{
+    if (validate(cfg) != MTA_OK) return nullptr;
+    if (use_fused(cfg)) {
+        const int bf = cfg->dtype == MTA_BF16;
+        const bool prep = bf && cfg->head_dim == 128 && cfg->c_h == 2 &&
+                          mta::find_launch_v4_prep(cfg->head_dim, cfg->c_h, cfg->c_q, cfg->c_k,
+                                                   cfg->kq_place == MTA_PRE_SOFTMAX_EXACT) &&
+                          mta::v4::layout(cfg->c_q, cfg->c_k, true).total <= 160 * 1024;
+        return prep ? "mta_bwd (fused: head-split forward with the gradient epilogue + mta_bwd_main)"
+                    : "mta_bwd (fused: mta_bwd_prep + mta_bwd_main)";
+    }
+    if (cfg->seq_len > mta::gen::MAX_T) return nullptr;
+    return "mta_bwd_gen (per-head maps in the workspace)";
+}
+
+// The least workspace a call accepts: the fused backward needs
+// mta_backward_workspace_size; the general one one head group's maps (it
+// then processes the groups in more chunks).
+static size_t workspace_min(const mta_config *cfg)
+{
+    if (use_fused(cfg)) return mta_backward_workspace_size(cfg);
+    return mta::gen::unit_bytes(cfg->seq_len, cfg->head_dim, cfg->c_h, cfg->kq_place, cfg->head_place);
 }
 
 static int backward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
@@ -522,7 +569,9 @@ int mta_backward_noalloc(const void *q, const void *k, const void *v, const floa
 {
     const int vs = validate(cfg);
     if (vs != MTA_OK) return vs;
-    if (mta_backward_workspace_size(cfg) > SCRATCH_BYTES) return MTA_ERR_SCRATCH;
+    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
+    if (!use_fused(cfg) && cfg->seq_len > mta::gen::MAX_T) return MTA_ERR_UNSUPPORTED;
+    if (workspace_min(cfg) > SCRATCH_BYTES) return MTA_ERR_SCRATCH;
     void *ws = scratch_on_current_device();
     if (!ws) return MTA_ERR_LAUNCH;
     return backward_impl(q, k, v, theta_kq, theta_head, gn_w, gn_b, gate, dout, cfg, dq, dk, dv, dtheta_kq,
@@ -533,39 +582,15 @@ int mta_backward_noalloc(const void *q, const void *k, const void *v, const floa
 
 extern "C" {
 
-static int backward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
-                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
-                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
-                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
-                         void *workspace, size_t workspace_bytes, void *stream)
+static bool fused_plan(const mta_config *cfg, mta::bwd::BParams &bp, size_t &lds_a, size_t &lds_b,
+                       mta::bwd::BwdFn &fn)
 {
-    const int vs = validate(cfg);
-    if (vs != MTA_OK) return vs;
-    if (cfg->kq_place == MTA_POST_SOFTMAX || cfg->head_place != MTA_POST_SOFTMAX || cfg->c_h > 2)
-        return MTA_ERR_UNSUPPORTED;
-    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
-    if (!q || !k || !v || !theta_kq || !theta_head || !gn_w || !gn_b || !dout || !dq || !dk || !dv ||
-        !dtheta_kq || !dtheta_head || !dgn_w || !dgn_b || !workspace || (gate && !dgate))
-        return MTA_ERR_NULL_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u))
-        return MTA_ERR_MISALIGNED;
-    const float *fl[] = {theta_kq, theta_head, gn_w, gn_b, gate, dq, dk, dv, dtheta_kq, dtheta_head,
-                         dgn_w, dgn_b, dgate};
-    for (const float *x : fl)
-        if (x && !aligned4(x)) return MTA_ERR_MISALIGNED;
-    if (workspace_bytes < mta_backward_workspace_size(cfg)) return MTA_ERR_BAD_VALUE;
-
+    if (cfg->kq_place == MTA_POST_SOFTMAX || cfg->head_place != MTA_POST_SOFTMAX || cfg->c_h > 2) return false;
     const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
     const int bf = cfg->dtype == MTA_BF16;
-    mta::bwd::BwdFn fn = mta::find_launch_bwd(bf, d, ch, cq, ck);
-    if (!fn) return MTA_ERR_UNSUPPORTED;
-
-    mta::bwd::BParams bp{};
+    fn = mta::find_launch_bwd(bf, d, ch, cq, ck);
+    if (!fn) return false;
     mta::Params &p = bp.f;
-    p.q = q; p.k = k; p.v = v;
-    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b; p.gate = gate;
-    p.out = nullptr;
     p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;
     p.G = cfg->heads / ch;
     p.units = cfg->batch * p.G;
@@ -579,16 +604,6 @@ static int backward_impl(const void *q, const void *k, const void *v, const floa
     p.sc = 1.4426950408889634f / sqrtf((float)d);
     p.eps = cfg->gn_eps;
     p.depth_scale = cfg->depth_scale;
-    bp.dout = dout;
-    bp.dq = dq; bp.dk = dk; bp.dv = dv;
-    bp.dtheta = dtheta_kq; bp.dw = dtheta_head; bp.dgn_w = dgn_w; bp.dgn_b = dgn_b; bp.dgate = dgate;
-    const size_t rows = (size_t)cfg->batch * cfg->heads * cfg->seq_len;
-    char *ws = static_cast<char *>(workspace);
-    bp.ws_m = reinterpret_cast<float *>(ws);
-    bp.ws_il = reinterpret_cast<float *>(ws + align256(rows * 4));
-    bp.ws_D = reinterpret_cast<float *>(ws + 2 * align256(rows * 4));
-    bp.ws_dO = ws + 3 * align256(rows * 4);
-    bp.ws_dOl = ws + 3 * align256(rows * 4) + align256(rows * d * (bf ? 2 : 4));
     bp.hr = ck / 2;
     bp.nEr = mta::BM + cq - 1;
     bp.nEc = mta::BN + ck - 1;
@@ -599,7 +614,6 @@ static int backward_impl(const void *q, const void *k, const void *v, const floa
     bp.xpitch = bp.nRcb * 16 + 4;
     bp.inv_sqrt_d = 1.0f / sqrtf((float)d);
     bp.inv_log2e = 0.6931471805599453f;
-
     auto pad4 = [](size_t x) { return (x + 3) & ~(size_t)3; };
     const size_t ckp = (size_t)((ck + 3) & ~3);
     const size_t vb = bf ? (d == 32 ? mta::vbuf_bytes<mta::bf16_t, 32>()
@@ -607,14 +621,74 @@ static int backward_impl(const void *q, const void *k, const void *v, const floa
                                               : mta::vbuf_bytes<mta::bf16_t, 128>())
                          : (d == 32 ? mta::vbuf_bytes<float, 32>()
                                     : d == 64 ? mta::vbuf_bytes<float, 64>() : mta::vbuf_bytes<float, 128>());
-    const size_t lds_a = ((size_t)mta::EXT_R * p.pitch + pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
+    lds_a = ((size_t)mta::EXT_R * p.pitch + pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
                           (size_t)4 * ch * 2 * d + pad4((size_t)4 * ch)) * 4 + vb;
     const size_t nEr4 = pad4(bp.nEr);
-    const size_t lds_b = ((size_t)bp.nRrb * 16 * bp.xpitch + (size_t)bp.nEr * bp.epitch +
+    lds_b = ((size_t)bp.nRrb * 16 * bp.xpitch + (size_t)bp.nEr * bp.epitch +
                           (size_t)ch * bp.nEr * bp.epitch + pad4(ch * cq * ckp) + pad4((size_t)ch * ch) +
                           pad4(ch * cq * ckp) + (size_t)ch * 3 * nEr4 + pad4((size_t)mta::bwd::NWB * ch * ch)) * 4 + vb +
                           mta::bwd::ms_bytes(mta::bwd_fixed_sizes(bf, d, ch, cq, ck), bp.nRrb, ch, cq);
-    if (lds_a > 160 * 1024 || lds_b > 160 * 1024) return MTA_ERR_UNSUPPORTED;
+    return lds_a <= 160 * 1024 && lds_b <= 160 * 1024;
+}
+
+static int backward_impl(const void *q, const void *k, const void *v, const float *theta_kq,
+                         const float *theta_head, const float *gn_w, const float *gn_b, const float *gate,
+                         const void *dout, const mta_config *cfg, float *dq, float *dk, float *dv,
+                         float *dtheta_kq, float *dtheta_head, float *dgn_w, float *dgn_b, float *dgate,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int vs = validate(cfg);
+    if (vs != MTA_OK) return vs;
+    if (cfg->batch == 0 || cfg->seq_len == 0) return MTA_OK;
+    if (!q || !k || !v || !theta_kq || !theta_head || !gn_w || !gn_b || !dout || !dq || !dk || !dv ||
+        !dtheta_kq || !dtheta_head || !dgn_w || !dgn_b || !workspace || (gate && !dgate))
+        return MTA_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return MTA_ERR_MISALIGNED;
+    const float *fl[] = {theta_kq, theta_head, gn_w, gn_b, gate, dq, dk, dv, dtheta_kq, dtheta_head,
+                         dgn_w, dgn_b, dgate};
+    for (const float *x : fl)
+        if (x && !aligned4(x)) return MTA_ERR_MISALIGNED;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    mta::bwd::BParams bp{};
+    size_t lds_a = 0, lds_b = 0;
+    mta::bwd::BwdFn fn = nullptr;
+    if (!fused_plan(cfg, bp, lds_a, lds_b, fn)) {
+        // every other placement: the backward with the maps in the workspace
+        if (cfg->seq_len > mta::gen::MAX_T) return MTA_ERR_UNSUPPORTED;
+        if (workspace_bytes < workspace_min(cfg)) return MTA_ERR_BAD_VALUE;
+        if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return MTA_ERR_MISALIGNED;
+        mta::gen::GenArgs ga{};
+        ga.q = q; ga.k = k; ga.v = v; ga.dout = dout;
+        ga.theta = theta_kq; ga.w = theta_head; ga.gn_w = gn_w; ga.gn_b = gn_b; ga.gate = gate;
+        ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dtheta = dtheta_kq; ga.dw = dtheta_head;
+        ga.dgn_w = dgn_w; ga.dgn_b = dgn_b; ga.dgate = gate ? dgate : nullptr;
+        ga.B = cfg->batch; ga.H = cfg->heads; ga.T = cfg->seq_len; ga.d = cfg->head_dim;
+        ga.c_q = cfg->c_q; ga.c_k = cfg->c_k; ga.c_h = cfg->c_h;
+        ga.kq_place = cfg->kq_place; ga.head_place = cfg->head_place; ga.bf16 = cfg->dtype == MTA_BF16;
+        ga.eps = cfg->gn_eps; ga.depth_scale = cfg->depth_scale;
+        return mta::gen::backward(ga, workspace, workspace_bytes, s) == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+    }
+    if (workspace_bytes < mta_backward_workspace_size(cfg)) return MTA_ERR_BAD_VALUE;
+
+    const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
+    const int bf = cfg->dtype == MTA_BF16;
+    mta::Params &p = bp.f;
+    p.q = q; p.k = k; p.v = v;
+    p.theta = theta_kq; p.wmix = theta_head; p.gn_w = gn_w; p.gn_b = gn_b; p.gate = gate;
+    p.out = nullptr;
+    bp.dout = dout;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    bp.dtheta = dtheta_kq; bp.dw = dtheta_head; bp.dgn_w = dgn_w; bp.dgn_b = dgn_b; bp.dgate = dgate;
+    const size_t rows = (size_t)cfg->batch * cfg->heads * cfg->seq_len;
+    char *ws = static_cast<char *>(workspace);
+    bp.ws_m = reinterpret_cast<float *>(ws);
+    bp.ws_il = reinterpret_cast<float *>(ws + align256(rows * 4));
+    bp.ws_D = reinterpret_cast<float *>(ws + 2 * align256(rows * 4));
+    bp.ws_dO = ws + 3 * align256(rows * 4);
+    bp.ws_dOl = ws + 3 * align256(rows * 4) + align256(rows * d * (bf ? 2 : 4));
 
     // bf16, d = 128, c_h = 2: the first kernel's work (row statistics, dO, D,
     // GroupNorm and gate gradients) is done by the one-pass head-split forward
@@ -627,7 +701,6 @@ static int backward_impl(const void *q, const void *k, const void *v, const floa
         if (lds_v4 > 160 * 1024) pfn = nullptr;
     }
 
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     mta::bwd::ZeroList z{};
     z.p[0] = dq;          z.n[0] = rows * d;
     z.p[1] = dtheta_kq;   z.n[1] = (size_t)cfg->heads * cq * ck;

@@ -44,7 +44,8 @@ namespace gen {
 
 constexpr int TB = 64;        // map tile edge
 constexpr int NTH = 256;      // threads per workgroup
-constexpr int XP = 96;        // LDS pitch of a stencil input region (64 + 31 columns, padded)
+constexpr int XP = 100;       // LDS pitch of a stencil input region: 64 + 31 columns, padded so
+                              // that the window reads (rows of 4 lanes x 16 B) hit distinct banks
 constexpr int WIN = 48;       // register window of a stencil row: 16 outputs + up to 31 taps
 
 enum Place { KQ_PRE = 0, KQ_POST = 1, KQ_EXACT = 2 };
@@ -213,6 +214,49 @@ __device__ inline void stage_tile(float *dst, int pitch, const float *map, int T
     }
 }
 
+// Register-staged copies of the same two loads, so that the next tile's
+// global reads are in flight while the current tile is multiplied.
+template <typename ET, int D>
+struct RowRegs {
+    float4 v[TB * D / 4 / NTH];
+    __device__ void load(const ET *src, int r0, int T, int tid)
+    {
+#pragma unroll
+        for (int k = 0; k < TB * D / 4 / NTH; ++k) {
+            const int idx = tid + k * NTH, r = idx / (D / 4), c4 = idx - r * (D / 4);
+            v[k] = r0 + r < T ? load4(src + (size_t)(r0 + r) * D + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    __device__ void store(float *dst, int pitch, int tid) const
+    {
+#pragma unroll
+        for (int k = 0; k < TB * D / 4 / NTH; ++k) {
+            const int idx = tid + k * NTH, r = idx / (D / 4), c4 = idx - r * (D / 4);
+            *reinterpret_cast<float4 *>(dst + r * pitch + 4 * c4) = v[k];
+        }
+    }
+};
+
+struct TileRegs {
+    float4 v[TB * TB / 4 / NTH];
+    __device__ void load(const float *map, int Tp, int i0, int j0, int tid)
+    {
+#pragma unroll
+        for (int k = 0; k < TB * TB / 4 / NTH; ++k) {
+            const int idx = tid + k * NTH, r = idx >> 4, c4 = idx & 15;
+            v[k] = load4(map + (size_t)(i0 + r) * Tp + j0 + 4 * c4);
+        }
+    }
+    __device__ void store(float *dst, int pitch, int tid) const
+    {
+#pragma unroll
+        for (int k = 0; k < TB * TB / 4 / NTH; ++k) {
+            const int idx = tid + k * NTH, r = idx >> 4, c4 = idx & 15;
+            *reinterpret_cast<float4 *>(dst + r * pitch + 4 * c4) = v[k];
+        }
+    }
+};
+
 // M[i][j] = alpha sum_c A[i][c] B[j][c] on every band tile (grid: n_band x
 // heads of the chunk).  A: Q (SRC_TENSOR) or dO (SRC_OBUF); B: K or V.
 template <typename DT, int D, int SRCA>
@@ -266,8 +310,8 @@ __global__ void __launch_bounds__(NTH) gen_gemm_nt(GParams p, const void *a_tens
             }
 }
 
-// Out[i][:] = alpha sum_j M[i][j] B[j][:] for the rows of row tile blockIdx.x,
-// j over the band (grid: nt x heads).  Out: the chunk's O buffer or a
+// Out[i][:] = alpha sum_j M[i][j] B[j][:] for the rows of row tile
+// nt - 1 - blockIdx.x, j over the band (grid: nt x heads).  Out: the chunk's O buffer or a
 // [B][H][T][d] fp32 gradient tensor.
 template <typename DT, int D, bool TO_OBUF>
 __global__ void __launch_bounds__(NTH) gen_gemm_mn(GParams p, const float *slot, const void *b_tensor, float *out,
@@ -276,7 +320,7 @@ __global__ void __launch_bounds__(NTH) gen_gemm_mn(GParams p, const float *slot,
     constexpr int MP = TB + 4, BP = D + 16;
     __shared__ __align__(16) float Ms[TB * MP];
     __shared__ __align__(16) float Bs[TB * BP];
-    const int it = blockIdx.x, y = blockIdx.y;
+    const int it = p.nt - 1 - (int)blockIdx.x, y = blockIdx.y;  // the longest rows first
     const HeadIx x = head_ix(p, y);
     const int i0 = it * TB;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -287,10 +331,18 @@ __global__ void __launch_bounds__(NTH) gen_gemm_mn(GParams p, const float *slot,
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int jt_end = it + 1 < p.nt ? it + 1 : p.nt - 1;
+    TileRegs mr;
+    RowRegs<DT, D> br;
+    mr.load(m, p.Tp, i0, 0, tid);
+    br.load(bsrc, 0, p.T, tid);
     for (int jt = 0; jt <= jt_end; ++jt) {
-        stage_tile(Ms, MP, m, p.Tp, i0, jt * TB, tid);
-        stage_rows<DT, D>(Bs, BP, bsrc, jt * TB, p.T, tid);
+        mr.store(Ms, MP, tid);
+        br.store(Bs, BP, tid);
         __syncthreads();
+        if (jt < jt_end) {  // the next tile's reads overlap this tile's products
+            mr.load(m, p.Tp, i0, (jt + 1) * TB, tid);
+            br.load(bsrc, (jt + 1) * TB, p.T, tid);
+        }
 #pragma unroll 4
         for (int kk = 0; kk < TB; kk += 4) {
             const float a = Ms[(16 * w + lr) * MP + kk + lk];
@@ -310,7 +362,7 @@ __global__ void __launch_bounds__(NTH) gen_gemm_mn(GParams p, const float *slot,
 }
 
 // Out[j][:] = alpha sum_i M[i][j] B[i][:] for the keys of column tile
-// blockIdx.x, i over the band (grid: nt x heads); Out a [B][H][T][d] fp32
+// blockIdx.x (the longest columns first), i over the band (grid: nt x heads); Out a [B][H][T][d] fp32
 // gradient tensor.  B: dO (SRC_OBUF) or Q (SRC_TENSOR).
 template <typename DT, int D, int SRCB>
 __global__ void __launch_bounds__(NTH) gen_gemm_tn(GParams p, const float *slot, const void *b_tensor, float *out,
@@ -330,10 +382,19 @@ __global__ void __launch_bounds__(NTH) gen_gemm_tn(GParams p, const float *slot,
     f32x4 acc[D / 16];
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int it = jt > 0 ? jt - 1 : 0; it < p.nt; ++it) {
-        stage_tile(Ms, MP, m, p.Tp, it * TB, j0, tid);
-        stage_rows<BT, D>(Bs, BP, bsrc, it * TB, p.T, tid);
+    const int it0 = jt > 0 ? jt - 1 : 0;
+    TileRegs mr;
+    RowRegs<BT, D> br;
+    mr.load(m, p.Tp, it0 * TB, j0, tid);
+    br.load(bsrc, it0 * TB, p.T, tid);
+    for (int it = it0; it < p.nt; ++it) {
+        mr.store(Ms, MP, tid);
+        br.store(Bs, BP, tid);
         __syncthreads();
+        if (it + 1 < p.nt) {  // the next tile's reads overlap this tile's products
+            mr.load(m, p.Tp, (it + 1) * TB, j0, tid);
+            br.load(bsrc, (it + 1) * TB, p.T, tid);
+        }
 #pragma unroll 4
         for (int kk = 0; kk < TB; kk += 4) {
             const float a = Ms[(kk + lk) * MP + 16 * w + lr];
@@ -357,6 +418,32 @@ __global__ void __launch_bounds__(NTH) gen_gemm_tn(GParams p, const float *slot,
 // 64 x 64 output tile; for each kernel row it loads a window of 16 + c_k - 1
 // input values into registers and walks the taps with register indices.
 
+// Stages rows r0 .. r0 + nr - 1, columns c0 .. c0 + XP - 1 of a map into LDS
+// (pitch XP): map[r][c] where 0 <= r < T, c < c0 + ncol and 0 <= c <= r +
+// cadd, else zero.  25 float4 per row, 10 rows per pass (threads 250..255
+// idle); no barrier inside.
+__device__ inline void stage_region(float *dst, const float *m, const GParams &p, int r0, int c0, int nr,
+                                    int ncol, int cadd, int tid)
+{
+    static_assert(XP == 100, "25 float4 per row");
+    if (tid >= 250) return;
+    const int c4 = tid % 25, rsub = tid / 25;
+    for (int rr = rsub; rr < nr; rr += 10) {
+        const int r = r0 + rr;
+        const bool rok = r >= 0 && r < p.T;
+        const float *row = m + (size_t)(rok ? r : 0) * p.Tp;
+        const int cmax = min(p.T - 1, r + cadd);
+        float4 v;
+        float *vv = reinterpret_cast<float *>(&v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int cc = 4 * c4 + e, c = c0 + cc;
+            vv[e] = (rok && cc < ncol && c >= 0 && c <= cmax) ? row[c] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(dst + rr * XP + 4 * c4) = v;
+    }
+}
+
 // Input region of the forward stencil and of the kernel gradient: rows
 // i0 - (c_q - 1) .. i0 + 63, columns j0 - hi .. j0 + 63 - lo (hi = c_k - 1 -
 // floor(c_k/2), lo = -floor(c_k/2)), with the mode's masks:
@@ -367,16 +454,8 @@ template <int MODE>
 __device__ inline void stage_input(float *Xs, const float *m, const GParams &p, int i0, int j0, int tid)
 {
     const int hi = p.c_k - 1 - p.c_k / 2;
-    const int nr = TB + p.c_q - 1;
-    const int ncol = TB + p.c_k - 1;
-    for (int idx = tid; idx < nr * XP; idx += NTH) {
-        const int rr = idx / XP, cc = idx - rr * XP;
-        const int r = i0 - (p.c_q - 1) + rr, c = j0 - hi + cc;
-        float v = 0.f;
-        const int cmax = MODE == M_EXACT ? r + p.c_q - 1 : r;
-        if (cc < ncol && r >= 0 && r < p.T && c >= 0 && c < p.T && c <= cmax) v = m[(size_t)r * p.Tp + c];
-        Xs[idx] = v;
-    }
+    stage_region(Xs, m, p, i0 - (p.c_q - 1), j0 - hi, TB + p.c_q - 1, TB + p.c_k - 1,
+                 MODE == M_EXACT ? p.c_q - 1 : 0, tid);
 }
 
 // Loads the register window win[x] = row[16 q + x] of an LDS region row.
@@ -394,11 +473,19 @@ __device__ inline void load_win(float (&win)[WIN], const float *row)
 
 // out = Eq. 4 on the input map (mode's masks), then Mask_0, on every band
 // tile (grid: n_band x heads).
+// Dynamic LDS of the stencil kernels: `regions` input regions of
+// (64 + c_q - 1) x XP floats, then the kernel taps (and their gradient).
+inline size_t conv_lds_bytes(int c_q, int regions)
+{
+    return ((size_t)regions * (TB + c_q - 1) * XP + 2 * MAX_CQ * 32) * sizeof(float);
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(NTH) gen_conv_fwd(GParams p, const float *in_slot, float *out_slot)
 {
-    __shared__ __align__(16) float Xs[(TB + MAX_CQ - 1) * XP];
-    __shared__ float th[MAX_CQ * 32];
+    extern __shared__ __align__(16) float lds_dyn[];
+    float *Xs = lds_dyn;
+    float *th = Xs + (TB + p.c_q - 1) * XP;
     int it, jt;
     band_tile(blockIdx.x, p.nt, it, jt);
     const int y = blockIdx.y;
@@ -459,10 +546,11 @@ template <int MODE>
 __global__ void __launch_bounds__(NTH) gen_conv_bwd(GParams p, const float *g_slot, const float *in_slot,
                                                     float *din_slot)
 {
-    __shared__ __align__(16) float Gs[(TB + MAX_CQ - 1) * XP];
-    __shared__ __align__(16) float Xs[(TB + MAX_CQ - 1) * XP];
-    __shared__ float th[MAX_CQ * 32];
-    __shared__ float dth[MAX_CQ * 32];
+    extern __shared__ __align__(16) float lds_dyn[];
+    float *Gs = lds_dyn;
+    float *Xs = Gs + (TB + p.c_q - 1) * XP;
+    float *th = Xs + (TB + p.c_q - 1) * XP;
+    float *dth = th + MAX_CQ * 32;
     int it, jt;
     band_tile(blockIdx.x, p.nt, it, jt);
     const int y = blockIdx.y;
@@ -483,14 +571,7 @@ __global__ void __launch_bounds__(NTH) gen_conv_bwd(GParams p, const float *g_sl
     }
     const float *gm = map_of(const_cast<float *>(g_slot), p, y);
     // G region: rows i0 .. i0 + 63 + c_q - 1, columns j0 + lo .. (Mask_0 applied)
-    const int nr = TB + p.c_q - 1, ncol = TB + p.c_k - 1;
-    for (int idx = tid; idx < nr * XP; idx += NTH) {
-        const int rr = idx / XP, cc = idx - rr * XP;
-        const int gi = i0 + rr, gj = j0 + lo + cc;
-        float v = 0.f;
-        if (cc < ncol && gi < p.T && gj >= 0 && gj <= gi) v = gm[(size_t)gi * p.Tp + gj];
-        Gs[idx] = v;
-    }
+    stage_region(Gs, gm, p, i0, j0 + lo, TB + p.c_q - 1, TB + p.c_k - 1, 0, tid);
     if (!upper) stage_input<MODE>(Xs, map_of(const_cast<float *>(in_slot), p, y), p, i0, j0, tid);
     for (int t = tid; t < p.c_q * p.c_k; t += NTH) {
         th[t] = p.theta[(size_t)x.h * p.c_q * p.c_k + t];

@@ -71,9 +71,28 @@ hipError_t mix(bool fwd, const GParams &p, const float *in, float *out, hipStrea
     }
 }
 
+// Launches a stencil kernel with its dynamic LDS (above 64 KB for large c_q).
+template <typename... A>
+hipError_t launch_conv(void (*k)(GParams, A...), dim3 grid, size_t lds, hipStream_t s, const GParams &p,
+                       A... args)
+{
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(NTH), lds, s, p, args...);
+    return hipGetLastError();
+}
+
+#define GEN_TRY(x)                      \
+    do {                                \
+        const hipError_t e_ = (x);      \
+        if (e_ != hipSuccess) return e_; \
+    } while (0)
+
 template <typename DT, int D>
 hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipStream_t s)
 {
+    const size_t lds1 = conv_lds_bytes(p.c_q, 1), lds2 = conv_lds_bytes(p.c_q, 2);
     const int heads = p.nu * p.c_h;
     const dim3 band(p.n_band, heads), rows_t(p.nt, heads), rows4(p.Tp / 4, heads);
     const dim3 blk(NTH);
@@ -84,11 +103,11 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
     hipLaunchKernelGGL((gen_gemm_nt<DT, D, SRC_TENSOR>), band, blk, 0, s, p, p.q, p.k, slot[sl.S], p.inv_sqrt_d);
     GEN_CHECK();
     if (kq != KQ_POST) {
+        const float *in = slot[sl.S];
         if (cmode == M_EXACT)
-            hipLaunchKernelGGL(gen_conv_fwd<M_EXACT>, band, blk, 0, s, p, slot[sl.S], slot[sl.C]);
+            GEN_TRY(launch_conv(gen_conv_fwd<M_EXACT>, band, lds1, s, p, in, slot[sl.C]));
         else
-            hipLaunchKernelGGL(gen_conv_fwd<M_PRE>, band, blk, 0, s, p, slot[sl.S], slot[sl.C]);
-        GEN_CHECK();
+            GEN_TRY(launch_conv(gen_conv_fwd<M_PRE>, band, lds1, s, p, in, slot[sl.C]));
     }
     if (hp == KQ_PRE) {
         const hipError_t e = mix(true, p, slot[sl.C], slot[sl.L], s);
@@ -97,8 +116,8 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
     hipLaunchKernelGGL(gen_softmax_fwd, rows4, blk, 0, s, p, slot[sl.P]);
     GEN_CHECK();
     if (kq == KQ_POST) {
-        hipLaunchKernelGGL(gen_conv_fwd<M_POST>, band, blk, 0, s, p, slot[sl.P], slot[sl.P2]);
-        GEN_CHECK();
+        const float *in = slot[sl.P];
+        GEN_TRY(launch_conv(gen_conv_fwd<M_POST>, band, lds1, s, p, in, slot[sl.P2]));
     }
     if (hp == KQ_POST) {
         const hipError_t e = mix(true, p, slot[sl.P2], slot[sl.P3], s);
@@ -120,8 +139,8 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
         if (e != hipSuccess) return e;
     }
     if (kq == KQ_POST) {  // dP2 -> dP, dtheta
-        hipLaunchKernelGGL(gen_conv_bwd<M_POST>, band, blk, 0, s, p, slot[cur], slot[sl.P], slot[other]);
-        GEN_CHECK();
+        const float *g = slot[cur], *in = slot[sl.P];
+        GEN_TRY(launch_conv(gen_conv_bwd<M_POST>, band, lds2, s, p, g, in, slot[other]));
         const int t = cur;
         cur = other;
         other = t;
@@ -133,11 +152,11 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
         if (e != hipSuccess) return e;
     }
     if (kq != KQ_POST) {  // dC -> dS, dtheta
+        const float *g = slot[cur], *in = slot[sl.S];
         if (cmode == M_EXACT)
-            hipLaunchKernelGGL(gen_conv_bwd<M_EXACT>, band, blk, 0, s, p, slot[cur], slot[sl.S], slot[other]);
+            GEN_TRY(launch_conv(gen_conv_bwd<M_EXACT>, band, lds2, s, p, g, in, slot[other]));
         else
-            hipLaunchKernelGGL(gen_conv_bwd<M_PRE>, band, blk, 0, s, p, slot[cur], slot[sl.S], slot[other]);
-        GEN_CHECK();
+            GEN_TRY(launch_conv(gen_conv_bwd<M_PRE>, band, lds2, s, p, g, in, slot[other]));
         const int t = cur;
         cur = other;
         other = t;

@@ -134,7 +134,8 @@ def test_small_full(cfg):
     inp = I.generate(cfg)
     got = run_gpu(cfg, inp)
     ref = oracle.forward_cfg(cfg, inp)
-    compare(cfg, got, ref, what="small")
+    err, tol = compare(cfg, got, ref, what="small")
+    _say(f"[parity]   closest element: err {err:.3e} of bar {tol:.3e}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "toy"])

@@ -71,7 +71,8 @@ def test_layer_forms(cfg):
     inp = I.generate(cfg)
     got = run_gpu(cfg, inp)
     ref = oracle.forward_cfg(cfg, inp)
-    compare(cfg, got, ref, what="layer")
+    err, tol = compare(cfg, got, ref, what="layer")
+    _say(f"[layer]   closest element: err {err:.3e} of bar {tol:.3e}")
 
 
 def _extra_mix(cfg, seed):

@@ -459,15 +459,16 @@ __device__ inline void stage_input(float *Xs, const float *m, const GParams &p, 
 }
 
 // Loads the register window win[x] = row[16 q + x] of an LDS region row.
+// (16-byte reads through a native vector type, so that they stay ds_read_b128)
 __device__ inline void load_win(float (&win)[WIN], const float *row)
 {
 #pragma unroll
     for (int x = 0; x < WIN; x += 4) {
-        const float4 t = *reinterpret_cast<const float4 *>(row + x);
-        win[x] = t.x;
-        win[x + 1] = t.y;
-        win[x + 2] = t.z;
-        win[x + 3] = t.w;
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(row + x);
+        win[x] = t[0];
+        win[x + 1] = t[1];
+        win[x + 2] = t[2];
+        win[x + 3] = t[3];
     }
 }
 

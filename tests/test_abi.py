@@ -38,10 +38,10 @@ def test_exports_every_declared_symbol(lib):
     ("needle4k", "mta_fwd_v4"), ("needle4k_exact", "mta_fwd_v4"), ("layer2k", "mta_fwd_v4"),
     ("sweep8k_8x15_ch2_pre", "mta_fwd_v4"),
     ("sweep8k_6x11_ch2_post", "mta_fwd_v4 (two passes"), ("sweep8k_4x9_ch2_post", "mta_fwd_v4 (two passes"),
-    # c_h = 4: the fp16 matrix-core stencil fits in LDS except for 8x15 after the softmax
-    ("sweep8k_8x15_ch4_pre", "mta_fwd_v2 (two passes, matrix-core stencil)"),
-    ("sweep8k_6x11_ch4_post", "mta_fwd_v2 (two passes, matrix-core stencil)"),
-    ("sweep8k_8x15_ch4_post", "mta_fwd_v2 (two passes, VALU stencil)"),
+    # c_h = 4: the head-split kernel per output head pair, one sweep per source pair
+    ("sweep8k_8x15_ch4_pre", "mta_fwd_v4 (four-head groups: two source-pair sweeps, head-split"),
+    ("sweep8k_6x11_ch4_post", "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes"),
+    ("sweep8k_8x15_ch4_post", "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes"),
     ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
     ("needle4k_3d", "mta_fwd_v4 (one pass, head-split waves, 3D"), ("needle4k_repeat", "mta_fwd_layer"),
 ])

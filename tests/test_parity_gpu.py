@@ -95,6 +95,22 @@ def _small_cases():
             c.append(I.small(f"hot_bf16_ch{ch}_H{H}_{cq}x{ck}_kq{kq}", B=1, H=H, T=256, d=128, c_q=cq, c_k=ck,
                              c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02,
                              layer=4, needles=6, needle_scale=9.0, needle_on_key=True, seed=760 + ch + H + kq))
+    # four-head groups on the head-split kernel (one workgroup per output head
+    # pair, one sweep per source pair): two groups, every instantiated size and
+    # placement, the workloads' near-identity mixing (weights N(0, 0.05) around
+    # I: the pairs' cross terms carry a few percent of each output)
+    for (cq, ck, kq) in ((6, 11, P), (6, 11, I.PRE_EXACT), (4, 9, Q), (8, 15, P), (8, 15, Q), (1, 1, Q)):
+        c.append(I.small(f"quad_bf16_{cq}x{ck}_kq{kq}", B=2, H=8, T=150, d=128, c_q=cq, c_k=ck, c_h=4,
+                         kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05,
+                         seed=900 + cq + ck + kq))
+    for kq in (P, Q):
+        c.append(I.small(f"quad_bf16_gated_kq{kq}", B=2, H=8, T=150, d=128, c_q=6, c_k=11, c_h=4, kq_place=kq,
+                         dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True,
+                         gate_std=1.0, gn_random=True, seed=940 + kq))
+    for T in (1, 3, 64, 65):
+        for kq in (P, Q):
+            c.append(I.small(f"quad_bf16_T{T}_kq{kq}", B=1, H=4, T=T, d=128, c_q=6, c_k=11, c_h=4, kq_place=kq,
+                             dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=950 + T + kq))
     # key-query convolution with Eq. 4's exact indicator: fast and runtime-sized
     # stencils, odd and even c_k, pre-softmax head mix, c_h = 4, both dtypes
     E = I.PRE_EXACT

@@ -161,6 +161,27 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 pl.grid = p.n_qt * p.units;
             }
         }
+        if (!fn && ch == 4 && !hpre) {
+            // four-head groups: the head-split kernel per output head pair, one
+            // sweep per source pair (the grid counts output pairs)
+            fn = mta::find_launch_v4_quad(d, cq, ck, post, exact);
+            if (fn) {
+                p.ncb = 5;
+                p.pitch = p.ncb * 16 + 4;
+                p.G = cfg->heads / 2;
+                p.units = cfg->batch * p.G;
+                pl.grid = p.n_qt * p.units;
+                lds = (size_t)mta::v4::layout(cq, ck, false, post != 0).total;
+                if (lds > LDS_MAX) fn = nullptr;
+                else pl.name = post ? "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes, head-split waves, fp16 matrix-core stencil)"
+                                    : "mta_fwd_v4 (four-head groups: two source-pair sweeps, head-split waves, fp16 matrix-core stencil)";
+            }
+            if (!fn) {
+                p.G = cfg->heads / ch;
+                p.units = cfg->batch * p.G;
+                pl.grid = p.n_qt * p.units;
+            }
+        }
         // else two passes: stencil on the matrix cores first, then the fp32 VALU stencil
         for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {
             // the matrix-core stencil reads a 32-column window past each

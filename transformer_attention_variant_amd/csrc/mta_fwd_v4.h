@@ -448,20 +448,32 @@ struct PrepArgs {
 // heads of the workgroup are neighbouring single-head groups, so only the
 // U[a][a] products are formed and each output head is its own head's mixed map
 // (the 1x1 mixing weight w_h, p.wmix[h]).  p.G and p.units count head pairs.
-template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false, bool NOMIX = false>
+template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false, bool NOMIX = false,
+          bool QUAD = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     static_assert(!(POST && (EXACT || PREP)), "post-softmax form: two-pass masks, forward only");
     static_assert(!(C3D && (EXACT || PREP || POST)), "3D form: two-pass masks, forward only");
     static_assert(!(NOMIX && (C3D || PREP)), "single-head groups: the forward of the per-head kernels");
+    static_assert(!(QUAD && (C3D || PREP || NOMIX)), "four-head groups: the forward with the mix after the softmax");
     constexpr bool DIAG = C3D || NOMIX;  // output head a uses only source head a
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63;
+    int pi = 0;  // QUAD: source pair of this sweep (see below)
+sweep:
+    // QUAD: the thread and workgroup indices pass through an empty asm that
+    // depends on the sweep, so that everything derived from them is computed
+    // again in each sweep rather than held across both
+    int tid0 = threadIdx.x, blk0 = blockIdx.x;
+    if constexpr (QUAD) {
+        asm volatile("" : "+v"(tid0) : "s"(pi));
+        asm volatile("" : "+s"(blk0) : "s"(pi));
+    }
+    const int tid = tid0, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers and branches
     const int rw = wave & 3, hs = wave >> 2;  // row block; head (stencil) = d half (P.V)
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int L = blockIdx.x;
+    const int L = blk0;
     const int unit = L % p.units;
     const int qt = p.n_qt - 1 - L / p.units;
     const int b = unit / p.G, g = unit % p.G;
@@ -486,11 +498,20 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     unsigned char *crbuf = smem + lay.cr_off;
     constexpr int CORR = POST ? 0 : (PREP ? 2 : 1);
 
+    // QUAD (four-head groups): the workgroup owns output heads h0, h0 + 1 (output
+    // pair g & 1 of the four-head group g / 2); O^a sums over the group's two
+    // source pairs, sum_s w_as U_{s,a} / l_s, one sweep over the key tiles per
+    // source pair with the two-head machinery below (that pair's logits,
+    // stencils and softmax statistics; P.V with the output pair's V).  The
+    // first sweep's share waits in this workgroup's own rows of the output
+    // (fp16) until the second sweep adds it.
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
     const size_t base0 = ((size_t)b * p.H + h0) * hstride;
-    const bf16_t *Q = reinterpret_cast<const bf16_t *>(p.q) + base0;
-    const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + base0;
+    const int hsrc0 = QUAD ? 4 * (g >> 1) + 2 * pi : h0;  // source heads of this sweep
+    const size_t sbase = ((size_t)b * p.H + hsrc0) * hstride;
+    const bf16_t *Q = reinterpret_cast<const bf16_t *>(p.q) + sbase;
+    const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + sbase;
     const bf16_t *V = reinterpret_cast<const bf16_t *>(p.v) + base0;
 
     // K of key tile 0 (POST: the statistics pass's 64 keys) and the Q rows above
@@ -522,10 +543,12 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     } else {
         for (int i = tid; i < CH * CQ * CKP; i += NT) {
             const int a = i / (CQ * CKP), r = (i / CKP) % CQ, c = i % CKP;
-            th_s[i] = c < CK ? p.theta[((size_t)(h0 + a) * CQ + r) * CK + c] : 0.f;
+            th_s[i] = c < CK ? p.theta[((size_t)(hsrc0 + a) * CQ + r) * CK + c] : 0.f;
         }
+        // w_s[a][s]: output head a of the pair, source head s of this sweep
         if (tid < CH * CH)
             w_s[tid] = NOMIX ? ((tid / CH == tid % CH) ? p.wmix[h0 + tid / CH] : 0.f)
+                     : QUAD  ? p.wmix[(size_t)(g >> 1) * 16 + (2 * (g & 1) + tid / CH) * 4 + 2 * pi + tid % CH]
                              : p.wmix[(size_t)g * CH * CH + tid];
     }
     wait_vm_all();
@@ -1139,6 +1162,34 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
         return;
     }
 
+    if constexpr (QUAD) {
+        // hand the first sweep's share over through the output rows this
+        // workgroup alone writes (fp16 in the bf16 slots; the same lane reads
+        // back what it wrote)
+        f16_t *part = reinterpret_cast<f16_t *>(p.out);
+#pragma unroll
+        for (int a = 0; a < CH; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = i0 + 16 * rw + 4 * g4 + r;
+                if (row < T) {
+                    f16_t *cell = part + ((size_t)b * p.H + h0 + a) * hstride + (size_t)row * D + dbase + l16;
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
+                        if (pi == 0)
+                            cell[16 * nb] = (f16_t)f16_range(acc[a][nb][r]);
+                        else
+                            acc[a][nb][r] += (float)cell[16 * nb];
+                    }
+                }
+            }
+        if (pi == 0) {
+            pi = 1;
+            __syncthreads();  // every wave is done with this sweep's LDS
+            goto sweep;
+        }
+    }
+
     // ---------------- epilogue: GroupNorm over d, head factor, store -------
     float mu[CH][4];
 #pragma unroll
@@ -1206,10 +1257,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     }
 }
 
-template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false>
+template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false, bool QUAD = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX, QUAD>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -48,4 +48,23 @@ LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
     return nullptr;
 }
 
+// Four-head groups (c_h = 4), one workgroup per output head pair sweeping the
+// group's two source pairs; either key-query placement; the caller counts
+// output pairs in p.G.
+#define MTA_V4Q_SIZE(CQ_, CK_)                                                                         \
+    if (cq == CQ_ && ck == CK_)                                                                        \
+        return post ? &v4::launch<CQ_, CK_, false, true, false, false, true>                          \
+                    : (exact ? &v4::launch<CQ_, CK_, true, false, false, false, true>                 \
+                             : &v4::launch<CQ_, CK_, false, false, false, false, true>);
+
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact)
+{
+    if (d != 128 || (post && exact)) return nullptr;
+    MTA_V4Q_SIZE(1, 1)
+    MTA_V4Q_SIZE(4, 9)
+    MTA_V4Q_SIZE(6, 11)
+    MTA_V4Q_SIZE(8, 15)
+    return nullptr;
+}
+
 }  // namespace mta

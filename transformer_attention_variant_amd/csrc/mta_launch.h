@@ -43,6 +43,9 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
 LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int exact);
 // Its 3D-convolution form (two-pass masks, no head mix); null when not instantiated.
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
+// Four-head groups: the head-split kernel per output head pair, two source-pair
+// sweeps (p.G counts output pairs); null when not instantiated.
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact);
 // Their gradient-preparation variants (key-query convolution before the
 // softmax, head mix after it); null when not instantiated.
 namespace v4 {

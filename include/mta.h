@@ -61,12 +61,19 @@ extern "C" {
  * of the head-split and two-pass bf16 kernels runs on the matrix cores with
  * fp16 operands (the logits or probabilities and the taps rounded to nearest,
  * 11 significant bits; magnitudes beyond 65504 clamped to 65504, which only
- * logits past ~5800 in natural units reach) and float32 accumulation.  In the
- * head-split kernels (head groups of two) the centre tap (query offset 0, key
- * offset 0) before the softmax is applied to the float32 logits, so a kernel
- * near the identity keeps float32 accuracy at large logits; the other kernels
- * round it like the other taps (2^-11 relative to the logit).  mta_kernel_name
- * tells which kernel a configuration runs. */
+ * logits past ~5800 in natural units reach) and float32 accumulation.  Before
+ * the softmax the centre tap (query offset 0, key offset 0) keeps float32
+ * accuracy: the head-split kernels apply it to the float32 logits, the
+ * two-pass kernel adds a correction wherever the fp16 centre product would
+ * round coarsely, so a kernel near the identity stays accurate at large
+ * logits.  The head-split kernels (bf16, d = 128, head mix after the softmax,
+ * the instantiated kernel sizes, c_h 1, 2 or 4) round each head's
+ * probabilities to bf16 before the head mix, which they apply to the per-head
+ * A·V products: under strongly cancelling mixing weights the output's error
+ * relative to its size grows accordingly.  With four-head groups the first
+ * source head pair's share of the output waits in the output buffer as fp16
+ * until the second pair's is added (shares beyond 65504 in magnitude clamp).
+ * mta_kernel_name tells which kernel a configuration runs. */
 #define MTA_F32 0
 #define MTA_BF16 1
 

@@ -38,10 +38,7 @@ FLUSH_MIB = 512
 # the HIP sources each forward kernel is built from (its header chain, its
 # instantiation unit and the launch helpers)
 KERNEL_SOURCES = {
-    "mta_fwd_v4": ["mta_fwd_v4.h", "mta_tiles.h", "mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v4.hip",
-                   "mta_launch.h"],
-    "mta_fwd_v2": ["mta_fwd_v2.h", "mta_fwd_kernel.h", "mta_inst_v2.hip", "mta_inst_v2.inc",
-                   "mta_inst_v2_exact.hip", "mta_launch.h"],
+    "mta_fwd_v4": ["mta_fwd_v4.h", "mta_tiles.h", "mta_fwd_kernel.h", "mta_inst_v4.hip", "mta_launch.h"],
     "mta_fwd_kernel": ["mta_fwd_kernel.h", "mta_inst.inc", "mta_inst_bf16.hip", "mta_inst_f32.hip",
                        "mta_launch.h"],
 }
@@ -65,7 +62,7 @@ def kernel_sources_hash(kernel: str = "") -> str:
 def stencil_on_matrix_cores(kname) -> bool:
     """Whether the named kernel runs the key-query stencil on the matrix cores
     (fp16 operands) rather than on the fp32 vector ALUs."""
-    return kname is not None and ("mta_fwd_v4" in kname or "matrix-core" in kname)
+    return kname is not None and kname.startswith("mta_fwd_v4")
 
 
 def parse():

@@ -58,15 +58,12 @@ extern "C" {
  * always float32.  Intermediate arithmetic is float32 (contractions accumulate
  * in float32 on the matrix cores; with MTA_BF16 the probabilities enter the A·V
  * product as bf16), with one exception: for MTA_BF16 the key-query convolution
- * of the head-split and two-pass bf16 kernels runs on the matrix cores with
- * fp16 operands (the logits or probabilities and the taps rounded to nearest,
+ * of the head-split kernels runs on the matrix cores with fp16 operands (the logits or probabilities and the taps rounded to nearest,
  * 11 significant bits; magnitudes beyond 65504 clamped to 65504, which only
  * logits past ~5800 in natural units reach) and float32 accumulation.  Before
  * the softmax the centre tap (query offset 0, key offset 0) keeps float32
- * accuracy: the head-split kernels apply it to the float32 logits, the
- * two-pass kernel adds a correction wherever the fp16 centre product would
- * round coarsely, so a kernel near the identity stays accurate at large
- * logits.  The head-split kernels (bf16, d = 128, head mix after the softmax,
+ * accuracy: the head-split kernels apply it to the float32 logits, so a
+ * kernel near the identity stays accurate at large logits.  The head-split kernels (bf16, d = 128, head mix after the softmax,
  * the instantiated kernel sizes, c_h 1, 2 or 4) round each head's
  * probabilities to bf16 before the head mix, which they apply to the per-head
  * A·V products: under strongly cancelling mixing weights the output's error

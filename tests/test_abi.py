@@ -62,13 +62,13 @@ def test_kernel_selection_head_mix_before_softmax(lib, kq, expect):
     assert got is not None and got.startswith(expect), got
 
 
-@pytest.mark.parametrize("kq", [I.PRE, I.PRE_EXACT])
-def test_kernel_selection_single_head_groups(lib, kq):
+@pytest.mark.parametrize("kq,form", [(I.PRE, "one pass"), (I.PRE_EXACT, "one pass"), (I.POST, "two passes")])
+def test_kernel_selection_single_head_groups(lib, kq, form):
     """Groups of one head run the head-split kernel two groups at a time when
     the head count is even, else the general kernel."""
     cfg = I.small("ch1", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=1, kq_place=kq, dtype="bf16")
     got = binding.kernel_name(cfg)
-    assert got is not None and got.startswith("mta_fwd_v4 (one pass, head-split waves, head pairs"), got
+    assert got is not None and got.startswith(f"mta_fwd_v4 ({form}, head-split waves, head pairs"), got
     odd = I.with_(cfg, H=3)
     got = binding.kernel_name(odd)
     assert got is not None and got.startswith("mta_fwd_kernel"), got

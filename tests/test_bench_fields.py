@@ -17,8 +17,9 @@ def _bench():
 def test_stencil_unit_by_kernel_name():
     b = _bench()
     assert b.stencil_on_matrix_cores("mta_fwd_v4 (one pass, head-split waves, fp16 matrix-core stencil)")
-    assert b.stencil_on_matrix_cores("mta_fwd_v2 (two passes, matrix-core stencil)")
-    assert not b.stencil_on_matrix_cores("mta_fwd_v2 (two passes, VALU stencil)")
+    assert b.stencil_on_matrix_cores("mta_fwd_v4 (four-head groups: two source-pair sweeps, head-split waves, "
+                                     "fp16 matrix-core stencil)")
+    assert not b.stencil_on_matrix_cores("mta_fwd_layer (fp32 VALU stencils)")
     assert not b.stencil_on_matrix_cores("mta_fwd_kernel (two passes, general)")
     assert not b.stencil_on_matrix_cores(None)
 

@@ -58,10 +58,16 @@ def _small_cases():
         c.append(I.small(f"bf16_{cq}x{ck}_hpre_T{T}", B=2, H=4, T=T, d=128, c_q=cq, c_k=ck, c_h=2, kq_place=P,
                          head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.3,
                          seed=260 + cq + T))
-    # one head per group (the one-pass kernel with a single accumulator pair)
-    for kq in (P, I.PRE_EXACT):
+    # one head per group: head pairs of single-head groups on the head-split
+    # kernel (one pass before the softmax, two after it); odd H: the general kernel
+    for kq in (P, I.PRE_EXACT, Q):
         c.append(I.small(f"bf16_6x11_ch1_kq{kq}", B=2, H=2, T=150, d=128, c_q=6, c_k=11, c_h=1, kq_place=kq,
                          dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=250 + kq))
+    for (cq, ck, T) in ((4, 9, 197), (8, 15, 65), (1, 1, 130)):
+        c.append(I.small(f"bf16_{cq}x{ck}_ch1_post_T{T}", B=1, H=4, T=T, d=128, c_q=cq, c_k=ck, c_h=1,
+                         kq_place=Q, dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=255 + cq + T))
+    c.append(I.small("bf16_6x11_ch1_post_H3", B=1, H=3, T=150, d=128, c_q=6, c_k=11, c_h=1, kq_place=Q,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=259))
     # runtime-sized stencils: odd/even c_k, head mix before the softmax, d in {32,64,128}
     for (d, dt) in ((32, "bf16"), (64, "bf16"), (128, "f32"), (128, "bf16")):
         for kq in (P, Q):
@@ -90,7 +96,7 @@ def _small_cases():
                              layer=4, needles=6, needle_scale=9.0, needle_on_key=True,
                              seed=730 + cq + T + kq))
         # the same through single-head groups (head pairs; odd H: the general
-        # kernel) and groups of four (the two-pass kernel)
+        # kernel) and four-head groups
         for (ch, H, cq, ck) in ((1, 2, 6, 11), (1, 3, 6, 11), (4, 4, 6, 11), (4, 4, 8, 15)):
             c.append(I.small(f"hot_bf16_ch{ch}_H{H}_{cq}x{ck}_kq{kq}", B=1, H=H, T=256, d=128, c_q=cq, c_k=ck,
                              c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02,

@@ -6,7 +6,6 @@
 #include <mutex>
 
 #include "mta.h"
-#include "mta_fwd_v2.h"
 #include "mta_fwd_v4.h"
 #include "mta_fwd_layer.h"
 #include "mta_bwd.h"
@@ -116,10 +115,11 @@ static int make_plan(const mta_config *cfg, Plan &pl)
     size_t lds = 0;
     if (cfg->dtype == MTA_BF16) {
         const int ncb0 = p.ncb, pitch0 = p.pitch;
-        // the head-split kernel for c_h = 2 with the head mix after the softmax
-        // (one pass with online softmax statistics when the key-query
-        // convolution comes before the softmax, two passes when after), else one
-        // pass with the key-split kernel (c_h = 1, convolution before the softmax)
+        // the head-split kernel in the form that fits the grouping: c_h = 2 with
+        // the head mix after the softmax (one pass with online softmax
+        // statistics when the key-query convolution comes before the softmax,
+        // two passes when after), the 3D form for the head mix before it, head
+        // pairs of single-head groups, four-head groups; else the general kernel
         fn = mta::find_launch_v4(d, ch, cq, ck, post, exact, hpre);
         if (fn) {
             p.ncb = 5;
@@ -141,19 +141,20 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 else pl.name = "mta_fwd_v4 (one pass, head-split waves, pre-softmax head mix as a 3D convolution, fp16 matrix-core stencil)";
             }
         }
-        if (!fn && ch == 1 && !post && cfg->heads % 2 == 0) {
+        if (!fn && ch == 1 && cfg->heads % 2 == 0) {
             // single-head groups, two per workgroup: the head-split kernel with
             // the 1x1 mix of each head (the grid counts head pairs)
-            fn = mta::find_launch_v4_pairs(d, cq, ck, exact);
+            fn = mta::find_launch_v4_pairs(d, cq, ck, post, exact);
             if (fn) {
                 p.ncb = 5;
                 p.pitch = p.ncb * 16 + 4;
                 p.G = cfg->heads / 2;
                 p.units = cfg->batch * p.G;
                 pl.grid = p.n_qt * p.units;
-                lds = (size_t)mta::v4::layout(cq, ck, false, false).total;
+                lds = (size_t)mta::v4::layout(cq, ck, false, post != 0).total;
                 if (lds > LDS_MAX) fn = nullptr;
-                else pl.name = "mta_fwd_v4 (one pass, head-split waves, head pairs of single-head groups, fp16 matrix-core stencil)";
+                else pl.name = post ? "mta_fwd_v4 (two passes, head-split waves, head pairs of single-head groups, fp16 matrix-core stencil)"
+                                    : "mta_fwd_v4 (one pass, head-split waves, head pairs of single-head groups, fp16 matrix-core stencil)";
             }
             if (!fn) {
                 p.G = cfg->heads / ch;
@@ -180,20 +181,6 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 p.G = cfg->heads / ch;
                 p.units = cfg->batch * p.G;
                 pl.grid = p.n_qt * p.units;
-            }
-        }
-        // else two passes: stencil on the matrix cores first, then the fp32 VALU stencil
-        for (int ms = (ck <= 17) ? 1 : 0; ms >= 0 && !fn; --ms) {
-            // the matrix-core stencil reads a 32-column window past each
-            // 16-key output block: the tile must span at least 80 columns
-            p.ncb = (ms && ncb0 < 5) ? 5 : ncb0;
-            p.pitch = p.ncb * 16 + 4;
-            fn = mta::find_launch_v2(d, ch, cq, ck, post, exact, hpre, ms);
-            if (fn) {
-                lds = (size_t)mta::v2::layout(d, ch, cq, ck, p.ncb, p.pitch, ms != 0, post != 0).total;
-                if (lds > LDS_MAX) fn = nullptr;
-                else pl.name = ms ? "mta_fwd_v2 (two passes, matrix-core stencil)"
-                                  : "mta_fwd_v2 (two passes, VALU stencil)";
             }
         }
         if (!fn) {

@@ -1,14 +1,18 @@
-// mta_fwd_v4.h — MTA forward with head-split waves, for head groups of two
-// (c_h = 2), d = 128, bf16, head mixing after the softmax: one pass with the
-// key-query convolution before the softmax (two-pass masks or Eq. 4's exact
-// indicator), two passes with it after the softmax (POST) (page "Multi-Token
-// Attention — Paper Graph", section 3.4, "Key-Query Convolution", "Head Mixing
-// Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").
+// mta_fwd_v4.h — MTA forward with head-split waves, bf16, d = 128, for the
+// kernel sizes instantiated in mta_inst_v4.hip (page "Multi-Token Attention —
+// Paper Graph", section 3.4, "Key-Query Convolution", "Head Mixing
+// Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").  A
+// workgroup owns two heads: a group of two (c_h = 2, head mix after the
+// softmax), two single-head groups (NOMIX), one output pair of a four-head
+// group (QUAD), or a group of two whose head mix precedes the softmax (C3D,
+// as a 3D convolution).  One pass with the key-query convolution before the
+// softmax (two-pass masks or Eq. 4's exact indicator), two passes with it
+// after the softmax (POST); PREP is the gradient-preparation variant.
 //
-// The two-pass kernels walk the key tiles twice: once for each row's softmax
-// statistics, once for the probabilities.  Here the statistics are kept online
-// instead.  Post-softmax mixing combines NORMALISED maps of different heads,
-// O^a = sum_b w_ab P^b V^a with P^b = exp(C^b - m_b) / l_b, and l_b is only
+// A two-pass softmax walks the key tiles twice: once for each row's softmax
+// statistics, once for the probabilities.  Before the softmax the statistics
+// are kept online instead.  Post-softmax mixing combines NORMALISED maps of
+// different heads, O^a = sum_b w_ab P^b V^a with P^b = exp(C^b - m_b) / l_b, and l_b is only
 // known at the end, so the kernel keeps one accumulator per (source head b,
 // output head a), U_{b,a} = sum_j exp(C^b_j - m_b) V^a_j (rescaled when m_b
 // grows), and forms O^a = sum_b w_ab U_{b,a} / l_b in the epilogue: c_h^2
@@ -42,8 +46,7 @@
 namespace mta {
 namespace v4 {
 
-using v2::NT;
-using v2::ColMask;
+constexpr int NT = 512;  // 8 waves, two per SIMD
 using tile::swz_k;
 using tile::swz_v;
 using tile::barrier_lds;
@@ -852,8 +855,8 @@ sweep:
 #pragma unroll
                     for (int a = 0; a < CH; ++a) {
                         const bf16_t *va = vbuf + a * BN * D;
-                        const v2::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
-                        const v2::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
+                        const tile::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
+                        const tile::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
                         typedef short s16x8 __attribute__((ext_vector_type(8)));
                         const s16x8 u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, u);

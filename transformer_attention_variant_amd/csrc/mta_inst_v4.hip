@@ -22,15 +22,18 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
     return nullptr;
 }
 
-// Head groups of one head (c_h = 1), two per workgroup, key-query convolution
-// before the softmax (either form); the caller counts head pairs in p.G.
-#define MTA_V4N_SIZE(CQ_, CK_) \
-    if (cq == CQ_ && ck == CK_) \
-        return exact ? &v4::launch<CQ_, CK_, true, false, false, true> : &v4::launch<CQ_, CK_, false, false, false, true>;
+// Head groups of one head (c_h = 1), two per workgroup: one pass with the
+// key-query convolution before the softmax (either form), two passes with it
+// after the softmax; the caller counts head pairs in p.G.
+#define MTA_V4N_SIZE(CQ_, CK_)                                                                         \
+    if (cq == CQ_ && ck == CK_)                                                                        \
+        return post ? &v4::launch<CQ_, CK_, false, true, false, true>                                 \
+                    : (exact ? &v4::launch<CQ_, CK_, true, false, false, true>                        \
+                             : &v4::launch<CQ_, CK_, false, false, false, true>);
 
-LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int exact)
+LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int post, int exact)
 {
-    if (d != 128) return nullptr;
+    if (d != 128 || (post && exact)) return nullptr;
     MTA_V4N_SIZE(1, 1)
     MTA_V4N_SIZE(4, 9)
     MTA_V4N_SIZE(6, 11)

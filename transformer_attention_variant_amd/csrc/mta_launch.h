@@ -26,8 +26,6 @@ hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 // same kernel template.
 LaunchFn find_launch_f32(int d, int ch, int cq, int ck, int post, int hpre);
 LaunchFn find_launch_bf16(int d, int ch, int cq, int ck, int post, int hpre);
-// Pipelined 8-wave bf16 kernels (mta_fwd_v2.h); null when not instantiated.
-LaunchFn find_launch_v2(int d, int ch, int cq, int ck, int post, int exact, int hpre, int ms);
 // General-layer kernels (mta_fwd_layer.h) per element type; null when (d, c_h)
 // is not instantiated.
 namespace layer {
@@ -38,9 +36,9 @@ layer::LayerFn find_launch_layer_f32(int d, int ch, int cq1, int ck1, int cq2, i
 layer::LayerFn find_launch_layer_bf16(int d, int ch, int cq1, int ck1, int cq2, int ck2);
 // Head-split bf16 kernels for c_h = 2 (mta_fwd_v4.h); null when not instantiated.
 LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int hpre);
-// Its form for head groups of one head, two groups per workgroup (key-query
-// convolution before the softmax); null when not instantiated.
-LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int exact);
+// Its form for head groups of one head, two groups per workgroup (p.G counts
+// head pairs); null when not instantiated.
+LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int post, int exact);
 // Its 3D-convolution form (two-pass masks, no head mix); null when not instantiated.
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
 // Four-head groups: the head-split kernel per output head pair, two source-pair

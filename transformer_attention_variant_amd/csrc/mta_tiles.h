@@ -3,7 +3,7 @@
 // publishes LDS writes only.
 #pragma once
 
-#include "mta_fwd_v2.h"
+#include "mta_fwd_kernel.h"
 
 namespace mta {
 namespace tile {
@@ -18,8 +18,9 @@ namespace tile {
 // transposing read of a 16-row V block keeps rows r and r + 8 apart.  With the
 // swizzles below every pass of the fragment reads and of the V reads touches
 // each bank once (checked with the bank-conflict counter).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_void_p;
-typedef __attribute__((address_space(3))) v2::s16x4 *lds_s16x4_p;
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_p;
 
 __device__ inline int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ inline int swz_v(int r) { return 2 * (r & 7); }
@@ -30,9 +31,12 @@ __device__ inline int swz_v(int r) { return 2 * (r & 7); }
 // which waits for them.
 __device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Transposing read of 4 keys kb + lane/4 (within the 16-lane group) of the
-// swizzled V tile: element e of lane i is V[kb + e][d0 + i] (see v2::lds_read_tr4).
-__device__ inline v2::s16x4 vread_tr4(const bf16_t *vbuf, int kb, int d0, int j)
+// Transposing read of the swizzled V tile (ds_read_b64_tr_b16): within each
+// 16-lane group, element e = 0..3 of lane i is the (i mod 4)-th element of the
+// 4-element row that lane 4e + i/4 addresses.  Lane j addresses
+// V[kb + j/4][d0 + 4(j mod 4)], so lane i receives V[kb + e][d0 + i]: four
+// consecutive keys of its own d column, the B operand of the P.V product.
+__device__ inline s16x4 vread_tr4(const bf16_t *vbuf, int kb, int d0, int j)
 {
     const int row = kb + (j >> 2), col = d0 + 4 * (j & 3);
     const bf16_t *a = vbuf + row * 128 + 8 * ((col >> 3) ^ swz_v(row)) + (col & 7);

@@ -596,7 +596,7 @@ static bool fused_plan(const mta_config *cfg, mta::bwd::BParams &bp, size_t &lds
     if (cfg->kq_place == MTA_POST_SOFTMAX || cfg->head_place != MTA_POST_SOFTMAX || cfg->c_h > 2) return false;
     const int d = cfg->head_dim, ch = cfg->c_h, cq = cfg->c_q, ck = cfg->c_k;
     const int bf = cfg->dtype == MTA_BF16;
-    fn = mta::find_launch_bwd(bf, d, ch, cq, ck);
+    fn = mta::find_launch_bwd(bf, d, ch, cq, ck, cfg->kq_place == MTA_PRE_SOFTMAX_EXACT);
     if (!fn) return false;
     mta::Params &p = bp.f;
     p.H = cfg->heads; p.T = cfg->seq_len; p.c_q = cq; p.c_k = ck;

@@ -43,6 +43,10 @@ typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 // fp16 copy of the logit region for the matrix-core stencil: halves per row
 constexpr int X16P = 104;
+// bf16 copy of the dC core for the matrix-core kernel gradient (in the fp16
+// logit copy's space, free by then): 72 halves per row, so that the 16 rows a
+// fragment read touches start on distinct 4-bank groups
+constexpr int DCP = 72;
 
 // Kernels with compile-time stencil sizes (bf16, d = 128) recompute the
 // convolved map on the matrix cores, as the head-split forward does: fp16
@@ -532,6 +536,50 @@ __device__ inline void dtheta16(const float *xbuf, int pitch, int rx0, int xc0, 
     }
 }
 
+// dtheta on the matrix cores (bf16 operands, fp32 sums; two-pass masks):
+//   dtheta[i'][jj] = sum over the core (r, c) of dC[r][c] X[r - i'][c + hr - jj]
+//                  = sum over logit rows r' and core keys c of A[jj][c] B[c][i'],
+//   A[jj][c] = X[r'][c + hr - jj] (a Toeplitz band of one logit row),
+//   B[c][i'] = dC[r' + i'][c]     (c_q consecutive dC rows),
+// one 16x16x32 product per (logit row, 32-key chunk), the tasks dealt to the
+// waves; each wave adds its sums (lane: tap 4*(lane/16) + q, query offset
+// lane%16) into dth [c_q][ckp] with LDS atomics.  xbuf: the fp32 logit region
+// (row r' + c_q - 1, column c + hr + c_k - 1 - jj for key c of the core); dcb:
+// the bf16 dC core.
+template <int CQ, int CK>
+__device__ inline void dtheta_mfma(float *dth, int ckp, const float *xbuf, int xp, const bf16_t *dcb, int hr,
+                                   int wave, int lane)
+{
+    const int m = lane & 15, g = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t = wave; t < 2 * (BM + CQ - 1); t += NWB) {
+        const int xr = t >> 1, c0 = 32 * (t & 1);
+        const int rd = xr - (CQ - 1) + m;  // the dC row of this lane's B column (query offset m)
+        bf16x8 a, bv;
+        if (m < CK) {
+            float xv[8];
+            __builtin_memcpy(xv, xbuf + xr * xp + c0 + 8 * g + hr + CK - 1 - m, sizeof(xv));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = (bf16_t)xv[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = (bf16_t)0.0f;
+        }
+        if (m < CQ && rd >= 0 && rd < BM) {
+            bv = *reinterpret_cast<const bf16x8 *>(dcb + rd * DCP + c0 + 8 * g);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = (bf16_t)0.0f;
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
+    }
+    if (m < CQ) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (4 * g + q < CK) atomicAdd(dth + m * ckp + 4 * g + q, acc[q]);
+    }
+}
+
 // The nrb x ncb 16x16 blocks of a region product, in row-major order, are dealt
 // to the NWB waves in contiguous runs; a run loads the row fragments again
 // where its row block changes and requests the next column fragments before
@@ -667,10 +715,14 @@ struct TileStage<float, D> {
 
 // ---------------------------------------------------------------------------
 // Kernel B
-template <typename DT, int D, int CH, int CQ, int CK>
+// EXM: 0 = the masking form from p.exact (runtime); 1 = two-pass masks, 2 =
+// Eq. 4's indicator, fixed at compile time (the kernels with compile-time
+// stencils, which then carry only one form's code)
+template <typename DT, int D, int CH, int CQ, int CK, int EXM = 0>
 __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
 {
     const Params &p = bp.f;
+    const bool exact = EXM == 0 ? p.exact != 0 : EXM == 2;
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = blockIdx.x;
@@ -700,6 +752,11 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
     // MS: fp16 copy of the logit region, then both heads' banded kernel matrices
     h16_t *x16 = reinterpret_cast<h16_t *>(reinterpret_cast<char *>(opbuf) + vbuf_bytes<DT, D>());
     h16x8 *tfl = reinterpret_cast<h16x8 *>(x16 + bp.nRrb * 16 * X16P);  // [s][i'][lane]
+    // MS, two-pass masks: the bf16 dC core for the kernel gradient on the
+    // matrix cores, in the fp16 logit copy's space (free once the convolved map
+    // of the head is formed)
+    bf16_t *dcb = reinterpret_cast<bf16_t *>(x16);
+    const bool grad_mfma = MS && !exact;
 
     const size_t hstride = (size_t)T * D;
     const DT *Q = reinterpret_cast<const DT *>(p.q);
@@ -757,7 +814,7 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
         }
 
     const int nlcb = (nEc + 15) / 16;
-    const int qt0 = p.exact ? (kt > 0 ? kt - 1 : 0) : kt;
+    const int qt0 = exact ? (kt > 0 ? kt - 1 : 0) : kt;
     // The 64-row tiles of one (query tile, head s) step, in order of use:
     // dO^a (and its low plane) for every output head a, K^s at the key tile,
     // Q^s at the query tile.  Each is fetched into registers one tile ahead.
@@ -810,10 +867,10 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
             __syncthreads();
             // X^s over the logit region (log2-scaled; Mask_0 unless exact)
             x_tile<DT, D>(xbuf, xp, bp.nRrb, bp.nRcb, 16 * bp.nRrb, Q + base0 + s * hstride, K + base0 + s * hstride,
-                          xr0, xc0, T, p.sc, p.exact != 0, wave, lane, (MS && !p.exact) ? x16 : nullptr);
+                          xr0, xc0, T, p.sc, exact, wave, lane, (MS && !exact) ? x16 : nullptr);
             __syncthreads();
             // C^s over the region -> P^s (in place)
-            if (MS && !p.exact) {
+            if (MS && !exact) {
                 // on the matrix cores (two-pass masks; Eq. 4's indicator keeps the
                 // VALU stencil): 16x16 blocks (region rows 16rb.., columns 16cb..)
                 // dealt to the waves; lane: row 16rb + lane%16, columns 16cb + 4*(lane/16) + r
@@ -859,7 +916,7 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
             for (int t = tid; t < nEr * nlcb; t += NTB) {
                 const int r = t / nlcb, cb = t % nlcb;
                 const int qi = i0 + r;
-                const int tlim = p.exact ? qi - (xc0 + 16 * cb) : (1 << 30);
+                const int tlim = exact ? qi - (xc0 + 16 * cb) : (1 << 30);
                 float o[16];
                 stencil16<CQ, CK>(xbuf, xp, r + cq - 1, 16 * cb, th_s + s * cq * ckp, cq, ck, ckp, tlim, o);
                 const float m = st[(s * 3 + 0) * nEr4 + r], il = st[(s * 3 + 1) * nEr4 + r];
@@ -905,25 +962,31 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
                     dp = __builtin_fmaf(w_s[a * CH + s], x, dp);
                     if (core) dwp[a * CH + s] = __builtin_fmaf(x, pv, dwp[a * CH + s]);
                 }
-                ebuf[r * ep + c] = pv * (dp - st[(s * 3 + 2) * nEr4 + r]);
+                const float dcv = pv * (dp - st[(s * 3 + 2) * nEr4 + r]);
+                ebuf[r * ep + c] = dcv;
+                if (grad_mfma && core) dcb[r * DCP + c - hr] = (bf16_t)dcv;
             }
             __syncthreads();
             // dtheta^s += corr(dC core, X^s)
-            {
+            if (grad_mfma) {
+                dtheta_mfma<CQ, CK>(dth + s * cq * ckp, ckp, xbuf, xp, dcb, hr, wave, lane);
+            } else {
                 float gc[16];
 #pragma unroll
                 for (int o = 0; o < 16; ++o) gc[o] = ebuf[io * ep + hr + jb + o];
                 const int qi = i0 + io;
                 // window of the lane: logit row (io + cq-1) - i', columns from jb + hr (key j0 + jb - hl)
-                const int tlim = p.exact ? qi - (xc0 + jb + hr) : (1 << 30);
+                const int tlim = exact ? qi - (xc0 + jb + hr) : (1 << 30);
                 dtheta16<CQ, CK>(xbuf, xp, io + cq - 1, jb + hr, gc, dth + s * cq * ckp, cq, ck, ckp, tlim, half);
             }
             // dS^s core = Mask_0(dX) (two-pass) or dX (exact): the transposed stencil,
             // this wave's query offsets; with Eq. 4's indicator the terms of offset
-            // i' count where key <= r + i'
+            // i' count where key <= r + i'.  (On the VALU in fp32: dS meets K and
+            // Q in products whose rows sum to about zero, which a bf16 dC would
+            // not survive.)
             float dsv[16];
             stencil16_t<CQ, CK>(ebuf, ep, io, jb, th_s + s * cq * ckp, cq, ck, ckp,
-                                p.exact ? i0 + io - j0 - jb : (1 << 30), half, dsv);
+                                exact ? i0 + io - j0 - jb : (1 << 30), half, dsv);
             __syncthreads();  // xbuf free (dtheta done), ebuf reads done
             // the second half's partial sums meet the first half's in LDS; the
             // first half writes dS core row-major (pitch BN + 4) into xbuf
@@ -941,7 +1004,7 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
 #pragma unroll
                 for (int o = 0; o < 16; ++o) {
                     const int c = j0 + jb + o;
-                    const bool keep = p.exact ? true : (c <= r);
+                    const bool keep = exact ? true : (c <= r);
                     const float v = dsv[o] + xch[o];
                     dsb[io * (BN + 4) + jb + o] = (keep && r < T && c < T) ? v : 0.f;
                 }
@@ -1016,7 +1079,7 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
 
 }  // namespace bwd
 
-bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck);
+bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck, int exact);
 // find_launch_bwd picks a main kernel with compile-time stencil sizes (whose
 // convolved-map recompute runs on the matrix cores)
 bool bwd_fixed_sizes(int dtype_bf16, int d, int ch, int cq, int ck);

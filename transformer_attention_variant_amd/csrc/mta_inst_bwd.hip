@@ -8,11 +8,11 @@ namespace bwd {
 
 // grid_a = 0: the first kernel's outputs come from elsewhere (the head-split
 // forward's gradient-preparation variant); only the main kernel runs.
-template <typename DT, int D, int CH, int CQ, int CK>
+template <typename DT, int D, int CH, int CQ, int CK, int EXM = 0>
 hipError_t launch(const BParams &p, int grid_a, size_t lds_a, int grid_b, size_t lds_b, hipStream_t s)
 {
     auto fa = mta_bwd_prep<DT, D, CH, CQ, CK>;
-    auto fb = mta_bwd_main<DT, D, CH, CQ, CK>;
+    auto fb = mta_bwd_main<DT, D, CH, CQ, CK, EXM>;
     hipError_t e;
     if (grid_a > 0) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(fa), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -38,13 +38,15 @@ bool bwd_fixed_sizes(int dtype_bf16, int d, int ch, int cq, int ck)
     return dtype_bf16 && d == 128 && ch == 2 && ((cq == 6 && ck == 11) || (cq == 4 && ck == 9) || (cq == 8 && ck == 15));
 }
 
-bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck)
+bwd::BwdFn find_launch_bwd(int dtype_bf16, int d, int ch, int cq, int ck, int exact)
 {
     using namespace bwd;
     if (bwd_fixed_sizes(dtype_bf16, d, ch, cq, ck)) {
-        if (cq == 6) return &launch<bf16_t, 128, 2, 6, 11>;
-        if (cq == 4) return &launch<bf16_t, 128, 2, 4, 9>;
-        return &launch<bf16_t, 128, 2, 8, 15>;
+        // the masking form fixed at compile time (two-pass masks: the kernel
+        // gradient and the transposed stencil on the matrix cores)
+        if (cq == 6) return exact ? &launch<bf16_t, 128, 2, 6, 11, 2> : &launch<bf16_t, 128, 2, 6, 11, 1>;
+        if (cq == 4) return exact ? &launch<bf16_t, 128, 2, 4, 9, 2> : &launch<bf16_t, 128, 2, 4, 9, 1>;
+        return exact ? &launch<bf16_t, 128, 2, 8, 15, 2> : &launch<bf16_t, 128, 2, 8, 15, 1>;
     }
 #define MTA_BWD_D(T_, D_)                                          \
     if (d == D_) {                                                 \

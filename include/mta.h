@@ -275,8 +275,8 @@ int mta_backward_noalloc(const void *q, const void *k, const void *v, const floa
 size_t mta_backward_scratch_bytes(void);
 
 /* Host-only: the name of the kernel mta_forward / mta_forward_gated launch for
- * this configuration (a static string, e.g. "mta_fwd_v3 (one pass,
- * matrix-core stencil)"), or NULL if the configuration is invalid or
+ * this configuration (a static string, e.g. "mta_fwd_v4 (one pass,
+ * head-split waves, fp16 matrix-core stencil)"), or NULL if the configuration is invalid or
  * unsupported.  For profiling and reports; it launches nothing. */
 const char *mta_kernel_name(const mta_config *cfg);
 

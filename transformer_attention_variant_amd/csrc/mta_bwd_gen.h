@@ -26,9 +26,11 @@
 // indicator reaches (keys up to c_q - 1 past a row).  Every kernel writes
 // every element of the band tiles it produces (zero where the map is zero),
 // and reads only elements that some kernel wrote.  Head groups are processed
-// in chunks that fit the workspace.  All arithmetic is float32: products on
-// the matrix cores with fp32 operands (v_mfma_f32_16x16x4_f32), the stencils,
-// softmax and GroupNorm on the VALU.
+// in chunks that fit the workspace.  All arithmetic keeps float32 precision:
+// products on the matrix cores with fp32 operands (v_mfma_f32_16x16x4_f32) or,
+// for bf16 inputs, with bf16 operands whose float32 side is split into three
+// bf16 parts (v_mfma_f32_16x16x32_bf16); the stencils, softmax and GroupNorm
+// on the VALU in float32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -400,6 +402,278 @@ __global__ void __launch_bounds__(NTH) gen_gemm_tn(GParams p, const float *slot,
             const float a = Ms[(kk + lk) * MP + 16 * w + lr];
 #pragma unroll
             for (int n = 0; n < D / 16; ++n) acc[n] = mfma4(a, Bs[(kk + lk) * BP + 16 * n + lr], acc[n]);
+        }
+        __syncthreads();
+    }
+    float *o = out + tensor_off(p, x);
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + 16 * w + 4 * lk + r;
+            if (j < p.T) o[(size_t)j * D + 16 * n + lr] = alpha * acc[n][r];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// The same products for bf16 inputs on the 16-bit matrix cores
+// (v_mfma_f32_16x16x32_bf16, float32 accumulation).  A bf16 input tensor (Q,
+// K, V) is an exact operand; a float32 operand (a map, dO) is split into three
+// bf16 parts x = h + m + l (h = bf16(x), m = bf16(x - h), l = bf16(x - h - m):
+// 24 significant bits, each remainder below 2^-8 of the previous part), and
+// the three parts' products with the exact operand accumulate in float32, so
+// the sums keep float32 precision at a third of the 16-bit rate (against an
+// eighth for float32 operands).  dV = P3^T dO, whose operands are both
+// float32, keeps the float32 products (six split products, staged half of d
+// at a time, measured 5% faster for that kernel: not worth the code).
+
+typedef short s16x4g __attribute__((ext_vector_type(4)));
+typedef short s16x8g __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4g __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4g *lds_s16x4g_p;
+
+// 4 consecutive values into NP bf16 planes (plane k at dst + k * pstride):
+// NP = 1 rounds (exact for values that came from bf16), NP = 3 splits.
+template <int NP>
+__device__ inline void put4_planes(bf16_t *dst, int pstride, float4 v)
+{
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    bf16x4g o[NP];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16_t h = (bf16_t)x[e];
+        o[0][e] = h;
+        if constexpr (NP == 3) {
+            const float r1 = x[e] - (float)h;
+            const bf16_t m = (bf16_t)r1;
+            o[1][e] = m;
+            o[2][e] = (bf16_t)(r1 - (float)m);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4g *>(dst + k * pstride) = o[k];
+}
+
+// Rows [r0, r0 + 64) x columns [c0, c0 + W) of a row-major [T][D] operand into
+// NP bf16 planes (pitch in halves; rows >= T are zero).
+template <int NP, typename ET, int D, int W>
+__device__ inline void stage_rows16(bf16_t *dst, int pitch, const ET *src, int r0, int T, int tid, int c0)
+{
+    for (int idx = tid; idx < TB * W / 4; idx += NTH) {
+        const int r = idx / (W / 4), c4 = idx - r * (W / 4);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r0 + r < T) x = load4(src + (size_t)(r0 + r) * D + c0 + 4 * c4);
+        put4_planes<NP>(dst + r * pitch + 4 * c4, TB * pitch, x);
+    }
+}
+
+// The register-staged loads of gen_gemm_mn / tn, stored as bf16 planes.
+template <int NP, typename ET, int D>
+__device__ inline void store_rows16(const RowRegs<ET, D> &rr, bf16_t *dst, int pitch, int tid)
+{
+#pragma unroll
+    for (int k = 0; k < TB * D / 4 / NTH; ++k) {
+        const int idx = tid + k * NTH, r = idx / (D / 4), c4 = idx - r * (D / 4);
+        put4_planes<NP>(dst + r * pitch + 4 * c4, TB * pitch, rr.v[k]);
+    }
+}
+template <int NP>
+__device__ inline void store_tile16(const TileRegs &tr, bf16_t *dst, int pitch, int tid)
+{
+#pragma unroll
+    for (int k = 0; k < TB * TB / 4 / NTH; ++k) {
+        const int idx = tid + k * NTH, r = idx >> 4, c4 = idx & 15;
+        put4_planes<NP>(dst + r * pitch + 4 * c4, TB * pitch, tr.v[k]);
+    }
+}
+
+// Operand of a 16x16x32 product along rows of a row-major bf16 tile: lane
+// (n = lane%16, g = lane/16) gets rows k0 + 8g .. k0 + 8g + 7 of column
+// c0 + n, with two transposing reads (ds_read_b64_tr_b16: within each
+// 16-lane group, element e of lane i is the (i mod 4)-th element of the
+// 4-element row that lane 4e + i/4 addresses; lane j addresses row
+// k0 + 8g + j/4, columns c0 + 4(j mod 4)).
+__device__ inline bf16x8 tr_frag(const bf16_t *tile, int pitch, int k0, int c0, int lane)
+{
+    const int j = lane & 15, g = lane >> 4;
+    const bf16_t *a = tile + (k0 + 8 * g + (j >> 2)) * pitch + c0 + 4 * (j & 3);
+    const s16x4g u0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g_p)(a));
+    const s16x4g u1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g_p)(a + 4 * pitch));
+    const s16x8g u = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// gen_gemm_nt for bf16 inputs: M[i][j] = alpha sum_c A[i][c] B[j][c], A = Q
+// (exact) or dO (split), B = K or V (exact).  d staged 64 columns at a time;
+// pitch 72 halves (the 8-lane groups of a 16-byte read start on distinct
+// 4-bank groups).
+template <int D, int SRCA>
+__global__ void __launch_bounds__(NTH) gen_gemm_nt16(GParams p, const void *a_tensor, const void *b_tensor,
+                                                     float *slot, float alpha)
+{
+    typedef typename std::conditional<SRCA == SRC_OBUF, float, bf16_t>::type AT;
+    constexpr int NPA = SRCA == SRC_OBUF ? 3 : 1;
+    constexpr int KC = D < 64 ? D : 64;
+    constexpr int P = KC + 8;
+    __shared__ __align__(16) bf16_t As[NPA * TB * P];
+    __shared__ __align__(16) bf16_t Bs[TB * P];
+    int it, jt;
+    band_tile(blockIdx.x, p.nt, it, jt);
+    const int y = blockIdx.y;
+    const HeadIx x = head_ix(p, y);
+    const int i0 = it * TB, j0 = jt * TB;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const AT *asrc = static_cast<const AT *>(rows_base<bf16_t, SRCA>(p, a_tensor, x, y));
+    const bf16_t *bsrc = static_cast<const bf16_t *>(rows_base<bf16_t, SRC_TENSOR>(p, b_tensor, x, y));
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+    const int lr = lane & 15, lk = lane >> 4;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < D; c0 += KC) {
+        if (c0) __syncthreads();
+        stage_rows16<NPA, AT, D, KC>(As, P, asrc, i0, p.T, tid, c0);
+        stage_rows16<1, bf16_t, D, KC>(Bs, P, bsrc, j0, p.T, tid, c0);
+        __syncthreads();
+#pragma unroll
+        for (int k0 = 0; k0 < KC; k0 += 32) {
+            bf16x8 bv[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                bv[nb] = *reinterpret_cast<const bf16x8 *>(Bs + (wc + 16 * nb + lr) * P + k0 + 8 * lk);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int pl = 0; pl < NPA; ++pl) {
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8 *>(As + pl * TB * P + (wr + 16 * mb + lr) * P + k0 + 8 * lk);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, bv[nb], acc[mb][nb]);
+                }
+        }
+    }
+    float *m = map_of(slot, p, y);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + wr + 16 * mb + 4 * lk + r, j = j0 + wc + 16 * nb + lr;
+                m[(size_t)i * p.Tp + j] = alpha * acc[mb][nb][r];
+            }
+}
+
+// gen_gemm_mn for bf16 inputs: Out[i][:] = alpha sum_j M[i][j] B[j][:], the
+// map split into three planes (pitch 72 halves), B = V or K (exact, pitch
+// D + 16 halves: the four rows of a transposing read start 8 banks apart).
+template <int D, bool TO_OBUF>
+__global__ void __launch_bounds__(NTH) gen_gemm_mn16(GParams p, const float *slot, const void *b_tensor, float *out,
+                                                     float alpha)
+{
+    constexpr int MP = TB + 8, BP = D + 16;
+    __shared__ __align__(16) bf16_t Ms[3 * TB * MP];
+    __shared__ __align__(16) bf16_t Bs[TB * BP];
+    const int it = p.nt - 1 - (int)blockIdx.x, y = blockIdx.y;  // the longest rows first
+    const HeadIx x = head_ix(p, y);
+    const int i0 = it * TB;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const float *m = map_of(const_cast<float *>(slot), p, y);
+    const bf16_t *bsrc = static_cast<const bf16_t *>(b_tensor) + tensor_off(p, x);
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int jt_end = it + 1 < p.nt ? it + 1 : p.nt - 1;
+    TileRegs mr;
+    RowRegs<bf16_t, D> br;
+    mr.load(m, p.Tp, i0, 0, tid);
+    br.load(bsrc, 0, p.T, tid);
+    for (int jt = 0; jt <= jt_end; ++jt) {
+        store_tile16<3>(mr, Ms, MP, tid);
+        store_rows16<1>(br, Bs, BP, tid);
+        __syncthreads();
+        if (jt < jt_end) {  // the next tile's reads overlap this tile's products
+            mr.load(m, p.Tp, i0, (jt + 1) * TB, tid);
+            br.load(bsrc, (jt + 1) * TB, p.T, tid);
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < TB; k0 += 32) {
+            bf16x8 a[3];
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                a[pl] = *reinterpret_cast<const bf16x8 *>(Ms + pl * TB * MP + (16 * w + lr) * MP + k0 + 8 * lk);
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n) {
+                const bf16x8 b = tr_frag(Bs, BP, k0, 16 * n, lane);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) acc[n] = mfma16(a[pl], b, acc[n]);
+            }
+        }
+        __syncthreads();
+    }
+    float *o = TO_OBUF ? p.obuf + (size_t)y * p.T * D : out + tensor_off(p, x);
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 16 * w + 4 * lk + r;
+            if (i < p.T) o[(size_t)i * D + 16 * n + lr] = alpha * acc[n][r];
+        }
+}
+
+// gen_gemm_tn for bf16 inputs with an exact B (dK = dS^T Q): Out[j][:] =
+// alpha sum_i M[i][j] B[i][:], both operands read along the rows i with
+// transposing reads (map planes: pitch 72 halves, the four rows of a read 36
+// banks apart mod 64).
+template <int D>
+__global__ void __launch_bounds__(NTH) gen_gemm_tn16(GParams p, const float *slot, const void *b_tensor, float *out,
+                                                     float alpha)
+{
+    constexpr int MP = TB + 8, BP = D + 16;
+    __shared__ __align__(16) bf16_t Ms[3 * TB * MP];
+    __shared__ __align__(16) bf16_t Bs[TB * BP];
+    const int jt = blockIdx.x, y = blockIdx.y;
+    const HeadIx x = head_ix(p, y);
+    const int j0 = jt * TB;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const float *m = map_of(const_cast<float *>(slot), p, y);
+    const bf16_t *bsrc = static_cast<const bf16_t *>(b_tensor) + tensor_off(p, x);
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int it0 = jt > 0 ? jt - 1 : 0;
+    TileRegs mr;
+    RowRegs<bf16_t, D> br;
+    mr.load(m, p.Tp, it0 * TB, j0, tid);
+    br.load(bsrc, it0 * TB, p.T, tid);
+    for (int it = it0; it < p.nt; ++it) {
+        store_tile16<3>(mr, Ms, MP, tid);
+        store_rows16<1>(br, Bs, BP, tid);
+        __syncthreads();
+        if (it + 1 < p.nt) {  // the next tile's reads overlap this tile's products
+            mr.load(m, p.Tp, (it + 1) * TB, j0, tid);
+            br.load(bsrc, (it + 1) * TB, p.T, tid);
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < TB; k0 += 32) {
+            bf16x8 a[3];
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) a[pl] = tr_frag(Ms + pl * TB * MP, MP, k0, 16 * w, lane);
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n) {
+                const bf16x8 b = tr_frag(Bs, BP, k0, 16 * n, lane);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) acc[n] = mfma16(a[pl], b, acc[n]);
+            }
         }
         __syncthreads();
     }

@@ -100,7 +100,11 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
     const int cmode = kq == KQ_EXACT ? M_EXACT : M_PRE;
 
     // forward: S, C, L, P, P2, P3, O
-    hipLaunchKernelGGL((gen_gemm_nt<DT, D, SRC_TENSOR>), band, blk, 0, s, p, p.q, p.k, slot[sl.S], p.inv_sqrt_d);
+    constexpr bool B16 = std::is_same<DT, bf16_t>::value;  // bf16 inputs: the 16-bit products
+    if constexpr (B16)
+        hipLaunchKernelGGL((gen_gemm_nt16<D, SRC_TENSOR>), band, blk, 0, s, p, p.q, p.k, slot[sl.S], p.inv_sqrt_d);
+    else
+        hipLaunchKernelGGL((gen_gemm_nt<DT, D, SRC_TENSOR>), band, blk, 0, s, p, p.q, p.k, slot[sl.S], p.inv_sqrt_d);
     GEN_CHECK();
     if (kq != KQ_POST) {
         const float *in = slot[sl.S];
@@ -123,7 +127,10 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
         const hipError_t e = mix(true, p, slot[sl.P2], slot[sl.P3], s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gen_gemm_mn<DT, D, true>), rows_t, blk, 0, s, p, slot[sl.P3], p.v, nullptr, 1.0f);
+    if constexpr (B16)
+        hipLaunchKernelGGL((gen_gemm_mn16<D, true>), rows_t, blk, 0, s, p, slot[sl.P3], p.v, nullptr, 1.0f);
+    else
+        hipLaunchKernelGGL((gen_gemm_mn<DT, D, true>), rows_t, blk, 0, s, p, slot[sl.P3], p.v, nullptr, 1.0f);
     GEN_CHECK();
 
     // backward
@@ -131,7 +138,10 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
     GEN_CHECK();
     hipLaunchKernelGGL((gen_gemm_tn<DT, D, SRC_OBUF>), rows_t, blk, 0, s, p, slot[sl.P3], nullptr, p.dv, 1.0f);
     GEN_CHECK();
-    hipLaunchKernelGGL((gen_gemm_nt<DT, D, SRC_OBUF>), band, blk, 0, s, p, nullptr, p.v, slot[sl.g1], 1.0f);
+    if constexpr (B16)
+        hipLaunchKernelGGL((gen_gemm_nt16<D, SRC_OBUF>), band, blk, 0, s, p, nullptr, p.v, slot[sl.g1], 1.0f);
+    else
+        hipLaunchKernelGGL((gen_gemm_nt<DT, D, SRC_OBUF>), band, blk, 0, s, p, nullptr, p.v, slot[sl.g1], 1.0f);
     GEN_CHECK();
     int cur = sl.g1, other = sl.g2;
     if (hp == KQ_POST) {  // dP3 -> dP2, dw
@@ -161,10 +171,16 @@ hipError_t run_chunk(const GParams &p, float *const *slot, const Slots &sl, hipS
         cur = other;
         other = t;
     }
-    hipLaunchKernelGGL((gen_gemm_mn<DT, D, false>), rows_t, blk, 0, s, p, slot[cur], p.k, p.dq, p.inv_sqrt_d);
-    GEN_CHECK();
-    hipLaunchKernelGGL((gen_gemm_tn<DT, D, SRC_TENSOR>), rows_t, blk, 0, s, p, slot[cur], p.q, p.dk,
-                       p.inv_sqrt_d);
+    if constexpr (B16) {
+        hipLaunchKernelGGL((gen_gemm_mn16<D, false>), rows_t, blk, 0, s, p, slot[cur], p.k, p.dq, p.inv_sqrt_d);
+        GEN_CHECK();
+        hipLaunchKernelGGL((gen_gemm_tn16<D>), rows_t, blk, 0, s, p, slot[cur], p.q, p.dk, p.inv_sqrt_d);
+    } else {
+        hipLaunchKernelGGL((gen_gemm_mn<DT, D, false>), rows_t, blk, 0, s, p, slot[cur], p.k, p.dq, p.inv_sqrt_d);
+        GEN_CHECK();
+        hipLaunchKernelGGL((gen_gemm_tn<DT, D, SRC_TENSOR>), rows_t, blk, 0, s, p, slot[cur], p.q, p.dk,
+                           p.inv_sqrt_d);
+    }
     GEN_CHECK();
     return hipSuccess;
 }

@@ -84,6 +84,12 @@ def _cases():
     c.append(I.small("gen_f32_post_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, kq_place=Q, seed=1705))
     c.append(I.small("gen_bf16_6x11_ch4_T600", B=1, H=4, T=600, d=128, c_q=6, c_k=11, c_h=4, kq_place=Q,
                      dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=1706))
+    # the 16-bit products of the map form at the smaller head dimensions
+    # (bf16 inputs: three-part split of the float32 operand), ragged T
+    for (d, kq, hp, T) in ((64, Q, Q, 130), (32, P, P, 77), (64, E, P, 200)):
+        c.append(I.small(f"gen_bf16_d{d}_kq{kq}_h{hp}_T{T}", B=2, H=4, T=T, d=d, c_q=4, c_k=7, c_h=2, kq_place=kq,
+                         head_place=hp, dtype="bf16", theta_std=0.2, head_std=0.2, gn_random=True,
+                         seed=1710 + d + kq + T))
     return c
 
 

@@ -752,11 +752,12 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
     // MS: fp16 copy of the logit region, then both heads' banded kernel matrices
     h16_t *x16 = reinterpret_cast<h16_t *>(reinterpret_cast<char *>(opbuf) + vbuf_bytes<DT, D>());
     h16x8 *tfl = reinterpret_cast<h16x8 *>(x16 + bp.nRrb * 16 * X16P);  // [s][i'][lane]
-    // MS, two-pass masks: the bf16 dC core for the kernel gradient on the
-    // matrix cores, in the fp16 logit copy's space (free once the convolved map
-    // of the head is formed)
+    // MS: the bf16 dC core for the kernel gradient on the matrix cores, in the
+    // fp16 logit copy's space (free once the convolved map of the head is
+    // formed); with Eq. 4's indicator only for query tiles two or more below
+    // the key tile, where every tap's key lies in the past of every output row
+    // (key <= j0 + 63 + hr < i0), so the indicator passes all of them
     bf16_t *dcb = reinterpret_cast<bf16_t *>(x16);
-    const bool grad_mfma = MS && !exact;
 
     const size_t hstride = (size_t)T * D;
     const DT *Q = reinterpret_cast<const DT *>(p.q);
@@ -842,6 +843,7 @@ __global__ void __launch_bounds__(NTB) mta_bwd_main(BParams bp)
     fetch_tile(qt0, 0, 0);
     for (int qt = qt0; qt < p.n_qt; ++qt) {
         const int i0 = qt * BM;
+        const bool grad_mfma = MS && (!exact || qt >= kt + 2);
         const int ec0 = j0 - hr;              // key of region column 0
         const int xr0 = i0 - (cq - 1);        // query of logit row 0
         const int xc0 = ec0 - hl;             // key of logit column 0

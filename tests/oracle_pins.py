@@ -359,8 +359,8 @@ def pin_brute_force_tiny(lib):
     for (kq, hd, T, cq, ck, ch) in [(I.PRE, I.POST, 8, 3, 5, 2), (I.POST, I.POST, 7, 2, 3, 2),
                                     (I.PRE, I.PRE, 6, 9, 4, 2), (I.POST, I.PRE, 5, 3, 6, 4),
                                     (I.PRE, I.POST, 1, 2, 3, 1), (I.PRE_EXACT, I.POST, 8, 3, 5, 2),
-                                    (I.PRE_EXACT, I.PRE, 6, 9, 4, 2)]:
-        cfg = I.small(B=2, H=4, T=T, d=4, c_q=cq, c_k=ck, c_h=ch, kq_place=kq, head_place=hd,
+                                    (I.PRE_EXACT, I.PRE, 6, 9, 4, 2), (I.PRE, I.POST, 5, 2, 3, 8)]:
+        cfg = I.small(B=2, H=max(4, ch), T=T, d=4, c_q=cq, c_k=ck, c_h=ch, kq_place=kq, head_place=hd,
                       theta_std=0.5, head_std=0.5, gn_random=True, layer=2, seed=31 + T)
         inp = I.generate(cfg)
         got = oracle.forward_cfg(cfg, inp, lib=lib, threads=1)
@@ -558,6 +558,30 @@ def pin_layer_causality(lib):
             assert not np.array_equal(base[:, :, t + 1:], o2[:, :, t + 1:])
 
 
+def pin_head_permutation_large_groups(lib):
+    """Groups of 8 and 16 heads (the page's default c_h is 16): with the
+    identity key-query kernel and a permutation pi as each group's mixing
+    matrix after the softmax, Eq. 7 hands head a the probabilities of head
+    pi(a), so O^a = softmax(Q^pi(a) K^pi(a)^T / sqrt(d)) V^a: causal attention
+    with the queries and keys of head pi(a) and the values of head a."""
+    for (ch, H, T) in ((8, 8, 27), (16, 16, 21)):
+        cfg = I.small(B=2, H=H, T=T, d=8, c_q=3, c_k=5, c_h=ch, gn_random=True, layer=2, seed=51 + ch)
+        inp = _identity_inputs(cfg)
+        g = torch.Generator().manual_seed(ch)
+        w = torch.zeros(cfg.groups, ch, ch, dtype=torch.float32)
+        perm = []
+        for grp in range(cfg.groups):
+            pi = torch.randperm(ch, generator=g)
+            w[grp, torch.arange(ch), pi] = 1.0
+            perm += [grp * ch + int(x) for x in pi]
+        inp["theta_head"] = w
+        got = oracle.forward_cfg(cfg, inp, lib=lib, threads=2)
+        src = torch.tensor(perm)
+        o = _sdpa64(inp["q"][:, src], inp["k"][:, src], inp["v"])
+        ref = _gn64(o, inp["gn_w"], inp["gn_b"], cfg.gn_eps, cfg.depth_scale)
+        _close(got, ref.numpy(), 1e-10, f"head permutation {cfg.short()}")
+
+
 ALL_PINS = [
     pin_identity_is_causal_attention,
     pin_sigmoid_gate,
@@ -570,6 +594,7 @@ ALL_PINS = [
     pin_causality,
     pin_hand_cases,
     pin_brute_force_tiny,
+    pin_head_permutation_large_groups,
     pin_layer_brute_force,
     pin_layer_identity_is_attention,
     pin_layer_separable_3d,

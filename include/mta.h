@@ -67,9 +67,10 @@ extern "C" {
  * the instantiated kernel sizes, c_h 1, 2 or 4) round each head's
  * probabilities to bf16 before the head mix, which they apply to the per-head
  * A·V products: under strongly cancelling mixing weights the output's error
- * relative to its size grows accordingly.  With four-head groups the first
- * source head pair's share of the output waits in the output buffer as fp16
- * until the second pair's is added (shares beyond 65504 in magnitude clamp).
+ * relative to its size grows accordingly.  With groups of 8 or 16 heads they
+ * keep the probabilities to ~16 bits in A·V (a bf16 high part and the bf16
+ * remainder), which removes that growth.  Groups of 4 or more heads sum the
+ * source head pairs' shares in float32.
  * mta_kernel_name tells which kernel a configuration runs. */
 #define MTA_F32 0
 #define MTA_BF16 1
@@ -83,7 +84,9 @@ extern "C" {
 #define MTA_ERR_MISALIGNED -5    /* a tensor pointer is not 16-byte aligned    */
 #define MTA_ERR_UNSUPPORTED -6   /* valid but outside the library's limits:
                                     head_dim not in {32,64,128}, c_h not in
-                                    {1,2,4}, c_q > 16, c_k > 31, T > 2^24      */
+                                    {1,2,4,8,16} (8, 16: see mta_config),
+                                    c_q > 16, c_k > 31, T > 2^24, or no kernel
+                                    of the configuration fits the LDS       */
 #define MTA_ERR_LAUNCH -7        /* the kernel launch reported an error        */
 #define MTA_ERR_BAD_VALUE -8     /* gn_eps <= 0 or not finite, depth_scale not
                                     finite                                      */
@@ -99,7 +102,9 @@ typedef struct mta_config {
     int32_t head_dim;   /* d in {32, 64, 128}                                  */
     int32_t c_q;        /* key-query kernel size along queries, 1..16         */
     int32_t c_k;        /* key-query kernel size along keys, 1..31            */
-    int32_t c_h;        /* heads per mixing group, 1, 2 or 4                   */
+    int32_t c_h;        /* heads per mixing group, 1, 2, 4, 8 or 16 (8 and 16: */
+                        /* the forward only with MTA_BF16, d = 128, head mix  */
+                        /* after the softmax, c_q x c_k 1x1, 4x9, 6x11, 8x15) */
     int32_t kq_place;   /* MTA_PRE_SOFTMAX (two-pass masking) | MTA_POST_SOFTMAX
                            | MTA_PRE_SOFTMAX_EXACT (Eq. 4's indicator)     */
     int32_t head_place; /* MTA_PRE_SOFTMAX | MTA_POST_SOFTMAX                  */
@@ -208,7 +213,7 @@ const char *mta_layer_kernel_name(const mta_layer_config *cfg, const mta_layer_w
 /*
  * mta_backward — gradients of mta_forward (mta_forward_gated when gate is not
  * NULL) for every placement of the two convolutions (kq_place, head_place),
- * c_h in {1, 2, 4}, d in {32, 64, 128}, either dtype: the chain rule of the
+ * c_h in {1, 2, 4, 8, 16}, d in {32, 64, 128}, either dtype: the chain rule of the
  * forward of page "Multi-Token Attention — Paper Graph", section 3.4 ("Key-Query
  * Convolution" Eq. 4 and its transpose, the softmax, "Head Mixing Convolution"
  * Eq. 7, A.V, "Group Normalization with Sigmoid Gating").  Given

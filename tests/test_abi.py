@@ -43,6 +43,9 @@ def test_exports_every_declared_symbol(lib):
     ("sweep8k_6x11_ch4_post", "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes"),
     ("sweep8k_8x15_ch4_post", "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes"),
     ("toy", "mta_fwd_kernel"), ("tiny", "mta_fwd_kernel"),
+    ("needle4k_ch8", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep per head pair"),
+    ("needle4k_ch16", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep per head pair"),
+    ("needle4k_ch16_post", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep of two passes"),
     ("needle4k_3d", "mta_fwd_v4 (one pass, head-split waves, 3D"), ("needle4k_repeat", "mta_fwd_layer"),
 ])
 def test_kernel_selection(lib, name, expect):
@@ -148,7 +151,8 @@ def test_backward_validation(lib):
                                 a_["dgw"], a_["dgb"], a_["dgate"], a_["ws"], a_["nws"], None)
     # every other placement runs the backward with its maps in the workspace:
     # a workspace below one head group's maps is refused, so is T > 32768
-    for other in (cfg(kq_place=1), cfg(head_place=0), cfg(H=8, c_h=4)):
+    for other in (cfg(kq_place=1), cfg(head_place=0), cfg(H=8, c_h=4), cfg(H=8, c_h=8), cfg(H=16, c_h=16),
+                  cfg(H=8, c_h=8, dtype=0, d=32)):
         name = lib.mta_backward_kernel_name(ctypes.byref(other))
         assert name is not None and name.decode().startswith("mta_bwd_gen"), name
         assert lib.mta_backward_workspace_size(ctypes.byref(other)) > 4096
@@ -187,7 +191,14 @@ def cfg(**kw):
     (dict(head_place=-1), -3), (dict(head_place=2), -3),
     (dict(dtype=7), -4),
     (dict(gn_eps=0.0), -8), (dict(gn_eps=float("nan")), -8), (dict(depth_scale=float("inf")), -8),
-    (dict(d=96), -6), (dict(d=256), -6), (dict(H=8, c_h=8), -6), (dict(H=3, c_h=3), -6),
+    (dict(d=96), -6), (dict(d=256), -6), (dict(H=3, c_h=3), -6), (dict(H=12, c_h=6), -6),
+    (dict(H=32, c_h=32), -6),
+    # groups of 8 or 16 heads: the head-split kernel's source-pair sweeps only
+    # (bf16, d = 128, head mix after the softmax, its compile-time kernel sizes)
+    (dict(H=8, c_h=8), 0), (dict(H=16, c_h=16), 0), (dict(H=16, c_h=16, kq_place=1), 0),
+    (dict(H=16, c_h=8, kq_place=2), 0), (dict(H=16, c_h=16, c_q=1, c_k=1), 0),
+    (dict(H=8, c_h=8, dtype=0), -6), (dict(H=8, c_h=8, head_place=0), -6),
+    (dict(H=8, c_h=8, c_q=5, c_k=7), -6), (dict(H=8, c_h=8, d=64), -6),
     (dict(c_q=17), -6), (dict(c_k=32), -6), (dict(T=(1 << 24) + 1), -6),
     (dict(c_q=16, c_k=31), 0), (dict(c_k=4), 0), (dict(d=32, dtype=0), 0),
 ])

@@ -90,6 +90,16 @@ def _cases():
         c.append(I.small(f"gen_bf16_d{d}_kq{kq}_h{hp}_T{T}", B=2, H=4, T=T, d=d, c_q=4, c_k=7, c_h=2, kq_place=kq,
                          head_place=hp, dtype="bf16", theta_std=0.2, head_std=0.2, gn_random=True,
                          seed=1710 + d + kq + T))
+    # groups of 8 and 16 heads (the wide head mixes, their weight gradient in
+    # a kernel of its own): both dtypes, each placement, dense mixing weights
+    for (ch, H, cq, ck, kq, hp, d, dt, T) in ((8, 8, 6, 11, P, Q, 128, "bf16", 150),
+                                              (16, 16, 4, 9, Q, Q, 128, "bf16", 100),
+                                              (16, 16, 6, 11, E, Q, 128, "bf16", 130),
+                                              (8, 16, 3, 5, P, P, 32, "f32", 77),
+                                              (16, 16, 4, 7, Q, P, 64, "f32", 90)):
+        c.append(I.small(f"gen_{dt}_ch{ch}_H{H}_{cq}x{ck}_kq{kq}_h{hp}", B=1, H=H, T=T, d=d, c_q=cq, c_k=ck,
+                         c_h=ch, kq_place=kq, head_place=hp, dtype=dt, theta_std=0.1, head_std=0.3,
+                         gn_random=True, seed=1750 + ch + H + cq + kq + hp))
     return c
 
 

@@ -2,7 +2,7 @@
 the same seeded inputs.
 
 * small shapes, compared element by element in full: every placement of the
-  two convolutions, c_h in {1,2,4}, ragged T (tails of the 64-row tiles,
+  two convolutions, c_h in {1,2,4,8,16}, ragged T (tails of the 64-row tiles,
   T = 1, T < c_q), d in {32,64,128}, both dtypes, compile-time and runtime-
   sized stencils, even c_k, the largest kernel (16 x 31);
 * the five workloads at their full sizes in the launch configuration the
@@ -97,7 +97,7 @@ def _small_cases():
                              seed=730 + cq + T + kq))
         # the same through single-head groups (head pairs; odd H: the general
         # kernel) and four-head groups
-        for (ch, H, cq, ck) in ((1, 2, 6, 11), (1, 3, 6, 11), (4, 4, 6, 11), (4, 4, 8, 15)):
+        for (ch, H, cq, ck) in ((1, 2, 6, 11), (1, 3, 6, 11), (4, 4, 6, 11), (4, 4, 8, 15), (16, 16, 6, 11)):
             c.append(I.small(f"hot_bf16_ch{ch}_H{H}_{cq}x{ck}_kq{kq}", B=1, H=H, T=256, d=128, c_q=cq, c_k=ck,
                              c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02,
                              layer=4, needles=6, needle_scale=9.0, needle_on_key=True, seed=760 + ch + H + kq))
@@ -113,6 +113,26 @@ def _small_cases():
         c.append(I.small(f"quad_bf16_gated_kq{kq}", B=2, H=8, T=150, d=128, c_q=6, c_k=11, c_h=4, kq_place=kq,
                          dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True,
                          gate_std=1.0, gn_random=True, seed=940 + kq))
+    # groups of 8 and 16 heads (c_h / 2 source-pair sweeps per output pair,
+    # the probabilities in P.V as a bf16 high part and remainder): the
+    # workloads' near-identity mix and dense ones (weights N(0, 0.5) around I:
+    # every source head carries a large share of each output, and for some
+    # output heads the weighted maps nearly cancel, so that one bf16 rounding
+    # of each source head's probabilities before the mix would exceed the bar)
+    for (ch, cq, ck, kq, hs) in ((8, 6, 11, P, 0.05), (8, 6, 11, I.PRE_EXACT, 0.05), (8, 4, 9, Q, 0.05),
+                                 (8, 8, 15, P, 0.5), (8, 1, 1, Q, 0.5), (16, 6, 11, P, 0.05),
+                                 (16, 6, 11, P, 0.5), (16, 8, 15, Q, 0.5), (16, 4, 9, I.PRE_EXACT, 0.5)):
+        c.append(I.small(f"wide_bf16_ch{ch}_{cq}x{ck}_kq{kq}_w{hs}", B=1, H=16, T=150, d=128, c_q=cq, c_k=ck,
+                         c_h=ch, kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=hs,
+                         seed=970 + ch + cq + kq + int(hs * 10)))
+    c.append(I.small("wide_bf16_ch16_gated", B=1, H=16, T=130, d=128, c_q=6, c_k=11, c_h=16, dtype="bf16",
+                     qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True, gate_std=1.0, gn_random=True,
+                     seed=990))
+    for T in (1, 65):
+        for kq in (P, Q):
+            c.append(I.small(f"wide_bf16_ch16_T{T}_kq{kq}", B=2, H=16, T=T, d=128, c_q=6, c_k=11, c_h=16,
+                             kq_place=kq, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.3,
+                             seed=992 + T + kq))
     for T in (1, 3, 64, 65):
         for kq in (P, Q):
             c.append(I.small(f"quad_bf16_T{T}_kq{kq}", B=1, H=4, T=T, d=128, c_q=6, c_k=11, c_h=4, kq_place=kq,
@@ -171,7 +191,8 @@ def test_workload_fp32_full(name):
     _say(f"[parity]   max abs err {err:.3e} (tol {tol:.1e})")
 
 
-@pytest.mark.parametrize("name", ["layer2k", "needle4k", "needle4k_gated", "needle4k_exact"] + I.SWEEP)
+@pytest.mark.parametrize("name", ["layer2k", "needle4k", "needle4k_gated", "needle4k_exact", "needle4k_ch8",
+                                  "needle4k_ch16", "needle4k_ch16_post"] + I.SWEEP)
 def test_workload_bf16_sampled(name):
     cfg = I.CONFIGS[name]
     _say(f"[parity] sampled {cfg.short()}")

@@ -29,7 +29,10 @@ int validate(const mta_config *c)
     if (c->dtype != MTA_F32 && c->dtype != MTA_BF16) return MTA_ERR_BAD_DTYPE;
     if (!(c->gn_eps > 0.0f) || !isfinite(c->gn_eps) || !isfinite(c->depth_scale)) return MTA_ERR_BAD_VALUE;
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return MTA_ERR_UNSUPPORTED;
-    if (c->c_h != 1 && c->c_h != 2 && c->c_h != 4) return MTA_ERR_UNSUPPORTED;
+    // groups of 8 or 16 heads: the forward on the head-split kernel only (bf16,
+    // d = 128, head mix after the softmax; make_plan decides) and the backward
+    // with the maps in the workspace
+    if (c->c_h != 1 && c->c_h != 2 && c->c_h != 4 && c->c_h != 8 && c->c_h != 16) return MTA_ERR_UNSUPPORTED;
     if (c->c_q > mta::MAX_CQ || c->c_k > mta::MAX_CK) return MTA_ERR_UNSUPPORTED;
     if (c->seq_len > (1 << 24)) return MTA_ERR_UNSUPPORTED;
     // the grid is one workgroup per (batch, head group, 64-row query tile)
@@ -69,7 +72,7 @@ const char *mta_status_string(int s)
     case MTA_ERR_BAD_PLACEMENT: return "placement must be pre- (0) or post-softmax (1), or exact pre-softmax (2) for kq";
     case MTA_ERR_BAD_DTYPE: return "dtype must be MTA_F32 or MTA_BF16";
     case MTA_ERR_MISALIGNED: return "tensor pointer not aligned (16 bytes for q,k,v,out; 4 for float params)";
-    case MTA_ERR_UNSUPPORTED: return "configuration outside the library's limits (d in {32,64,128}, c_h in {1,2,4}, c_q<=16, c_k<=31, T<=2^24)";
+    case MTA_ERR_UNSUPPORTED: return "configuration outside the library's limits (d in {32,64,128}, c_h in {1,2,4,8,16}, c_q<=16, c_k<=31, T<=2^24; the forward at c_h 8 or 16: bf16, d=128, head mix after the softmax, c_q x c_k in {1x1,4x9,6x11,8x15})";
     case MTA_ERR_LAUNCH: return "kernel launch failed";
     case MTA_ERR_BAD_VALUE: return "gn_eps must be finite and > 0, depth_scale finite";
     case MTA_ERR_SCRATCH: return "the problem needs more workspace than the library's device scratch array holds";
@@ -162,20 +165,31 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 pl.grid = p.n_qt * p.units;
             }
         }
-        if (!fn && ch == 4 && !hpre) {
-            // four-head groups: the head-split kernel per output head pair, one
-            // sweep per source pair (the grid counts output pairs)
-            fn = mta::find_launch_v4_quad(d, cq, ck, post, exact);
+        if (!fn && (ch == 4 || ch == 8 || ch == 16) && !hpre) {
+            // groups of four or more heads: the head-split kernel per output
+            // head pair, one sweep per source pair (the grid counts output pairs)
+            // groups of 8 and 16: the probabilities in P.V as two bf16 planes
+            // (high part, remainder), since the error of one rounding per
+            // source head grows with the head mix's cancellation
+            const bool two_planes = ch > 4;
+            fn = mta::find_launch_v4_quad(d, cq, ck, post, exact, two_planes);
+            // the grid counts head pairs, c_h / 2 times the groups validate() bounded
+            if ((int64_t)p.n_qt * cfg->batch * (cfg->heads / 2) > INT32_MAX) fn = nullptr;
             if (fn) {
                 p.ncb = 5;
                 p.pitch = p.ncb * 16 + 4;
                 p.G = cfg->heads / 2;
                 p.units = cfg->batch * p.G;
+                p.npair = ch / 2;
                 pl.grid = p.n_qt * p.units;
-                lds = (size_t)mta::v4::layout(cq, ck, false, post != 0).total;
+                lds = (size_t)mta::v4::layout(cq, ck, two_planes, post != 0).total;
                 if (lds > LDS_MAX) fn = nullptr;
-                else pl.name = post ? "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes, head-split waves, fp16 matrix-core stencil)"
-                                    : "mta_fwd_v4 (four-head groups: two source-pair sweeps, head-split waves, fp16 matrix-core stencil)";
+                else if (ch == 4)
+                    pl.name = post ? "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes, head-split waves, fp16 matrix-core stencil)"
+                                   : "mta_fwd_v4 (four-head groups: two source-pair sweeps, head-split waves, fp16 matrix-core stencil)";
+                else
+                    pl.name = post ? "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep of two passes per head pair, head-split waves, fp16 matrix-core stencil)"
+                                   : "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep per head pair, head-split waves, fp16 matrix-core stencil)";
             }
             if (!fn) {
                 p.G = cfg->heads / ch;

@@ -1114,6 +1114,120 @@ __global__ void __launch_bounds__(NTH) gen_mix_bwd(GParams p, float *g_slot, con
     if (tid < CH * CH) atomicAdd(p.dw + (size_t)g * CH * CH + tid, dws[tid]);
 }
 
+// Groups of 8 or 16 heads: the same mixes with the group's weights in LDS
+// (c_h^2 of them would not fit the registers), and the dw sums in a kernel
+// of their own, one output head a per grid z, run before the gradient is
+// transformed in place.
+template <int CH>
+__global__ void __launch_bounds__(NTH) gen_mix_fwd_wide(GParams p, const float *in_slot, float *out_slot)
+{
+    __shared__ float ws[CH * CH];
+    int it, jt;
+    band_tile(blockIdx.x, p.nt, it, jt);
+    const int uu = blockIdx.y, g = (p.u0 + uu) % p.G;
+    for (int t = threadIdx.x; t < CH * CH; t += NTH) ws[t] = p.w[(size_t)g * CH * CH + t];
+    __syncthreads();
+    const size_t msz = (size_t)p.Tp * p.Tp;
+    const float *in = in_slot + (size_t)uu * CH * msz;
+    float *out = out_slot + (size_t)uu * CH * msz;
+    for (int idx = threadIdx.x; idx < TB * TB / 4; idx += NTH) {
+        const int rr = idx >> 4, c4 = idx & 15;
+        const size_t off = (size_t)(it * TB + rr) * p.Tp + jt * TB + 4 * c4;
+        float4 v[CH];
+#pragma unroll
+        for (int b = 0; b < CH; ++b) v[b] = load4(in + b * msz + off);
+#pragma unroll 2
+        for (int a = 0; a < CH; ++a) {
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int b = 0; b < CH; ++b) {
+                const float wab = ws[a * CH + b];
+                o.x = fmaf(wab, v[b].x, o.x);
+                o.y = fmaf(wab, v[b].y, o.y);
+                o.z = fmaf(wab, v[b].z, o.z);
+                o.w = fmaf(wab, v[b].w, o.w);
+            }
+            *reinterpret_cast<float4 *>(out + a * msz + off) = o;
+        }
+    }
+}
+
+// dw[g][a][b] += sum over causal entries of dOut^a x in^b, a = blockIdx.z
+// (grid: n_band x units of the chunk x c_h).
+template <int CH>
+__global__ void __launch_bounds__(NTH) gen_mix_dw_wide(GParams p, const float *g_slot, const float *in_slot)
+{
+    static_assert(CH <= 16, "one partial per source head and lane group");
+    __shared__ float dws[16];
+    int it, jt;
+    band_tile(blockIdx.x, p.nt, it, jt);
+    const int uu = blockIdx.y, g = (p.u0 + uu) % p.G, a = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 16) dws[tid] = 0.f;
+    const size_t msz = (size_t)p.Tp * p.Tp;
+    const float *gm = g_slot + ((size_t)uu * CH + a) * msz;
+    const float *in = in_slot + (size_t)uu * CH * msz;
+    float part[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) part[t] = 0.f;
+    for (int idx = tid; idx < TB * TB / 4; idx += NTH) {
+        const int rr = idx >> 4, c4 = idx & 15;
+        const int i = it * TB + rr, j = jt * TB + 4 * c4;
+        const size_t off = (size_t)i * p.Tp + j;
+        float4 go = load4(gm + off);
+        const bool row_in = i < p.T;
+        go.x = (row_in && j <= i) ? go.x : 0.f;
+        go.y = (row_in && j + 1 <= i) ? go.y : 0.f;
+        go.z = (row_in && j + 2 <= i) ? go.z : 0.f;
+        go.w = (row_in && j + 3 <= i) ? go.w : 0.f;
+#pragma unroll
+        for (int b = 0; b < CH; ++b) {
+            const float4 xi = load4(in + b * msz + off);
+            part[b] += go.x * xi.x + go.y * xi.y + go.z * xi.z + go.w * xi.w;
+        }
+    }
+    __syncthreads();
+    const float tot = reduce16(part, lane);
+    const int slot = reduce16_slot(lane);
+    if ((lane & 3) == 0 && slot < CH) atomicAdd(&dws[slot], tot);
+    __syncthreads();
+    if (tid < CH) atomicAdd(p.dw + ((size_t)g * CH + a) * CH + tid, dws[tid]);
+}
+
+// In place in the gradient slot: dOut -> dIn^b = sum_a w_ab dOut^a.
+template <int CH>
+__global__ void __launch_bounds__(NTH) gen_mix_bwd_wide(GParams p, float *g_slot)
+{
+    __shared__ float ws[CH * CH];
+    int it, jt;
+    band_tile(blockIdx.x, p.nt, it, jt);
+    const int uu = blockIdx.y, g = (p.u0 + uu) % p.G;
+    for (int t = threadIdx.x; t < CH * CH; t += NTH) ws[t] = p.w[(size_t)g * CH * CH + t];
+    __syncthreads();
+    const size_t msz = (size_t)p.Tp * p.Tp;
+    float *gm = g_slot + (size_t)uu * CH * msz;
+    for (int idx = threadIdx.x; idx < TB * TB / 4; idx += NTH) {
+        const int rr = idx >> 4, c4 = idx & 15;
+        const size_t off = (size_t)(it * TB + rr) * p.Tp + jt * TB + 4 * c4;
+        float4 go[CH];
+#pragma unroll
+        for (int a = 0; a < CH; ++a) go[a] = load4(gm + a * msz + off);
+#pragma unroll 2
+        for (int b = 0; b < CH; ++b) {
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int a = 0; a < CH; ++a) {
+                const float wab = ws[a * CH + b];
+                o.x = fmaf(wab, go[a].x, o.x);
+                o.y = fmaf(wab, go[a].y, o.y);
+                o.z = fmaf(wab, go[a].z, o.z);
+                o.w = fmaf(wab, go[a].w, o.w);
+            }
+            *reinterpret_cast<float4 *>(gm + b * msz + off) = o;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // GroupNorm backward, one wave per token of one head (grid: ceil(T / 64) x
 // heads; each workgroup 64 tokens).  In place in the O buffer: O -> dO.

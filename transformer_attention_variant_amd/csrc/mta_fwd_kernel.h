@@ -61,6 +61,7 @@ struct Params {
     int pitch;            // floats per logit-tile row in LDS
     int hl;               // left key halo = ceil(c_k/2) - 1
     int nbuf;             // logit-tile buffers in LDS (c_h when every head's tile is needed at once)
+    int npair;            // head-split kernel, groups of c_h >= 4 heads: source head pairs per group (c_h / 2)
     float sc;             // log2(e) / sqrt(d)
     float eps, depth_scale;
 };

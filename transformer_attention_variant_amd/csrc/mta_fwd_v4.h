@@ -3,8 +3,8 @@
 // Paper Graph", section 3.4, "Key-Query Convolution", "Head Mixing
 // Convolution" Eq. 7, "Group Normalization with Sigmoid Gating").  A
 // workgroup owns two heads: a group of two (c_h = 2, head mix after the
-// softmax), two single-head groups (NOMIX), one output pair of a four-head
-// group (QUAD), or a group of two whose head mix precedes the softmax (C3D,
+// softmax), two single-head groups (NOMIX), one output pair of a group of
+// 4, 8 or 16 heads (QUAD), or a group of two whose head mix precedes the softmax (C3D,
 // as a 3D convolution).  One pass with the key-query convolution before the
 // softmax (two-pass masks or Eq. 4's exact indicator), two passes with it
 // after the softmax (POST); PREP is the gradient-preparation variant.
@@ -452,17 +452,27 @@ struct PrepArgs {
 // U[a][a] products are formed and each output head is its own head's mixed map
 // (the 1x1 mixing weight w_h, p.wmix[h]).  p.G and p.units count head pairs.
 template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false, bool NOMIX = false,
-          bool QUAD = false>
+          bool QUAD = false, bool PPL = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
     static_assert(!(POST && (EXACT || PREP)), "post-softmax form: two-pass masks, forward only");
     static_assert(!(C3D && (EXACT || PREP || POST)), "3D form: two-pass masks, forward only");
     static_assert(!(NOMIX && (C3D || PREP)), "single-head groups: the forward of the per-head kernels");
-    static_assert(!(QUAD && (C3D || PREP || NOMIX)), "four-head groups: the forward with the mix after the softmax");
+    static_assert(!(QUAD && (C3D || PREP || NOMIX)), "groups of four or more heads: the forward with the mix after the softmax");
     constexpr bool DIAG = C3D || NOMIX;  // output head a uses only source head a
+    // probabilities kept to ~16 bits in P.V (a bf16 high part and the bf16
+    // remainder, two planes): the gradients need it, and so do large head
+    // groups (PPL), whose head mix would otherwise add up one bf16 rounding of
+    // every source head's map, weighted by |w_ab|, however much the weighted
+    // maps cancel
+    static_assert(!PPL || QUAD, "two probability planes in the forward: the large-group form");
+    constexpr bool PP = PREP || PPL;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int pi = 0;  // QUAD: source pair of this sweep (see below)
+    // QUAD: the finished sweeps' sum of this lane's output elements, kept in
+    // its private memory between sweeps (volatile: memory, not registers)
+    volatile float keep[QUAD ? CH * 4 * 4 : 1];
 sweep:
     // QUAD: the thread and workgroup indices pass through an empty asm that
     // depends on the sweep, so that everything derived from them is computed
@@ -484,7 +494,7 @@ sweep:
     const int T = p.T;
     constexpr int CKP = ((CK + 3) / 4) * 4;
 
-    const Layout lay = layout(CQ, CK, PREP, POST, C3D);
+    const Layout lay = layout(CQ, CK, PP, POST, C3D);
     f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
@@ -497,21 +507,22 @@ sweep:
     float *th_s = reinterpret_cast<float *>(smem + lay.th_off);
     float *stm = reinterpret_cast<float *>(smem + lay.st_off);  // POST: [h][row] maximum (log2 domain)
     float *stil = stm + CH * EXT_R;                             // POST: [h][row] 1 / sum
-    // before the softmax: the centre-tap plane [h][row][CRP] (fp32; PREP: fp16)
+    // before the softmax: the centre-tap plane [h][row][CRP] (fp32; PP: fp16 residuals)
     unsigned char *crbuf = smem + lay.cr_off;
-    constexpr int CORR = POST ? 0 : (PREP ? 2 : 1);
+    constexpr int CORR = POST ? 0 : (PP ? 2 : 1);
 
-    // QUAD (four-head groups): the workgroup owns output heads h0, h0 + 1 (output
-    // pair g & 1 of the four-head group g / 2); O^a sums over the group's two
-    // source pairs, sum_s w_as U_{s,a} / l_s, one sweep over the key tiles per
-    // source pair with the two-head machinery below (that pair's logits,
-    // stencils and softmax statistics; P.V with the output pair's V).  The
-    // first sweep's share waits in this workgroup's own rows of the output
-    // (fp16) until the second sweep adds it.
+    // QUAD (groups of c_h = 2 * p.npair >= 4 heads): the workgroup owns output
+    // heads h0, h0 + 1 (output pair g % npair of the group g / npair); O^a sums
+    // over the group's source pairs, sum_s w_as U_{s,a} / l_s, one sweep over
+    // the key tiles per source pair with the two-head machinery below (that
+    // pair's logits, stencils and softmax statistics; P.V with the output
+    // pair's V).  The running sum of the finished sweeps waits in each lane's
+    // private memory (float32) until the last sweep adds it.
     const size_t hstride = (size_t)T * D;
     const int h0 = g * CH;
     const size_t base0 = ((size_t)b * p.H + h0) * hstride;
-    const int hsrc0 = QUAD ? 4 * (g >> 1) + 2 * pi : h0;  // source heads of this sweep
+    const int grp = QUAD ? g / p.npair : g;
+    const int hsrc0 = QUAD ? 2 * p.npair * grp + 2 * pi : h0;  // source heads of this sweep
     const size_t sbase = ((size_t)b * p.H + hsrc0) * hstride;
     const bf16_t *Q = reinterpret_cast<const bf16_t *>(p.q) + sbase;
     const bf16_t *K = reinterpret_cast<const bf16_t *>(p.k) + sbase;
@@ -551,7 +562,8 @@ sweep:
         // w_s[a][s]: output head a of the pair, source head s of this sweep
         if (tid < CH * CH)
             w_s[tid] = NOMIX ? ((tid / CH == tid % CH) ? p.wmix[h0 + tid / CH] : 0.f)
-                     : QUAD  ? p.wmix[(size_t)(g >> 1) * 16 + (2 * (g & 1) + tid / CH) * 4 + 2 * pi + tid % CH]
+                     : QUAD  ? p.wmix[((size_t)grp * 2 * p.npair + (h0 - 2 * p.npair * grp) + tid / CH) * 2 * p.npair +
+                                      2 * pi + tid % CH]
                              : p.wmix[(size_t)g * CH * CH + tid];
     }
     wait_vm_all();
@@ -591,7 +603,7 @@ sweep:
 
     const int io = 16 * rw + l16;  // the lane's stencil row within the query tile
     // its row of the centre-tap plane (before the softmax)
-    void *crow = crbuf + (size_t)(hs * BM + io) * CRP * (PREP ? 2 : 4);
+    void *crow = crbuf + (size_t)(hs * BM + io) * CRP * (PP ? 2 : 4);
     const int qabs = i0 + io;
     const int rho = HALO + io;
     const int dbase = 64 * hs;
@@ -743,11 +755,11 @@ sweep:
                     f32x4 xs;
                     v = cvt_block<M>(1 + rw, cb, qk(kf[cb & 1], qown), i0, j0, XL, T, EXACT, lane, xs);
                     if (cb == 0)
-                        store_centre<0, !PREP>(crow, xs, v, t, lane);
+                        store_centre<0, !PP>(crow, xs, v, t, lane);
                     else if (cb == NCB - 1)
-                        store_centre<NCB - 1, !PREP>(crow, xs, v, t, lane);
+                        store_centre<NCB - 1, !PP>(crow, xs, v, t, lane);
                     else
-                        store_centre<1, !PREP>(reinterpret_cast<unsigned char *>(crow) + 16 * (cb - 1) * (PREP ? 2 : 4),
+                        store_centre<1, !PP>(reinterpret_cast<unsigned char *>(crow) + 16 * (cb - 1) * (PP ? 2 : 4),
                                                xs, v, t, lane);
                 }
                 if ((cb - CB0) & 1)
@@ -847,7 +859,7 @@ sweep:
 #pragma unroll
                 for (int s = 0; s < CH; ++s) {
                     av[s] = pbuf[((s * 4 + rw) * 2 + cs) * 64 + lane];
-                    if (PREP) avl[s] = pbuf[CH * 4 * 2 * 64 + ((s * 4 + rw) * 2 + cs) * 64 + lane];
+                    if (PP) avl[s] = pbuf[CH * 4 * 2 * 64 + ((s * 4 + rw) * 2 + cs) * 64 + lane];
                 }
                 const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
 #pragma unroll
@@ -864,8 +876,8 @@ sweep:
                         for (int s = 0; s < CH; ++s) {
                             if (DIAG && s != a) continue;
                             U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
-                            // the gradients use P . V with P kept to ~16 bits (high part + remainder)
-                            if (PREP)
+                            // P kept to ~16 bits: the remainder's product
+                            if (PP)
                                 U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
                         }
                     }
@@ -894,11 +906,18 @@ sweep:
                         c[o] = (j0 + key <= qabs) ? c[o] : 0.f;
                     }
                 }
-                bf16x8 v8[2];
+                bf16x8 v8[2], v8l[2];
 #pragma unroll
-                for (int o = 0; o < 16; ++o) v8[o >> 3][o & 7] = (bf16_t)c[o];
+                for (int o = 0; o < 16; ++o) {
+                    v8[o >> 3][o & 7] = (bf16_t)c[o];
+                    if (PP) v8l[o >> 3][o & 7] = (bf16_t)(c[o] - (float)v8[o >> 3][o & 7]);
+                }
                 pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
                 pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+                if (PP) {
+                    pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
+                    pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
+                }
                 if (lane == 0) fl[hs * 4 + rw] = 0;  // no rescale
             } else {
                 // Mask_-inf (only the diagonal tile has keys in the future of its
@@ -925,12 +944,12 @@ sweep:
                     const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
                     ls += e;
                     v8[o >> 3][o & 7] = (bf16_t)e;
-                    if (PREP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
+                    if (PP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
                 }
                 l_run = __builtin_fmaf(l_run, alpha, ls);
                 pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
                 pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
-                if (PREP) {
+                if (PP) {
                     pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8l[0];
                     pbuf[CH * 4 * 2 * 64 + ((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8l[1];
                 }
@@ -1166,28 +1185,22 @@ sweep:
     }
 
     if constexpr (QUAD) {
-        // hand the first sweep's share over through the output rows this
-        // workgroup alone writes (fp16 in the bf16 slots; the same lane reads
-        // back what it wrote)
-        f16_t *part = reinterpret_cast<f16_t *>(p.out);
+        // the first sweep stores its share, each later one adds the stored
+        // sum, and all but the last store the new sum (float32 throughout, so
+        // that mixing weights which cancel keep the precision of one sweep)
+        const bool last = pi + 1 == p.npair;
 #pragma unroll
         for (int a = 0; a < CH; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = i0 + 16 * rw + 4 * g4 + r;
-                if (row < T) {
-                    f16_t *cell = part + ((size_t)b * p.H + h0 + a) * hstride + (size_t)row * D + dbase + l16;
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        if (pi == 0)
-                            cell[16 * nb] = (f16_t)f16_range(acc[a][nb][r]);
-                        else
-                            acc[a][nb][r] += (float)cell[16 * nb];
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const int i = (a * 4 + nb) * 4 + r;
+                    if (pi > 0) acc[a][nb][r] += keep[i];
+                    if (!last) keep[i] = acc[a][nb][r];
                 }
-            }
-        if (pi == 0) {
-            pi = 1;
+        if (!last) {
+            ++pi;
             __syncthreads();  // every wave is done with this sweep's LDS
             goto sweep;
         }
@@ -1260,10 +1273,11 @@ sweep:
     }
 }
 
-template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false, bool QUAD = false>
+template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false, bool QUAD = false,
+          bool PPL = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX, QUAD>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX, QUAD, PPL>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

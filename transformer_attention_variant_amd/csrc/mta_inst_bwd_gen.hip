@@ -61,12 +61,31 @@ hipError_t mix_bwd(const GParams &p, float *g, const float *in, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int CH>
+hipError_t mix_fwd_wide(const GParams &p, const float *in, float *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(gen_mix_fwd_wide<CH>, dim3(p.n_band, p.nu), dim3(NTH), 0, s, p, in, out);
+    return hipGetLastError();
+}
+
+// dw first (it reads the gradient slot), then the in-place transform
+template <int CH>
+hipError_t mix_bwd_wide(const GParams &p, float *g, const float *in, hipStream_t s)
+{
+    hipLaunchKernelGGL(gen_mix_dw_wide<CH>, dim3(p.n_band, p.nu, CH), dim3(NTH), 0, s, p, g, in);
+    GEN_CHECK();
+    hipLaunchKernelGGL(gen_mix_bwd_wide<CH>, dim3(p.n_band, p.nu), dim3(NTH), 0, s, p, g);
+    return hipGetLastError();
+}
+
 hipError_t mix(bool fwd, const GParams &p, const float *in, float *out, hipStream_t s)
 {
     switch (p.c_h) {
     case 1: return fwd ? mix_fwd<1>(p, in, out, s) : mix_bwd<1>(p, out, in, s);
     case 2: return fwd ? mix_fwd<2>(p, in, out, s) : mix_bwd<2>(p, out, in, s);
     case 4: return fwd ? mix_fwd<4>(p, in, out, s) : mix_bwd<4>(p, out, in, s);
+    case 8: return fwd ? mix_fwd_wide<8>(p, in, out, s) : mix_bwd_wide<8>(p, out, in, s);
+    case 16: return fwd ? mix_fwd_wide<16>(p, in, out, s) : mix_bwd_wide<16>(p, out, in, s);
     default: return hipErrorInvalidValue;
     }
 }

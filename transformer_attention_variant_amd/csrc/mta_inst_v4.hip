@@ -1,4 +1,4 @@
-// Head-split kernels (bf16, d = 128, c_h = 2, head mix after the softmax) for
+// Head-split kernels (bf16, d = 128, head mix after the softmax) for
 // the kernel sizes of the 2K/4K/8K workloads and 1x1: one pass with the
 // key-query convolution before the softmax (either form), two passes with it
 // after the softmax.
@@ -51,22 +51,29 @@ LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
     return nullptr;
 }
 
-// Four-head groups (c_h = 4), one workgroup per output head pair sweeping the
-// group's two source pairs; either key-query placement; the caller counts
-// output pairs in p.G.
-#define MTA_V4Q_SIZE(CQ_, CK_)                                                                         \
+// Groups of 4, 8 or 16 heads, one workgroup per output head pair sweeping the
+// group's source pairs; either key-query placement; the caller counts output
+// pairs in p.G and source pairs per group in p.npair.  two_planes: the
+// probabilities in P.V as a bf16 high part and remainder (groups of 8 and 16).
+#define MTA_V4Q_SIZE(CQ_, CK_, PPL_)                                                                   \
     if (cq == CQ_ && ck == CK_)                                                                        \
-        return post ? &v4::launch<CQ_, CK_, false, true, false, false, true>                          \
-                    : (exact ? &v4::launch<CQ_, CK_, true, false, false, false, true>                 \
-                             : &v4::launch<CQ_, CK_, false, false, false, false, true>);
+        return post ? &v4::launch<CQ_, CK_, false, true, false, false, true, PPL_>                    \
+                    : (exact ? &v4::launch<CQ_, CK_, true, false, false, false, true, PPL_>           \
+                             : &v4::launch<CQ_, CK_, false, false, false, false, true, PPL_>);
+#define MTA_V4Q_SIZES(PPL_)        \
+    MTA_V4Q_SIZE(1, 1, PPL_)       \
+    MTA_V4Q_SIZE(4, 9, PPL_)       \
+    MTA_V4Q_SIZE(6, 11, PPL_)      \
+    MTA_V4Q_SIZE(8, 15, PPL_)
 
-LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact)
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int two_planes)
 {
     if (d != 128 || (post && exact)) return nullptr;
-    MTA_V4Q_SIZE(1, 1)
-    MTA_V4Q_SIZE(4, 9)
-    MTA_V4Q_SIZE(6, 11)
-    MTA_V4Q_SIZE(8, 15)
+    if (two_planes) {
+        MTA_V4Q_SIZES(true)
+    } else {
+        MTA_V4Q_SIZES(false)
+    }
     return nullptr;
 }
 

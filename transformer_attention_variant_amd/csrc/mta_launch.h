@@ -41,9 +41,11 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
 LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int post, int exact);
 // Its 3D-convolution form (two-pass masks, no head mix); null when not instantiated.
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
-// Four-head groups: the head-split kernel per output head pair, two source-pair
-// sweeps (p.G counts output pairs); null when not instantiated.
-LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact);
+// Groups of 4, 8 or 16 heads: the head-split kernel per output head pair, one
+// sweep per source pair (p.G counts output pairs, p.npair source pairs per
+// group); two_planes: the probabilities in P.V as a bf16 high part and
+// remainder.  Null when not instantiated.
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int two_planes);
 // Their gradient-preparation variants (key-query convolution before the
 // softmax, head mix after it); null when not instantiated.
 namespace v4 {

@@ -143,6 +143,11 @@ def _configs() -> Dict[str, MTAConfig]:
     # softmax ("Putting Everything Together"), on the same layer
     c["needle4k_3d"] = replace(c["needle4k"], name="needle4k_3d", form="3d", head_place=PRE)
     c["needle4k_repeat"] = replace(c["needle4k"], name="needle4k_repeat", form="repeat", c_q2=6, c_k2=11)
+    # the same layer with larger head groups: all sixteen heads in one group
+    # (the pages' default c_h) and two groups of eight, both masking forms
+    c["needle4k_ch8"] = replace(c["needle4k"], name="needle4k_ch8", c_h=8)
+    c["needle4k_ch16"] = replace(c["needle4k"], name="needle4k_ch16", c_h=16)
+    c["needle4k_ch16_post"] = replace(c["needle4k"], name="needle4k_ch16_post", c_h=16, kq_place=POST)
     for (cq, ck) in ((4, 9), (6, 11), (8, 15)):
         for ch in (2, 4):
             for kq in (PRE, POST):

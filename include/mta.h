@@ -68,8 +68,10 @@ extern "C" {
  * probabilities to bf16 before the head mix, which they apply to the per-head
  * A·V products: under strongly cancelling mixing weights the output's error
  * relative to its size grows accordingly.  With groups of 8 or 16 heads they
- * keep the probabilities to ~16 bits in A·V (a bf16 high part and the bf16
- * remainder), which removes that growth.  Groups of 4 or more heads sum the
+ * run A·V with fp16 operands instead (11 significant bits: the probabilities,
+ * and V converted exactly for 2^-14 <= |v| <= 65504, magnitudes beyond 65504
+ * clamped, smaller ones rounded to the fp16 subnormal grid), which keeps that
+ * growth within the bf16 tolerance.  Groups of 4 or more heads sum the
  * source head pairs' shares in float32.
  * mta_kernel_name tells which kernel a configuration runs. */
 #define MTA_F32 0

@@ -168,11 +168,11 @@ static int make_plan(const mta_config *cfg, Plan &pl)
         if (!fn && (ch == 4 || ch == 8 || ch == 16) && !hpre) {
             // groups of four or more heads: the head-split kernel per output
             // head pair, one sweep per source pair (the grid counts output pairs)
-            // groups of 8 and 16: the probabilities in P.V as two bf16 planes
-            // (high part, remainder), since the error of one rounding per
-            // source head grows with the head mix's cancellation
-            const bool two_planes = ch > 4;
-            fn = mta::find_launch_v4_quad(d, cq, ck, post, exact, two_planes);
+            // groups of 8 and 16: P.V with fp16 operands, since the error of
+            // one rounding per source head grows with the head mix's
+            // cancellation
+            const bool f16pv = ch > 4;
+            fn = mta::find_launch_v4_quad(d, cq, ck, post, exact, f16pv);
             // the grid counts head pairs, c_h / 2 times the groups validate() bounded
             if ((int64_t)p.n_qt * cfg->batch * (cfg->heads / 2) > INT32_MAX) fn = nullptr;
             if (fn) {
@@ -182,7 +182,7 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 p.units = cfg->batch * p.G;
                 p.npair = ch / 2;
                 pl.grid = p.n_qt * p.units;
-                lds = (size_t)mta::v4::layout(cq, ck, two_planes, post != 0).total;
+                lds = (size_t)mta::v4::layout(cq, ck, false, post != 0).total;
                 if (lds > LDS_MAX) fn = nullptr;
                 else if (ch == 4)
                     pl.name = post ? "mta_fwd_v4 (four-head groups: two source-pair sweeps of two passes, head-split waves, fp16 matrix-core stencil)"

@@ -141,6 +141,27 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // its largest finite value (never inf, so a zero tap never meets an infinity)
 __device__ inline float f16_range(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
 
+// fp16 P.V: a wave's own pieces of a V tile (those dma_pair<true, NROWS>
+// gave it: 1 KB each, lane l's 16 bytes at 16 l), bf16 -> fp16 in place,
+// elementwise, so the rows' swizzle is kept.  Exact for 2^-14 <= |v| <= 65504
+// (bf16's 8 significant bits fit fp16's 11); smaller magnitudes round to the
+// fp16 subnormal grid (absolute error <= 2^-25), larger ones clamp to 65504.
+template <int NROWS>
+__device__ inline void v_to_f16(bf16_t *lds, int wave, int lane)
+{
+    constexpr int PER = NROWS / 4;
+#pragma unroll 1
+    for (int k = 0; k < CH * PER / 8; ++k) {  // one piece at a time: few registers
+        const int i = wave + 8 * k, h = i / PER, piece = i % PER;
+        bf16x8 *cell = reinterpret_cast<bf16x8 *>(lds + h * NROWS * D + 512 * piece) + lane;
+        const bf16x8 x = *cell;
+        f16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (f16_t)f16_range((float)x[e]);
+        *cell = __builtin_bit_cast(bf16x8, y);
+    }
+}
+
 // fp16 logit tiles: row rho (0..EXT_R-1) holds 80 columns in ten 16-byte
 // chunks; chunk c of row rho is stored at chunk c ^ ((rho >> 2) & 1).  With the
 // 160-byte row pitch this keeps the stencil's 16-byte reads and the paired
@@ -452,7 +473,7 @@ struct PrepArgs {
 // U[a][a] products are formed and each output head is its own head's mixed map
 // (the 1x1 mixing weight w_h, p.wmix[h]).  p.G and p.units count head pairs.
 template <int CQ, int CK, bool EXACT, bool PREP = false, bool POST = false, bool C3D = false, bool NOMIX = false,
-          bool QUAD = false, bool PPL = false>
+          bool QUAD = false, bool F16PV = false>
 __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
 {
     static_assert(CK <= 17, "matrix-core stencil: 32-column window");
@@ -461,13 +482,14 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_v4(Params p, PrepArgs pa)
     static_assert(!(NOMIX && (C3D || PREP)), "single-head groups: the forward of the per-head kernels");
     static_assert(!(QUAD && (C3D || PREP || NOMIX)), "groups of four or more heads: the forward with the mix after the softmax");
     constexpr bool DIAG = C3D || NOMIX;  // output head a uses only source head a
-    // probabilities kept to ~16 bits in P.V (a bf16 high part and the bf16
-    // remainder, two planes): the gradients need it, and so do large head
-    // groups (PPL), whose head mix would otherwise add up one bf16 rounding of
+    // PREP: probabilities kept to ~16 bits in P.V (a bf16 high part and the
+    // bf16 remainder, two planes), as the gradients need.  F16PV: P.V in fp16
+    // (11 significant bits against bf16's 8; V converted in LDS), for large
+    // head groups, whose head mix would otherwise add up one bf16 rounding of
     // every source head's map, weighted by |w_ab|, however much the weighted
     // maps cancel
-    static_assert(!PPL || QUAD, "two probability planes in the forward: the large-group form");
-    constexpr bool PP = PREP || PPL;
+    static_assert(!(F16PV && PREP), "fp16 P.V: the forward");
+    constexpr bool PP = PREP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int pi = 0;  // QUAD: source pair of this sweep (see below)
     // QUAD: the finished sweeps' sum of this lane's output elements, kept in
@@ -875,7 +897,11 @@ sweep:
 #pragma unroll
                         for (int s = 0; s < CH; ++s) {
                             if (DIAG && s != a) continue;
-                            U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
+                            if constexpr (F16PV)
+                                U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    __builtin_bit_cast(f16x8, av[s]), __builtin_bit_cast(f16x8, bv), U[s][a][nb], 0, 0, 0);
+                            else
+                                U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv, U[s][a][nb], 0, 0, 0);
                             // P kept to ~16 bits: the remainder's product
                             if (PP)
                                 U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
@@ -912,6 +938,13 @@ sweep:
                     v8[o >> 3][o & 7] = (bf16_t)c[o];
                     if (PP) v8l[o >> 3][o & 7] = (bf16_t)(c[o] - (float)v8[o >> 3][o & 7]);
                 }
+                if constexpr (F16PV) {
+                    f16x8 h8[2];
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) h8[o >> 3][o & 7] = (f16_t)f16_range(c[o]);
+                    v8[0] = __builtin_bit_cast(bf16x8, h8[0]);
+                    v8[1] = __builtin_bit_cast(bf16x8, h8[1]);
+                }
                 pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
                 pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
                 if (PP) {
@@ -939,12 +972,21 @@ sweep:
                 m_run = m_new;
                 float ls = 0.f;
                 bf16x8 v8[2], v8l[2];
+                f16x8 h8[2];
 #pragma unroll
                 for (int o = 0; o < 16; ++o) {
                     const float e = __builtin_amdgcn_exp2f(c[o] - m_new);  // exp2(-inf) = 0 in the future
                     ls += e;
-                    v8[o >> 3][o & 7] = (bf16_t)e;
-                    if (PP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
+                    if constexpr (F16PV) {
+                        h8[o >> 3][o & 7] = (f16_t)e;  // in [0, 1]
+                    } else {
+                        v8[o >> 3][o & 7] = (bf16_t)e;
+                        if (PP) v8l[o >> 3][o & 7] = (bf16_t)(e - (float)v8[o >> 3][o & 7]);
+                    }
+                }
+                if constexpr (F16PV) {
+                    v8[0] = __builtin_bit_cast(bf16x8, h8[0]);
+                    v8[1] = __builtin_bit_cast(bf16x8, h8[1]);
                 }
                 l_run = __builtin_fmaf(l_run, alpha, ls);
                 pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
@@ -958,6 +1000,9 @@ sweep:
                 if (lane == 0) fl[hs * 4 + rw] = moved ? 1 : 0;
             }
             wait_vm_all();  // K(t+1) and V(t) have landed
+            // F16PV: this wave's own V pieces to fp16 in place (published, with
+            // the other waves', by the next barrier)
+            if constexpr (F16PV) v_to_f16<BN>(vbuf, wave, lane);
         }
         };
     step(0, std::true_type{});
@@ -1274,10 +1319,10 @@ sweep:
 }
 
 template <int CQ, int CK, bool EXACT, bool POST = false, bool C3D = false, bool NOMIX = false, bool QUAD = false,
-          bool PPL = false>
+          bool F16PV = false>
 hipError_t launch(const Params &p, int grid, size_t lds, hipStream_t s)
 {
-    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX, QUAD, PPL>;
+    auto fn = mta_fwd_v4<CQ, CK, EXACT, false, POST, C3D, NOMIX, QUAD, F16PV>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

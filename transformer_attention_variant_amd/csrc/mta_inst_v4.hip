@@ -53,8 +53,8 @@ LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
 
 // Groups of 4, 8 or 16 heads, one workgroup per output head pair sweeping the
 // group's source pairs; either key-query placement; the caller counts output
-// pairs in p.G and source pairs per group in p.npair.  two_planes: the
-// probabilities in P.V as a bf16 high part and remainder (groups of 8 and 16).
+// pairs in p.G and source pairs per group in p.npair.  f16pv: P.V with fp16
+// operands (groups of 8 and 16).
 #define MTA_V4Q_SIZE(CQ_, CK_, PPL_)                                                                   \
     if (cq == CQ_ && ck == CK_)                                                                        \
         return post ? &v4::launch<CQ_, CK_, false, true, false, false, true, PPL_>                    \
@@ -66,10 +66,10 @@ LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
     MTA_V4Q_SIZE(6, 11, PPL_)      \
     MTA_V4Q_SIZE(8, 15, PPL_)
 
-LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int two_planes)
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int f16pv)
 {
     if (d != 128 || (post && exact)) return nullptr;
-    if (two_planes) {
+    if (f16pv) {
         MTA_V4Q_SIZES(true)
     } else {
         MTA_V4Q_SIZES(false)

@@ -43,9 +43,8 @@ LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int post, int exact);
 LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck);
 // Groups of 4, 8 or 16 heads: the head-split kernel per output head pair, one
 // sweep per source pair (p.G counts output pairs, p.npair source pairs per
-// group); two_planes: the probabilities in P.V as a bf16 high part and
-// remainder.  Null when not instantiated.
-LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int two_planes);
+// group); f16pv: P.V with fp16 operands.  Null when not instantiated.
+LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int f16pv);
 // Their gradient-preparation variants (key-query convolution before the
 // softmax, head mix after it); null when not instantiated.
 namespace v4 {

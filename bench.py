@@ -62,7 +62,7 @@ def kernel_sources_hash(kernel: str = "") -> str:
 def stencil_on_matrix_cores(kname) -> bool:
     """Whether the named kernel runs the key-query stencil on the matrix cores
     (fp16 operands) rather than on the fp32 vector ALUs."""
-    return kname is not None and kname.startswith("mta_fwd_v4")
+    return kname is not None and kname.startswith(("mta_fwd_v4", "mta_fwd_rep"))
 
 
 def parse():
@@ -229,7 +229,10 @@ def main():
             "peak": mfma_peak,
             "unit": "TFLOP/s",
             "frac": round(all_flops / t / 1e12 / mfma_peak, 4),
-            "work": "4*d (QK^T, PV) + 2*c_q*c_k (stencil) + 2*c_h (head mix) FLOP per causal logit",
+            "work": ("4*d (QK^T, PV) + 2*(c_q*c_k + c_q2*c_k2) (both key-query convolutions) + 4*c_h "
+                     "(both head mixes) FLOP per causal logit" if cfg.form == "repeat" else
+                     "4*d (QK^T, PV) + 2*c_q*c_k*c_h (the 3D kernel) FLOP per causal logit" if cfg.form == "3d" else
+                     "4*d (QK^T, PV) + 2*c_q*c_k (stencil) + 2*c_h (head mix) FLOP per causal logit"),
         }
     else:
         roof = {

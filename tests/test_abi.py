@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
     ("needle4k_ch8", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep per head pair"),
     ("needle4k_ch16", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep per head pair"),
     ("needle4k_ch16_post", "mta_fwd_v4 (groups of 8 or 16 heads: one source-pair sweep of two passes"),
-    ("needle4k_3d", "mta_fwd_v4 (one pass, head-split waves, 3D"), ("needle4k_repeat", "mta_fwd_layer"),
+    ("needle4k_3d", "mta_fwd_v4 (one pass, head-split waves, 3D"), ("needle4k_repeat", "mta_fwd_rep (two passes"),
 ])
 def test_kernel_selection(lib, name, expect):
     """Host-only query of the kernel each workload runs (no launch)."""
@@ -119,7 +119,14 @@ def test_layer_validation(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    ({}, "mta_fwd_layer"),                                                  # the repeated form
+    ({}, "mta_fwd_layer"),                                                  # the repeated form, 6x11 then 3x5
+    (dict(c_q2=6, c_k2=11), "mta_fwd_rep (two passes"),                     # 6x11 before and after: head-split
+    (dict(c_q=4, c_k=9, c_q2=4, c_k2=9), "mta_fwd_rep (two passes"),
+    (dict(c_q2=6, c_k2=11, head_post=None, head_post2=None), "mta_fwd_rep (two passes"),
+    (dict(c_q2=6, c_k2=11, exact=1), "mta_fwd_layer"),                      # Eq. 4's indicator: general kernel
+    (dict(c_q2=6, c_k2=11, dtype=0), "mta_fwd_layer"),                      # float32
+    (dict(c_q2=6, c_k2=11, d=64), "mta_fwd_layer"),
+    (dict(c_q2=6, c_k2=11, head_pre=0x1000), "mta_fwd_layer"),              # a head mix before the softmax
     (dict(kq_post=None, head_post2=None), "mta_fwd_v4"),                    # kq pre + head post
     (dict(kq_pre=None, head_post=None, c_q2=6, c_k2=11), "mta_fwd_v4 (two passes"),  # kq post + head post
     (dict(kq_pre=None, head_post2=None), "mta_fwd_layer"),                  # head mix before the kq conv

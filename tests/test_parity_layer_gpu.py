@@ -5,6 +5,7 @@ Everything Together"), layers with every stage, without a pre-softmax
 convolution or with head mixes only, and layers that are one of mta_forward's
 placements (which must give bitwise mta_forward's result).  Same tolerances as
 the other parity tests."""
+import ctypes
 import sys
 
 import numpy as np
@@ -55,6 +56,21 @@ def _cases():
         c.append(I.small(f"repeat_{dt}_d{d}_ch{ch}_{cq}x{ck}_{cq2}x{ck2}", B=1, H=4, T=130, d=d, c_q=cq, c_k=ck,
                          c_h=ch, form="repeat", c_q2=cq2, c_k2=ck2, dtype=dt, theta_std=0.1, head_std=0.1,
                          seed=920 + cq + ck2))
+    # the repeated form's head-split kernel (bf16, d = 128, c_h = 2, 6x11 and 4x9):
+    # ragged and tiny sequences, several batches and groups, a gate with a
+    # random GroupNorm affine, needle rows
+    for (T, B, H) in ((65, 2, 4), (3, 1, 2), (200, 3, 4), (64, 1, 2), (129, 1, 8)):
+        c.append(I.small(f"repeat_bf16_6x11_T{T}_B{B}_H{H}", B=B, H=H, T=T, d=128, c_q=6, c_k=11, c_h=2,
+                         form="repeat", c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.05,
+                         head_std=0.05, seed=960 + T + B))
+    c.append(I.small("repeat_bf16_4x9_4x9_ch2", B=2, H=4, T=150, d=128, c_q=4, c_k=9, c_h=2, form="repeat",
+                     c_q2=4, c_k2=9, dtype="bf16", qkv_std=0.7071, theta_std=0.1, head_std=0.1, seed=970))
+    c.append(I.small("repeat_bf16_6x11_gated", B=1, H=4, T=190, d=128, c_q=6, c_k=11, c_h=2, form="repeat",
+                     c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, gated=True,
+                     gate_std=1.0, gn_random=True, seed=971))
+    c.append(I.small("repeat_bf16_6x11_needles", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=2, form="repeat",
+                     c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.02, head_std=0.02, layer=4,
+                     needles=6, seed=972))
     c.append(I.small("repeat_exact_f32", B=2, H=2, T=77, d=32, c_q=3, c_k=6, c_h=2, form="repeat", c_q2=2,
                      c_k2=5, kq_place=E, theta_std=0.2, head_std=0.2, gn_random=True, seed=931))
     c.append(I.small("repeat_f32_T3", B=1, H=2, T=3, d=32, c_q=3, c_k=5, c_h=2, form="repeat", c_q2=4, c_k2=3,
@@ -110,6 +126,43 @@ def test_layer_stage_combinations(dt):
                            c_h=cfg.c_h, c_q2=cfg.c_q2, c_k2=cfg.c_k2, exact=exact, eps=cfg.gn_eps,
                            depth_scale=cfg.depth_scale, gate=inp["gate"], **w)
         compare(cfg, got, ref, what=f"layer {name}")
+
+
+def test_repeat_kernel_head_mixes():
+    """The repeated form's head-split kernel with both head mixes, with either
+    one absent (the identity) and with neither."""
+    cfg = I.small("rep_mixes", B=1, H=4, T=150, d=128, c_q=6, c_k=11, c_h=2, form="repeat", c_q2=6, c_k2=11,
+                  dtype="bf16", qkv_std=0.7071, theta_std=0.1, head_std=0.2, seed=975)
+    inp = I.generate(cfg)
+    dev = to_dev(inp)
+    base = I.layer_weights(cfg, inp)
+    exact = base.pop("exact")
+    for c in ("c_q2", "c_k2"):
+        base.pop(c)
+    combos = {
+        "both": dict(base),
+        "no_head_post": {k: v for k, v in base.items() if k != "head_post"},
+        "no_head_post2": {k: v for k, v in base.items() if k != "head_post2"},
+        "no_mix": {k: v for k, v in base.items() if k not in ("head_post", "head_post2")},
+    }
+    for name, w in combos.items():
+        ptrs = {k: 0x1000 for k in w}
+        ptrs.update(gn_w=0x1000, gn_b=0x1000)
+        lc, lw = binding._layer_structs(cfg.B, cfg.H, cfg.T, cfg.d, I.BF16, cfg.c_h, cfg.c_q, cfg.c_k, cfg.c_q2,
+                                        cfg.c_k2, exact, cfg.gn_eps, cfg.depth_scale, ptrs)
+        kname = binding.load().mta_layer_kernel_name(ctypes.byref(lc), ctypes.byref(lw)).decode()
+        assert kname.startswith("mta_fwd_rep"), kname
+        _say(f"[layer] repeated form, head mixes {name}")
+        got = binding.forward_layer(dev["q"], dev["k"], dev["v"], dev["gn_w"], dev["gn_b"], c_h=cfg.c_h,
+                                    c_q=cfg.c_q, c_k=cfg.c_k, c_q2=cfg.c_q2, c_k2=cfg.c_k2, exact=exact,
+                                    gn_eps=cfg.gn_eps, depth_scale=cfg.depth_scale,
+                                    **{k: v.cuda() for k, v in w.items()})
+        torch.cuda.synchronize()
+        ref = oracle.layer(inp["q"], inp["k"], inp["v"], inp["gn_w"], inp["gn_b"], c_q=cfg.c_q, c_k=cfg.c_k,
+                           c_h=cfg.c_h, c_q2=cfg.c_q2, c_k2=cfg.c_k2, exact=exact, eps=cfg.gn_eps,
+                           depth_scale=cfg.depth_scale, **w)
+        err, tol = compare(cfg, got, ref, what=f"repeated form {name}")
+        _say(f"[layer]   closest element: err {err:.3e} of bar {tol:.3e}")
 
 
 @pytest.mark.parametrize("kq,hd", [(I.PRE, I.POST), (I.POST, I.POST), (I.PRE, I.PRE), (I.POST, I.PRE),

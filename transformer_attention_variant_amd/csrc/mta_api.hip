@@ -8,6 +8,7 @@
 #include "mta.h"
 #include "mta_fwd_v4.h"
 #include "mta_fwd_layer.h"
+#include "mta_fwd_rep.h"
 #include "mta_bwd.h"
 #include "mta_bwd_gen_api.h"
 #include "mta_launch.h"
@@ -420,6 +421,41 @@ static bool as_v4_3d(const mta_layer_config *c, const mta_layer_weights *w, Plan
     return true;
 }
 
+// The repeated convolution (a key-query convolution before the softmax with
+// the two-pass masks, and one after it; head mixes after the softmax or none)
+// runs the head-split two-pass kernel where it is instantiated (bf16, d = 128,
+// c_h = 2): the post-softmax stages fold into one 3D stencil.
+struct RepPlan {
+    mta::rep::RepFn fn = nullptr;
+    size_t lds = 0;
+    int grid = 0;
+    mta::rep::RParams p{};
+};
+
+static const char *const REP_NAME =
+    "mta_fwd_rep (two passes, head-split waves, the repeated convolution after the softmax as a 3D stencil, "
+    "fp16 matrix-core stencils)";
+
+static bool as_rep(const mta_layer_config *c, const mta_layer_weights *w, RepPlan &pl)
+{
+    if (!w->kq_pre || !w->kq_post || w->conv3d || w->head_pre || c->exact) return false;
+    if (c->dtype != MTA_BF16 || c->head_dim != 128 || c->c_h != 2) return false;
+    pl.fn = mta::rep::find_launch(c->head_dim, c->c_h, c->c_q, c->c_k, c->c_q2, c->c_k2);
+    pl.lds = mta::rep::lds_bytes(c->c_q, c->c_k, c->c_q2, c->c_k2);
+    if (!pl.fn || pl.lds == 0 || pl.lds > 160 * 1024) return false;
+    mta::rep::RParams &p = pl.p;
+    p.H = c->heads;
+    p.T = c->seq_len;
+    p.G = c->heads / 2;
+    p.units = c->batch * p.G;
+    p.n_qt = (c->seq_len + mta::BM - 1) / mta::BM;
+    p.sc = 1.4426950408889634f / sqrtf((float)c->head_dim);
+    p.eps = c->gn_eps;
+    p.depth_scale = c->depth_scale;
+    pl.grid = p.n_qt * p.units;
+    return true;
+}
+
 int mta_forward_layer(const void *q, const void *k, const void *v, const mta_layer_weights *w,
                       const mta_layer_config *c, void *out, void *stream)
 {
@@ -445,6 +481,16 @@ int mta_forward_layer(const void *q, const void *k, const void *v, const mta_lay
         const hipError_t e = p3.fn(p, p3.grid, p3.lds, reinterpret_cast<hipStream_t>(stream));
         return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
     }
+    RepPlan rp;
+    if (as_rep(c, w, rp)) {
+        mta::rep::RParams &p = rp.p;
+        p.q = q; p.k = k; p.v = v;
+        p.theta1 = w->kq_pre; p.w1 = w->head_post; p.theta2 = w->kq_post; p.w2 = w->head_post2;
+        p.gn_w = w->gn_w; p.gn_b = w->gn_b; p.gate = w->gate;
+        p.out = out;
+        const hipError_t e = rp.fn(p, rp.grid, rp.lds, reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? MTA_OK : MTA_ERR_LAUNCH;
+    }
     LayerPlan pl;
     const int ps = make_layer_plan(c, w, pl);
     if (ps != MTA_OK) return ps;
@@ -465,6 +511,8 @@ const char *mta_layer_kernel_name(const mta_layer_config *c, const mta_layer_wei
     if (as_placement(c, w, sc, th_kq, th_head)) return mta_kernel_name(&sc);
     Plan p3;
     if (as_v4_3d(c, w, p3)) return p3.name;
+    RepPlan rp;
+    if (as_rep(c, w, rp)) return REP_NAME;
     LayerPlan pl;
     return make_layer_plan(c, w, pl) == MTA_OK ? "mta_fwd_layer (general layer, two passes)" : nullptr;
 }

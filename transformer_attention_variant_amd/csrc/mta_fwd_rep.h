@@ -72,7 +72,7 @@ struct RParams {
 };
 
 struct RLayout {
-    int x_off, k_off, v_off, qh_off, pt_off, st_off, hp_off, gn_off, th_off, total;
+    int x_off, k_off, v_off, qh_off, pt_off, st_off, hp_off, th_off, total;
 };
 
 template <int CQ1, int CK1, int CQ2, int CK2>
@@ -80,14 +80,13 @@ __host__ __device__ constexpr RLayout rlayout()
 {
     RLayout L{};
     int o = 0;
-    L.x_off = o;  o += CH * EXT_R * XP2 * 2;    // logit tiles (pass 1 uses pitch XP1); P.V operands of pass 2
+    L.x_off = o;  o += CH * EXT_R * XP2 * 2;    // logit tiles (pass 1 uses pitch XP1)
     L.k_off = o;  o += CH * KR2 * D * 2;        // K tiles (swizzled rows)
     L.v_off = o;  o += CH * BN * D * 2;         // V tiles (swizzled rows)
     L.qh_off = o; o += CH * HALO * D * 2;       // Q rows above the query tile
     L.pt_off = o; o += CH * EXT_R * PT * 2;     // probability tiles (fp16)
     L.st_off = o; o += 2 * CH * EXT_R * 4;      // [h][row] maximum (log2 domain), 1 / sum
     L.hp_off = o; o += CH * 4 * 16 * 2 * 4;     // pass 1, rows above the tile: [h][key block][row][max, sum]
-    L.gn_off = o; o += 2 * CH * BM * 4;         // GroupNorm partial sums [d half][a][row]
     L.th_off = o; o += (CH * CQ1 * ((CK1 + 3) & ~3) + CH * CH * CQ2 * ((CK2 + 3) & ~3)) * 4;
     L.total = o;
     return L;
@@ -178,7 +177,6 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     constexpr RLayout lay = rlayout<CQ1, CK1, CQ2, CK2>();
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     f16_t *xbuf = reinterpret_cast<f16_t *>(smem + lay.x_off);
-    bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + lay.x_off);  // pass 2: after the first convolution
     bf16_t *kbuf = reinterpret_cast<bf16_t *>(smem + lay.k_off);
     bf16_t *vbuf = reinterpret_cast<bf16_t *>(smem + lay.v_off);
     bf16_t *qhbuf = reinterpret_cast<bf16_t *>(smem + lay.qh_off);
@@ -186,7 +184,6 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     float *stm = reinterpret_cast<float *>(smem + lay.st_off);  // [h][row]
     float *stil = stm + CH * EXT_R;                             // [h][row]
     float *hpart = reinterpret_cast<float *>(smem + lay.hp_off);
-    float *gnx = reinterpret_cast<float *>(smem + lay.gn_off);
     float *th1 = reinterpret_cast<float *>(smem + lay.th_off);  // [h][row][col]
     float *th2 = th1 + CH * CQ1 * CK1P;                         // [c][b][row][col]
 
@@ -337,12 +334,14 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     const float sm_h = stm[hs * EXT_R + l16], sil_h = stil[hs * EXT_R + l16];
 
     // ---------------- pass 2: probabilities, second convolution, P.V ----------------
-    f32x4 U[CH][4];  // U[a][nb]: rows 16rw + 4g4 + r, d-columns 64hs + 16nb + l16 of output head a
+    // wave (rw, s) forms output head s's mixed map for its 16 rows and multiplies
+    // it by V^s over all 128 d-columns: the stencil's output layout is the P.V
+    // A operand, so the map never leaves the registers
+    f32x4 U[8];  // rows 16rw + 4g4 + r, d-columns 16nb + l16 of output head hs
 #pragma unroll
-    for (int a = 0; a < CH; ++a)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) U[a][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 8; ++nb) U[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     f16_t *po = ptile + hs * EXT_R * PT;
+    const bf16_t *vh = vbuf + hs * BN * D;
 
     // probabilities of one output block of the first convolution (tile row rr,
     // query qi, keys k0 + 4*(lane/16) + r): exp2(C - m) / l with Mask_-inf and
@@ -362,8 +361,11 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
 
     for (int t = 0; t <= qt; ++t) {
         const int j0 = t * BN;
-        barrier_lds();  // A: K(t) in LDS (each wave waited for its pieces); P.V of t - 1 is done
-        dma<true, BN>(vbuf, V, hstride, j0, T, wave, lane);  // V(t)
+        if (t > 0) {
+            wait_vm_all();  // K(t): this wave's pieces
+            barrier_lds();  // A: K(t) in LDS; P.V of t - 1 (its V reads) and the second convolution are done
+        }
+        dma<true, BN>(vbuf, V, hstride, j0, T, wave, lane);  // V(t): four pieces per wave
         {
             // logits: own row block (six column blocks) and the row block above
             // the tile (column blocks rw, rw + 4 of head hs); keys j0 - 16 ...
@@ -382,7 +384,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
             }
         }
         barrier_lds();  // B: logit tiles published; the K buffer is free
-        if (t < qt) dma<false, KR2>(kbuf, K, hstride, j0 + BN - 16, T, wave, lane);  // K(t+1)
+        if (t < qt) dma<false, KR2>(kbuf, K, hstride, j0 + BN - 16, T, wave, lane);  // K(t+1): six pieces per wave
         // first convolution over keys j0 - 8 ... j0 + 71 (five output blocks)
         // -> probabilities: own rows, and output blocks rw, rw + 4 of the rows above
 #pragma unroll
@@ -394,115 +396,81 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
             const f32x4 a = sten<CQ1, XP2>(xo, l16, tf1, 16 * u, g4, f32x4{0.f, 0.f, 0.f, 0.f});
             to_prob(a, l16, qh, j0 - 8 + 16 * u, 16 * u, sm_h, sil_h);
         }
-        barrier_lds();  // C: probability tiles published; the logit tiles are free
-        {
-            // second convolution (3D: both source heads into output head hs),
-            // own rows, the tile's 64 keys; Mask_0 on the diagonal tile
-            f32x4 acc[4];
+        // V(t) has landed (issued before K(t+1), whose six pieces may stay in flight)
+        if (t < qt)
+            __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6)
+        else
+            wait_vm_all();
+        barrier_lds();  // C: probability tiles and V(t) published; the logit tiles are free
+        // second convolution (3D: both source heads into output head hs), own
+        // rows, the tile's 64 keys; Mask_0 on the diagonal tile; then P.V
+        f32x4 acc[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 4; ++u) {
+            acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < CH; ++s)
-                    acc[u] = sten<CQ2, PT>(ptile + s * EXT_R * PT, rho, tf2[s], 16 * u, g4, acc[u]);
-            }
-            float c[16];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c[4 * u + r] = (j0 + 16 * u + 4 * g4 + r <= qown_row) ? acc[u][r] : 0.f;
-            bf16x8 v8[2];
-#pragma unroll
-            for (int o = 0; o < 16; ++o) v8[o >> 3][o & 7] = (bf16_t)c[o];
-            pbuf[((hs * 4 + rw) * 2 + 0) * 64 + lane] = v8[0];
-            pbuf[((hs * 4 + rw) * 2 + 1) * 64 + lane] = v8[1];
+            for (int s = 0; s < CH; ++s)
+                acc[u] = sten<CQ2, PT>(ptile + s * EXT_R * PT, rho, tf2[s], 16 * u, g4, acc[u]);
         }
-        wait_vm_all();  // V(t) and K(t+1): this wave's pieces have landed
-        barrier_lds();  // D: P.V operands and V(t) published
-        const int dbase = 64 * hs;
+        bf16x8 av[2];  // keys 4g4 + r and 16 + 4g4 + r (slots 0-3, 4-7) of key halves 0 and 1
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                av[u >> 1][4 * (u & 1) + r] = (bf16_t)((j0 + 16 * u + 4 * g4 + r <= qown_row) ? acc[u][r] : 0.f);
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
-            bf16x8 av[CH];
-#pragma unroll
-            for (int a = 0; a < CH; ++a) av[a] = pbuf[((a * 4 + rw) * 2 + cs) * 64 + lane];
             const int kb0 = 32 * cs + 4 * g4;  // keys of slots 0-3 and 4-7, in the producing lanes' order
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int a = 0; a < CH; ++a) {
-                    const bf16_t *va = vbuf + a * BN * D;
-                    const tile::s16x4 u0 = vread_tr4(va, kb0, dbase + 16 * nb, l16);
-                    const tile::s16x4 u1 = vread_tr4(va, kb0 + 16, dbase + 16 * nb, l16);
-                    typedef short s16x8 __attribute__((ext_vector_type(8)));
-                    const s16x8 uu = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-                    U[a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, uu), U[a][nb],
-                                                                       0, 0, 0);
-                }
+            for (int nb = 0; nb < 8; ++nb) {
+                const tile::s16x4 u0 = vread_tr4(vh, kb0, 16 * nb, l16);
+                const tile::s16x4 u1 = vread_tr4(vh, kb0 + 16, 16 * nb, l16);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 uu = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                U[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cs], __builtin_bit_cast(bf16x8, uu), U[nb], 0, 0,
+                                                                0);
+            }
         }
     }
 
-    // ---------------- epilogue: GroupNorm over d, head factor, store -------
-    const int dbase = 64 * hs;
-    float mu[CH][4];
+    // ---------------- epilogue: GroupNorm over d (inside the wave), head factor, store -------
+    float mu[4], rstd[4];
 #pragma unroll
-    for (int a = 0; a < CH; ++a)
+    for (int r = 0; r < 4; ++r) {
+        float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float sum = 0.f;
+        for (int nb = 0; nb < 8; ++nb) sum += U[nb][r];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        mu[r] = sum * (1.0f / D);
+        float v2s = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) sum += U[a][nb][r];
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            sum += __shfl_xor(sum, 4);
-            sum += __shfl_xor(sum, 8);
-            if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = sum;
+        for (int nb = 0; nb < 8; ++nb) {
+            const float dl = U[nb][r] - mu[r];
+            v2s = __builtin_fmaf(dl, dl, v2s);
         }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < CH; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rw + 4 * g4 + r;
-            mu[a][r] = (gnx[(0 * CH + a) * BM + row] + gnx[(1 * CH + a) * BM + row]) * (1.0f / D);
-        }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < CH; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v2s = 0.f;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const float dl = U[a][nb][r] - mu[a][r];
-                v2s = __builtin_fmaf(dl, dl, v2s);
-            }
-            v2s += __shfl_xor(v2s, 1);
-            v2s += __shfl_xor(v2s, 2);
-            v2s += __shfl_xor(v2s, 4);
-            v2s += __shfl_xor(v2s, 8);
-            if (l16 == 0) gnx[(hs * CH + a) * BM + 16 * rw + 4 * g4 + r] = v2s;
-        }
-    __syncthreads();
+        v2s += __shfl_xor(v2s, 1);
+        v2s += __shfl_xor(v2s, 2);
+        v2s += __shfl_xor(v2s, 4);
+        v2s += __shfl_xor(v2s, 8);
+        rstd[r] = 1.0f / __builtin_sqrtf(v2s * (1.0f / D) + p.eps);
+    }
     bf16_t *O = reinterpret_cast<bf16_t *>(p.out);
+    const int h = h0 + hs;
+    const float *gw = p.gn_w + (size_t)h * D;
+    const float *gb = p.gn_b + (size_t)h * D;
+    const float hf = rhead_factor(p, h);
 #pragma unroll
-    for (int a = 0; a < CH; ++a) {
-        const int h = h0 + a;
-        const float *gw = p.gn_w + (size_t)h * D;
-        const float *gb = p.gn_b + (size_t)h * D;
-        const float hf = rhead_factor(p, h);
+    for (int r = 0; r < 4; ++r) {
+        const int row = i0 + 16 * rw + 4 * g4 + r;
+        if (row < T) {
+            bf16_t *dst = O + ((size_t)b * p.H + h) * hstride + (size_t)row * D;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rowt = 16 * rw + 4 * g4 + r;
-            const float var = (gnx[(0 * CH + a) * BM + rowt] + gnx[(1 * CH + a) * BM + rowt]) * (1.0f / D);
-            const float rstd = 1.0f / __builtin_sqrtf(var + p.eps);
-            const int row = i0 + rowt;
-            if (row < T) {
-                bf16_t *dst = O + ((size_t)b * p.H + h) * hstride + (size_t)row * D;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const int col = dbase + 16 * nb + l16;
-                    dst[col] = (bf16_t)(((U[a][nb][r] - mu[a][r]) * rstd * gw[col] + gb[col]) * hf);
-                }
+            for (int nb = 0; nb < 8; ++nb) {
+                const int col = 16 * nb + l16;
+                dst[col] = (bf16_t)(((U[nb][r] - mu[r]) * rstd[r] * gw[col] + gb[col]) * hf);
             }
         }
     }

@@ -204,9 +204,9 @@ typedef struct {
  * head_dim 128, c_h 2, 6x11 or 1x1); the repeated form (kq_pre with the
  * two-pass masks and kq_post, head_post and head_post2 each optional, no
  * head_pre) runs a head-split two-pass kernel where it is built (bf16,
- * head_dim 128, c_h 2, c_q x c_k and c_q2 x c_k2 both 6x11 or both 4x9; its
- * first convolution multiplies fp16-rounded logits by every tap, the centre
- * one included); any other layer runs the general layer
+ * head_dim 128, c_h 2, c_q x c_k and c_q2 x c_k2 both 6x11 or both 4x9;
+ * fp16 operands in both convolutions as in mta_forward, the first one's
+ * centre tap applied to the float32 logits); any other layer runs the general layer
  * kernel, limited to c_q, c_q2 <= 16, c_k, c_k2 <= 31 and 160 KB of LDS per
  * workgroup (MTA_ERR_UNSUPPORTED beyond).
  */

@@ -25,9 +25,12 @@
 // Both convolutions run on the matrix cores with fp16 operands (the logits or
 // probabilities and the taps rounded to nearest, 11 significant bits) and fp32
 // accumulation, one product per kernel row and 16-key output block, as in the
-// head-split kernel; here the centre tap of the first convolution stays in the
-// fp16 band (the float32 centre-tap planes of an 80-row tile do not fit in LDS
-// next to everything else).
+// head-split kernel.  The centre tap of the first convolution (the largest tap
+// of a kernel near the identity) stays out of the fp16 band and is applied to
+// the float32 logit, which the lane gets from its partner lane 32 away (same
+// row, eight keys over) for its own rows and from a small float32 plane in LDS
+// for the rows above the tile, so that its term keeps float32 accuracy at any
+// logit size.
 #pragma once
 
 #include "mta_fwd_v4.h"
@@ -56,6 +59,8 @@ constexpr int KR2 = 96;   // pass 2: K rows per head (keys j0 - 16 .. j0 + 79)
 constexpr int XP1 = 80;   // pass 1 logit tile pitch (fp16; 16-byte chunks per row = 2 mod 4)
 constexpr int XP2 = 112;  // pass 2 logit tile pitch (96 columns used)
 constexpr int PT = 80;    // probability tile pitch (80 columns: keys j0 - 8 .. j0 + 71)
+constexpr int HCR = 8;    // rows above the tile whose first-convolution output is used (c_q2 - 1 <= 8)
+constexpr int HCP = 96;   // float32 pitch of their centre-tap plane
 
 struct RParams {
     const void *q, *k, *v;
@@ -72,7 +77,7 @@ struct RParams {
 };
 
 struct RLayout {
-    int x_off, k_off, v_off, qh_off, pt_off, st_off, hp_off, th_off, total;
+    int x_off, k_off, v_off, qh_off, pt_off, st_off, hp_off, th_off, hc_off, total;
 };
 
 template <int CQ1, int CK1, int CQ2, int CK2>
@@ -88,6 +93,7 @@ __host__ __device__ constexpr RLayout rlayout()
     L.st_off = o; o += 2 * CH * EXT_R * 4;      // [h][row] maximum (log2 domain), 1 / sum
     L.hp_off = o; o += CH * 4 * 16 * 2 * 4;     // pass 1, rows above the tile: [h][key block][row][max, sum]
     L.th_off = o; o += (CH * CQ1 * ((CK1 + 3) & ~3) + CH * CH * CQ2 * ((CK2 + 3) & ~3)) * 4;
+    L.hc_off = o; o += CH * HCR * HCP * 4;     // float32 logits of the lowest HCR rows above the tile
     L.total = o;
     return L;
 }
@@ -102,15 +108,16 @@ __device__ inline float rhead_factor(const RParams &p, int h)
 // Banded kernel matrix rows of one kernel row (MFMA A operand, fp16): row m =
 // lane%16 is output key 16t + m of a block, column k = 8*(lane/16) + s of the
 // 32-column window starting 8 keys left of the block, so j' = m + 8 - k.
+// nocentre: the centre tap (j' = 0) left out (applied in float32 by the caller).
 template <int CK>
-__device__ inline f16x8 band(const float *th_row, float kap, int lane)
+__device__ inline f16x8 band(const float *th_row, float kap, int lane, bool nocentre = false)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
     f16x8 r;
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
         const int jj = l16 + 8 - (8 * g4 + s8) + CK / 2;
-        const float t = (jj >= 0 && jj < CK) ? th_row[jj] : 0.f;
+        const float t = (jj >= 0 && jj < CK && !(nocentre && jj == CK / 2)) ? th_row[jj] : 0.f;
         r[s8] = (f16_t)f16_range(t * kap);
     }
     return r;
@@ -133,26 +140,49 @@ __device__ inline f32x4 sten(const f16_t *x, int rho, const f16x8 (&tf)[CQ], int
 }
 
 // A 16x16 logit block (lane: tile row 16rb + lane%16, keys k0 + 4*(lane/16) + r)
-// with Mask_0 and the zero padding outside [0, T), as fp16, stored 8 bytes per lane.
+// with Mask_0 and the zero padding outside [0, T), as fp16, stored 8 bytes per
+// lane; returns the masked logits in float32.
 template <int P>
-__device__ inline void store_logits(f16_t *x, int rb, int cb, f32x4 acc, int qi, int k0, int T, int lane)
+__device__ inline f32x4 store_logits(f16_t *x, int rb, int cb, f32x4 acc, int qi, int k0, int T, int lane)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
     f16x4 h;
+    f32x4 xs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int kj = k0 + 4 * g4 + r;
         const bool ok = kj >= 0 && kj <= qi && qi >= 0 && qi < T;
-        h[r] = (f16_t)f16_range(ok ? acc[r] : 0.f);
+        xs[r] = ok ? acc[r] : 0.f;
+        h[r] = (f16_t)f16_range(xs[r]);
     }
     *reinterpret_cast<u32x2 *>(x + (16 * rb + l16) * P + 16 * cb + 4 * g4) = __builtin_bit_cast(u32x2, h);
+    return xs;
 }
 
-// DMA of NROWS consecutive rows of a K or V tile for both heads (as v4::dma_pair).
+// The centre logits of a 16-key stencil output block whose window starts at
+// logit column block u (output keys 8 + 16u + 4*(lane/16) + r of the row): for
+// lanes 0..31 they sit in block u of the partner lane 32 above, for lanes
+// 32..63 in block u + 1 of the partner lane 32 below (one permlane32 swap).
+__device__ inline f32x4 centre_pair(f32x4 xu, f32x4 xu1, int lane)
+{
+    f32x4 c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(xu[r]), __float_as_uint(xu1[r]), false, false);
+        c[r] = __uint_as_float(lane < 32 ? w[1] : w[0]);
+    }
+    return c;
+}
+
+
+// DMA of NROWS consecutive rows of a K or V tile for both heads (as
+// v4::dma_pair).  The lane index passes through an empty asm, so that the
+// per-piece lane offsets are computed where they are used: held across the
+// loop they were spilled, and each reload waited for every DMA in flight.
 template <bool VTILE, int NROWS>
 __device__ inline void dma(bf16_t *lds, const bf16_t *g, size_t hstride, int key0, int T, int wave, int lane)
 {
-    v4::dma_pair<VTILE, NROWS>(lds, g, hstride, key0, T, wave, lane);
+    v4::dma_pair<VTILE, NROWS>(lds, g, hstride, key0, T, wave, v4::fresh(lane));
 }
 
 // Running maximum and sum (log2 domain) over n values; a finite floor instead
@@ -172,6 +202,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
 {
     static_assert(CK1 <= 17 && CK2 <= 17, "32-column stencil windows");
     static_assert(CQ1 + CQ2 - 2 <= HALO, "the rows above the tile that both convolutions reach");
+    static_assert(CQ2 - 1 <= HCR, "the centre-tap plane covers the rows above the tile that are used");
     constexpr int CK1P = (CK1 + 3) & ~3, CK2P = (CK2 + 3) & ~3;
     constexpr float FLOOR = -1e30f;
     constexpr RLayout lay = rlayout<CQ1, CK1, CQ2, CK2>();
@@ -186,8 +217,9 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     float *hpart = reinterpret_cast<float *>(smem + lay.hp_off);
     float *th1 = reinterpret_cast<float *>(smem + lay.th_off);  // [h][row][col]
     float *th2 = th1 + CH * CQ1 * CK1P;                         // [c][b][row][col]
+    float *hcen = reinterpret_cast<float *>(smem + lay.hc_off); // [h][row - (HALO - HCR)][col]
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane_id = tid & 63, lane = lane_id;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rw = wave & 3, hs = wave >> 2;  // row block; head (logits, stencils) = d half (P.V)
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -234,15 +266,14 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     wait_vm_all();
     __syncthreads();
 
-    // banded matrices: the first kernel of head hs (log2(e)/sqrt(d) folded in:
-    // the logit tiles hold raw Q K^T), and the 3D kernel into output head hs
-    f16x8 tf1[CQ1], tf2[CH][CQ2];
+    // banded matrices of the first kernel of head hs (log2(e)/sqrt(d) folded
+    // in: the logit tiles hold raw Q K^T; the centre tap left out)
+    f16x8 tf1[CQ1];
 #pragma unroll
-    for (int ip = 0; ip < CQ1; ++ip) tf1[ip] = band<CK1>(th1 + (hs * CQ1 + ip) * CK1P, p.sc, lane);
-#pragma unroll
-    for (int s = 0; s < CH; ++s)
-#pragma unroll
-        for (int ip = 0; ip < CQ2; ++ip) tf2[s][ip] = band<CK2>(th2 + ((hs * CH + s) * CQ2 + ip) * CK2P, 1.f, lane);
+    for (int ip = 0; ip < CQ1; ++ip) tf1[ip] = band<CK1>(th1 + (hs * CQ1 + ip) * CK1P, p.sc, lane, ip == 0);
+    // the first kernel's centre tap (left out of its banded matrices), applied
+    // to the float32 logits
+    const float c00 = th1[hs * CQ1 * CK1P + CK1 / 2] * p.sc;
 
     int koff[4];  // swizzled chunk offsets of the K / Q-halo fragment reads
 #pragma unroll
@@ -257,6 +288,10 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     const int qh = i0 - HALO + l16;  // the lane's row above the tile
     const int rho = HALO + 16 * rw + l16;  // the lane's own tile row
     f16_t *xo = xbuf + hs * EXT_R * XP2;  // head hs's logit tile (pass 1: pitch XP1)
+    // the lane's row of the centre-tap plane (rows above the tile; the lanes of
+    // the rows that are not used read row 0 and write nothing)
+    float *hcrow = hcen + (hs * HCR + (l16 >= HALO - HCR ? l16 - (HALO - HCR) : 0)) * HCP;
+    const bool hcw = l16 >= HALO - HCR;
 
     // ---------------- pass 1: softmax statistics of every tile row ----------------
     float m1 = FLOOR, l1 = 0.f, m2 = FLOOR, l2 = 0.f;  // own row; row above the tile (key block rw)
@@ -266,35 +301,44 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
             wait_vm_all();
             __syncthreads();  // K(t) in LDS; the stencil reads of t - 1 are done
         }
+        f32x4 cen[4];  // centre-tap terms of the own rows' four output blocks (float32)
         {
             const bf16_t *kh = kbuf + hs * KR1 * D + l16 * D;
             QFrag<D> kf;
+            f32x4 xp;
 #pragma unroll
             for (int cb = 0; cb < 5; ++cb) {
                 kload(kf, kh, cb);
-                store_logits<XP1>(xo, 1 + rw, cb, qk(kf, qown), qown_row, j0 - 8 + 16 * cb, T, lane);
+                const f32x4 x = store_logits<XP1>(xo, 1 + rw, cb, qk(kf, qown), qown_row, j0 - 8 + 16 * cb, T, lane);
+                if (cb > 0) cen[cb - 1] = c00 * centre_pair(xp, x, lane);
+                xp = x;
             }
             for (int cb = rw; cb < 5; cb += 4) {
                 QFrag<D> hq;
                 kload(hq, qhrows, 0);
                 kload(kf, kh, cb);
-                store_logits<XP1>(xo, 0, cb, qk(kf, hq), qh, j0 - 8 + 16 * cb, T, lane);
+                const f32x4 x = store_logits<XP1>(xo, 0, cb, qk(kf, hq), qh, j0 - 8 + 16 * cb, T, lane);
+                if (hcw) *reinterpret_cast<f32x4 *>(hcrow + 16 * cb + 4 * g4) = x;
             }
         }
-        barrier_lds();  // logit tiles published; the K buffer is free
+        barrier_lds();  // logit tiles and the centre-tap plane published; the K buffer is free
         if (t < qt) dma<false, KR1>(kbuf, K, hstride, j0 + BN - 8, T, wave, lane);
         // own rows: the 64 keys of the tile
         float c[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 a = sten<CQ1, XP1>(xo, rho, tf1, 16 * u, g4, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 a = sten<CQ1, XP1>(xo, rho, tf1, 16 * u, g4, cen[u]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) c[4 * u + r] = (j0 + 16 * u + 4 * g4 + r <= qown_row) ? a[r] : NEG_INF;
         }
         online(m1, l1, c, 16);
         // the row above the tile: key block rw
         {
-            const f32x4 a = sten<CQ1, XP1>(xo, l16, tf1, 16 * rw, g4, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 hc = *reinterpret_cast<const f32x4 *>(hcrow + 16 * rw + 8 + 4 * g4);
+            f32x4 h0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h0[r] = c00 * hc[r];
+            const f32x4 a = sten<CQ1, XP1>(xo, l16, tf1, 16 * rw, g4, h0);
             float w[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) w[r] = (j0 + 16 * rw + 4 * g4 + r <= qh) ? a[r] : NEG_INF;
@@ -340,60 +384,94 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     f32x4 U[8];  // rows 16rw + 4g4 + r, d-columns 16nb + l16 of output head hs
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) U[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f16_t *po = ptile + hs * EXT_R * PT;
-    const bf16_t *vh = vbuf + hs * BN * D;
-
-    // probabilities of one output block of the first convolution (tile row rr,
-    // query qi, keys k0 + 4*(lane/16) + r): exp2(C - m) / l with Mask_-inf and
-    // the zero padding of the second convolution; entries whose exp2 may be out
-    // of range are selected away, never multiplied
-    auto to_prob = [&](f32x4 a, int rr, int qi, int k0, int col0, float m, float il) {
-        f16x4 h;
+    // banded matrices of the 3D kernel into output head hs
+    f16x8 tf2[CH][CQ2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int kj = k0 + 4 * g4 + r;
-            const bool ok = kj >= 0 && kj <= qi && qi >= 0 && qi < T;
-            const float e = __builtin_amdgcn_exp2f(a[r] - m) * il;
-            h[r] = (f16_t)(ok ? e : 0.f);
-        }
-        *reinterpret_cast<u32x2 *>(po + rr * PT + col0 + 4 * g4) = __builtin_bit_cast(u32x2, h);
-    };
+    for (int s = 0; s < CH; ++s)
+#pragma unroll
+        for (int ip = 0; ip < CQ2; ++ip) tf2[s][ip] = band<CK2>(th2 + ((hs * CH + s) * CQ2 + ip) * CK2P, 1.f, lane);
 
     for (int t = 0; t <= qt; ++t) {
         const int j0 = t * BN;
+        f32x4 cen[5];  // centre-tap terms of the own rows' five output blocks (float32)
         if (t > 0) {
             wait_vm_all();  // K(t): this wave's pieces
             barrier_lds();  // A: K(t) in LDS; P.V of t - 1 (its V reads) and the second convolution are done
         }
         dma<true, BN>(vbuf, V, hstride, j0, T, wave, lane);  // V(t): four pieces per wave
+        // The lane's row, key group and addresses, derived in each key tile from
+        // a copy of the lane index that passes through an empty asm: held across
+        // the key loop they were spilled, and each reload waited for the DMA in
+        // flight.
+        const int lane = v4::fresh(lane_id);
+        const int l16 = lane & 15, g4 = lane >> 4;
+        const int rho = HALO + 16 * rw + l16, qown_row = i0 + 16 * rw + l16, qh = i0 - HALO + l16;
+        const bf16_t *qhrows = qhbuf + (hs * HALO + l16) * D;
+        float *hcrow = hcen + (hs * HCR + (l16 >= HALO - HCR ? l16 - (HALO - HCR) : 0)) * HCP;
+        const bool hcw = l16 >= HALO - HCR;
+        f16_t *po = ptile + hs * EXT_R * PT;
+        const bf16_t *vh = vbuf + hs * BN * D;
+        int koff[4];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) koff[t4] = 8 * ((4 * g4 + t4) ^ swz_k(l16));
+        auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+                f.x[t4] = *reinterpret_cast<const bf16x8 *>(rows + 16 * cb * D + koff[t4]);
+        };
+        // probabilities of one output block of the first convolution (tile row
+        // rr, query qi, keys k0 + 4*(lane/16) + r): exp2(C - m) / l with Mask_-inf
+        // and the zero padding of the second convolution; entries whose exp2 may
+        // be out of range are selected away, never multiplied
+        auto to_prob = [&](f32x4 a, int rr, int qi, int k0, int col0, float m, float il) {
+            f16x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kj = k0 + 4 * g4 + r;
+                const bool ok = kj >= 0 && kj <= qi && qi >= 0 && qi < T;
+                const float e = __builtin_amdgcn_exp2f(a[r] - m) * il;
+                h[r] = (f16_t)(ok ? e : 0.f);
+            }
+            *reinterpret_cast<u32x2 *>(po + rr * PT + col0 + 4 * g4) = __builtin_bit_cast(u32x2, h);
+        };
         {
             // logits: own row block (six column blocks) and the row block above
-            // the tile (column blocks rw, rw + 4 of head hs); keys j0 - 16 ...
+            // the tile (column blocks rw, rw + 4 of head hs); keys j0 - 16 ...;
+            // the float32 centre logits of the own rows' five output blocks kept
+            // in registers, those of the rows above in the centre-tap plane
             const bf16_t *kh = kbuf + hs * KR2 * D + l16 * D;
             QFrag<D> kf;
+            f32x4 xp;
 #pragma unroll
             for (int cb = 0; cb < 6; ++cb) {
                 kload(kf, kh, cb);
-                store_logits<XP2>(xo, 1 + rw, cb, qk(kf, qown), qown_row, j0 - 16 + 16 * cb, T, lane);
+                const f32x4 x = store_logits<XP2>(xo, 1 + rw, cb, qk(kf, qown), qown_row, j0 - 16 + 16 * cb, T, lane);
+                if (cb > 0) cen[cb - 1] = c00 * centre_pair(xp, x, lane);
+                xp = x;
             }
             for (int cb = rw; cb < 6; cb += 4) {
                 QFrag<D> hq;
                 kload(hq, qhrows, 0);
                 kload(kf, kh, cb);
-                store_logits<XP2>(xo, 0, cb, qk(kf, hq), qh, j0 - 16 + 16 * cb, T, lane);
+                const f32x4 x = store_logits<XP2>(xo, 0, cb, qk(kf, hq), qh, j0 - 16 + 16 * cb, T, lane);
+                if (hcw) *reinterpret_cast<f32x4 *>(hcrow + 16 * cb + 4 * g4) = x;
             }
         }
-        barrier_lds();  // B: logit tiles published; the K buffer is free
+        barrier_lds();  // B: logit tiles and the centre-tap plane published; the K buffer is free
         if (t < qt) dma<false, KR2>(kbuf, K, hstride, j0 + BN - 16, T, wave, lane);  // K(t+1): six pieces per wave
         // first convolution over keys j0 - 8 ... j0 + 71 (five output blocks)
         // -> probabilities: own rows, and output blocks rw, rw + 4 of the rows above
 #pragma unroll
         for (int u = 0; u < 5; ++u) {
-            const f32x4 a = sten<CQ1, XP2>(xo, rho, tf1, 16 * u, g4, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 a = sten<CQ1, XP2>(xo, rho, tf1, 16 * u, g4, cen[u]);
             to_prob(a, rho, qown_row, j0 - 8 + 16 * u, 16 * u, sm_o, sil_o);
         }
         for (int u = rw; u < 5; u += 4) {
-            const f32x4 a = sten<CQ1, XP2>(xo, l16, tf1, 16 * u, g4, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 hc = *reinterpret_cast<const f32x4 *>(hcrow + 16 * u + 8 + 4 * g4);
+            f32x4 h0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h0[r] = c00 * hc[r];
+            const f32x4 a = sten<CQ1, XP2>(xo, l16, tf1, 16 * u, g4, h0);
             to_prob(a, l16, qh, j0 - 8 + 16 * u, 16 * u, sm_h, sil_h);
         }
         // V(t) has landed (issued before K(t+1), whose six pieces may stay in flight)

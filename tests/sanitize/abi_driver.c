@@ -163,14 +163,17 @@ static void scalar_checks(void)
 
 static void layer_sweep(void)
 {
-    long n_ok = 0;
+    long n_ok = 0, n_rep = 0;
     for (int dt = 0; dt < 2; ++dt)
         for (int ch = 1; ch <= 4; ch *= 2)
             for (int exact = 0; exact <= 1; ++exact)
                 for (int mask = 0; mask < 64; ++mask)
-                    for (int ks = 0; ks < 3; ++ks) {
-                        const int cq[] = {6, 16, 1}, ck[] = {11, 31, 1};
-                        mta_layer_config c = {2, 4, 77, 64, cq[ks], ck[ks], 2, 3, ch, exact, dt, 1e-5f, 1.0f};
+                    for (int ks = 0; ks < 6; ++ks) {
+                        /* ks >= 3: head_dim 128 with the same kernel size after the
+                           softmax (the repeated form's head-split kernel at 6x11, 4x9) */
+                        const int cq[] = {6, 16, 1, 6, 4, 1}, ck[] = {11, 31, 1, 11, 9, 1};
+                        const int d = ks < 3 ? 64 : 128, cq2 = ks < 3 ? 2 : cq[ks], ck2 = ks < 3 ? 3 : ck[ks];
+                        mta_layer_config c = {2, 4, 77, d, cq[ks], ck[ks], cq2, ck2, ch, exact, dt, 1e-5f, 1.0f};
                         mta_layer_weights w;
                         memset(&w, 0, sizeof w);
                         w.kq_pre = (mask & 1) ? fbuf : NULL;
@@ -185,6 +188,12 @@ static void layer_sweep(void)
                         if (name) {
                             EXPECT(strlen(name) > 8, "short layer kernel name");
                             ++n_ok;
+                            if (strncmp(name, "mta_fwd_rep", 11) == 0) {
+                                ++n_rep;
+                                EXPECT(dt == MTA_BF16 && d == 128 && ch == 2 && !exact && w.kq_pre && w.kq_post &&
+                                           !w.head_pre && !w.conv3d,
+                                       "repeated-form kernel chosen outside its scope");
+                            }
                         }
                         const int rc = mta_forward_layer((const char *)fbuf + 4, fbuf, fbuf, &w, &c, fbuf, NULL);
                         EXPECT(rc < 0, "layer forward with a misaligned q returned %d", rc);
@@ -194,7 +203,8 @@ static void layer_sweep(void)
                     }
     EXPECT(mta_layer_kernel_name(NULL, NULL) == NULL, "layer NULL");
     EXPECT(n_ok > 50, "only %ld layer forms accepted", n_ok);
-    printf("layer sweep: %ld accepted\n", n_ok);
+    EXPECT(n_rep == 8, "the repeated-form kernel chosen %ld times (expected 8)", n_rep);
+    printf("layer sweep: %ld accepted, %ld on the repeated form's kernel\n", n_ok, n_rep);
 }
 
 int main(void)

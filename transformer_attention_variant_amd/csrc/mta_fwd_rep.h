@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
     float *th2 = th1 + CH * CQ1 * CK1P;                         // [c][b][row][col]
     float *hcen = reinterpret_cast<float *>(smem + lay.hc_off); // [h][row - (HALO - HCR)][col]
 
-    const int tid = threadIdx.x, lane_id = tid & 63, lane = lane_id;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rw = wave & 3, hs = wave >> 2;  // row block; head (logits, stencils) = d half (P.V)
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -399,26 +399,8 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
             barrier_lds();  // A: K(t) in LDS; P.V of t - 1 (its V reads) and the second convolution are done
         }
         dma<true, BN>(vbuf, V, hstride, j0, T, wave, lane);  // V(t): four pieces per wave
-        // The lane's row, key group and addresses, derived in each key tile from
-        // a copy of the lane index that passes through an empty asm: held across
-        // the key loop they were spilled, and each reload waited for the DMA in
-        // flight.
-        const int lane = v4::fresh(lane_id);
-        const int l16 = lane & 15, g4 = lane >> 4;
-        const int rho = HALO + 16 * rw + l16, qown_row = i0 + 16 * rw + l16, qh = i0 - HALO + l16;
-        const bf16_t *qhrows = qhbuf + (hs * HALO + l16) * D;
-        float *hcrow = hcen + (hs * HCR + (l16 >= HALO - HCR ? l16 - (HALO - HCR) : 0)) * HCP;
-        const bool hcw = l16 >= HALO - HCR;
         f16_t *po = ptile + hs * EXT_R * PT;
         const bf16_t *vh = vbuf + hs * BN * D;
-        int koff[4];
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) koff[t4] = 8 * ((4 * g4 + t4) ^ swz_k(l16));
-        auto kload = [&](QFrag<D> &f, const bf16_t *rows, int cb) {
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4)
-                f.x[t4] = *reinterpret_cast<const bf16x8 *>(rows + 16 * cb * D + koff[t4]);
-        };
         // probabilities of one output block of the first convolution (tile row
         // rr, query qi, keys k0 + 4*(lane/16) + r): exp2(C - m) / l with Mask_-inf
         // and the zero padding of the second convolution; entries whose exp2 may

@@ -585,6 +585,34 @@ __device__ inline void dtheta_mfma(float *dth, int ckp, const float *xbuf, int x
 // where its row block changes and requests the next column fragments before
 // each product.  f(rb, cb, acc) stores one block (lane: row lane%16, columns
 // 4*(lane/16) .. +3).
+// A row fragment as load_frag, addressed as the wave-uniform head base plus a
+// 32-bit lane offset (row < T <= 2^24, so row * D * sizeof(DT) < 2^32 at d =
+// 128 in bf16 and at d <= 64 in float32): the compiler can keep the base in
+// scalar registers and use the scalar-base form of the load, one VGPR per
+// fragment stream instead of a 64-bit address.  Held as 64-bit addresses
+// across the query-tile loop they were spilled, and each reload waited for
+// every global load in flight.
+template <int D>
+__device__ inline void load_frag_s(QFrag<D> &f, const bf16_t *base, int row, int T, int lane)
+{
+    const unsigned off = (unsigned)row * (unsigned)(D * 2) + (unsigned)((lane >> 4) * (D / 4) * 2);
+    if ((unsigned)row < (unsigned)T) {
+        const bf16x8 *p = reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + off);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) f.x[t] = p[t];
+    } else {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f.x[t][e] = (bf16_t)0.0f;
+    }
+}
+template <int D>
+__device__ inline void load_frag_s(QFrag32<D> &f, const float *base, int row, int T, int lane)
+{
+    load_frag<D>(f, base, row, T, lane);
+}
+
 template <typename DT, int D, bool SPLIT, typename F>
 __device__ inline void region_product(int nrb, int ncb, const DT *rh, const DT *rl, int r0, const DT *ch, int c0,
                                       int T, int wave, int lane, F &&f)
@@ -594,16 +622,16 @@ __device__ inline void region_product(int nrb, int ncb, const DT *rh, const DT *
     if (t0 >= t1) return;
     Frag hf, lf, cf, cn;
     int rcur = -1;
-    load_frag<D>(cf, ch, c0 + 16 * (t0 % ncb) + (lane & 15), T, lane);
+    load_frag_s<D>(cf, ch, c0 + 16 * (t0 % ncb) + (lane & 15), T, lane);
     for (int t = t0; t < t1; ++t) {
         const int rb = t / ncb, cb = t % ncb;
         if (rb != rcur) {
             const int qi = r0 + 16 * rb + (lane & 15);
-            load_frag<D>(hf, rh, qi, T, lane);
-            if (SPLIT) load_frag<D>(lf, rl, qi, T, lane);
+            load_frag_s<D>(hf, rh, qi, T, lane);
+            if (SPLIT) load_frag_s<D>(lf, rl, qi, T, lane);
             rcur = rb;
         }
-        if (t + 1 < t1) load_frag<D>(cn, ch, c0 + 16 * ((t + 1) % ncb) + (lane & 15), T, lane);
+        if (t + 1 < t1) load_frag_s<D>(cn, ch, c0 + 16 * ((t + 1) % ncb) + (lane & 15), T, lane);
         f32x4 acc = qk_mfma<D>(cf, hf);
         if (SPLIT) {
             const f32x4 a2 = qk_mfma<D>(cf, lf);
@@ -670,7 +698,9 @@ struct TileStage<bf16_t, D> {
         for (int it = 0; it < IT; ++it) {
             const int ch = (tid >> 6) + NWB * it;
             if (ch < NC && kj < T) {
-                x[it] = *reinterpret_cast<const bf16x8 *>(g + (size_t)kj * D + 8 * ch);
+                // wave-uniform head base + 32-bit lane offset (as load_frag_s)
+                const unsigned off = (unsigned)kj * (unsigned)(D * 2) + 16u * (unsigned)ch;
+                x[it] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(g) + off);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[it][e] = (bf16_t)0.0f;

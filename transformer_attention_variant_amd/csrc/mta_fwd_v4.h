@@ -25,9 +25,9 @@
 //   the d-columns [64s, 64s + 64) of every (source b, output a) pair.
 // Per key tile t there are two barriers, each publishing LDS writes only, and
 // the P.V of a tile runs one phase late, beside the next tile's logit products:
-//   A | K tiles of t, V tiles and probabilities of t - 1 are in LDS: logit
-//     | tiles of both heads -> LDS (fp16); rescale of the accumulators, P.V
-//     | of t - 1
+//   A | K tiles of t, V tiles and probabilities of t - 1 are in LDS: rescale
+//     | of the accumulators, P.V of t - 1; logit tiles of both heads -> LDS
+//     | (fp16)
 //   B | the K tiles of t + 1 and the V tiles of t start loading (DMA);
 //     | stencil, Mask_-inf, row maximum, rescale factor, probabilities -> LDS
 // The key-query convolution runs on the matrix cores with fp16 operands (the
@@ -824,40 +824,10 @@ sweep:
                 store_pair<CQ>(xo, 1 + rw, NCB - 1, prev, xo, 1 + rw, NCB - 1, prev, lane, true);
             }
         };
-        // key tiles whose logit blocks (halo rows included) are all inside
-        // [0, T) and, with Mask_0, all in the past of every row: no masks
-        const int kfirst = j0 - XL, klast = j0 - XL + 16 * NCB - 1;
-        const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
-        if (!FIRST && cur) {
-            // column block 4 of tile t-1 is column block 0 of tile t: 16-byte
-            // chunks 8, 9 -> 0, 1 (which keeps the row swizzle), each wave for the
-            // rows whose block 4 it writes next (own rows; halo rows: the waves of
-            // halo column block 4), so its own program order keeps the read first
-            if (lane < 32) {
-                f16_t *rp = xo + (HALO + 16 * rw + (lane >> 1)) * XP;
-                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
-                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
-            } else if (CQ > 1 && (wave & 3) == 3) {
-                f16_t *rp = xbuf + (wave >> 2) * EXT_R * XP + ((lane - 32) >> 1) * XP;
-                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
-                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
-            }
-        }
-        if (cur) {
-            if constexpr (!FIRST) {
-                if (inner)
-                    logits(std::false_type{}, std::true_type{});
-                else
-                    logits(std::true_type{}, std::true_type{});
-            } else {
-                if (inner)
-                    logits(std::false_type{}, std::false_type{});
-                else
-                    logits(std::true_type{}, std::false_type{});
-            }
-        }
         if constexpr (!FIRST) {
-            // P.V of tile t - 1: bring the accumulators into the frame of its maxima first
+            // P.V of tile t - 1 (ahead of the logit products of t in program
+            // order; the two touch disjoint buffers): bring the accumulators
+            // into the frame of its maxima first
             const int tp = t - 1;
 #pragma unroll
             for (int s = 0; s < CH; ++s) {
@@ -907,6 +877,38 @@ sweep:
                                 U[s][a][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(avl[s], bv, U[s][a][nb], 0, 0, 0);
                         }
                     }
+            }
+        }
+        // key tiles whose logit blocks (halo rows included) are all inside
+        // [0, T) and, with Mask_0, all in the past of every row: no masks
+        const int kfirst = j0 - XL, klast = j0 - XL + 16 * NCB - 1;
+        const bool inner = kfirst >= 0 && i0 >= HALO && i0 + BM <= T && (EXACT ? klast < T : klast <= i0 - HALO);
+        if (!FIRST && cur) {
+            // column block 4 of tile t-1 is column block 0 of tile t: 16-byte
+            // chunks 8, 9 -> 0, 1 (which keeps the row swizzle), each wave for the
+            // rows whose block 4 it writes next (own rows; halo rows: the waves of
+            // halo column block 4), so its own program order keeps the read first
+            if (lane < 32) {
+                f16_t *rp = xo + (HALO + 16 * rw + (lane >> 1)) * XP;
+                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
+                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
+            } else if (CQ > 1 && (wave & 3) == 3) {
+                f16_t *rp = xbuf + (wave >> 2) * EXT_R * XP + ((lane - 32) >> 1) * XP;
+                *reinterpret_cast<u32x4 *>(rp + 8 * (lane & 1)) =
+                    *reinterpret_cast<const u32x4 *>(rp + 8 * (8 + (lane & 1)));
+            }
+        }
+        if (cur) {
+            if constexpr (!FIRST) {
+                if (inner)
+                    logits(std::false_type{}, std::true_type{});
+                else
+                    logits(std::true_type{}, std::true_type{});
+            } else {
+                if (inner)
+                    logits(std::false_type{}, std::false_type{});
+                else
+                    logits(std::true_type{}, std::false_type{});
             }
         }
         barrier_lds();  // B: logit tiles of t published; K, V and probability buffers free

@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(NT, 1) mta_fwd_rep(RParams p)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rw = wave & 3, hs = wave >> 2;  // row block; head (logits, stencils) = d half (P.V)
+    const int rw = wave & 3, hs = wave >> 2;  // row block; head (logits, stencils, P.V)
     const int l16 = lane & 15, g4 = lane >> 4;
     const int L = blockIdx.x;
     const int unit = L % p.units;

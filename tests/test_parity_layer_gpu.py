@@ -78,6 +78,10 @@ def _cases():
         c.append(I.small(f"repeat_bf16_6x11_hot{int(sc)}", B=1, H=4, T=256, d=128, c_q=6, c_k=11, c_h=2,
                          form="repeat", c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.02,
                          head_std=0.02, layer=4, needles=6, needle_scale=sc, needle_on_key=True, seed=922))
+    # dense head mixes (weights N(0, 1) around I; the folded 3D kernel's output
+    # map can cancel, which the bf16 rounding of the P.V operand must survive)
+    c.append(I.small("repeat_bf16_6x11_dense_mix", B=1, H=4, T=200, d=128, c_q=6, c_k=11, c_h=2, form="repeat",
+                     c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=1.0, seed=981))
     c.append(I.small("repeat_exact_f32", B=2, H=2, T=77, d=32, c_q=3, c_k=6, c_h=2, form="repeat", c_q2=2,
                      c_k2=5, kq_place=E, theta_std=0.2, head_std=0.2, gn_random=True, seed=931))
     c.append(I.small("repeat_f32_T3", B=1, H=2, T=3, d=32, c_q=3, c_k=5, c_h=2, form="repeat", c_q2=4, c_k2=3,

@@ -122,6 +122,8 @@ def test_layer_validation(lib, kw, code):
     ({}, "mta_fwd_layer"),                                                  # the repeated form, 6x11 then 3x5
     (dict(c_q2=6, c_k2=11), "mta_fwd_rep (two passes"),                     # 6x11 before and after: head-split
     (dict(c_q=4, c_k=9, c_q2=4, c_k2=9), "mta_fwd_rep (two passes"),
+    (dict(c_q=1, c_k=1, c_q2=1, c_k2=1), "mta_fwd_rep (two passes"),
+    (dict(c_q=6, c_k=11, c_q2=4, c_k2=9), "mta_fwd_layer"),                 # unequal sizes: general kernel
     (dict(c_q2=6, c_k2=11, head_post=None, head_post2=None), "mta_fwd_rep (two passes"),
     (dict(c_q2=6, c_k2=11, exact=1), "mta_fwd_layer"),                      # Eq. 4's indicator: general kernel
     (dict(c_q2=6, c_k2=11, dtype=0), "mta_fwd_layer"),                      # float32

@@ -63,6 +63,8 @@ def _cases():
         c.append(I.small(f"repeat_bf16_6x11_T{T}_B{B}_H{H}", B=B, H=H, T=T, d=128, c_q=6, c_k=11, c_h=2,
                          form="repeat", c_q2=6, c_k2=11, dtype="bf16", qkv_std=0.7071, theta_std=0.05,
                          head_std=0.05, seed=960 + T + B))
+    c.append(I.small("repeat_bf16_1x1_1x1", B=2, H=4, T=150, d=128, c_q=1, c_k=1, c_h=2, form="repeat",
+                     c_q2=1, c_k2=1, dtype="bf16", qkv_std=0.7071, theta_std=0.3, head_std=0.2, seed=969))
     c.append(I.small("repeat_bf16_4x9_4x9_ch2", B=2, H=4, T=150, d=128, c_q=4, c_k=9, c_h=2, form="repeat",
                      c_q2=4, c_k2=9, dtype="bf16", qkv_std=0.7071, theta_std=0.1, head_std=0.1, seed=970))
     c.append(I.small("repeat_bf16_6x11_gated", B=1, H=4, T=190, d=128, c_q=6, c_k=11, c_h=2, form="repeat",

@@ -75,6 +75,11 @@ def test_kernel_selection_single_head_groups(lib, kq, form):
     odd = I.with_(cfg, H=3)
     got = binding.kernel_name(odd)
     assert got is not None and got.startswith("mta_fwd_kernel"), got
+    # the 1x1 head mix before the softmax scales the logits, which the head-pair
+    # form does not do: the general kernel
+    pre = I.with_(cfg, head_place=I.PRE)
+    got = binding.kernel_name(pre)
+    assert got is not None and got.startswith("mta_fwd_kernel"), got
 
 
 def test_kernel_name_of_invalid_config(lib):

@@ -68,6 +68,17 @@ def _small_cases():
                          kq_place=Q, dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=255 + cq + T))
     c.append(I.small("bf16_6x11_ch1_post_H3", B=1, H=3, T=150, d=128, c_q=6, c_k=11, c_h=1, kq_place=Q,
                      dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=259))
+    # one head per group with the 1x1 head mix before the softmax (it scales the
+    # logits): the general kernel, every key-query placement, even and odd H
+    for kq in (P, I.PRE_EXACT, Q):
+        c.append(I.small(f"bf16_6x11_ch1_hpre_kq{kq}", B=2, H=2, T=128, d=128, c_q=6, c_k=11, c_h=1, kq_place=kq,
+                         head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.3, gn_random=True,
+                         seed=270 + kq))
+    c.append(I.small("bf16_4x9_ch1_hpre_gated", B=3, H=4, T=65, d=128, c_q=4, c_k=9, c_h=1, kq_place=P,
+                     head_place=P, dtype="bf16", qkv_std=0.7071, theta_std=0.1, head_std=0.3, gated=True,
+                     gn_random=True, seed=274))
+    c.append(I.small("f32_6x11_ch1_hpre_H3", B=1, H=3, T=100, d=64, c_q=6, c_k=11, c_h=1, kq_place=Q,
+                     head_place=P, theta_std=0.05, head_std=0.3, seed=275))
     # runtime-sized stencils: odd/even c_k, head mix before the softmax, d in {32,64,128}
     for (d, dt) in ((32, "bf16"), (64, "bf16"), (128, "f32"), (128, "bf16")):
         for kq in (P, Q):

@@ -145,9 +145,11 @@ static int make_plan(const mta_config *cfg, Plan &pl)
                 else pl.name = "mta_fwd_v4 (one pass, head-split waves, pre-softmax head mix as a 3D convolution, fp16 matrix-core stencil)";
             }
         }
-        if (!fn && ch == 1 && cfg->heads % 2 == 0) {
+        if (!fn && ch == 1 && !hpre && cfg->heads % 2 == 0) {
             // single-head groups, two per workgroup: the head-split kernel with
-            // the 1x1 mix of each head (the grid counts head pairs)
+            // the 1x1 mix of each head after the softmax (the grid counts head
+            // pairs); before the softmax the 1x1 mix scales the logits, which
+            // that kernel does not do, so such groups take the general kernel
             fn = mta::find_launch_v4_pairs(d, cq, ck, post, exact);
             if (fn) {
                 p.ncb = 5;

@@ -288,3 +288,15 @@ def test_python_binding_refuses_cpu_tensors(lib):
     inp = I.generate(c)
     with pytest.raises(ValueError):
         binding.forward_cfg(c, inp)
+
+
+@pytest.mark.parametrize("kq,ch,expect", [
+    (I.PRE, 2, "mta_fwd_v4 (one pass"), (I.PRE_EXACT, 2, "mta_fwd_v4 (one pass"),
+    (I.POST, 2, "mta_fwd_v4 (two passes"), (I.POST, 1, "mta_fwd_v4 (two passes, head-split waves, head pairs"),
+    (I.PRE, 4, "mta_fwd_v4 (four-head groups"), (I.POST, 16, "mta_fwd_v4 (groups of 8 or 16 heads")])
+def test_kernel_selection_8x13(lib, kq, ch, expect):
+    """The 8x13 kernel of the pages' kernel-size ablation runs the head-split
+    kernel in every family that the workload sizes run."""
+    cfg = I.small("k8x13", B=1, H=16, T=256, d=128, c_q=8, c_k=13, c_h=ch, kq_place=kq, dtype="bf16")
+    got = binding.kernel_name(cfg)
+    assert got is not None and got.startswith(expect), got

@@ -46,7 +46,7 @@ def _small_cases():
     for ch in (1, 2, 4):
         c.append(I.small(f"f32_d64_2x9_ch{ch}", B=1, H=4, T=130, d=64, c_q=2, c_k=9, c_h=ch, seed=110 + ch))
     # bf16 d128, the workload kernel sizes, ragged T, both kq placements
-    for (cq, ck) in ((6, 11), (4, 9), (8, 15), (1, 1)):
+    for (cq, ck) in ((6, 11), (4, 9), (8, 15), (8, 13), (1, 1)):
         for kq in (P, Q):
             for ch in (2, 4):
                 c.append(I.small(f"bf16_{cq}x{ck}_kq{kq}_ch{ch}", B=1, H=4, T=197, d=128, c_q=cq, c_k=ck,
@@ -163,6 +163,11 @@ def _small_cases():
         c.append(I.small(f"exact_bf16_{cq}x{ck}", B=1, H=4, T=197, d=128, c_q=cq, c_k=ck, c_h=2,
                          kq_place=E, dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05,
                          seed=810 + cq))
+    # the pages' 8x13 ablation size (Table 5), with the exact indicator and single-head groups
+    c.append(I.small("exact_bf16_8x13", B=1, H=4, T=197, d=128, c_q=8, c_k=13, c_h=2, kq_place=E,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, head_std=0.05, seed=830))
+    c.append(I.small("bf16_8x13_ch1_post_T130", B=1, H=4, T=130, d=128, c_q=8, c_k=13, c_h=1, kq_place=Q,
+                     dtype="bf16", qkv_std=0.7071, theta_std=0.05, seed=831))
     c.append(I.small("exact_bf16_5x4_d64", B=2, H=4, T=77, d=64, c_q=5, c_k=4, c_h=2, kq_place=E,
                      dtype="bf16", seed=820))
     c.append(I.small("exact_f32_T3", B=1, H=2, T=3, d=32, c_q=4, c_k=5, c_h=2, kq_place=E, seed=821))

@@ -1,5 +1,5 @@
 // Head-split kernels (bf16, d = 128, head mix after the softmax) for
-// the kernel sizes of the 2K/4K/8K workloads and 1x1: one pass with the
+// the kernel sizes of the 2K/4K/8K workloads, 8x13 and 1x1: one pass with the
 // key-query convolution before the softmax (either form), two passes with it
 // after the softmax.
 #include "mta_fwd_v4.h"
@@ -18,6 +18,7 @@ LaunchFn find_launch_v4(int d, int ch, int cq, int ck, int post, int exact, int 
     MTA_V4_SIZE(1, 1)
     MTA_V4_SIZE(4, 9)
     MTA_V4_SIZE(6, 11)
+    MTA_V4_SIZE(8, 13)
     MTA_V4_SIZE(8, 15)
     return nullptr;
 }
@@ -37,6 +38,7 @@ LaunchFn find_launch_v4_pairs(int d, int cq, int ck, int post, int exact)
     MTA_V4N_SIZE(1, 1)
     MTA_V4N_SIZE(4, 9)
     MTA_V4N_SIZE(6, 11)
+    MTA_V4N_SIZE(8, 13)
     MTA_V4N_SIZE(8, 15)
     return nullptr;
 }
@@ -64,6 +66,7 @@ LaunchFn find_launch_v4_3d(int d, int ch, int cq, int ck)
     MTA_V4Q_SIZE(1, 1, PPL_)       \
     MTA_V4Q_SIZE(4, 9, PPL_)       \
     MTA_V4Q_SIZE(6, 11, PPL_)      \
+    MTA_V4Q_SIZE(8, 13, PPL_)      \
     MTA_V4Q_SIZE(8, 15, PPL_)
 
 LaunchFn find_launch_v4_quad(int d, int cq, int ck, int post, int exact, int f16pv)

@@ -15,6 +15,7 @@ PrepFn find_launch_v4_prep(int d, int ch, int cq, int ck, int exact)
     MTA_V4P_SIZE(1, 1)
     MTA_V4P_SIZE(4, 9)
     MTA_V4P_SIZE(6, 11)
+    MTA_V4P_SIZE(8, 13)
     MTA_V4P_SIZE(8, 15)
     return nullptr;
 }
